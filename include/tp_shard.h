@@ -1,0 +1,203 @@
+/*
+ * tp_shard.h - one tensor-parallel rank's share of a Llama-style decoder
+ * layer's linear path, computed on one AMD Instinct MI355X (gfx950).
+ *
+ * Every shard of a t-way split lives in the one GPU's HBM. Column-parallel
+ * linears (qkv_proj, gate_up_proj, the vocab-parallel LM head) produce the
+ * rank's slice of the output; row-parallel linears (o_proj, down_proj)
+ * produce partial sums; tp_reduce_partials is the arithmetic of the
+ * all-reduce and tp_concat_logits that of the logits all-gather, both over
+ * buffers resident in this GPU's memory.
+ *
+ * Pages cited (title, section):
+ *   [P1] "第 9 章 多进程与张量并行", sections 3.1 (communication) and 3.2 (splitting)
+ *   [P2] "Tensor Parallelism 执行路径", weight-split diagram and forward flow
+ *   [P3] "张量、流水线与数据并行", sections "线性层怎么切" and
+ *        "每 token 的通信量（估算）"
+ *
+ * Conventions shared by every call
+ *   Layout     Row-major, contiguous. Weights are stored [out, in], so a linear
+ *              computes Y = X W^T and K (the input dimension) is contiguous.
+ *              Full fused QKV rows are [Q (n_h d); K (n_kv d); V (n_kv d)];
+ *              full fused gate_up rows are [gate (I); up (I)].
+ *   Types      Activations and weights are bfloat16; every sum is accumulated
+ *              in fp32; every bf16 result is rounded once, to nearest even.
+ *              Partials and logits may be fp32 instead (tp_dtype). Token ids
+ *              are int32.
+ *   Memory     Device pointers unless stated. The caller allocates and owns
+ *              every buffer; inputs are never written. Base pointers must be
+ *              16-byte aligned. Outputs must not overlap inputs, except that
+ *              tp_reduce_partials accepts out == partials[0] (in place).
+ *   Streams    `stream` is a hipStream_t (NULL = the null stream). Every device
+ *              call is asynchronous on it and does not synchronise.
+ *   Workspace  The linears may split their K dimension across workgroups.
+ *              They then use a per-(device, stream) fp32 workspace that the
+ *              library allocates (hipMalloc) on the first such call on that
+ *              stream and keeps until the process ends; make one call per
+ *              stream before capturing it into a graph. Calls on different
+ *              streams never share a workspace.
+ *   Errors     Arguments are validated on the host before any HIP call; on
+ *              failure a negative tp_status is returned and nothing runs.
+ *              M == 0 (or numel == 0) is a valid no-op. A launch failure
+ *              reported by the runtime is returned as TP_ERR_HIP. No C++
+ *              exception crosses this interface.
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TP_OK = 0,
+    TP_ERR_NULL = -1,          /* a required pointer is NULL                        */
+    TP_ERR_SHAPE = -2,         /* negative or inconsistent sizes                    */
+    TP_ERR_DIVISIBILITY = -3,  /* a split rule of [P1 3.2] does not hold            */
+    TP_ERR_ALIGNMENT = -4,     /* pointer not 16-byte aligned or a size not % 8     */
+    TP_ERR_DTYPE = -5,         /* unknown tp_dtype or weight kind                   */
+    TP_ERR_RANGE = -6,         /* t outside [1, 64], rank outside [0, t)            */
+    TP_ERR_HIP = -7,           /* the HIP runtime reported an error                 */
+    TP_ERR_ALLOC = -8          /* the workspace could not be allocated              */
+} tp_status;
+
+typedef enum { TP_BF16 = 0, TP_F32 = 1 } tp_dtype;
+
+typedef enum {
+    TP_W_QKV = 0,      /* fused qkv_proj   full [(n_h + 2 n_kv) d, H]  column split by heads */
+    TP_W_O = 1,        /* o_proj           full [H, n_h d]             row split             */
+    TP_W_GATE_UP = 2,  /* fused gate_up    full [2 I, H]               column split          */
+    TP_W_DOWN = 3,     /* down_proj        full [H, I]                 row split             */
+    TP_W_EMBED = 4,    /* embedding table  full [V, H]                 vocab split, padded   */
+    TP_W_LM_HEAD = 5   /* LM head          full [V, H]                 vocab split, padded   */
+} tp_weight_kind;
+
+typedef struct {
+    int32_t hidden;        /* H   */
+    int32_t num_q_heads;   /* n_h */
+    int32_t num_kv_heads;  /* n_kv */
+    int32_t head_dim;      /* d   */
+    int32_t intermediate;  /* I   */
+    int32_t vocab;         /* V (unpadded) */
+} tp_model_cfg;
+
+#define TP_MAX_SHARDS 64
+
+/* ------------------------------------------------------------------------
+ * Host-only queries. They make no HIP call and work without a GPU.
+ * ------------------------------------------------------------------------ */
+
+/* Static message for a tp_status value. Never NULL. */
+const char* tp_status_string(int status);
+
+/* Shape [rows, cols] of the full weight of `kind`. */
+int tp_full_shape(const tp_model_cfg* cfg, int kind, int64_t* rows, int64_t* cols);
+
+/* Shape [rows, cols] of one rank's shard of `kind` for a t-way split, after
+ * checking the split rules of [P1 3.2]: n_h % t == 0; n_kv % t == 0 when
+ * n_kv >= t, t % n_kv == 0 when n_kv < t (KV heads replicated); I % t == 0.
+ * QKV: (n_h/t + 2 kv) d x H with kv = max(1, n_kv/t); O: H x n_h d/t;
+ * GATE_UP: 2I/t x H; DOWN: H x I/t; EMBED / LM_HEAD: ceil(V/t) x H. */
+int tp_shard_shape(const tp_model_cfg* cfg, int t, int kind, int64_t* rows, int64_t* cols);
+
+/* Rows per vocab shard: the vocab padded to a multiple of t and split evenly,
+ * [P1 3.2] (Vocab Parallel). Returns ceil(vocab / t), or a negative tp_status. */
+int64_t tp_vocab_shard_rows(int64_t vocab, int t);
+
+/* KV heads held by `rank`: `count` consecutive heads starting at `first`.
+ * count = n_kv / t when n_kv >= t; otherwise count = 1 and the head is
+ * rank / (t / n_kv), shared by t / n_kv consecutive ranks, so each rank's
+ * query heads keep the KV head of their GQA group ([P1 3.2]; [P3 线性层怎么切],
+ * num_kv_head_replicas). */
+int tp_kv_heads_of_rank(const tp_model_cfg* cfg, int t, int rank, int* first, int* count);
+
+/* ------------------------------------------------------------------------
+ * Device calls
+ * ------------------------------------------------------------------------ */
+
+/* S1. Copy rank `rank`'s shard of a full bf16 weight into `shard_w`
+ * (shape from tp_shard_shape). [P1 3.2]; [P3 线性层怎么切].
+ *   QKV      rows of the rank's n_h/t Q heads, then its KV heads' K rows, then
+ *            the same heads' V rows.
+ *   GATE_UP  gate rows [r I/t, (r+1) I/t), then up rows I + the same range.
+ *   O, DOWN  input columns [r K/t, (r+1) K/t) of every row, packed contiguous.
+ *   EMBED, LM_HEAD  rows [r Vs, (r+1) Vs) with Vs = ceil(V/t); rows past V are
+ *            written as zeros.
+ * full_w: [full rows, full cols] bf16; shard_w: [shard rows, shard cols] bf16.
+ * hidden, head_dim and the shard's column count must be multiples of 8. */
+int tp_shard_weights(const tp_model_cfg* cfg, int t, int rank, int kind,
+                     const void* full_w, void* shard_w, void* stream);
+
+/* S2, S3. Column-parallel linear: y[M, N] = x[M, K] w_shard[N, K]^T (+ bias[N]),
+ * bf16 in, fp32 accumulate, bf16 out. The input is replicated, the output is
+ * the rank's slice and is not gathered ([P3 线性层怎么切]: gather_output off;
+ * [P1 3.2] Column Parallel). bias_or_null: bf16 [N] or NULL. K % 8 == 0. */
+int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_shard, int64_t N,
+                     const void* bias_or_null, void* y, void* stream);
+
+/* S4. SwiGLU on a rank's fused gate_up output: out[m, j] =
+ * silu(gu[m, j]) * gu[m, i_shard + j], silu(g) = g / (1 + e^-g), computed in
+ * fp32 and rounded once. gu: [M, 2 i_shard] bf16; out: [M, i_shard] bf16.
+ * [P3 线性层怎么切] (SiLU x up between gate_up and down). i_shard % 8 == 0. */
+int tp_swiglu(const void* gu, int64_t M, int64_t i_shard, void* out, void* stream);
+
+/* S5, S7. Row-parallel linear, local part: partial[M, N] =
+ * x_shard[M, K_shard] w_shard[N, K_shard]^T, fp32 accumulate, stored as
+ * `partial_dtype` (TP_BF16 or TP_F32). The partial still needs the sum over
+ * ranks ([P1 3.2] Row Parallel; [P2] output_partial). K_shard % 8 == 0. */
+int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard,
+                          int64_t N, void* partial, int partial_dtype, void* stream);
+
+/* S6, S8, S9b. Sum of t partial buffers: out = sum_{i=0}^{t-1} partials[i],
+ * accumulated in fp32 in the fixed order i = 0, 1, ..., t-1 starting from
+ * partials[0], and rounded once to `out_dtype` ([P1 3.1] All-Reduce:
+ * Y = Y_0 + ... + Y_{p-1}). `partials` is a HOST array of t device pointers,
+ * each to `numel` elements of `in_dtype`. out may equal partials[0]. */
+int tp_reduce_partials(const void* const* partials, int t, int64_t numel, int in_dtype,
+                       void* out, int out_dtype, void* stream);
+
+/* S9a. Vocab-parallel embedding, one shard's contribution: for each token m,
+ * out[m, :] = e_shard[ids[m] - rank Vs, :] when rank Vs <= ids[m] <
+ * min((rank+1) Vs, vocab), else a row of -0.0 (Vs = ceil(vocab / t)). Ids
+ * outside [0, vocab) are masked in every shard, so padded rows are never
+ * read. Summing the t contributions with tp_reduce_partials reproduces the
+ * direct lookup bit for bit, since -0.0 is an exact additive identity
+ * ([P1 3.2] Vocab Parallel; [P3 线性层怎么切], embedding then all-reduce).
+ * ids: [M] int32; e_shard: [Vs, H] bf16; out_partial: [M, H] bf16; H % 8 == 0. */
+int tp_vocab_embed(const int32_t* ids, int64_t M, const void* e_shard, int64_t vocab, int t,
+                   int rank, int64_t H, void* out_partial, void* stream);
+
+/* S10. LM-head shard: logits_shard[M, v_shard] = h[M, K] w_lm_shard[v_shard, K]^T,
+ * fp32 accumulate, stored as `out_dtype`; padded rows of the shard (zeros)
+ * give zero logits. Only sampled positions are passed in ([P3 线性层怎么切]:
+ * each card computes V/t logits for the positions to be sampled). */
+int tp_lm_head_shard(const void* h, int64_t M, int64_t K, const void* w_lm_shard, int64_t v_shard,
+                     void* logits_shard, int out_dtype, void* stream);
+
+/* S11. Concatenate t shard logits in vocab order and drop the padding:
+ * out[m, r v_shard + j] = shard_logits[r][m, j] for r v_shard + j < vocab
+ * ([P1 3.1] All-Gather, Y = cat(Y_0, ..., Y_{p-1})). `shard_logits` is a HOST
+ * array of t device pointers to [M, v_shard] buffers of `dtype`; out is
+ * [M, vocab] of the same dtype. v_shard must equal ceil(vocab / t). */
+int tp_concat_logits(const void* const* shard_logits, int t, int64_t M, int64_t v_shard,
+                     int64_t vocab, int dtype, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Tuning
+ * ------------------------------------------------------------------------ */
+
+/* Override the shape of the decode-sized (M <= 64) linear kernel for every
+ * later call in this process: `ksteps` 32-wide k steps per wave, `nwn` waves
+ * along the output rows (16 rows each) and `nwk` waves along K per
+ * workgroup; K is split across as many workgroups as it takes to cover it.
+ * (0, 0, 0) restores the automatic choice. Returns TP_ERR_SHAPE if no such
+ * kernel variant is built. Results are the same up to fp32 summation order. */
+int tp_tune_skinny(int ksteps, int nwn, int nwk);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_SHARD_H */

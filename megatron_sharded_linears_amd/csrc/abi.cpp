@@ -1,0 +1,383 @@
+// C ABI of libtpshard: host-side validation, shape queries, workspace
+// management and dispatch to the gfx950 kernels. Every entry point checks its
+// arguments before making any HIP call, so argument errors are reported (and
+// testable) without a GPU. No C++ exception escapes: each entry point catches
+// everything and maps it to a tp_status.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "kernels.h"
+#include "tp_shard.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // sizes must fit the kernels' int ranges
+constexpr int64_t kSkinnyMaxM = 64;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int d) { return d == TP_BF16 || d == TP_F32; }
+
+int check_cfg(const tp_model_cfg* c, int t) {
+    if (c == nullptr) return TP_ERR_NULL;
+    if (t < 1 || t > TP_MAX_SHARDS) return TP_ERR_RANGE;
+    if (c->hidden <= 0 || c->num_q_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 ||
+        c->intermediate <= 0 || c->vocab <= 0)
+        return TP_ERR_SHAPE;
+    if (c->num_kv_heads > c->num_q_heads || c->num_q_heads % c->num_kv_heads != 0) return TP_ERR_SHAPE;
+    if (c->num_q_heads % t != 0) return TP_ERR_DIVISIBILITY;
+    if (c->num_kv_heads >= t) {
+        if (c->num_kv_heads % t != 0) return TP_ERR_DIVISIBILITY;
+    } else if (t % c->num_kv_heads != 0) {
+        return TP_ERR_DIVISIBILITY;
+    }
+    if (c->intermediate % t != 0) return TP_ERR_DIVISIBILITY;
+    return TP_OK;
+}
+
+void kv_of_rank(const tp_model_cfg* c, int t, int rank, int* first, int* count) {
+    if (c->num_kv_heads >= t) {
+        *count = c->num_kv_heads / t;
+        *first = rank * *count;
+    } else {
+        *count = 1;
+        *first = rank / (t / c->num_kv_heads);
+    }
+}
+
+// --------------------------------------------------------------- workspace
+
+constexpr int64_t kWsFloats = tpk::kSkinnyWsFloats;
+constexpr int64_t kWsCounters = tpk::kSkinnyWsCounters;
+
+struct StreamWs {
+    float* partials = nullptr;
+    unsigned* counters = nullptr;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, StreamWs> g_ws;
+
+int get_workspace(hipStream_t s, tpk::Workspace* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TP_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    StreamWs& w = g_ws[std::make_pair(dev, s)];
+    if (w.partials == nullptr) {
+        void* p = nullptr;
+        void* c = nullptr;
+        if (hipMalloc(&p, kWsFloats * sizeof(float)) != hipSuccess) return TP_ERR_ALLOC;
+        if (hipMalloc(&c, kWsCounters * sizeof(unsigned)) != hipSuccess) {
+            (void)hipFree(p);
+            return TP_ERR_ALLOC;
+        }
+        if (hipMemset(c, 0, kWsCounters * sizeof(unsigned)) != hipSuccess) {
+            (void)hipFree(p);
+            (void)hipFree(c);
+            return TP_ERR_HIP;
+        }
+        w.partials = static_cast<float*>(p);
+        w.counters = static_cast<unsigned*>(c);
+    }
+    out->partials = w.partials;
+    out->partial_floats = kWsFloats;
+    out->counters = w.counters;
+    out->num_counters = kWsCounters;
+    return TP_OK;
+}
+
+// A process-wide override of the decode kernel's shape, for tuning and for
+// tests that exercise every variant. Zero means automatic.
+int g_force_ksteps = 0, g_force_nwn = 0, g_force_nwk = 0;
+
+int run_linear(const void* x, int64_t M, int64_t K, const void* w, int64_t N, const void* bias,
+               void* y, int out_dtype, void* stream) {
+    if (x == nullptr || w == nullptr || y == nullptr) return TP_ERR_NULL;
+    if (M < 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return TP_ERR_SHAPE;
+    if (!dtype_ok(out_dtype)) return TP_ERR_DTYPE;
+    if (K % 8 != 0) return TP_ERR_ALIGNMENT;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return TP_ERR_ALIGNMENT;
+    if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TP_ERR_ALIGNMENT;
+    if (M == 0) return TP_OK;
+
+    tpk::GemmArgs a{x, w, bias, y, M, N, K, out_dtype};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (M <= kSkinnyMaxM) {
+        tpk::SkinnyPlan p = tpk::plan_skinny(M, N, K);
+        if (g_force_ksteps > 0) {
+            p.ksteps = g_force_ksteps;
+            p.nwn = g_force_nwn;
+            p.nwk = g_force_nwk;
+            p.ntiles = (N + 16LL * p.nwn - 1) / (16LL * p.nwn);
+            const int64_t gk = 32LL * p.ksteps * p.nwk;
+            p.splits = (int)((K + gk - 1) / gk);
+        }
+        tpk::Workspace ws{nullptr, 0, nullptr, 0};
+        if (p.splits > 1) {
+            const int st = get_workspace(s, &ws);
+            if (st != TP_OK) return st;
+            if (tpk::skinny_workspace_floats(p, M, N) > ws.partial_floats || p.ntiles > ws.num_counters)
+                return TP_ERR_SHAPE;
+        }
+        e = tpk::launch_skinny(a, p, ws, s);
+    } else {
+        e = tpk::launch_tiled(a, s);
+    }
+    return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_status_string(int status) {
+    switch (status) {
+    case TP_OK: return "ok";
+    case TP_ERR_NULL: return "a required pointer is NULL";
+    case TP_ERR_SHAPE: return "negative, inconsistent or too large sizes";
+    case TP_ERR_DIVISIBILITY: return "a tensor-parallel split rule does not hold (n_h % t, n_kv vs t, I % t)";
+    case TP_ERR_ALIGNMENT: return "pointer not 16-byte aligned or a size not a multiple of 8";
+    case TP_ERR_DTYPE: return "unknown dtype or weight kind";
+    case TP_ERR_RANGE: return "t outside [1, 64] or rank outside [0, t)";
+    case TP_ERR_HIP: return "the HIP runtime reported an error";
+    case TP_ERR_ALLOC: return "workspace allocation failed";
+    default: return "unknown status";
+    }
+}
+
+int tp_full_shape(const tp_model_cfg* cfg, int kind, int64_t* rows, int64_t* cols) {
+    if (cfg == nullptr || rows == nullptr || cols == nullptr) return TP_ERR_NULL;
+    const int st = check_cfg(cfg, 1);
+    if (st != TP_OK) return st;
+    const int64_t H = cfg->hidden, d = cfg->head_dim;
+    switch (kind) {
+    case TP_W_QKV: *rows = ((int64_t)cfg->num_q_heads + 2LL * cfg->num_kv_heads) * d; *cols = H; break;
+    case TP_W_O: *rows = H; *cols = (int64_t)cfg->num_q_heads * d; break;
+    case TP_W_GATE_UP: *rows = 2LL * cfg->intermediate; *cols = H; break;
+    case TP_W_DOWN: *rows = H; *cols = cfg->intermediate; break;
+    case TP_W_EMBED:
+    case TP_W_LM_HEAD: *rows = cfg->vocab; *cols = H; break;
+    default: return TP_ERR_DTYPE;
+    }
+    return TP_OK;
+}
+
+int64_t tp_vocab_shard_rows(int64_t vocab, int t) {
+    if (t < 1 || t > TP_MAX_SHARDS) return TP_ERR_RANGE;
+    if (vocab <= 0) return TP_ERR_SHAPE;
+    return (vocab + t - 1) / t;
+}
+
+int tp_shard_shape(const tp_model_cfg* cfg, int t, int kind, int64_t* rows, int64_t* cols) {
+    if (cfg == nullptr || rows == nullptr || cols == nullptr) return TP_ERR_NULL;
+    const int st = check_cfg(cfg, t);
+    if (st != TP_OK) return st;
+    const int64_t H = cfg->hidden, d = cfg->head_dim;
+    int kv_first = 0, kv_count = 0;
+    kv_of_rank(cfg, t, 0, &kv_first, &kv_count);
+    switch (kind) {
+    case TP_W_QKV: *rows = ((int64_t)cfg->num_q_heads / t + 2LL * kv_count) * d; *cols = H; break;
+    case TP_W_O: *rows = H; *cols = (int64_t)cfg->num_q_heads / t * d; break;
+    case TP_W_GATE_UP: *rows = 2LL * cfg->intermediate / t; *cols = H; break;
+    case TP_W_DOWN: *rows = H; *cols = cfg->intermediate / t; break;
+    case TP_W_EMBED:
+    case TP_W_LM_HEAD: *rows = tp_vocab_shard_rows(cfg->vocab, t); *cols = H; break;
+    default: return TP_ERR_DTYPE;
+    }
+    return TP_OK;
+}
+
+int tp_kv_heads_of_rank(const tp_model_cfg* cfg, int t, int rank, int* first, int* count) {
+    if (cfg == nullptr || first == nullptr || count == nullptr) return TP_ERR_NULL;
+    const int st = check_cfg(cfg, t);
+    if (st != TP_OK) return st;
+    if (rank < 0 || rank >= t) return TP_ERR_RANGE;
+    kv_of_rank(cfg, t, rank, first, count);
+    return TP_OK;
+}
+
+int tp_shard_weights(const tp_model_cfg* cfg, int t, int rank, int kind, const void* full_w,
+                     void* shard_w, void* stream) {
+    try {
+        if (cfg == nullptr || full_w == nullptr || shard_w == nullptr) return TP_ERR_NULL;
+        int st = check_cfg(cfg, t);
+        if (st != TP_OK) return st;
+        if (rank < 0 || rank >= t) return TP_ERR_RANGE;
+        tpk::ShardMap m;
+        std::memset(&m, 0, sizeof(m));
+        m.kind = kind;
+        st = tp_full_shape(cfg, kind, &m.src_rows, &m.src_cols);
+        if (st != TP_OK) return st;
+        st = tp_shard_shape(cfg, t, kind, &m.dst_rows, &m.dst_cols);
+        if (st != TP_OK) return st;
+        if (m.src_cols % 8 != 0 || m.dst_cols % 8 != 0) return TP_ERR_ALIGNMENT;
+        if (!aligned16(full_w) || !aligned16(shard_w)) return TP_ERR_ALIGNMENT;
+        if (m.src_rows * m.src_cols >= ((int64_t)1 << 40)) return TP_ERR_SHAPE;
+        switch (kind) {
+        case TP_W_QKV: {
+            m.head_dim = cfg->head_dim;
+            m.num_q_heads = cfg->num_q_heads;
+            m.num_kv_heads = cfg->num_kv_heads;
+            m.q_count = cfg->num_q_heads / t;
+            m.q_first = rank * m.q_count;
+            int f = 0, c = 0;
+            kv_of_rank(cfg, t, rank, &f, &c);
+            m.kv_first = f;
+            m.kv_count = c;
+            break;
+        }
+        case TP_W_GATE_UP:
+            m.inter = cfg->intermediate;
+            m.inter_shard = cfg->intermediate / t;
+            m.inter_first = (int64_t)rank * m.inter_shard;
+            break;
+        case TP_W_O:
+        case TP_W_DOWN:
+            m.src_col0 = (int64_t)rank * m.dst_cols;
+            break;
+        case TP_W_EMBED:
+        case TP_W_LM_HEAD:
+            m.vocab = cfg->vocab;
+            m.vocab_first = (int64_t)rank * m.dst_rows;
+            break;
+        default:
+            return TP_ERR_DTYPE;
+        }
+        const hipError_t e = tpk::launch_shard_copy(m, full_w, shard_w, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_shard, int64_t N,
+                     const void* bias_or_null, void* y, void* stream) {
+    try {
+        return run_linear(x, M, K, w_shard, N, bias_or_null, y, TP_BF16, stream);
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard,
+                          int64_t N, void* partial, int partial_dtype, void* stream) {
+    try {
+        return run_linear(x_shard, M, K_shard, w_shard, N, nullptr, partial, partial_dtype, stream);
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_lm_head_shard(const void* h, int64_t M, int64_t K, const void* w_lm_shard, int64_t v_shard,
+                     void* logits_shard, int out_dtype, void* stream) {
+    try {
+        return run_linear(h, M, K, w_lm_shard, v_shard, nullptr, logits_shard, out_dtype, stream);
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_swiglu(const void* gu, int64_t M, int64_t i_shard, void* out, void* stream) {
+    try {
+        if (gu == nullptr || out == nullptr) return TP_ERR_NULL;
+        if (M < 0 || i_shard <= 0 || M >= kMaxDim || i_shard >= kMaxDim) return TP_ERR_SHAPE;
+        if (i_shard % 8 != 0 || !aligned16(gu) || !aligned16(out)) return TP_ERR_ALIGNMENT;
+        if (M == 0) return TP_OK;
+        const hipError_t e = tpk::launch_swiglu(gu, M, i_shard, out, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_reduce_partials(const void* const* partials, int t, int64_t numel, int in_dtype, void* out,
+                       int out_dtype, void* stream) {
+    try {
+        if (partials == nullptr || out == nullptr) return TP_ERR_NULL;
+        if (t < 1 || t > TP_MAX_SHARDS) return TP_ERR_RANGE;
+        if (numel < 0) return TP_ERR_SHAPE;
+        if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return TP_ERR_DTYPE;
+        tpk::PartialPtrs ptrs;
+        std::memset(&ptrs, 0, sizeof(ptrs));
+        for (int i = 0; i < t; ++i) {
+            if (partials[i] == nullptr) return TP_ERR_NULL;
+            if (!aligned16(partials[i])) return TP_ERR_ALIGNMENT;
+            ptrs.p[i] = partials[i];
+        }
+        if (!aligned16(out)) return TP_ERR_ALIGNMENT;
+        if (numel == 0) return TP_OK;
+        const hipError_t e = tpk::launch_reduce(ptrs, t, numel, in_dtype, out, out_dtype,
+                                                static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_vocab_embed(const int32_t* ids, int64_t M, const void* e_shard, int64_t vocab, int t, int rank,
+                   int64_t H, void* out_partial, void* stream) {
+    try {
+        if (ids == nullptr || e_shard == nullptr || out_partial == nullptr) return TP_ERR_NULL;
+        if (t < 1 || t > TP_MAX_SHARDS || rank < 0 || rank >= t) return TP_ERR_RANGE;
+        if (M < 0 || vocab <= 0 || H <= 0 || M >= kMaxDim || vocab >= kMaxDim || H >= kMaxDim) return TP_ERR_SHAPE;
+        if (H % 8 != 0 || !aligned16(e_shard) || !aligned16(out_partial) ||
+            (reinterpret_cast<uintptr_t>(ids) & 3u))
+            return TP_ERR_ALIGNMENT;
+        if (M == 0) return TP_OK;
+        const int64_t vs = (vocab + t - 1) / t;
+        const int64_t lo = (int64_t)rank * vs;
+        const int64_t hi = lo + vs < vocab ? lo + vs : vocab;
+        const hipError_t e = tpk::launch_vocab_embed(ids, M, e_shard, lo, hi, H, out_partial,
+                                                     static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_concat_logits(const void* const* shard_logits, int t, int64_t M, int64_t v_shard, int64_t vocab,
+                     int dtype, void* out, void* stream) {
+    try {
+        if (shard_logits == nullptr || out == nullptr) return TP_ERR_NULL;
+        if (t < 1 || t > TP_MAX_SHARDS) return TP_ERR_RANGE;
+        if (!dtype_ok(dtype)) return TP_ERR_DTYPE;
+        if (M < 0 || vocab <= 0 || M >= kMaxDim || vocab >= kMaxDim) return TP_ERR_SHAPE;
+        if (v_shard != (vocab + t - 1) / t) return TP_ERR_SHAPE;
+        tpk::PartialPtrs ptrs;
+        std::memset(&ptrs, 0, sizeof(ptrs));
+        for (int i = 0; i < t; ++i) {
+            if (shard_logits[i] == nullptr) return TP_ERR_NULL;
+            if (!aligned16(shard_logits[i])) return TP_ERR_ALIGNMENT;
+            ptrs.p[i] = shard_logits[i];
+        }
+        if (!aligned16(out)) return TP_ERR_ALIGNMENT;
+        if (M == 0) return TP_OK;
+        const hipError_t e = tpk::launch_concat(ptrs, t, M, v_shard, vocab, dtype, out,
+                                                static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_tune_skinny(int ksteps, int nwn, int nwk) {
+    if (ksteps == 0 && nwn == 0 && nwk == 0) {
+        g_force_ksteps = g_force_nwn = g_force_nwk = 0;
+        return TP_OK;
+    }
+    for (int m = 1; m <= 4; m *= 2) {
+        tpk::SkinnyPlan p{m, ksteps, nwn, nwk, 1, 1};
+        if (!tpk::skinny_variant_exists(p)) return TP_ERR_SHAPE;
+    }
+    g_force_ksteps = ksteps;
+    g_force_nwn = nwn;
+    g_force_nwk = nwk;
+    return TP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Device-side helpers shared by the gfx950 kernels of libtpshard.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpk {
+
+// bf16 is handled as raw 16-bit patterns in memory.
+typedef uint16_t bf16_t;
+
+// MFMA operand / accumulator vector types (gfx950 builtins).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte loads with the non-temporal hint (data read exactly once: keep it
+// from displacing reusable lines in L2).
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+__device__ __forceinline__ float4 ld_nt16f(const void* p) {
+    return __builtin_bit_cast(float4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even. NaN stays NaN (quieted);
+// overflow past the largest finite bf16 rounds to infinity; subnormals round
+// on the same grid as normals (bf16 and fp32 share the exponent field).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x0040u) & 0xffffu;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Pack two fp32 values as bf16 into one 32-bit word (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Unpack the 8 bf16 values of a 16-byte vector to fp32.
+__device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+    f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+    f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float* f) {
+    uint4 v;
+    v.x = pack_bf16x2(f[0], f[1]);
+    v.y = pack_bf16x2(f[2], f[3]);
+    v.z = pack_bf16x2(f[4], f[5]);
+    v.w = pack_bf16x2(f[6], f[7]);
+    return v;
+}
+
+}  // namespace tpk

@@ -1,0 +1,83 @@
+// Internal launch interface between the C ABI (abi.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by the ABI layer and
+// returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tp_shard.h"
+
+namespace tpk {
+
+// Row map of a weight shard copy (tp_shard_weights): destination row i of the
+// shard reads source row src_row(i) starting at column src_col0, or is zero.
+struct ShardMap {
+    int kind;
+    int64_t dst_rows, dst_cols;    // shard shape
+    int64_t src_rows, src_cols;    // full shape
+    int64_t src_col0;              // first source column (row-split kinds)
+    // QKV
+    int32_t head_dim, q_first, q_count, kv_first, kv_count, num_q_heads, num_kv_heads;
+    // GATE_UP
+    int64_t inter, inter_shard, inter_first;
+    // EMBED / LM_HEAD
+    int64_t vocab_first, vocab;
+};
+
+hipError_t launch_shard_copy(const ShardMap& map, const void* full, void* shard, hipStream_t s);
+
+hipError_t launch_swiglu(const void* gu, int64_t M, int64_t i_shard, void* out, hipStream_t s);
+
+struct PartialPtrs { const void* p[TP_MAX_SHARDS]; };
+hipError_t launch_reduce(const PartialPtrs& ptrs, int t, int64_t numel, int in_dtype,
+                         void* out, int out_dtype, hipStream_t s);
+
+hipError_t launch_vocab_embed(const int32_t* ids, int64_t M, const void* table, int64_t lo,
+                              int64_t hi, int64_t H, void* out, hipStream_t s);
+
+hipError_t launch_concat(const PartialPtrs& ptrs, int t, int64_t M, int64_t v_shard,
+                         int64_t vocab, int dtype, void* out, hipStream_t s);
+
+// Linear Y[M, N] = X[M, K] W[N, K]^T (+ bias[N]); out_dtype TP_BF16 / TP_F32.
+struct GemmArgs {
+    const void* x;
+    const void* w;
+    const void* bias;   // bf16 [N] or nullptr
+    void* y;
+    int64_t M, N, K;
+    int out_dtype;
+};
+
+// Scratch for K split across workgroups: fp32 partial tiles and one arrival
+// counter per output tile. Counters must be zero before a launch; every
+// kernel that uses them leaves them zero again.
+struct Workspace {
+    float* partials;
+    int64_t partial_floats;
+    unsigned* counters;
+    int64_t num_counters;
+};
+
+// Plan of a decode-sized (M <= 64) linear; describes how K is split.
+struct SkinnyPlan {
+    int mt;          // token tiles of 16
+    int ksteps;      // 32-wide k steps per wave
+    int nwn;         // waves along N per workgroup (16 rows each)
+    int nwk;         // waves along K per workgroup
+    int splits;      // workgroups along K
+    int64_t ntiles;  // workgroups along N
+};
+
+// Workspace the library keeps per (device, stream) for split-K partials.
+constexpr int64_t kSkinnyWsFloats = (int64_t)4 << 20;   // 16 MiB
+constexpr int64_t kSkinnyWsCounters = 65536;
+
+SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K);
+bool skinny_variant_exists(const SkinnyPlan& p);
+int64_t skinny_workspace_floats(const SkinnyPlan& p, int64_t M, int64_t N);
+hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace& ws, hipStream_t s);
+
+hipError_t launch_tiled(const GemmArgs& a, hipStream_t s);
+
+}  // namespace tpk

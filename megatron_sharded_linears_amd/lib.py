@@ -1,0 +1,290 @@
+"""ctypes binding of libtpshard, with the names of its C entry points.
+
+Argument marshalling only: each wrapper takes torch tensors, checks that their
+shapes, dtypes and devices agree with one another, and passes data pointers,
+sizes and the current HIP stream to the C function of the same name. Every
+step of the computation runs in the library's gfx950 kernels; there is no
+fallback of any kind. If the shared library is missing, importing this module
+fails with an ImportError.
+
+torch is imported before the library is loaded so that the process uses
+torch's HIP runtime (the library links libamdhip64.so.7 by soname and binds to
+the already-loaded copy); stream handles from torch are then valid here.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpshard.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is not built; run `python -m megatron_sharded_linears_amd.build` "
+        "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+# ----------------------------------------------------------------- constants
+
+TP_OK = 0
+TP_BF16, TP_F32 = 0, 1
+TP_W_QKV, TP_W_O, TP_W_GATE_UP, TP_W_DOWN, TP_W_EMBED, TP_W_LM_HEAD = range(6)
+TP_MAX_SHARDS = 64
+
+KIND = {"qkv": TP_W_QKV, "o": TP_W_O, "gate_up": TP_W_GATE_UP, "down": TP_W_DOWN,
+        "embed": TP_W_EMBED, "lm_head": TP_W_LM_HEAD}
+
+STATUS_NAMES = {0: "TP_OK", -1: "TP_ERR_NULL", -2: "TP_ERR_SHAPE", -3: "TP_ERR_DIVISIBILITY",
+                -4: "TP_ERR_ALIGNMENT", -5: "TP_ERR_DTYPE", -6: "TP_ERR_RANGE",
+                -7: "TP_ERR_HIP", -8: "TP_ERR_ALLOC"}
+
+
+class tp_model_cfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("intermediate", ctypes.c_int32), ("vocab", ctypes.c_int32)]
+
+
+class TPError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.tp_status_string(status).decode()
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({msg})")
+
+
+# --------------------------------------------------------------- prototypes
+
+_vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_cfgp = ctypes.POINTER(tp_model_cfg)
+_ptr_array = ctypes.POINTER(ctypes.c_void_p)
+
+_PROTOS = {
+    "tp_status_string": (ctypes.c_char_p, [_int]),
+    "tp_full_shape": (_int, [_cfgp, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "tp_shard_shape": (_int, [_cfgp, _int, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "tp_vocab_shard_rows": (_i64, [_i64, _int]),
+    "tp_kv_heads_of_rank": (_int, [_cfgp, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
+    "tp_shard_weights": (_int, [_cfgp, _int, _int, _int, _vp, _vp, _vp]),
+    "tp_column_linear": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "tp_swiglu": (_int, [_vp, _i64, _i64, _vp, _vp]),
+    "tp_row_linear_partial": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp]),
+    "tp_reduce_partials": (_int, [_ptr_array, _int, _i64, _int, _vp, _int, _vp]),
+    "tp_vocab_embed": (_int, [_vp, _i64, _vp, _i64, _int, _int, _i64, _vp, _vp]),
+    "tp_lm_head_shard": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp]),
+    "tp_concat_logits": (_int, [_ptr_array, _int, _i64, _i64, _i64, _int, _vp, _vp]),
+    "tp_tune_skinny": (_int, [_int, _int, _int]),
+}
+for _name, (_res, _args) in _PROTOS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_PROTOS)
+
+
+def library_path():
+    return _LIB_PATH
+
+
+# ------------------------------------------------------------------ helpers
+
+def _check(status, where):
+    if status != TP_OK:
+        raise TPError(status, where)
+
+
+def _cfg(cfg):
+    if isinstance(cfg, tp_model_cfg):
+        return cfg
+    return tp_model_cfg(cfg["hidden"], cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"],
+                        cfg["intermediate"], cfg["vocab"])
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return TP_BF16
+    if dt == torch.float32:
+        return TP_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _ptrs(tensors):
+    arr = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    return ctypes.cast(arr, _ptr_array), arr
+
+
+# ------------------------------------------------------------ host queries
+
+def tp_status_string(status):
+    return _lib.tp_status_string(status).decode()
+
+
+def tp_full_shape(cfg, kind):
+    r, c = _i64(), _i64()
+    _check(_lib.tp_full_shape(ctypes.byref(_cfg(cfg)), KIND.get(kind, kind), ctypes.byref(r), ctypes.byref(c)),
+           "tp_full_shape")
+    return r.value, c.value
+
+
+def tp_shard_shape(cfg, t, kind):
+    r, c = _i64(), _i64()
+    _check(_lib.tp_shard_shape(ctypes.byref(_cfg(cfg)), t, KIND.get(kind, kind), ctypes.byref(r), ctypes.byref(c)),
+           "tp_shard_shape")
+    return r.value, c.value
+
+
+def tp_vocab_shard_rows(vocab, t):
+    v = _lib.tp_vocab_shard_rows(vocab, t)
+    if v < 0:
+        raise TPError(int(v), "tp_vocab_shard_rows")
+    return v
+
+
+def tp_kv_heads_of_rank(cfg, t, rank):
+    f, c = _int(), _int()
+    _check(_lib.tp_kv_heads_of_rank(ctypes.byref(_cfg(cfg)), t, rank, ctypes.byref(f), ctypes.byref(c)),
+           "tp_kv_heads_of_rank")
+    return f.value, c.value
+
+
+def tp_tune_skinny(ksteps=0, nwn=0, nwk=0):
+    _check(_lib.tp_tune_skinny(ksteps, nwn, nwk), "tp_tune_skinny")
+
+
+# ------------------------------------------------------------ device calls
+
+def tp_shard_weights(cfg, t, rank, kind, full_w, shard_w, stream=None):
+    c = _cfg(cfg)
+    k = KIND.get(kind, kind)
+    if tuple(full_w.shape) != tp_full_shape(c, k):
+        raise ValueError(f"full weight shape {tuple(full_w.shape)} != {tp_full_shape(c, k)}")
+    if tuple(shard_w.shape) != tp_shard_shape(c, t, k):
+        raise ValueError(f"shard shape {tuple(shard_w.shape)} != {tp_shard_shape(c, t, k)}")
+    _check(_lib.tp_shard_weights(ctypes.byref(c), t, rank, k, _dev(full_w, "full_w", torch.bfloat16, 2),
+                                 _dev(shard_w, "shard_w", torch.bfloat16, 2), _stream(stream)),
+           "tp_shard_weights")
+    return shard_w
+
+
+def _linear_shapes(x, w, y, name):
+    M, K = x.shape
+    N, K2 = w.shape
+    if K != K2:
+        raise ValueError(f"{name}: x has K={K}, weight has K={K2}")
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"{name}: output shape {tuple(y.shape)} != {(M, N)}")
+    return M, K, N
+
+
+def tp_column_linear(x, w_shard, y, bias=None, stream=None):
+    M, K, N = _linear_shapes(x, w_shard, y, "tp_column_linear")
+    b = None
+    if bias is not None:
+        b = _dev(bias, "bias", torch.bfloat16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias length != N")
+    _check(_lib.tp_column_linear(_dev(x, "x", torch.bfloat16, 2), M, K, _dev(w_shard, "w_shard", torch.bfloat16, 2),
+                                 N, b, _dev(y, "y", torch.bfloat16, 2), _stream(stream)),
+           "tp_column_linear")
+    return y
+
+
+def tp_swiglu(gu, out, stream=None):
+    M, two_i = gu.shape
+    if two_i % 2 or tuple(out.shape) != (M, two_i // 2):
+        raise ValueError("tp_swiglu: out must be [M, gu.shape[1] / 2]")
+    _check(_lib.tp_swiglu(_dev(gu, "gu", torch.bfloat16, 2), M, two_i // 2, _dev(out, "out", torch.bfloat16, 2),
+                          _stream(stream)), "tp_swiglu")
+    return out
+
+
+def tp_row_linear_partial(x_shard, w_shard, partial, stream=None):
+    M, K, N = _linear_shapes(x_shard, w_shard, partial, "tp_row_linear_partial")
+    _check(_lib.tp_row_linear_partial(_dev(x_shard, "x_shard", torch.bfloat16, 2), M, K,
+                                      _dev(w_shard, "w_shard", torch.bfloat16, 2), N,
+                                      _dev(partial, "partial", partial.dtype, 2), _dtype_code(partial.dtype),
+                                      _stream(stream)), "tp_row_linear_partial")
+    return partial
+
+
+def tp_reduce_partials(partials, out, stream=None):
+    t = len(partials)
+    if t < 1 or t > TP_MAX_SHARDS:
+        raise ValueError("need 1..64 partials")
+    numel = partials[0].numel()
+    in_dt = partials[0].dtype
+    for i, p in enumerate(partials):
+        _dev(p, f"partials[{i}]", in_dt)
+        if p.numel() != numel:
+            raise ValueError("partials differ in size")
+    _dev(out, "out", out.dtype)
+    if out.numel() != numel:
+        raise ValueError("out size != partial size")
+    arr, keep = _ptrs(partials)
+    _check(_lib.tp_reduce_partials(arr, t, numel, _dtype_code(in_dt), ctypes.c_void_p(out.data_ptr()),
+                                   _dtype_code(out.dtype), _stream(stream)), "tp_reduce_partials")
+    del keep
+    return out
+
+
+def tp_vocab_embed(ids, e_shard, vocab, t, rank, out_partial, stream=None):
+    M = ids.shape[0]
+    Vs, H = e_shard.shape
+    if Vs != tp_vocab_shard_rows(vocab, t):
+        raise ValueError("e_shard rows != ceil(vocab / t)")
+    if tuple(out_partial.shape) != (M, H):
+        raise ValueError("out_partial must be [M, H]")
+    _check(_lib.tp_vocab_embed(_dev(ids, "ids", torch.int32, 1), M, _dev(e_shard, "e_shard", torch.bfloat16, 2),
+                               vocab, t, rank, H, _dev(out_partial, "out_partial", torch.bfloat16, 2),
+                               _stream(stream)), "tp_vocab_embed")
+    return out_partial
+
+
+def tp_lm_head_shard(h, w_lm_shard, logits_shard, stream=None):
+    M, K, N = _linear_shapes(h, w_lm_shard, logits_shard, "tp_lm_head_shard")
+    _check(_lib.tp_lm_head_shard(_dev(h, "h", torch.bfloat16, 2), M, K, _dev(w_lm_shard, "w_lm_shard", torch.bfloat16, 2),
+                                 N, _dev(logits_shard, "logits_shard", logits_shard.dtype, 2),
+                                 _dtype_code(logits_shard.dtype), _stream(stream)), "tp_lm_head_shard")
+    return logits_shard
+
+
+def tp_concat_logits(shard_logits, vocab, out, stream=None):
+    t = len(shard_logits)
+    M, v_shard = shard_logits[0].shape
+    dt = shard_logits[0].dtype
+    for i, s in enumerate(shard_logits):
+        _dev(s, f"shard_logits[{i}]", dt, 2)
+        if tuple(s.shape) != (M, v_shard):
+            raise ValueError("shard logits differ in shape")
+    _dev(out, "out", dt, 2)
+    if tuple(out.shape) != (M, vocab):
+        raise ValueError("out must be [M, vocab]")
+    arr, keep = _ptrs(shard_logits)
+    _check(_lib.tp_concat_logits(arr, t, M, v_shard, vocab, _dtype_code(dt), ctypes.c_void_p(out.data_ptr()),
+                                 _stream(stream)), "tp_concat_logits")
+    del keep
+    return out

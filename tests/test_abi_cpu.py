@@ -1,0 +1,157 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/tp_shard.h declares, its host-only shape queries agree with
+the oracle's independent head and vocab maps, and argument errors are
+reported before any HIP call (so no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from megatron_sharded_linears_amd import lib
+from megatron_sharded_linears_amd.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+C = lib._lib
+
+
+def _declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(tp_[a-z_]+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_every_declared_function_is_exported_and_bound():
+    names = _declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(C, n), n
+        assert n in lib.EXPORTED, n
+        assert callable(getattr(lib, n)), n
+    # the eight device calls of the path
+    for n in ["tp_shard_weights", "tp_column_linear", "tp_swiglu", "tp_row_linear_partial",
+              "tp_reduce_partials", "tp_vocab_embed", "tp_lm_head_shard", "tp_concat_logits"]:
+        assert n in names
+
+
+def test_library_links_hip_runtime_by_soname():
+    import subprocess
+    out = subprocess.run(["readelf", "-d", lib.library_path()], capture_output=True, text=True).stdout
+    assert "libamdhip64.so.7" in out
+
+
+@pytest.mark.parametrize("w", WORKLOADS, ids=lambda w: w.name)
+def test_shard_shapes_agree_with_oracle_maps(w):
+    cfg = w.cfg()
+    t = w.t
+    d = w.head_dim
+    assert lib.tp_shard_shape(cfg, t, "qkv") == (len(oracle.qkv_shard_rows(w.num_q_heads, w.num_kv_heads, d, t, 0)), w.hidden)
+    assert lib.tp_shard_shape(cfg, t, "gate_up") == (len(oracle.gate_up_shard_rows(w.intermediate, t, 0)), w.hidden)
+    assert lib.tp_shard_shape(cfg, t, "o") == (w.hidden, len(oracle.o_shard_cols(w.num_q_heads, d, t, 0)))
+    assert lib.tp_shard_shape(cfg, t, "down") == (w.hidden, len(oracle.down_shard_cols(w.intermediate, t, 0)))
+    assert lib.tp_shard_shape(cfg, t, "embed") == (oracle.vocab_shard_rows(w.vocab, t), w.hidden)
+    assert lib.tp_vocab_shard_rows(w.vocab, t) == oracle.vocab_shard_rows(w.vocab, t)
+    for r in range(t):
+        first, count = lib.tp_kv_heads_of_rank(cfg, t, r)
+        assert list(range(first, first + count)) == oracle.kv_heads_of_rank(w.num_kv_heads, t, r)
+    full = {k: lib.tp_full_shape(cfg, k) for k in lib.KIND}
+    assert full["qkv"] == ((w.num_q_heads + 2 * w.num_kv_heads) * d, w.hidden)
+    assert full["gate_up"] == (2 * w.intermediate, w.hidden)
+
+
+def test_kv_replication_and_split_rule_errors():
+    base = {"hidden": 64, "num_q_heads": 8, "num_kv_heads": 2, "head_dim": 8, "intermediate": 64, "vocab": 10}
+    for t in (1, 2, 4, 8):
+        for r in range(t):
+            f, c = lib.tp_kv_heads_of_rank(base, t, r)
+            assert list(range(f, f + c)) == oracle.kv_heads_of_rank(2, t, r)
+    with pytest.raises(lib.TPError) as e:
+        lib.tp_shard_shape(base, 3, "qkv")             # 8 % 3
+    assert e.value.status == -3
+    with pytest.raises(lib.TPError) as e:
+        lib.tp_shard_shape(dict(base, num_kv_heads=4, num_q_heads=12), 3, "qkv")  # 4 >= 3, 4 % 3
+    assert e.value.status == -3
+    with pytest.raises(lib.TPError) as e:
+        lib.tp_shard_shape(dict(base, intermediate=60), 8, "gate_up")
+    assert e.value.status == -3
+    with pytest.raises(lib.TPError) as e:
+        lib.tp_shard_shape(base, 65, "qkv")
+    assert e.value.status == -6
+    with pytest.raises(lib.TPError) as e:
+        lib.tp_kv_heads_of_rank(base, 4, 4)
+    assert e.value.status == -6
+    with pytest.raises(lib.TPError) as e:
+        lib.tp_shard_shape(base, 2, 17)
+    assert e.value.status == -5
+    assert lib.tp_vocab_shard_rows(1001, 2) == 501
+    assert lib.tp_vocab_shard_rows(5, 4) == 2
+    assert C.tp_vocab_shard_rows(10, 0) == -6
+    assert C.tp_status_string(12345) == b"unknown status"
+
+
+# Fake device addresses: validation must reject (or accept as a no-op) before
+# touching them, so nothing is ever dereferenced.
+A = ctypes.c_void_p(0x10000)      # 16-byte aligned
+B = ctypes.c_void_p(0x20000)
+Y = ctypes.c_void_p(0x30000)
+MIS = ctypes.c_void_p(0x10008)    # 8-byte aligned only
+NULL = ctypes.c_void_p(0)
+S = ctypes.c_void_p(0)
+
+
+def test_linear_validation_before_any_hip_call():
+    f = C.tp_column_linear
+    assert f(NULL, 16, 64, B, 32, NULL, Y, S) == -1
+    assert f(A, 16, 64, NULL, 32, NULL, Y, S) == -1
+    assert f(A, -1, 64, B, 32, NULL, Y, S) == -2
+    assert f(A, 16, 0, B, 32, NULL, Y, S) == -2
+    assert f(A, 16, 60, B, 32, NULL, Y, S) == -4          # K % 8
+    assert f(MIS, 16, 64, B, 32, NULL, Y, S) == -4
+    assert f(A, 16, 64, B, 32, ctypes.c_void_p(0x40001), Y, S) == -4
+    assert f(A, 0, 64, B, 32, NULL, Y, S) == 0            # M == 0: no-op
+    g = C.tp_row_linear_partial
+    assert g(A, 16, 64, B, 32, Y, 7, S) == -5
+    assert g(A, 0, 64, B, 32, Y, 1, S) == 0
+    h = C.tp_lm_head_shard
+    assert h(A, 4, 64, B, 32, Y, 2, S) == -5
+    assert h(A, 0, 64, B, 32, Y, 0, S) == 0
+
+
+def test_elementwise_validation_before_any_hip_call():
+    assert C.tp_swiglu(A, 4, 12, Y, S) == -4               # i_shard % 8
+    assert C.tp_swiglu(NULL, 4, 16, Y, S) == -1
+    assert C.tp_swiglu(A, 0, 16, Y, S) == 0
+    arr = (ctypes.c_void_p * 3)(0x10000, 0x20000, 0x30008)
+    pp = ctypes.cast(arr, lib._ptr_array)
+    assert C.tp_reduce_partials(pp, 3, 64, 0, Y, 0, S) == -4  # third partial misaligned
+    assert C.tp_reduce_partials(pp, 0, 64, 0, Y, 0, S) == -6
+    assert C.tp_reduce_partials(pp, 65, 64, 0, Y, 0, S) == -6
+    assert C.tp_reduce_partials(pp, 2, 64, 3, Y, 0, S) == -5
+    assert C.tp_reduce_partials(pp, 2, 0, 0, Y, 0, S) == 0
+    assert C.tp_vocab_embed(A, 4, B, 1000, 2, 2, 64, Y, S) == -6      # rank == t
+    assert C.tp_vocab_embed(A, 4, B, 1000, 2, 0, 60, Y, S) == -4      # H % 8
+    assert C.tp_vocab_embed(A, 0, B, 1000, 2, 0, 64, Y, S) == 0
+    arr2 = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    pp2 = ctypes.cast(arr2, lib._ptr_array)
+    assert C.tp_concat_logits(pp2, 2, 4, 499, 1000, 0, Y, S) == -2    # v_shard != ceil(V/t)
+    assert C.tp_concat_logits(pp2, 2, 0, 500, 1000, 0, Y, S) == 0
+    cfg = lib._cfg({"hidden": 64, "num_q_heads": 8, "num_kv_heads": 2, "head_dim": 8,
+                    "intermediate": 64, "vocab": 10})
+    assert C.tp_shard_weights(ctypes.byref(cfg), 2, 2, 0, A, B, S) == -6
+    assert C.tp_shard_weights(ctypes.byref(cfg), 3, 0, 0, A, B, S) == -3
+    assert C.tp_shard_weights(ctypes.byref(cfg), 2, 0, 0, MIS, B, S) == -4
+    assert C.tp_shard_weights(ctypes.byref(cfg), 2, 0, 9, A, B, S) == -5
+
+
+def test_tune_rejects_unbuilt_variants():
+    assert C.tp_tune_skinny(3, 4, 2) == -2
+    assert C.tp_tune_skinny(8, 4, 2) == 0
+    assert C.tp_tune_skinny(0, 0, 0) == 0
