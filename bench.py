@@ -1,0 +1,368 @@
+"""Benchmark of one tensor-parallel rank's share of the linear path on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--eager]
+
+A step is one pass of the whole path over one batch of synthetic tokens, for
+one rank r = 0 of a t-way split, with every input already resident in HBM:
+
+    embedding   tp_vocab_embed (rank r) + tp_reduce_partials over t shards
+    per layer   tp_column_linear (qkv) ; tp_row_linear_partial (o) ;
+                tp_reduce_partials ; tp_column_linear (gate_up) ; tp_swiglu ;
+                tp_row_linear_partial (down) ; tp_reduce_partials
+    LM head     tp_lm_head_shard (rank r) + tp_concat_logits over t shards
+
+The other t-1 ranks' partial sums and logits (which would arrive over the
+interconnect) are seeded synthetic buffers resident in HBM. Attention is not
+on this path: o_proj reads a seeded synthetic context. gate_up reads the value
+after all-reduce 1 and the next layer reads the value after all-reduce 2
+(norms and residuals are not on this path). Weight shards are drawn on the
+device from seeded generators; distinct per layer, so they stream from HBM.
+
+The step's launches are captured once into a HIP graph; the timed region is K
+replays of it (decode is launch-bound: ~200 small kernels per step). The same
+calls issued eagerly from Python are timed too (`eager_ms_per_step`).
+
+Prints ONE JSON line (the driver's contract). `value` is the shard-GEMM
+TFLOP/s of the whole step: the flops of every shard GEMM in the step divided
+by the time of the step. `roofline` is that of the decode-linear kernel (the
+dominant one): each op's launches of one step are captured into a graph of
+their own and replayed K times between HIP events on the replaying stream,
+giving the average duration per launch. `cpu_baseline` is the float64 CPU
+oracle on a bounded sample of the same per-rank work.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+METRIC = "shard-GEMM TFLOP/s + reduce GB/s (% roofline), Llama-8B t=8 decode B=16"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="llama8b_t8_decode_m16")
+    p.add_argument("--eager", action="store_true", help="time eager launches instead of the captured step")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------- work model
+
+def gemm_bytes(M, N, K, out_bytes=2):
+    return 2 * N * K + 2 * M * K + out_bytes * M * N
+
+
+def gemm_flops(M, N, K):
+    return 2 * M * N * K
+
+
+class Rank:
+    """Every buffer of rank 0's share, resident on the device."""
+
+    def __init__(self, w, lib, I, torch):
+        self.w = w
+        dev = "cuda"
+        t, M, H, L = w.t, w.tokens, w.hidden, w.layers
+        cfg = w.cfg()
+        seed = 1000 * (w.index + 1)
+        bf = torch.bfloat16
+
+        def dn(shape, std, s):
+            return I.device_normal_bf16(shape, std, seed + s, dev)
+
+        self.shapes = {k: lib.tp_shard_shape(cfg, t, k) for k in lib.KIND}
+        self.layers = []
+        for l in range(L):
+            s = 100 * (l + 1)
+            self.layers.append({
+                "qkv": dn(self.shapes["qkv"], 0.02, s + 1),
+                "o": dn(self.shapes["o"], 0.02, s + 2),
+                "gate_up": dn(self.shapes["gate_up"], 0.02, s + 3),
+                "down": dn(self.shapes["down"], 0.02, s + 4),
+                "ctx": dn((M, self.shapes["o"][1]), 1.0, s + 5),
+                # peers' partial sums for the two all-reduce sites
+                "peers_o": [dn((M, H), 0.5, s + 10 + j) for j in range(t - 1)],
+                "peers_d": [dn((M, H), 0.5, s + 40 + j) for j in range(t - 1)],
+            })
+        self.x = dn((M, H), 1.0, 7)
+        self.qkv = torch.empty((M, self.shapes["qkv"][0]), dtype=bf, device=dev)
+        self.po = torch.empty((M, H), dtype=bf, device=dev)
+        self.y1 = torch.empty((M, H), dtype=bf, device=dev)
+        self.gu = torch.empty((M, self.shapes["gate_up"][0]), dtype=bf, device=dev)
+        self.act = torch.empty((M, self.shapes["gate_up"][0] // 2), dtype=bf, device=dev)
+        self.pd = torch.empty((M, H), dtype=bf, device=dev)
+        self.h = torch.empty((M, H), dtype=bf, device=dev)
+        self.vocab = w.has_vocab
+        if self.vocab:
+            vs = self.shapes["embed"][0]
+            self.vs = vs
+            self.ids = torch.randint(0, w.vocab, (M,), generator=torch.Generator().manual_seed(seed + 3),
+                                     dtype=torch.int32).to(dev)
+            self.embed = dn((vs, H), 0.02, 21)
+            self.lm = dn((vs, H), 0.02, 22)
+            self.peers_e = [dn((M, H), 0.02, 60 + j) for j in range(t - 1)]
+            self.ze = torch.empty((M, H), dtype=bf, device=dev)
+            Ms = w.lm_positions
+            self.hs_rows = Ms
+            self.logits = torch.empty((Ms, vs), dtype=bf, device=dev)
+            self.peer_logits = [dn((Ms, vs), 1.0, 80 + j) for j in range(t - 1)]
+            self.full_logits = torch.empty((Ms, w.vocab), dtype=bf, device=dev)
+
+    def work(self):
+        """Algorithmic flops and bytes per step, by op."""
+        w = self.w
+        M, H, t = w.tokens, w.hidden, w.t
+        q, o, g, d = self.shapes["qkv"], self.shapes["o"], self.shapes["gate_up"], self.shapes["down"]
+        ops = {
+            "qkv": (w.layers, gemm_flops(M, q[0], q[1]), gemm_bytes(M, q[0], q[1])),
+            "o": (w.layers, gemm_flops(M, o[0], o[1]), gemm_bytes(M, o[0], o[1])),
+            "gate_up": (w.layers, gemm_flops(M, g[0], g[1]), gemm_bytes(M, g[0], g[1])),
+            "down": (w.layers, gemm_flops(M, d[0], d[1]), gemm_bytes(M, d[0], d[1])),
+            "swiglu": (w.layers, 0, 6 * M * (g[0] // 2)),
+            "reduce": (2 * w.layers, 0, (2 * t + 2) * M * H),
+        }
+        if self.vocab:
+            Ms, vs = self.hs_rows, self.vs
+            ops["lm_head"] = (1, gemm_flops(Ms, vs, H), gemm_bytes(Ms, vs, H))
+            ops["embed"] = (1, 0, 4 * M + 2 * H * M + 2 * M * H)   # upper bound: every id owned
+            ops["embed_reduce"] = (1, 0, (2 * t + 2) * M * H)
+            ops["concat"] = (1, 0, 4 * Ms * w.vocab)
+        return ops
+
+
+def build_ops(R, lib):
+    """The step as a list of (name, fn, args): every launch of one pass."""
+    w = R.w
+    t = w.t
+    ops = []
+    h = R.x
+    if R.vocab:
+        ops.append(("embed", lib.tp_vocab_embed, (R.ids, R.embed, w.vocab, t, 0, R.ze)))
+        ops.append(("embed_reduce", lib.tp_reduce_partials, ([R.ze] + R.peers_e, R.h)))
+        h = R.h
+    for L in R.layers:
+        ops.append(("qkv", lib.tp_column_linear, (h, L["qkv"], R.qkv)))
+        ops.append(("o", lib.tp_row_linear_partial, (L["ctx"], L["o"], R.po)))
+        ops.append(("reduce", lib.tp_reduce_partials, ([R.po] + L["peers_o"], R.y1)))
+        ops.append(("gate_up", lib.tp_column_linear, (R.y1, L["gate_up"], R.gu)))
+        ops.append(("swiglu", lib.tp_swiglu, (R.gu, R.act)))
+        ops.append(("down", lib.tp_row_linear_partial, (R.act, L["down"], R.pd)))
+        ops.append(("reduce", lib.tp_reduce_partials, ([R.pd] + L["peers_d"], R.h)))
+        h = R.h
+    if R.vocab:
+        hs = h[h.shape[0] - R.hs_rows:]
+        ops.append(("lm_head", lib.tp_lm_head_shard, (hs, R.lm, R.logits)))
+        ops.append(("concat", lib.tp_concat_logits, ([R.logits] + R.peer_logits, w.vocab, R.full_logits)))
+    return ops
+
+
+def run_ops(ops, only=None):
+    for name, fn, args in ops:
+        if only is None or name == only:
+            fn(*args)
+
+
+def capture(torch, ops, only=None):
+    """HIP graph of the step's launches (or of one op's launches)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run_ops(ops, only)            # per-stream workspace is allocated before capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            run_ops(ops, only)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps, warmup):
+    """Events around `reps` replays on the replaying (current) stream; ms per replay."""
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+# ----------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w, seconds):
+    """The float64 oracle on this host, on a bounded sample of the same
+    per-rank work: the shard GEMMs, SwiGLU and reduces of two layers, looped
+    until `seconds` have passed. Returns shard-GEMM TFLOP/s."""
+    import numpy as np
+    import oracle
+    from megatron_sharded_linears_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    from megatron_sharded_linears_amd import lib
+    cfg, t, M, H = w.cfg(), w.t, w.tokens, w.hidden
+    sh = {k: lib.tp_shard_shape(cfg, t, k) for k in ("qkv", "o", "gate_up", "down")}
+    f64 = I.to_f64
+    layers = []
+    for l in range(2):
+        layers.append({k: f64(I.normal_bf16((w.index, l, 50 + j), sh[k], 0.02))
+                       for j, k in enumerate(sh)})
+        layers[-1]["ctx"] = f64(I.normal_bf16((w.index, l, 60), (M, sh["o"][1])))
+        layers[-1]["peers"] = [f64(I.normal_bf16((w.index, l, 70 + j), (M, H), 0.5)) for j in range(t - 1)]
+    x = f64(I.normal_bf16((w.index, 99), (M, H)))
+    flops_layer = sum(gemm_flops(M, sh[k][0], sh[k][1]) for k in sh)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for L in layers:
+            oracle.linear(x, L["qkv"])
+            po = oracle.linear(L["ctx"], L["o"])
+            y1 = oracle.round_bf16(oracle.all_reduce_sum([po] + L["peers"]))
+            gu = oracle.round_bf16(oracle.linear(y1, L["gate_up"]))
+            i_s = gu.shape[1] // 2
+            act = oracle.round_bf16(oracle.swiglu(gu[:, :i_s], gu[:, i_s:]))
+            pd = oracle.linear(act, L["down"])
+            x = oracle.round_bf16(oracle.all_reduce_sum([pd] + L["peers"]))
+            n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": flops_layer * n / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} layer passes (qkv, o, reduce, gate_up, SwiGLU, down, reduce at this workload's "
+                      f"rank-share shapes, float64 NumPy) over 2 seeded layers in {el:.1f} s"}
+
+
+# ------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: every shard of the t-way split is computed on that one "
+              "device and there is no cross-GPU path to scale. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from megatron_sharded_linears_amd import inputs as I
+    from megatron_sharded_linears_amd import lib
+    from megatron_sharded_linears_amd.workloads import BY_NAME
+
+    w = BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    R = Rank(w, lib, I, torch)
+    torch.cuda.synchronize()
+    work = R.work()
+
+    ops = build_ops(R, lib)
+    names = []
+    for n, _, _ in ops:
+        if n not in names:
+            names.append(n)
+
+    # --- eager: the same calls issued one by one from Python
+    for _ in range(args.warmup):
+        run_ops(ops)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        run_ops(ops)
+    b.record()
+    torch.cuda.synchronize()
+    ms_eager = a.elapsed_time(b) / args.steps
+
+    # --- timed region: exactly K steps, each the replay of the captured step
+    g_step = capture(torch, ops)
+    for _ in range(args.warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        g_step.replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall0
+    ms_step = start.elapsed_time(end) / args.steps
+    if args.eager:
+        ms_step = ms_eager
+
+    # --- per kernel: each op's launches of one step, captured and replayed K times
+    per_op = {}
+    for name in names:
+        g = capture(torch, ops, only=name)
+        ms = time_graph(torch, g, args.steps, 2)
+        del g
+        n_per_step, flops, byts = work[name]
+        us = ms * 1e3 / n_per_step
+        per_op[name] = {"launches_per_step": n_per_step, "us_per_launch": round(us, 3),
+                        "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                        "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2) if flops else None,
+                        "bytes_per_launch": byts}
+
+    gemm_ops = [k for k in ("qkv", "o", "gate_up", "down", "lm_head") if k in work]
+    flops_step = sum(work[k][0] * work[k][1] for k in gemm_ops)
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    gemm_us = sum(per_op[k]["us_per_launch"] * work[k][0] for k in gemm_ops)
+    gemm_bytes_step = sum(work[k][0] * work[k][2] for k in gemm_ops)
+    achieved = gemm_bytes_step / (gemm_us * 1e-6) / 1e9
+    red = per_op["reduce"]
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "t": w.t, "rank": 0, "tokens": w.tokens, "layers": w.layers,
+                   "hidden": w.hidden, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "intermediate": w.intermediate,
+                   "vocab": w.vocab if w.has_vocab else None, "lm_positions": w.lm_positions if w.has_vocab else 0,
+                   "parallelism": f"tp{w.t} rank share on 1 GPU",
+                   "execution": "eager launches" if args.eager else "HIP graph of the step"},
+        "roofline": {"bound": "hbm", "kernel": "decode linear (skinny_kernel), all launches of a step",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "launches_per_step": sum(work[k][0] for k in gemm_ops),
+                     "us_per_step": round(gemm_us, 2)},
+        "reduce": {"GBps": red["GBps"], "frac": round(red["GBps"] / HBM_PEAK_GBPS, 4),
+                   "us_per_call": red["us_per_launch"], "calls_per_step": work["reduce"][0],
+                   "bytes_per_call": work["reduce"][2]},
+        "eager_ms_per_step": round(ms_eager, 4),
+        "gemm_only_TFLOPs": round(flops_step / (gemm_us * 1e-6) / 1e12, 2),
+        "step_GBps": round(sum(n * b for n, _, b in work.values()) / (ms_step * 1e-3) / 1e9, 1),
+        "per_op": per_op,
+        "wall_s_timed": round(wall_s, 3),
+    }
+
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -192,9 +192,14 @@ int tp_concat_logits(const void* const* shard_logits, int t, int64_t M, int64_t 
  * later call in this process: `ksteps` 32-wide k steps per wave, `nwn` waves
  * along the output rows (16 rows each) and `nwk` waves along K per
  * workgroup; K is split across as many workgroups as it takes to cover it.
- * (0, 0, 0) restores the automatic choice. Returns TP_ERR_SHAPE if no such
- * kernel variant is built. Results are the same up to fp32 summation order. */
-int tp_tune_skinny(int ksteps, int nwn, int nwk);
+ * `x_direct` = 1 makes each wave load its activation fragments from global
+ * memory instead of sharing a copy staged in LDS. (0, 0, 0, 0) restores the
+ * automatic choice. Returns TP_ERR_SHAPE if no such
+ * kernel variant is built. A shape whose X chunk does not fit in LDS for a
+ * given M, or whose split partials do not fit the workspace, keeps the
+ * automatic choice for that call. Results are the same up
+ * to fp32 summation order. */
+int tp_tune_skinny(int ksteps, int nwn, int nwk, int x_direct);
 
 #ifdef __cplusplus
 }

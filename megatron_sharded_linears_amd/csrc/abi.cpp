@@ -92,7 +92,7 @@ int get_workspace(hipStream_t s, tpk::Workspace* out) {
 
 // A process-wide override of the decode kernel's shape, for tuning and for
 // tests that exercise every variant. Zero means automatic.
-int g_force_ksteps = 0, g_force_nwn = 0, g_force_nwk = 0;
+int g_force_ksteps = 0, g_force_nwn = 0, g_force_nwk = 0, g_force_xd = 0;
 
 int run_linear(const void* x, int64_t M, int64_t K, const void* w, int64_t N, const void* bias,
                void* y, int out_dtype, void* stream) {
@@ -110,12 +110,19 @@ int run_linear(const void* x, int64_t M, int64_t K, const void* w, int64_t N, co
     if (M <= kSkinnyMaxM) {
         tpk::SkinnyPlan p = tpk::plan_skinny(M, N, K);
         if (g_force_ksteps > 0) {
-            p.ksteps = g_force_ksteps;
-            p.nwn = g_force_nwn;
-            p.nwk = g_force_nwk;
-            p.ntiles = (N + 16LL * p.nwn - 1) / (16LL * p.nwn);
-            const int64_t gk = 32LL * p.ksteps * p.nwk;
-            p.splits = (int)((K + gk - 1) / gk);
+            tpk::SkinnyPlan f = p;
+            f.ksteps = g_force_ksteps;
+            f.nwn = g_force_nwn;
+            f.nwk = g_force_nwk;
+            f.xd = g_force_xd;
+            f.ntiles = (N + 16LL * f.nwn - 1) / (16LL * f.nwn);
+            const int64_t gk = 32LL * f.ksteps * f.nwk;
+            f.splits = (int)((K + gk - 1) / gk);
+            // a forced shape that does not fit this M (LDS) or the workspace
+            // keeps the automatic plan
+            const bool fits = f.splits == 1 || (tpk::skinny_workspace_floats(f, M, N) <= kWsFloats &&
+                                                f.ntiles <= kWsCounters && f.splits <= 65535);
+            if (tpk::skinny_variant_exists(f) && tpk::skinny_plan_fits(f, M) && fits) p = f;
         }
         tpk::Workspace ws{nullptr, 0, nullptr, 0};
         if (p.splits > 1) {
@@ -365,18 +372,17 @@ int tp_concat_logits(const void* const* shard_logits, int t, int64_t M, int64_t 
     }
 }
 
-int tp_tune_skinny(int ksteps, int nwn, int nwk) {
+int tp_tune_skinny(int ksteps, int nwn, int nwk, int x_direct) {
     if (ksteps == 0 && nwn == 0 && nwk == 0) {
-        g_force_ksteps = g_force_nwn = g_force_nwk = 0;
+        g_force_ksteps = g_force_nwn = g_force_nwk = g_force_xd = 0;
         return TP_OK;
     }
-    for (int m = 1; m <= 4; m *= 2) {
-        tpk::SkinnyPlan p{m, ksteps, nwn, nwk, 1, 1};
-        if (!tpk::skinny_variant_exists(p)) return TP_ERR_SHAPE;
-    }
+    tpk::SkinnyPlan p{1, ksteps, nwn, nwk, x_direct ? 1 : 0, 1, 1};
+    if (!tpk::skinny_variant_exists(p)) return TP_ERR_SHAPE;
     g_force_ksteps = ksteps;
     g_force_nwn = nwn;
     g_force_nwk = nwk;
+    g_force_xd = x_direct ? 1 : 0;
     return TP_OK;
 }
 

@@ -18,15 +18,24 @@
 //     the weight has too few rows to fill 256 CUs, across workgroups: each
 //     writes an fp32 partial tile to the workspace and the last workgroup to
 //     arrive on a tile (one atomic counter per tile) sums the partials in
-//     split order, so the result does not depend on arrival order.
+//     split order, so the result does not depend on arrival order. Partials
+//     travel through relaxed device-scope atomic stores and loads.
 #include "common.h"
 #include "kernels.h"
+
+#ifndef TP_SKINNY_W_NT
+#define TP_SKINNY_W_NT 0
+#endif
 
 namespace tpk {
 
 namespace {
 
-template <int MT, int KSTEPS, int NWN, int NWK>
+// XD = 0: X's K-chunk is staged once per workgroup in LDS (shared by the NWN
+// waves that own different weight rows). XD = 1: every wave loads its own X
+// fragments straight from global memory (L2-resident), which needs no LDS
+// and no barrier before the MFMAs.
+template <int MT, int KSTEPS, int NWN, int NWK, int XD>
 struct SkinnyCfg {
     static constexpr int kThreads = 64 * NWN * NWK;
     static constexpr int kRows = 16 * NWN;             // weight rows per workgroup
@@ -34,9 +43,9 @@ struct SkinnyCfg {
     static constexpr int kGroupK = kWaveK * NWK;       // K per workgroup
     static constexpr int kTokens = 16 * MT;
     static constexpr int kXStride = kGroupK + 8;       // LDS row stride (elements), 16 B pad
-    static constexpr int kXBytes = kTokens * kXStride * 2;
     static constexpr int kRedBytes = NWK > 1 ? (NWK - 1) * NWN * MT * 4 * 64 * 4 : 0;
-    static constexpr int kLdsBytes = kXBytes > kRedBytes ? kXBytes : kRedBytes;
+    // LDS for xrows staged token rows plus the cross-wave reduction buffer
+    static int lds_bytes(int xrows) { return (XD ? 0 : xrows * kXStride * 2) + kRedBytes; }
 };
 
 __device__ __forceinline__ void store_out4(const GemmArgs& a, int64_t m, int64_t n, const float* v) {
@@ -67,12 +76,14 @@ __device__ __forceinline__ void store_out4(const GemmArgs& a, int64_t m, int64_t
     }
 }
 
-template <int MT, int KSTEPS, int NWN, int NWK>
+template <int MT, int KSTEPS, int NWN, int NWK, int XD>
 __global__ void __launch_bounds__(64 * NWN * NWK)
-skinny_kernel(GemmArgs a, int splits, float* __restrict__ ws, unsigned* __restrict__ counters) {
-    using C = SkinnyCfg<MT, KSTEPS, NWN, NWK>;
+skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restrict__ ws,
+              unsigned* __restrict__ counters) {
+    using C = SkinnyCfg<MT, KSTEPS, NWN, NWK, XD>;
     extern __shared__ __align__(16) unsigned char smem[];
-    bf16_t* xs = reinterpret_cast<bf16_t*>(smem);
+    bf16_t* xs = reinterpret_cast<bf16_t*>(smem);                       // [xrows][kXStride]
+    float* red = reinterpret_cast<float*>(smem + (XD ? 0 : (size_t)xrows * C::kXStride * 2));
     __shared__ unsigned s_last;
 
     const int tid = threadIdx.x;
@@ -81,94 +92,133 @@ skinny_kernel(GemmArgs a, int splits, float* __restrict__ ws, unsigned* __restri
     const int wn = wave % NWN;
     const int wk = wave / NWN;
     const int64_t M = a.M, N = a.N, K = a.K;
-    const int64_t tile = blockIdx.x;
     const int split = blockIdx.y;
     const int64_t k_group = (int64_t)split * C::kGroupK;
-    const int64_t n_wave = tile * C::kRows + wn * 16;
+    int64_t tile = blockIdx.x;
 
     const bf16_t* __restrict__ X = reinterpret_cast<const bf16_t*>(a.x);
     const bf16_t* __restrict__ W = reinterpret_cast<const bf16_t*>(a.w);
 
-    // 1. Stage X[:, k_group : k_group + kGroupK] into registers (issued first so
-    //    that waiting for it does not wait for the weight stream).
-    constexpr int kXChunks = C::kTokens * (C::kGroupK / 8);
-    constexpr int kXPerThread = (kXChunks + C::kThreads - 1) / C::kThreads;
+    // 1. Stage X[0:xrows, k_group : k_group + kGroupK] into registers (issued
+    //    first so that waiting for it does not wait for the weight stream).
+    //    Only the xrows = min(M, 16 MT) real token rows are staged.
+    constexpr int kXPerThread = XD ? 1 : (C::kTokens * (C::kGroupK / 8) + C::kThreads - 1) / C::kThreads;
+    const int x_chunks = XD ? 0 : xrows * (C::kGroupK / 8);
     uint4 xr[kXPerThread];
+    if (!XD) {
 #pragma unroll
-    for (int j = 0; j < kXPerThread; ++j) {
-        const int c = tid + j * C::kThreads;
-        const int m = c / (C::kGroupK / 8);
-        const int kc = c % (C::kGroupK / 8);
-        const int64_t k = k_group + kc * 8;
-        xr[j] = make_uint4(0u, 0u, 0u, 0u);
-        if (c < kXChunks && m < M && k < K)
-            xr[j] = *reinterpret_cast<const uint4*>(X + (int64_t)m * K + k);
+        for (int j = 0; j < kXPerThread; ++j) {
+            const int c = tid + j * C::kThreads;
+            const int m = c / (C::kGroupK / 8);
+            const int kc = c % (C::kGroupK / 8);
+            const int64_t k = k_group + kc * 8;
+            xr[j] = make_uint4(0u, 0u, 0u, 0u);
+            if (c < x_chunks && k < K)
+                xr[j] = *reinterpret_cast<const uint4*>(X + (int64_t)m * K + k);
+        }
     }
 
-    // 2. Issue every weight load of this wave.
-    const int64_t n_lane = n_wave + (lane & 15);
+    // 2. Issue the first tile's weight loads (and, with XD, the wave's X
+    //    fragments, which are the same for every tile).
     const int64_t k_wave = k_group + (int64_t)wk * C::kWaveK + 8 * (lane >> 4);
     uint4 wr[KSTEPS];
+    auto load_w = [&](int64_t t, uint4* dst) {
+        const int64_t n_lane = t * C::kRows + wn * 16 + (lane & 15);
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        const int64_t k = k_wave + 32 * s;
-        wr[s] = make_uint4(0u, 0u, 0u, 0u);
-        if (n_lane < N && k < K)
-            wr[s] = ld_nt16(W + n_lane * K + k);
+        for (int s = 0; s < KSTEPS; ++s) {
+            const int64_t k = k_wave + 32 * s;
+            dst[s] = make_uint4(0u, 0u, 0u, 0u);
+            if (n_lane < N && k < K) {
+#if TP_SKINNY_W_NT
+                dst[s] = ld_nt16(W + n_lane * K + k);
+#else
+                dst[s] = *reinterpret_cast<const uint4*>(W + n_lane * K + k);
+#endif
+            }
+        }
+    };
+    load_w(tile, wr);
+    uint4 xd[XD ? KSTEPS : 1][XD ? MT : 1];
+    if (XD) {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int64_t m = 16 * mt + (lane & 15);
+                const int64_t k = k_wave + 32 * s;
+                xd[XD ? s : 0][XD ? mt : 0] = make_uint4(0u, 0u, 0u, 0u);
+                if (m < M && k < K)
+                    xd[XD ? s : 0][XD ? mt : 0] = *reinterpret_cast<const uint4*>(X + m * K + k);
+            }
     }
 
     // 3. X chunk -> LDS.
+    if (!XD) {
 #pragma unroll
-    for (int j = 0; j < kXPerThread; ++j) {
-        const int c = tid + j * C::kThreads;
-        if (c < kXChunks) {
-            const int m = c / (C::kGroupK / 8);
-            const int kc = c % (C::kGroupK / 8);
-            *reinterpret_cast<uint4*>(xs + m * C::kXStride + kc * 8) = xr[j];
-        }
-    }
-    __syncthreads();
-
-    // 4. MFMAs: acc[mt] holds D[n = 4*(lane/16) + i][m = 16*mt + lane%16].
-    f32x4_t acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int xcol = wk * C::kWaveK + 8 * (lane >> 4);
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, wr[s]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(xs + (16 * mt + (lane & 15)) * C::kXStride + xcol + 32 * s);
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, xv), acc[mt], 0, 0, 0);
-        }
-    }
-
-    // 5. Sum the NWK waves that share rows, in wave order, through LDS.
-    if (NWK > 1) {
-        __syncthreads();  // X chunk no longer needed: reuse its LDS
-        float* red = reinterpret_cast<float*>(smem);
-        if (wk > 0) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    red[((((wk - 1) * NWN + wn) * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
+        for (int j = 0; j < kXPerThread; ++j) {
+            const int c = tid + j * C::kThreads;
+            if (c < x_chunks) {
+                const int m = c / (C::kGroupK / 8);
+                const int kc = c % (C::kGroupK / 8);
+                *reinterpret_cast<uint4*>(xs + m * C::kXStride + kc * 8) = xr[j];
+            }
         }
         __syncthreads();
-        if (wk == 0) {
+    }
+
+    const int xcol = wk * C::kWaveK + 8 * (lane >> 4);
+    f32x4_t acc[MT];
+    for (;;) {
+        // Prefetch the next tile's weights (unsplit grids loop over tiles).
+        const int64_t next = tile + gridDim.x;
+        const bool has_next = splits == 1 && next < ntiles;
+        uint4 wnext[KSTEPS];
+        if (has_next) load_w(next, wnext);
+
+        // 4. MFMAs: acc[mt] holds D[n = 4*(lane/16) + i][m = 16*mt + lane%16].
 #pragma unroll
-            for (int w = 1; w < NWK; ++w)
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, wr[s]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                uint4 xv;
+                if (XD) {
+                    xv = xd[XD ? s : 0][XD ? mt : 0];
+                } else {
+                    const int m = 16 * mt + (lane & 15);
+                    xv = m < xrows ? *reinterpret_cast<const uint4*>(xs + m * C::kXStride + xcol + 32 * s)
+                                   : make_uint4(0u, 0u, 0u, 0u);
+                }
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, xv), acc[mt], 0, 0, 0);
+            }
+        }
+
+        // 5. Sum the NWK waves that share rows, in wave order, through LDS.
+        if (NWK > 1) {
+            if (wk > 0) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        acc[mt][i] += red[((((w - 1) * NWN + wn) * MT + mt) * 4 + i) * 64 + lane];
+                        red[((((wk - 1) * NWN + wn) * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
+            }
+            __syncthreads();
+            if (wk == 0) {
+#pragma unroll
+                for (int w = 1; w < NWK; ++w)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[mt][i] += red[((((w - 1) * NWN + wn) * MT + mt) * 4 + i) * 64 + lane];
+            }
+            __syncthreads();   // the buffer is rewritten for the next tile
         }
-    }
+        if (splits > 1) break;
 
-    const int64_t n_out = n_wave + 4 * (lane >> 4);   // first of this lane's 4 outputs
-    if (splits == 1) {
+        const int64_t n_out = tile * C::kRows + wn * 16 + 4 * (lane >> 4);
         if (wk == 0) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -179,10 +229,23 @@ skinny_kernel(GemmArgs a, int splits, float* __restrict__ ws, unsigned* __restri
                 }
             }
         }
-        return;
+        if (!has_next) return;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) wr[s] = wnext[s];
+        tile = next;
     }
 
-    // 6. K split across workgroups: publish this split's partial tile.
+    const int64_t n_out = tile * C::kRows + wn * 16 + 4 * (lane >> 4);   // first of this lane's 4 outputs
+
+    // 6. K split across workgroups. The partial tile is published with
+    //    relaxed device-scope atomic stores (global_store ... sc1: written
+    //    through to the device-coherent level, no read-modify-write) and read
+    //    back with relaxed device-scope atomic loads (sc1: never served from a
+    //    stale line of another XCD's L2). Each thread waits until its stores
+    //    are acknowledged before the barrier that precedes the arrival
+    //    counter, so the last workgroup to arrive sees every partial. No
+    //    agent-scope fence is used: on this GPU it writes back and
+    //    invalidates the whole L2 of the XCD, once per workgroup.
     if (wk == 0) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -191,19 +254,19 @@ skinny_kernel(GemmArgs a, int splits, float* __restrict__ ws, unsigned* __restri
                 float* p = ws + ((int64_t)split * M + m) * N;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (n_out + i < N) p[n_out + i] = acc[mt][i];
+                    if (n_out + i < N)
+                        __hip_atomic_store(p + n_out + i, acc[mt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
         const unsigned prev = atomicAdd(&counters[tile], 1u);
         s_last = (prev == (unsigned)(splits - 1)) ? 1u : 0u;
     }
     __syncthreads();
-    if (s_last == 0u) return;
-    __threadfence();
+    if (s_last != 1u) return;
 
     // 7. Last workgroup on this tile: sum the partials in split order.
     if (wk == 0) {
@@ -213,10 +276,11 @@ skinny_kernel(GemmArgs a, int splits, float* __restrict__ ws, unsigned* __restri
             if (m < M && n_out < N) {
                 float v[4] = {0.f, 0.f, 0.f, 0.f};
                 for (int sp = 0; sp < splits; ++sp) {
-                    const float* p = ws + ((int64_t)sp * M + m) * N;
+                    float* p = ws + ((int64_t)sp * M + m) * N;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (n_out + i < N) v[i] += __builtin_nontemporal_load(p + n_out + i);
+                        if (n_out + i < N)
+                            v[i] += __hip_atomic_load(p + n_out + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 store_out4(a, m, n_out, v);
             }
@@ -225,63 +289,115 @@ skinny_kernel(GemmArgs a, int splits, float* __restrict__ ws, unsigned* __restri
     if (tid == 0) atomicExch(&counters[tile], 0u);
 }
 
-typedef void (*SkinnyFn)(GemmArgs, int, float*, unsigned*);
+typedef void (*SkinnyFn)(GemmArgs, int, int64_t, int, float*, unsigned*);
+typedef int (*SkinnyLdsFn)(int);
 
 struct SkinnyEntry {
-    int mt, ksteps, nwn, nwk;
+    int mt, ksteps, nwn, nwk, xd;
     SkinnyFn fn;
     int threads;
-    int lds;
+    SkinnyLdsFn lds;
+    int group_k;
 };
 
-#define TP_SK(MT, KS, NN, NK)                                                        \
-    {MT, KS, NN, NK, skinny_kernel<MT, KS, NN, NK>, SkinnyCfg<MT, KS, NN, NK>::kThreads, \
-     SkinnyCfg<MT, KS, NN, NK>::kLdsBytes}
-#define TP_SK_MT(MT)                                                                  \
-    TP_SK(MT, 4, 4, 1), TP_SK(MT, 8, 4, 1), TP_SK(MT, 4, 2, 2), TP_SK(MT, 8, 2, 2),     \
-    TP_SK(MT, 4, 1, 4), TP_SK(MT, 8, 1, 4), TP_SK(MT, 4, 4, 2), TP_SK(MT, 8, 4, 2),     \
-    TP_SK(MT, 8, 4, 4), TP_SK(MT, 4, 4, 4)
+#define TP_SK(MT, KS, NN, NK, XD)                                                          \
+    {MT, KS, NN, NK, XD, skinny_kernel<MT, KS, NN, NK, XD>, SkinnyCfg<MT, KS, NN, NK, XD>::kThreads, \
+     SkinnyCfg<MT, KS, NN, NK, XD>::lds_bytes, SkinnyCfg<MT, KS, NN, NK, XD>::kGroupK}
+// M <= 16: every variant. M in (16, 64]: the ones that fit in registers.
+#define TP_SK_MT1                                                                                    \
+    TP_SK(1, 4, 4, 1, 0), TP_SK(1, 8, 4, 1, 0), TP_SK(1, 4, 2, 2, 0), TP_SK(1, 8, 2, 2, 0),             \
+    TP_SK(1, 4, 1, 4, 0), TP_SK(1, 8, 1, 4, 0), TP_SK(1, 4, 4, 2, 0), TP_SK(1, 8, 4, 2, 0),             \
+    TP_SK(1, 8, 4, 4, 0), TP_SK(1, 4, 4, 4, 0), TP_SK(1, 8, 1, 8, 0), TP_SK(1, 8, 2, 8, 0),             \
+    TP_SK(1, 4, 2, 8, 0), TP_SK(1, 4, 1, 16, 0), TP_SK(1, 8, 1, 16, 0), TP_SK(1, 16, 1, 8, 0),          \
+    TP_SK(1, 16, 2, 4, 0), TP_SK(1, 16, 4, 2, 0),                                                    \
+    TP_SK(1, 4, 1, 4, 1), TP_SK(1, 8, 1, 4, 1), TP_SK(1, 8, 1, 8, 1), TP_SK(1, 4, 1, 16, 1),            \
+    TP_SK(1, 8, 1, 16, 1), TP_SK(1, 16, 1, 8, 1), TP_SK(1, 4, 2, 8, 1), TP_SK(1, 20, 1, 8, 0)
+#define TP_SK_MTN(MT)                                                                                \
+    TP_SK(MT, 4, 4, 1, 0), TP_SK(MT, 8, 4, 1, 0), TP_SK(MT, 4, 2, 2, 0), TP_SK(MT, 8, 2, 2, 0),         \
+    TP_SK(MT, 4, 1, 4, 0), TP_SK(MT, 8, 1, 4, 0), TP_SK(MT, 4, 4, 2, 0), TP_SK(MT, 8, 4, 2, 0),         \
+    TP_SK(MT, 4, 4, 4, 0), TP_SK(MT, 4, 2, 8, 0), TP_SK(MT, 4, 1, 4, 1)
 
-const SkinnyEntry kSkinnyTable[] = {TP_SK_MT(1), TP_SK_MT(2), TP_SK_MT(4)};
-#undef TP_SK_MT
+const SkinnyEntry kSkinnyTable[] = {TP_SK_MT1, TP_SK_MTN(2), TP_SK_MTN(4)};
+#undef TP_SK_MT1
+#undef TP_SK_MTN
 #undef TP_SK
 
-const SkinnyEntry* find_skinny(const SkinnyPlan& p) {
-    for (const SkinnyEntry& e : kSkinnyTable)
-        if (e.mt == p.mt && e.ksteps == p.ksteps && e.nwn == p.nwn && e.nwk == p.nwk) return &e;
-    return nullptr;
+constexpr int kMaxLds = 160 * 1024 - 1024;   // dynamic LDS; the rest is the kernel's static LDS
+constexpr int kNumSkinny = sizeof(kSkinnyTable) / sizeof(kSkinnyTable[0]);
+int g_lds_attr[kNumSkinny] = {};            // dynamic LDS limit set so far per kernel
+int g_occupancy[kNumSkinny][2] = {};     // cached (lds bytes, workgroups per CU)
+int g_num_cus[16] = {};
+
+int find_skinny(const SkinnyPlan& p) {
+    for (int i = 0; i < kNumSkinny; ++i) {
+        const SkinnyEntry& e = kSkinnyTable[i];
+        if (e.mt == p.mt && e.ksteps == p.ksteps && e.nwn == p.nwn && e.nwk == p.nwk && e.xd == p.xd) return i;
+    }
+    return -1;
+}
+
+int xrows_for(const SkinnyEntry& e, int64_t M) { return (int)(M < 16 * e.mt ? M : 16 * e.mt); }
+
+SkinnyPlan make_plan(const SkinnyEntry& e, int64_t N, int64_t K) {
+    SkinnyPlan p{e.mt, e.ksteps, e.nwn, e.nwk, e.xd, 1, 1};
+    p.ntiles = (N + 16LL * e.nwn - 1) / (16LL * e.nwn);
+    p.splits = (int)((K + e.group_k - 1) / e.group_k);
+    return p;
 }
 
 }  // namespace
 
-bool skinny_variant_exists(const SkinnyPlan& p) { return find_skinny(p) != nullptr; }
+bool skinny_variant_exists(const SkinnyPlan& p) { return find_skinny(p) >= 0; }
 
-// Pick the decode kernel shape for one linear. The cost model counts HBM
-// bytes (the weight once, plus the fp32 partial round trip when K is split
-// across workgroups, plus a quarter weight for X re-reads from L2) and
-// divides by how well the grid fills the 256 CUs (at least 8 waves per CU).
+bool skinny_plan_fits(const SkinnyPlan& p, int64_t M) {
+    const int idx = find_skinny(p);
+    if (idx < 0) return false;
+    const SkinnyEntry& e = kSkinnyTable[idx];
+    return e.lds(xrows_for(e, M)) <= kMaxLds;
+}
+
+// Pick the decode kernel shape for one linear.
+//
+// M <= 16: one workgroup covers all of K for 16 weight rows (no exchange
+// between workgroups), choosing the variant whose K coverage fits K with the
+// least waste; on the measured MI355X sweep this beat every split-K variant at
+// the Llama-8B decode shapes (an exchange costs three serialized memory round
+// trips at the end of the kernel). Otherwise a cost model counts HBM bytes
+// (the weight once, the fp32 partial round trip when K is split across
+// workgroups, a quarter weight for X re-reads from L2) divided by how well the
+// grid fills the 256 CUs.
 SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
     const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    SkinnyPlan best{mt, 8, 4, 2, 1, 1};
+    if (mt == 1) {
+        struct Rule { int64_t kmax; int ks, nwn, nwk, xd; };
+        static const Rule rules[] = {
+            {512, 4, 1, 4, 1}, {1024, 8, 1, 4, 1}, {2048, 4, 1, 16, 0}, {4096, 8, 1, 16, 0},
+            {5120, 20, 1, 8, 0},
+        };
+        for (const Rule& r : rules) {
+            if (K > r.kmax) continue;
+            SkinnyPlan p{1, r.ks, r.nwn, r.nwk, r.xd, 1, 1};
+            const int idx = find_skinny(p);
+            if (idx >= 0 && skinny_plan_fits(p, M)) return make_plan(kSkinnyTable[idx], N, K);
+        }
+    }
+    SkinnyPlan best{mt, 8, 4, 2, 0, 1, 1};
     double best_cost = -1.0;
     for (const SkinnyEntry& e : kSkinnyTable) {
-        if (e.mt != mt) continue;
-        const int64_t rows = 16LL * e.nwn;
-        const int64_t gk = 32LL * e.ksteps * e.nwk;
-        const int64_t ntiles = (N + rows - 1) / rows;
-        const int64_t splits = (K + gk - 1) / gk;
-        if (splits > 1 && (splits * M * N > kSkinnyWsFloats || ntiles > kSkinnyWsCounters)) continue;
-        if (splits > 65535) continue;
-        const double wgs = (double)ntiles * (double)splits;
+        if (e.mt != mt || e.lds(xrows_for(e, M)) > kMaxLds) continue;
+        const SkinnyPlan p = make_plan(e, N, K);
+        if (p.splits > 1 && (p.splits * M * N > kSkinnyWsFloats || p.ntiles > kSkinnyWsCounters)) continue;
+        if (p.splits > 65535) continue;
+        const double wgs = (double)p.ntiles * (double)p.splits;
         double bytes = 2.0 * (double)N * (double)K;
-        if (splits > 1) bytes += 8.0 * (double)splits * (double)M * (double)N;
-        bytes += 0.25 * wgs * 16.0 * mt * (double)gk * 2.0;
+        if (p.splits > 1) bytes += 8.0 * (double)p.splits * (double)M * (double)N;
+        bytes += 0.25 * wgs * 16.0 * mt * (double)e.group_k * 2.0;
         double fill = wgs * e.threads / (256.0 * 512.0);
         if (fill > 1.0) fill = 1.0;
         const double cost = bytes / fill;
         if (best_cost < 0.0 || cost < best_cost) {
             best_cost = cost;
-            best = SkinnyPlan{mt, e.ksteps, e.nwn, e.nwk, (int)splits, ntiles};
+            best = p;
         }
     }
     return best;
@@ -292,15 +408,44 @@ int64_t skinny_workspace_floats(const SkinnyPlan& p, int64_t M, int64_t N) {
 }
 
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace& ws, hipStream_t s) {
-    const SkinnyEntry* e = find_skinny(p);
-    if (e == nullptr) return hipErrorInvalidValue;
-    if (e->lds > 65536) {
+    const int idx = find_skinny(p);
+    if (idx < 0) return hipErrorInvalidValue;
+    const SkinnyEntry* e = &kSkinnyTable[idx];
+    const int xrows = xrows_for(*e, a.M);
+    const int lds = e->lds(xrows);
+    if (lds > kMaxLds) return hipErrorInvalidValue;
+    if (lds > 65536 && lds > g_lds_attr[idx]) {
         const hipError_t ae = hipFuncSetAttribute(reinterpret_cast<const void*>(e->fn),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, e->lds);
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (ae != hipSuccess) return ae;
+        g_lds_attr[idx] = lds;
     }
-    dim3 grid((unsigned)p.ntiles, (unsigned)p.splits);
-    hipLaunchKernelGGL(e->fn, grid, dim3(e->threads), e->lds, s, a, p.splits, ws.partials, ws.counters);
+    int64_t grid_x = p.ntiles;
+    if (p.splits == 1) {
+        // Unsplit: as many workgroups as fit on the GPU at once, each looping
+        // over row tiles (X is staged once per workgroup).
+        int dev = 0;
+        hipError_t he = hipGetDevice(&dev);
+        if (he != hipSuccess) return he;
+        if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
+        if (g_num_cus[dev] == 0) {
+            he = hipDeviceGetAttribute(&g_num_cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+            if (he != hipSuccess) return he;
+        }
+        if (g_occupancy[idx][0] != lds || g_occupancy[idx][1] == 0) {
+            int per_cu = 0;
+            he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(e->fn),
+                                                              e->threads, lds);
+            if (he != hipSuccess) return he;
+            g_occupancy[idx][0] = lds;
+            g_occupancy[idx][1] = per_cu > 0 ? per_cu : 1;
+        }
+        const int64_t cap = (int64_t)g_occupancy[idx][1] * g_num_cus[dev];
+        if (grid_x > cap) grid_x = cap;
+    }
+    dim3 grid((unsigned)grid_x, (unsigned)p.splits);
+    hipLaunchKernelGGL(e->fn, grid, dim3(e->threads), lds, s, a, p.splits, p.ntiles, xrows, ws.partials,
+                       ws.counters);
     return hipGetLastError();
 }
 

@@ -65,6 +65,7 @@ struct SkinnyPlan {
     int ksteps;      // 32-wide k steps per wave
     int nwn;         // waves along N per workgroup (16 rows each)
     int nwk;         // waves along K per workgroup
+    int xd;          // 1: X fragments loaded per wave from global; 0: X staged in LDS
     int splits;      // workgroups along K
     int64_t ntiles;  // workgroups along N
 };
@@ -75,6 +76,7 @@ constexpr int64_t kSkinnyWsCounters = 65536;
 
 SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K);
 bool skinny_variant_exists(const SkinnyPlan& p);
+bool skinny_plan_fits(const SkinnyPlan& p, int64_t M);   // LDS need for M tokens within limits
 int64_t skinny_workspace_floats(const SkinnyPlan& p, int64_t M, int64_t N);
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace& ws, hipStream_t s);
 

@@ -17,7 +17,9 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpshard.so")
+# TPSHARD_LIB may name another build of the same library (e.g. a tuning build).
+_LIB_PATH = os.environ.get("TPSHARD_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libtpshard.so")
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
@@ -74,7 +76,7 @@ _PROTOS = {
     "tp_vocab_embed": (_int, [_vp, _i64, _vp, _i64, _int, _int, _i64, _vp, _vp]),
     "tp_lm_head_shard": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp]),
     "tp_concat_logits": (_int, [_ptr_array, _int, _i64, _i64, _i64, _int, _vp, _vp]),
-    "tp_tune_skinny": (_int, [_int, _int, _int]),
+    "tp_tune_skinny": (_int, [_int, _int, _int, _int]),
 }
 for _name, (_res, _args) in _PROTOS.items():
     _f = getattr(_lib, _name)
@@ -171,8 +173,8 @@ def tp_kv_heads_of_rank(cfg, t, rank):
     return f.value, c.value
 
 
-def tp_tune_skinny(ksteps=0, nwn=0, nwk=0):
-    _check(_lib.tp_tune_skinny(ksteps, nwn, nwk), "tp_tune_skinny")
+def tp_tune_skinny(ksteps=0, nwn=0, nwk=0, x_direct=0):
+    _check(_lib.tp_tune_skinny(ksteps, nwn, nwk, x_direct), "tp_tune_skinny")
 
 
 # ------------------------------------------------------------ device calls

@@ -152,6 +152,7 @@ def test_elementwise_validation_before_any_hip_call():
 
 
 def test_tune_rejects_unbuilt_variants():
-    assert C.tp_tune_skinny(3, 4, 2) == -2
-    assert C.tp_tune_skinny(8, 4, 2) == 0
-    assert C.tp_tune_skinny(0, 0, 0) == 0
+    assert C.tp_tune_skinny(3, 4, 2, 0) == -2
+    assert C.tp_tune_skinny(8, 4, 2, 0) == 0
+    assert C.tp_tune_skinny(8, 1, 16, 1) == 0
+    assert C.tp_tune_skinny(0, 0, 0, 0) == 0

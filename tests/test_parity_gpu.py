@@ -81,12 +81,18 @@ def test_linear_exact_integer_mode(M, N, K):
     assert np.array_equal(bits(yb), oracle.bf16_bits(oracle.round_bf16(ref)))
 
 
-SKINNY_VARIANTS = [(ks, nn, nk) for ks in (4, 8) for (nn, nk) in ((4, 1), (2, 2), (1, 4), (4, 2), (4, 4))]
+# every decode-kernel variant the library builds: (ksteps, nwn, nwk, x_direct)
+SKINNY_VARIANTS = (
+    [v + (0,) for v in [(4, 4, 1), (8, 4, 1), (4, 2, 2), (8, 2, 2), (4, 1, 4), (8, 1, 4), (4, 4, 2), (8, 4, 2),
+                        (8, 4, 4), (4, 4, 4), (8, 1, 8), (8, 2, 8), (4, 2, 8), (4, 1, 16), (8, 1, 16),
+                        (16, 1, 8), (16, 2, 4), (16, 4, 2)]]
+    + [v + (1,) for v in [(4, 1, 4), (8, 1, 4), (8, 1, 8), (4, 1, 16), (8, 1, 16), (16, 1, 8), (4, 2, 8)]]
+    + [(20, 1, 8, 0)])
 
 
-@pytest.mark.parametrize("ks,nn,nk", SKINNY_VARIANTS)
-def test_every_decode_kernel_variant_exact_and_deterministic(ks, nn, nk):
-    lib.tp_tune_skinny(ks, nn, nk)
+@pytest.mark.parametrize("ks,nn,nk,xd", SKINNY_VARIANTS)
+def test_every_decode_kernel_variant_exact_and_deterministic(ks, nn, nk, xd):
+    lib.tp_tune_skinny(ks, nn, nk, xd)
     try:
         for (M, N, K) in [(16, 768, 4096), (64, 200, 1032), (3, 50, 520), (40, 96, 8192)]:
             x = I.small_int_bf16((SEED, 3, M, N, K), (M, K))
@@ -104,9 +110,27 @@ def test_every_decode_kernel_variant_exact_and_deterministic(ks, nn, nk):
             lib.tp_row_linear_partial(xr, wr, y1)
             lib.tp_row_linear_partial(xr, wr, y2)
             assert torch.equal(y1, y2)
-            assert_close(f64(y1), oracle.linear(f64(xr.cpu()), f64(wr.cpu())), f"variant {(ks, nn, nk)} {(M, N, K)}")
+            assert_close(f64(y1), oracle.linear(f64(xr.cpu()), f64(wr.cpu())), f"variant {(ks, nn, nk, xd)} {(M, N, K)}")
     finally:
-        lib.tp_tune_skinny(0, 0, 0)
+        lib.tp_tune_skinny(0, 0, 0, 0)
+
+
+def test_split_k_partials_are_never_stale():
+    """Heavily split variants reuse one workspace call after call: every call
+    gets new inputs, so a partial read before its writer's store was visible
+    (a stale value from the previous call) would break exactness."""
+    for variant in [(4, 4, 1, 0), (4, 2, 2, 0), (8, 4, 2, 0)]:
+        lib.tp_tune_skinny(*variant)
+        try:
+            for it in range(6):
+                M, N, K = (16, 1000, 4096) if it % 2 == 0 else (40, 777, 2056)
+                x = I.small_int_bf16((SEED, 30, it) + variant, (M, K))
+                w = I.small_int_bf16((SEED, 31, it) + variant, (N, K))
+                y = empty((M, N), torch.float32)
+                lib.tp_row_linear_partial(dev(x), dev(w), y)
+                assert np.array_equal(f64(y), oracle.linear(f64(x), f64(w))), (variant, it)
+        finally:
+            lib.tp_tune_skinny(0, 0, 0, 0)
 
 
 # ------------------------------------------------ linears, random tolerance
