@@ -1,6 +1,7 @@
 """Benchmark of one tensor-parallel rank's share of the linear path on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--eager]
+    python bench.py --summarize-trace PATH/TO/kernel_trace.csv
 
 A step is one pass of the whole path over one batch of synthetic tokens, for
 one rank r = 0 of a t-way split, with every input already resident in HBM:
@@ -25,9 +26,9 @@ calls issued eagerly from Python are timed too (`eager_ms_per_step`).
 Prints ONE JSON line (the driver's contract). `value` is the shard-GEMM
 TFLOP/s of the whole step: the flops of every shard GEMM in the step divided
 by the time of the step. `roofline` is that of the decode-linear kernel (the
-dominant one): each op's launches of one step are captured into a graph of
-their own and replayed K times between HIP events on the replaying stream,
-giving the average duration per launch. `cpu_baseline` is the float64 CPU
+dominant one): each op's launches of one step (repeated to at least 32
+launches) are captured into a graph of their own and replayed K times between
+HIP events on the replaying stream, giving the average duration per launch. `cpu_baseline` is the float64 CPU
 oracle on a bounded sample of the same per-rank work.
 """
 
@@ -84,6 +85,13 @@ class Rank:
 
         self.shapes = {k: lib.tp_shard_shape(cfg, t, k) for k in lib.KIND}
         self.layers = []
+        # Peers' partial sums for the two all-reduce sites: distinct per layer
+        # while small (so no cache holds them across layers); shared by all
+        # layers when a buffer is larger than 8 MiB (no cache can hold those).
+        shared_peers = M * H * 2 > (8 << 20)
+        if shared_peers:
+            peers_o = [dn((M, H), 0.5, 10 + j) for j in range(t - 1)]
+            peers_d = [dn((M, H), 0.5, 40 + j) for j in range(t - 1)]
         for l in range(L):
             s = 100 * (l + 1)
             self.layers.append({
@@ -92,9 +100,8 @@ class Rank:
                 "gate_up": dn(self.shapes["gate_up"], 0.02, s + 3),
                 "down": dn(self.shapes["down"], 0.02, s + 4),
                 "ctx": dn((M, self.shapes["o"][1]), 1.0, s + 5),
-                # peers' partial sums for the two all-reduce sites
-                "peers_o": [dn((M, H), 0.5, s + 10 + j) for j in range(t - 1)],
-                "peers_d": [dn((M, H), 0.5, s + 40 + j) for j in range(t - 1)],
+                "peers_o": peers_o if shared_peers else [dn((M, H), 0.5, s + 10 + j) for j in range(t - 1)],
+                "peers_d": peers_d if shared_peers else [dn((M, H), 0.5, s + 40 + j) for j in range(t - 1)],
             })
         self.x = dn((M, H), 1.0, 7)
         self.qkv = torch.empty((M, self.shapes["qkv"][0]), dtype=bf, device=dev)
@@ -174,8 +181,9 @@ def run_ops(ops, only=None):
             fn(*args)
 
 
-def capture(torch, ops, only=None):
-    """HIP graph of the step's launches (or of one op's launches)."""
+def capture(torch, ops, only=None, repeat=1):
+    """HIP graph of the step's launches (or of one op's launches, `repeat`
+    times over)."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -183,7 +191,8 @@ def capture(torch, ops, only=None):
         run_ops(ops, only)            # per-stream workspace is allocated before capture
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
-            run_ops(ops, only)
+            for _ in range(repeat):
+                run_ops(ops, only)
     torch.cuda.synchronize()
     return g
 
@@ -200,6 +209,20 @@ def time_graph(torch, g, reps, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps
+
+
+def pages_context(w):
+    """The traffic the pages estimate for this workload's all-reduces and
+    logits all-gather (arithmetic only; the pages measure nothing)."""
+    from megatron_sharded_linears_amd import traffic as T
+    one, total = T.per_step(w.tokens, w.hidden, w.layers)
+    ctx = {"all_reduces_per_forward": T.all_reduces_per_forward(w.layers),
+           "all_reduce_payload_KiB": one / T.KIB, "all_reduce_payload_per_forward_MiB": round(total / T.MIB, 2),
+           "ring_sent_per_rank_per_token_KiB": T.ring_sent_per_rank_per_token(w.hidden, w.layers, w.t) / T.KIB}
+    if w.has_vocab:
+        ctx["logits_gather_received_per_sampled_token_KiB"] = round(
+            T.logits_gather_received_per_token(w.vocab, w.t) / T.KIB, 1)
+    return ctx
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -251,7 +274,33 @@ def cpu_baseline(w, seconds):
 
 # ------------------------------------------------------------------- main
 
+def summarize_trace(path, top=30):
+    """Per (kernel, workgroups) duration stats from a rocprofv3
+    --kernel-trace --output-format csv trace: a row per distinct launch shape,
+    so each op of the step can be matched to its kernel."""
+    import csv
+    import re
+    groups = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            m = re.search(r"(\w+_kernel)(<[^>]*>)?", name)
+            short = (m.group(1) + (m.group(2) or "")) if m else name[:60]
+            wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+            wgs = (int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]), int(r["Grid_Size_Y"]) // int(r["Workgroup_Size_Y"]))
+            d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            groups.setdefault((short, wgs, wg), []).append(d)
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]
+    print(f"{'kernel':44s} {'workgroups':>12s} {'threads':>7s} {'calls':>6s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} {'total_ms':>9s}")
+    for (short, wgs, wg), ds in rows:
+        print(f"{short[:44]:44s} {str(wgs):>12s} {wg:7d} {len(ds):6d} {sum(ds) / len(ds) / 1e3:8.2f} "
+              f"{min(ds) / 1e3:8.2f} {max(ds) / 1e3:8.2f} {sum(ds) / 1e6:9.2f}")
+
+
 def main():
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-trace":
+        summarize_trace(sys.argv[2])
+        return
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: every shard of the t-way split is computed on that one "
@@ -307,11 +356,12 @@ def main():
     # --- per kernel: each op's launches of one step, captured and replayed K times
     per_op = {}
     for name in names:
-        g = capture(torch, ops, only=name)
+        n_per_step, flops, byts = work[name]
+        repeat = max(1, -(-32 // n_per_step))   # at least 32 launches per replay
+        g = capture(torch, ops, only=name, repeat=repeat)
         ms = time_graph(torch, g, args.steps, 2)
         del g
-        n_per_step, flops, byts = work[name]
-        us = ms * 1e3 / n_per_step
+        us = ms * 1e3 / (n_per_step * repeat)
         per_op[name] = {"launches_per_step": n_per_step, "us_per_launch": round(us, 3),
                         "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                         "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2) if flops else None,
@@ -324,6 +374,17 @@ def main():
     gemm_bytes_step = sum(work[k][0] * work[k][2] for k in gemm_ops)
     achieved = gemm_bytes_step / (gemm_us * 1e-6) / 1e9
     red = per_op["reduce"]
+    if w.tokens <= 64:
+        roofline = {"bound": "hbm", "kernel": "decode linear (skinny_kernel), all launches of a step",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "launches_per_step": sum(work[k][0] for k in gemm_ops), "us_per_step": round(gemm_us, 2)}
+    else:
+        tflops = flops_step / (gemm_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": "prefill linear (tiled_kernel), all launches of a step",
+                    "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "launches_per_step": sum(work[k][0] for k in gemm_ops), "us_per_step": round(gemm_us, 2)}
 
     line = {
         "metric": METRIC,
@@ -344,11 +405,7 @@ def main():
                    "vocab": w.vocab if w.has_vocab else None, "lm_positions": w.lm_positions if w.has_vocab else 0,
                    "parallelism": f"tp{w.t} rank share on 1 GPU",
                    "execution": "eager launches" if args.eager else "HIP graph of the step"},
-        "roofline": {"bound": "hbm", "kernel": "decode linear (skinny_kernel), all launches of a step",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "launches_per_step": sum(work[k][0] for k in gemm_ops),
-                     "us_per_step": round(gemm_us, 2)},
+        "roofline": roofline,
         "reduce": {"GBps": red["GBps"], "frac": round(red["GBps"] / HBM_PEAK_GBPS, 4),
                    "us_per_call": red["us_per_launch"], "calls_per_step": work["reduce"][0],
                    "bytes_per_call": work["reduce"][2]},
@@ -357,6 +414,7 @@ def main():
         "step_GBps": round(sum(n * b for n, _, b in work.values()) / (ms_step * 1e-3) / 1e9, 1),
         "per_op": per_op,
         "wall_s_timed": round(wall_s, 3),
+        "pages_context": pages_context(w),
     }
 
     if not args.no_cpu:
