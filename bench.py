@@ -143,7 +143,9 @@ class Rank:
         if self.vocab:
             Ms, vs = self.hs_rows, self.vs
             ops["lm_head"] = (1, gemm_flops(Ms, vs, H), gemm_bytes(Ms, vs, H))
-            ops["embed"] = (1, 0, 4 * M + 2 * H * M + 2 * M * H)   # upper bound: every id owned
+            lo, hi = 0, min(self.vs, w.vocab)                        # rank 0's vocab range
+            owned = int(((self.ids >= lo) & (self.ids < hi)).sum().item())
+            ops["embed"] = (1, 0, 4 * M + 2 * H * owned + 2 * M * H)
             ops["embed_reduce"] = (1, 0, (2 * t + 2) * M * H)
             ops["concat"] = (1, 0, 4 * Ms * w.vocab)
         return ops

@@ -386,4 +386,10 @@ int tp_tune_skinny(int ksteps, int nwn, int nwk, int x_direct) {
     return TP_OK;
 }
 
+int tp_tune_tiled(int variant) {
+    if (variant < -1 || variant >= tpk::tiled_variant_count()) return TP_ERR_RANGE;
+    tpk::tiled_force_variant(variant);
+    return TP_OK;
+}
+
 }  // extern "C"

@@ -4,7 +4,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace tpk {
+
+// Compile-time loop: f(std::integral_constant<int, 0>{}), ..., up to N - 1.
+// Register-resident arrays indexed through it see constant indices from the
+// start, so they are never demoted to scratch memory.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // bf16 is handled as raw 16-bit patterns in memory.
 typedef uint16_t bf16_t;

@@ -1,15 +1,25 @@
 // Prefill-sized linear on gfx950: Y[M, N] = X[M, K] W[N, K]^T (+ bias) with
-// M > 64 tokens. These shard GEMMs are dense contractions well above the
-// MI355X ridge point, so they are bound by the bf16 matrix cores.
+// M > 64 tokens. These shard GEMMs are dense contractions far above the
+// MI355X ridge point (~315 flop/B), so they are bound by the bf16 matrix
+// cores (2.5 PFLOP/s dense).
 //
-// Tiling: a 256-thread workgroup owns a 128 (tokens) x 128 (weight rows)
-// output tile and walks K in steps of 64. Both operands are K-contiguous; each
-// k-tile of X and W is copied global -> VGPR -> LDS (rows padded by 16 bytes
-// so the 16 lanes of an MFMA operand read hit distinct banks), double
-// buffered so the next tile's global loads are in flight while the current
-// one feeds the MFMAs. Each wave computes a 64 x 64 block as 4 x 4
-// v_mfma_f32_16x16x32_bf16 with W as the A operand, so each lane ends with 4
-// consecutive outputs of one token row.
+// Common to both kernels:
+//   * v_mfma_f32_32x32x16_bf16 with W as the A operand (32 weight rows) and
+//     X as the B operand (32 tokens): D[n][m] = Y[m][n].
+//   * A workgroup owns a BN (weight rows) x BM (tokens) tile, split over
+//     2 x WGM waves; each wave owns (BN/2) x (BM/WGM) as a grid of 32 x 32
+//     MFMA blocks whose accumulators stay in registers (every access to them
+//     uses compile-time indices).
+//   * Tiles are numbered so that each of the 8 XCDs (workgroup id mod 8)
+//     gets a contiguous range, walked with the token tile fastest: the W
+//     k-slices of a range stay in that XCD's L2 while its CUs reuse them.
+//   * Epilogue: accumulators go through LDS one block row at a time, then all
+//     threads write rows of Y in 16-byte runs (bias added there).
+//
+// tiled_dma_kernel (K % 32 == 0): k-tiles of 32 land in LDS by direct
+// global -> LDS loads in a 4-stage ring (details below). tiled_reg_kernel
+// (any K % 8 == 0): k-tiles of 64 go global -> VGPR -> LDS, double buffered,
+// 128-byte rows XOR-swizzled by (row / 2) mod 8.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,13 +27,26 @@ namespace tpk {
 
 namespace {
 
-constexpr int kBM = 128;   // tokens per tile
-constexpr int kBN = 128;   // weight rows per tile
-constexpr int kBK = 64;    // K per stage
-constexpr int kStride = kBK + 8;               // LDS row stride in elements
-constexpr int kThreads = 256;
-constexpr int kChunksPerThread = kBM * (kBK / 8) / kThreads;   // 4 (same for W)
-constexpr int kStageElems = (kBM + kBN) * kStride;
+constexpr int kBK = 64;         // K per stage
+constexpr int kThreads = 256;   // 4 waves, 2 x 2
+constexpr int kXcds = 8;
+
+template <int BN, int BM>
+struct TileCfg {
+    static constexpr int kWN = BN / 2;           // weight rows per wave
+    static constexpr int kWM = BM / 2;           // tokens per wave
+    static constexpr int kBlkN = kWN / 32;       // 32x32 blocks per wave along N
+    static constexpr int kBlkM = kWM / 32;
+    static constexpr int kWChunks = BN * (kBK / 8) / kThreads;   // 16-B loads per thread per k-tile
+    static constexpr int kXChunks = BM * (kBK / 8) / kThreads;
+    static constexpr int kStageElems = (BN + BM) * kBK;
+    static constexpr int kLdsBytes = 2 * kStageElems * 2;
+};
+
+// Element offset of (row, 16-byte chunk c) in a [rows][64] bf16 LDS tile.
+__device__ __forceinline__ int swz(int row, int c) {
+    return row * kBK + ((c ^ ((row >> 1) & 7)) << 3);
+}
 
 __device__ __forceinline__ void store_out4(const GemmArgs& a, int64_t m, int64_t n, const float* v) {
     float o[4];
@@ -46,107 +69,400 @@ __device__ __forceinline__ void store_out4(const GemmArgs& a, int64_t m, int64_t
     }
 }
 
-__global__ void __launch_bounds__(kThreads)
-tiled_kernel(GemmArgs a) {
-    __shared__ __align__(16) bf16_t lds[2 * kStageElems];
+template <int BN, int BM>
+__global__ void __launch_bounds__(kThreads, 1)
+tiled_reg_kernel(GemmArgs a, int tiles_n, int tiles_m) {
+    using C = TileCfg<BN, BM>;
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    bf16_t* lds = reinterpret_cast<bf16_t*>(lds_raw);
+
+    // XCD-aware tile order: workgroups id, id + 8, id + 16, ... run on one XCD;
+    // give each XCD a contiguous range of tiles, token tile fastest.
+    const int ntiles = tiles_n * tiles_m;
+    const int per_xcd = (ntiles + kXcds - 1) / kXcds;
+    const int t = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (t >= ntiles) return;
+    const int tile_n = t / tiles_m;
+    const int tile_m = t % tiles_m;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1;      // token half
-    const int wn = wave & 1;       // weight-row half
+    const int wn = wave >> 1;
+    const int wm = wave & 1;
     const int64_t M = a.M, N = a.N, K = a.K;
-    const int64_t n0 = (int64_t)blockIdx.x * kBN;
-    const int64_t m0 = (int64_t)blockIdx.y * kBM;
+    const int64_t n0 = (int64_t)tile_n * BN;
+    const int64_t m0 = (int64_t)tile_m * BM;
     const bf16_t* __restrict__ X = reinterpret_cast<const bf16_t*>(a.x);
     const bf16_t* __restrict__ W = reinterpret_cast<const bf16_t*>(a.w);
 
-    uint4 xr[kChunksPerThread], wr[kChunksPerThread];
+    // Global -> VGPR staging of one k-tile. Thread tid loads chunk tid % 8 of
+    // rows tid / 8 + 32 j: 8 consecutive lanes cover one 128-byte row segment.
+    const int crow = tid >> 3;
+    const int cchunk = tid & 7;
+    u32x4_t wr[C::kWChunks], xr[C::kXChunks];     // native vectors: kept in VGPRs
+#define TP_TILED_LOAD(K0)                                                                   \
+    do {                                                                                    \
+        const int64_t k_ = (K0) + cchunk * 8;                                               \
+        const bool kin_ = k_ < K;                                                           \
+        _Pragma("unroll") for (int j = 0; j < C::kWChunks; ++j) {                           \
+            const int64_t r_ = n0 + crow + 32 * j;                                          \
+            wr[j] = u32x4_t{0u, 0u, 0u, 0u};                                                \
+            if (kin_ && r_ < N) wr[j] = *reinterpret_cast<const u32x4_t*>(W + r_ * K + k_); \
+        }                                                                                   \
+        _Pragma("unroll") for (int j = 0; j < C::kXChunks; ++j) {                           \
+            const int64_t r_ = m0 + crow + 32 * j;                                          \
+            xr[j] = u32x4_t{0u, 0u, 0u, 0u};                                                \
+            if (kin_ && r_ < M) xr[j] = *reinterpret_cast<const u32x4_t*>(X + r_ * K + k_); \
+        }                                                                                   \
+    } while (0)
+#define TP_TILED_STORE(STAGE)                                                               \
+    do {                                                                                    \
+        bf16_t* ws_ = lds + (STAGE) * C::kStageElems;                                       \
+        bf16_t* xs_ = ws_ + BN * kBK;                                                       \
+        _Pragma("unroll") for (int j = 0; j < C::kWChunks; ++j)                             \
+            *reinterpret_cast<u32x4_t*>(ws_ + swz(crow + 32 * j, cchunk)) = wr[j];          \
+        _Pragma("unroll") for (int j = 0; j < C::kXChunks; ++j)                             \
+            *reinterpret_cast<u32x4_t*>(xs_ + swz(crow + 32 * j, cchunk)) = xr[j];          \
+    } while (0)
 
-    auto load_tile = [&](int64_t k0) {
+    f32x16_t acc[C::kBlkN][C::kBlkM];
+    static_for<C::kBlkN>([&](auto i) {
+        static_for<C::kBlkM>([&](auto j) { acc[i][j] = f32x16_t{}; });
+    });
+
+    const int ktiles = (int)((K + kBK - 1) / kBK);
+    TP_TILED_LOAD(0);
+    TP_TILED_STORE(0);
+    __syncthreads();
+    if (ktiles > 1) TP_TILED_LOAD(kBK);
+
+    // Operand reads: lane reads row (lane % 32) of a 32-row block, logical
+    // chunk 2 s + lane / 32 for k16 step s. Fragments are double buffered:
+    // the reads of step s + 1 are issued before the MFMAs of step s, so LDS
+    // latency hides under 16 (at 256 x 256) back-to-back MFMAs.
+    const int orow = lane & 31;
+    const int ohalf = lane >> 5;
+    bf16x8_t fa[2][C::kBlkN], fb[2][C::kBlkM];
+    auto read_frags = [&](auto buf, const bf16_t* ws, const bf16_t* xs, int s) {
+        const int c = 2 * s + ohalf;
+        static_for<C::kBlkN>([&](auto i) {
+            fa[buf][i] = __builtin_bit_cast(bf16x8_t,
+                *reinterpret_cast<const u32x4_t*>(ws + swz(wn * C::kWN + i * 32 + orow, c)));
+        });
+        static_for<C::kBlkM>([&](auto j) {
+            fb[buf][j] = __builtin_bit_cast(bf16x8_t,
+                *reinterpret_cast<const u32x4_t*>(xs + swz(wm * C::kWM + j * 32 + orow, c)));
+        });
+    };
+    read_frags(std::integral_constant<int, 0>{}, lds, lds + BN * kBK, 0);
+    for (int kt = 0; kt < ktiles; ++kt) {
+        const bf16_t* ws = lds + (kt & 1) * C::kStageElems;
+        const bf16_t* xs = ws + BN * kBK;
+        static_for<kBK / 16>([&](auto s) {
+            constexpr int cur = s & 1;
+            if constexpr (s + 1 < kBK / 16) read_frags(std::integral_constant<int, cur ^ 1>{}, ws, xs, s + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<C::kBlkN>([&](auto i) {
+                static_for<C::kBlkM>([&](auto j) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+                });
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if (kt + 1 < ktiles) TP_TILED_STORE((kt + 1) & 1);
+        __syncthreads();
+        if (kt + 2 < ktiles) TP_TILED_LOAD((int64_t)(kt + 2) * kBK);
+        if (kt + 1 < ktiles) {
+            const bf16_t* wn_ = lds + ((kt + 1) & 1) * C::kStageElems;
+            read_frags(std::integral_constant<int, 0>{}, wn_, wn_ + BN * kBK, 0);
+        }
+    }
+
+    // Epilogue, one block row i at a time. acc[i][j][e] holds D row (weight
+    // row) 8 (e / 4) + 4 (lane / 32) + e % 4 and column (token) lane % 32 of
+    // block (i, j). The accumulators go to LDS with constant indices (so they
+    // stay in registers), as slab[wn][token][32 rows], then all 256 threads
+    // write rows of Y with 16-byte runs.
+    float* slab = reinterpret_cast<float*>(lds);
+    constexpr int kSlabStride = 36;                     // floats per token row (32 + pad)
+    static_for<C::kBlkN>([&](auto i) {
+        static_for<C::kBlkM>([&](auto j) {
+            const int mt = wm * C::kWM + j * 32 + (lane & 31);
+            static_for<4>([&](auto g) {
+                const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                *reinterpret_cast<f32x4_t*>(slab + (wn * BM + mt) * kSlabStride + 8 * g + 4 * (lane >> 5)) = v;
+            });
+        });
+        __syncthreads();
+        // 2 slabs x BM tokens x 8 runs of 4 rows
+        constexpr int kRuns = 2 * BM * 8;
+        static_assert(kRuns % kThreads == 0, "store loop must divide evenly");
 #pragma unroll
-        for (int j = 0; j < kChunksPerThread; ++j) {
-            const int c = tid + j * kThreads;
-            const int r = c >> 3;
-            const int64_t k = k0 + (c & 7) * 8;
-            xr[j] = make_uint4(0u, 0u, 0u, 0u);
-            wr[j] = make_uint4(0u, 0u, 0u, 0u);
-            if (k < K) {
-                if (m0 + r < M) xr[j] = *reinterpret_cast<const uint4*>(X + (m0 + r) * K + k);
-                if (n0 + r < N) wr[j] = *reinterpret_cast<const uint4*>(W + (n0 + r) * K + k);
+        for (int it = 0; it < kRuns / kThreads; ++it) {
+            const int q = tid + it * kThreads;
+            const int half = q / (BM * 8);
+            const int rem = q - half * (BM * 8);
+            const int mt = rem >> 3;
+            const int run = rem & 7;
+            const int64_t m = m0 + mt;
+            const int64_t n = n0 + half * C::kWN + i * 32 + 4 * run;
+            if (m < M && n < N) {
+                const float4 v = *reinterpret_cast<const float4*>(slab + (half * BM + mt) * kSlabStride + 4 * run);
+                float o[4] = {v.x, v.y, v.z, v.w};
+                store_out4(a, m, n, o);
             }
         }
+        __syncthreads();
+    });
+}
+
+#undef TP_TILED_LOAD
+#undef TP_TILED_STORE
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant (K % 32 == 0): k-tiles of 32 land in LDS through
+// global_load_lds_dwordx4 (no VGPR staging) in a ring of NS stages issued
+// NS - 1 k-tiles ahead, so global latency hides behind several k-tiles of
+// MFMAs. Waits are explicit: s_waitcnt vmcnt(n) for this wave's own DMA, then
+// s_barrier (not __syncthreads, whose release fence would wait for every
+// outstanding DMA). Each iteration reads the step-1 fragments, runs the
+// step-0 MFMAs, crosses the barrier for the next stage, issues the DMA three
+// stages ahead into the slot freed by the previous iteration, reads the next
+// stage's step-0 fragments and runs the step-1 MFMAs.
+// LDS stage: W tile [BN][32] then X tile [BM][32], 64-byte rows, 16-byte
+// chunks XOR-swizzled by (row / 4) mod 4; a lane's DMA destination is fixed
+// (wave base + 16 * lane), so the swizzle is realized by choosing which
+// global chunk each lane loads.
+
+template <int BN, int BM, int NS, int WGM>
+struct DmaCfg {
+    static constexpr int kBK = 32;
+    static constexpr int kWaves = 2 * WGM;                // 2 along weight rows x WGM along tokens
+    static constexpr int kThreadsWG = 64 * kWaves;
+    static constexpr int kWN = BN / 2, kWM = BM / WGM;
+    static constexpr int kBlkN = kWN / 32, kBlkM = kWM / 32;
+    static constexpr int kStageBytes = (BN + BM) * 64;
+    static constexpr int kInstrW = BN / 16, kInstrX = BM / 16;
+    static constexpr int kInstrPerWave = (kInstrW + kInstrX) / kWaves;
+    static constexpr int kSlabBytes = 2 * BM * 36 * 4;
+    static constexpr int kLdsBytes = NS * kStageBytes > kSlabBytes ? NS * kStageBytes : kSlabBytes;
+    static_assert((kInstrW + kInstrX) % kWaves == 0, "DMA instructions must split evenly over the waves");
+    static_assert(kBlkM >= 1, "at least one 32-token block per wave");
+};
+
+__device__ __forceinline__ int swz64(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BN, int BM, int NS, int WGM>
+__global__ void __launch_bounds__(128 * WGM, 1)
+tiled_dma_kernel(GemmArgs a, int tiles_n, int tiles_m) {
+    using C = DmaCfg<BN, BM, NS, WGM>;
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    unsigned char* lds8 = lds_raw;
+
+    const int ntiles = tiles_n * tiles_m;
+    const int per_xcd = (ntiles + kXcds - 1) / kXcds;
+    const int t = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (t >= ntiles) return;
+    const int tile_n = t / tiles_m;
+    const int tile_m = t % tiles_m;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wn = wave / WGM;
+    const int wm = wave % WGM;
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t n0 = (int64_t)tile_n * BN;
+    const int64_t m0 = (int64_t)tile_m * BM;
+    const bf16_t* __restrict__ X = reinterpret_cast<const bf16_t*>(a.x);
+    const bf16_t* __restrict__ W = reinterpret_cast<const bf16_t*>(a.w);
+    const int ktiles = (int)(K / C::kBK);
+
+    // Per-lane DMA source rows (clamped into the matrix: rows past the end
+    // only feed outputs that are never stored) and swizzled chunks.
+    const bf16_t* src[C::kInstrPerWave];
+    int dst_off[C::kInstrPerWave];
+    static_for<C::kInstrPerWave>([&](auto q) {
+        const int instr = wave + C::kWaves * q;
+        const bool is_w = instr < C::kInstrW;
+        const int rbase = (is_w ? instr : instr - C::kInstrW) * 16;
+        const int r = rbase + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        int64_t g = is_w ? n0 + r : m0 + r;
+        const int64_t lim = is_w ? N : M;
+        if (g > lim - 1) g = lim - 1;
+        src[q] = (is_w ? W : X) + g * K + 8 * c;
+        dst_off[q] = (is_w ? 0 : BN * 64) + rbase * 64;
+    });
+    auto issue = [&](int kt) {
+        unsigned char* base = lds8 + (kt % NS) * C::kStageBytes;
+        const int64_t k0 = (int64_t)kt * C::kBK;
+        static_for<C::kInstrPerWave>([&](auto q) {
+            __builtin_amdgcn_global_load_lds(src[q] + k0, base + dst_off[q], 16, 0, 0);
+        });
     };
-    auto store_tile = [&](int stage) {
-        bf16_t* xs = lds + stage * kStageElems;
-        bf16_t* wsm = xs + kBM * kStride;
-#pragma unroll
-        for (int j = 0; j < kChunksPerThread; ++j) {
-            const int c = tid + j * kThreads;
-            const int r = c >> 3;
-            const int kc = (c & 7) * 8;
-            *reinterpret_cast<uint4*>(xs + r * kStride + kc) = xr[j];
-            *reinterpret_cast<uint4*>(wsm + r * kStride + kc) = wr[j];
+
+    f32x16_t acc[C::kBlkN][C::kBlkM];
+    static_for<C::kBlkN>([&](auto i) {
+        static_for<C::kBlkM>([&](auto j) { acc[i][j] = f32x16_t{}; });
+    });
+
+    const int orow = lane & 31;
+    const int ohalf = lane >> 5;
+    bf16x8_t fa[2][C::kBlkN], fb[2][C::kBlkM];
+    auto read_frags = [&](auto buf, int kt, int s) {
+        const unsigned char* ws = lds8 + (kt % NS) * C::kStageBytes;
+        const unsigned char* xs = ws + BN * 64;
+        const int c = 2 * s + ohalf;
+        static_for<C::kBlkN>([&](auto i) {
+            fa[buf][i] = __builtin_bit_cast(bf16x8_t,
+                *reinterpret_cast<const u32x4_t*>(ws + swz64(wn * C::kWN + i * 32 + orow, c)));
+        });
+        static_for<C::kBlkM>([&](auto j) {
+            fb[buf][j] = __builtin_bit_cast(bf16x8_t,
+                *reinterpret_cast<const u32x4_t*>(xs + swz64(wm * C::kWM + j * 32 + orow, c)));
+        });
+    };
+    auto mfmas = [&](auto buf) {
+        static_for<C::kBlkN>([&](auto i) {
+            static_for<C::kBlkM>([&](auto j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+            });
+        });
+    };
+    // wait until this wave's DMA of the stage `ahead` stages before the most
+    // recently issued one has landed: `pending` stages may stay in flight
+    auto wait_stage = [&](int pending) {
+        if (pending <= 0) wait_vmcnt<0>();
+        else if (pending == 1) wait_vmcnt<C::kInstrPerWave>();
+        else wait_vmcnt<2 * C::kInstrPerWave>();
+    };
+    constexpr int kF0 = 0, kF1 = 1;
+
+    // prologue: stages 0 .. NS-2 in flight, wait for stage 0
+    const int pro = ktiles < NS - 1 ? ktiles : NS - 1;
+    for (int kt = 0; kt < pro; ++kt) issue(kt);
+    wait_stage(pro - 1);
+    __builtin_amdgcn_s_barrier();
+    read_frags(std::integral_constant<int, kF0>{}, 0, 0);
+
+    for (int kt = 0; kt < ktiles; ++kt) {
+        read_frags(std::integral_constant<int, kF1>{}, kt, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(std::integral_constant<int, kF0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < ktiles) {
+            // stages issued after kt + 1: up to kt + NS - 2
+            const int last = kt + NS - 2 < ktiles - 1 ? kt + NS - 2 : ktiles - 1;
+            wait_stage(last - (kt + 1));
+            __builtin_amdgcn_s_barrier();
+            if (kt + NS - 1 < ktiles) issue(kt + NS - 1);
+            read_frags(std::integral_constant<int, kF0>{}, kt + 1, 0);
         }
-    };
-
-    f32x4_t acc[4][4];   // [weight block nb][token block mb]
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    const int64_t ktiles = (K + kBK - 1) / kBK;
-    load_tile(0);
-    store_tile(0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(std::integral_constant<int, kF1>{});
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<0>();
     __syncthreads();
 
-    for (int64_t kt = 0; kt < ktiles; ++kt) {
-        const int stage = (int)(kt & 1);
-        if (kt + 1 < ktiles) load_tile((kt + 1) * kBK);
-        const bf16_t* xs = lds + stage * kStageElems;
-        const bf16_t* wsm = xs + kBM * kStride;
-#pragma unroll
-        for (int s = 0; s < kBK / 32; ++s) {
-            const int col = s * 32 + 8 * (lane >> 4);
-            bf16x8_t av[4], bv[4];
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-                av[nb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                    wsm + (wn * 64 + nb * 16 + (lane & 15)) * kStride + col));
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-                bv[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                    xs + (wm * 64 + mb * 16 + (lane & 15)) * kStride + col));
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[nb], bv[mb], acc[nb][mb], 0, 0, 0);
-        }
-        if (kt + 1 < ktiles) store_tile(stage ^ 1);
+    // Epilogue (as in the register-staged kernel): LDS slab per block row.
+    float* slab = reinterpret_cast<float*>(lds8);
+    constexpr int kSlabStride = 36;
+    static_for<C::kBlkN>([&](auto i) {
+        static_for<C::kBlkM>([&](auto j) {
+            const int mt = wm * C::kWM + j * 32 + (lane & 31);
+            static_for<4>([&](auto g) {
+                const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                *reinterpret_cast<f32x4_t*>(slab + (wn * BM + mt) * kSlabStride + 8 * g + 4 * (lane >> 5)) = v;
+            });
+        });
         __syncthreads();
-    }
-
+        constexpr int kRuns = 2 * BM * 8;
+        static_assert(kRuns % C::kThreadsWG == 0, "store loop must divide evenly");
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int64_t n = n0 + wn * 64 + nb * 16 + 4 * (lane >> 4);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            const int64_t m = m0 + wm * 64 + mb * 16 + (lane & 15);
+        for (int it = 0; it < kRuns / C::kThreadsWG; ++it) {
+            const int q = tid + it * C::kThreadsWG;
+            const int half = q / (BM * 8);
+            const int rem = q - half * (BM * 8);
+            const int mt = rem >> 3;
+            const int run = rem & 7;
+            const int64_t m = m0 + mt;
+            const int64_t n = n0 + half * C::kWN + i * 32 + 4 * run;
             if (m < M && n < N) {
-                float v[4] = {acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]};
-                store_out4(a, m, n, v);
+                const float4 v = *reinterpret_cast<const float4*>(slab + (half * BM + mt) * kSlabStride + 4 * run);
+                float o[4] = {v.x, v.y, v.z, v.w};
+                store_out4(a, m, n, o);
             }
         }
-    }
+        __syncthreads();
+    });
 }
+
+typedef void (*TiledFn)(GemmArgs, int, int);
+struct TiledEntry {
+    int bn, bm;
+    bool dma;          // needs K % 32 == 0
+    TiledFn fn;
+    int lds;
+    int threads;
+};
+
+#define TP_DMA(BN, BM, NS, WGM) \
+    {BN, BM, true, tiled_dma_kernel<BN, BM, NS, WGM>, DmaCfg<BN, BM, NS, WGM>::kLdsBytes, DmaCfg<BN, BM, NS, WGM>::kThreadsWG}
+const TiledEntry kTiled[] = {
+    TP_DMA(256, 256, 4, 2),
+    TP_DMA(256, 128, 4, 2),
+    TP_DMA(128, 128, 4, 2),
+    {128, 128, false, tiled_reg_kernel<128, 128>, TileCfg<128, 128>::kLdsBytes, kThreads},
+    TP_DMA(256, 256, 4, 4),
+    TP_DMA(256, 128, 4, 4),
+    TP_DMA(128, 128, 4, 4),
+};
+#undef TP_DMA
+constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);
+bool g_tiled_attr[kNumTiled] = {};
+int g_tiled_force = -1;
 
 }  // namespace
 
+int tiled_variant_count() { return kNumTiled; }
+void tiled_force_variant(int idx) { g_tiled_force = idx; }
+
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)((a.N + kBN - 1) / kBN), (unsigned)((a.M + kBM - 1) / kBM));
-    hipLaunchKernelGGL(tiled_kernel, grid, dim3(kThreads), 0, s, a);
+    // Kernel choice, from MI355X measurements at the Llama-8B and Qwen-32B
+    // prefill shard shapes: 256 x 256 tiles on 8 waves when they give at
+    // least 192 tiles; else 256 x 128 tiles on 8 waves when those do; else
+    // (few tiles, or K <= 1024 where a tile's fixed prologue/epilogue cost
+    // weighs most) 128 x 128 tiles on 8 waves. K % 32 != 0 takes the
+    // register-staged kernel.
+    auto tiles = [&](int bn, int bm) { return ((a.N + bn - 1) / bn) * ((a.M + bm - 1) / bm); };
+    int best;
+    if (a.K % 32 != 0) best = 3;
+    else if (a.K > 1024 && tiles(256, 256) >= 192) best = 4;
+    else if (a.K > 1024 && tiles(256, 128) >= 192) best = 5;
+    else best = 6;
+    if (g_tiled_force >= 0 && g_tiled_force < kNumTiled && (!kTiled[g_tiled_force].dma || a.K % 32 == 0))
+        best = g_tiled_force;
+    const TiledEntry& e = kTiled[best];
+    if (!g_tiled_attr[best]) {
+        const hipError_t ae = hipFuncSetAttribute(reinterpret_cast<const void*>(e.fn),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, e.lds);
+        if (ae != hipSuccess) return ae;
+        g_tiled_attr[best] = true;
+    }
+    const int tn = (int)((a.N + e.bn - 1) / e.bn);
+    const int tm = (int)((a.M + e.bm - 1) / e.bm);
+    const int ntiles = tn * tm;
+    const int grid = ((ntiles + kXcds - 1) / kXcds) * kXcds;
+    hipLaunchKernelGGL(e.fn, dim3(grid), dim3(e.threads), e.lds, s, a, tn, tm);
     return hipGetLastError();
 }
 

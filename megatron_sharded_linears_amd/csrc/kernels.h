@@ -81,5 +81,7 @@ int64_t skinny_workspace_floats(const SkinnyPlan& p, int64_t M, int64_t N);
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace& ws, hipStream_t s);
 
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t s);
+int tiled_variant_count();
+void tiled_force_variant(int idx);   // -1: automatic
 
 }  // namespace tpk

@@ -77,6 +77,7 @@ _PROTOS = {
     "tp_lm_head_shard": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp]),
     "tp_concat_logits": (_int, [_ptr_array, _int, _i64, _i64, _i64, _int, _vp, _vp]),
     "tp_tune_skinny": (_int, [_int, _int, _int, _int]),
+    "tp_tune_tiled": (_int, [_int]),
 }
 for _name, (_res, _args) in _PROTOS.items():
     _f = getattr(_lib, _name)
@@ -175,6 +176,10 @@ def tp_kv_heads_of_rank(cfg, t, rank):
 
 def tp_tune_skinny(ksteps=0, nwn=0, nwk=0, x_direct=0):
     _check(_lib.tp_tune_skinny(ksteps, nwn, nwk, x_direct), "tp_tune_skinny")
+
+
+def tp_tune_tiled(variant=-1):
+    _check(_lib.tp_tune_tiled(variant), "tp_tune_tiled")
 
 
 # ------------------------------------------------------------ device calls

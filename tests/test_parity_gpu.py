@@ -133,6 +133,26 @@ def test_split_k_partials_are_never_stale():
             lib.tp_tune_skinny(0, 0, 0, 0)
 
 
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 6])
+def test_every_prefill_tile_shape_exact(variant):
+    lib.tp_tune_tiled(variant)
+    try:
+        for (M, N, K) in [(65, 70, 64), (300, 257, 200), (512, 768, 1032), (2048, 300, 640), (130, 1024, 4096),
+                          (700, 520, 96), (257, 4100, 32)]:
+            x = I.small_int_bf16((SEED, 40, M, N, K), (M, K))
+            w = I.small_int_bf16((SEED, 41, M, N, K), (N, K))
+            y = empty((M, N), torch.float32)
+            lib.tp_row_linear_partial(dev(x), dev(w), y)
+            assert np.array_equal(f64(y), oracle.linear(f64(x), f64(w))), (variant, M, N, K)
+            b = I.normal_bf16((SEED, 42, N), (N,))
+            yb = empty((M, N))
+            xr, wr = I.normal_bf16((SEED, 43, M, K), (M, K)), I.normal_bf16((SEED, 44, N, K), (N, K), 0.02)
+            lib.tp_column_linear(dev(xr), dev(wr), yb, bias=dev(b))
+            assert_close(f64(yb), oracle.linear(f64(xr), f64(wr), f64(b)), f"tile {variant} {(M, N, K)}")
+    finally:
+        lib.tp_tune_tiled(-1)
+
+
 # ------------------------------------------------ linears, random tolerance
 
 @pytest.mark.parametrize("M,N,K", [(16, 768, 4096), (64, 1792, 4096), (1, 1000, 256), (200, 300, 512), (2048, 256, 1024)])
