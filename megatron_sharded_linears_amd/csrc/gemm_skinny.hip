@@ -246,16 +246,25 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     //    counter, so the last workgroup to arrive sees every partial. No
     //    agent-scope fence is used: on this GPU it writes back and
     //    invalidates the whole L2 of the XCD, once per workgroup.
+    // 4 consecutive floats per lane: two 64-bit stores when 8-byte aligned.
+    const bool pair = (N % 2 == 0) && (n_out + 3 < N);
     if (wk == 0) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int64_t m = 16 * mt + (lane & 15);
             if (m < M) {
-                float* p = ws + ((int64_t)split * M + m) * N;
+                float* p = ws + ((int64_t)split * M + m) * N + n_out;
+                if (pair) {
+                    const uint64_t lo = (uint64_t)__float_as_uint(acc[mt][0]) | ((uint64_t)__float_as_uint(acc[mt][1]) << 32);
+                    const uint64_t hi = (uint64_t)__float_as_uint(acc[mt][2]) | ((uint64_t)__float_as_uint(acc[mt][3]) << 32);
+                    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(reinterpret_cast<uint64_t*>(p) + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (n_out + i < N)
-                        __hip_atomic_store(p + n_out + i, acc[mt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int i = 0; i < 4; ++i)
+                        if (n_out + i < N)
+                            __hip_atomic_store(p + i, acc[mt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
         }
     }
@@ -268,19 +277,42 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     __syncthreads();
     if (s_last != 1u) return;
 
-    // 7. Last workgroup on this tile: sum the partials in split order.
+    // 7. Last workgroup on this tile: sum the partials in split order. The
+    //    loads of up to 8 splits are issued back to back before any is used,
+    //    so they cost one memory round trip, not one each.
     if (wk == 0) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int64_t m = 16 * mt + (lane & 15);
             if (m < M && n_out < N) {
                 float v[4] = {0.f, 0.f, 0.f, 0.f};
-                for (int sp = 0; sp < splits; ++sp) {
-                    float* p = ws + ((int64_t)sp * M + m) * N;
+                for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+                    float t[8][4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (n_out + i < N)
-                            v[i] += __hip_atomic_load(p + n_out + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int j = 0; j < 8; ++j) {
+                        t[j][0] = t[j][1] = t[j][2] = t[j][3] = 0.f;
+                        if (sp0 + j < splits) {
+                            float* p = ws + ((int64_t)(sp0 + j) * M + m) * N + n_out;
+                            if (pair) {
+                                const uint64_t lo = __hip_atomic_load(reinterpret_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                const uint64_t hi = __hip_atomic_load(reinterpret_cast<uint64_t*>(p) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                t[j][0] = __uint_as_float((uint32_t)lo);
+                                t[j][1] = __uint_as_float((uint32_t)(lo >> 32));
+                                t[j][2] = __uint_as_float((uint32_t)hi);
+                                t[j][3] = __uint_as_float((uint32_t)(hi >> 32));
+                            } else {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    if (n_out + i < N)
+                                        t[j][i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (sp0 + j < splits)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) v[i] += t[j][i];
                 }
                 store_out4(a, m, n_out, v);
             }
@@ -356,30 +388,51 @@ bool skinny_plan_fits(const SkinnyPlan& p, int64_t M) {
     return e.lds(xrows_for(e, M)) <= kMaxLds;
 }
 
-// Pick the decode kernel shape for one linear.
+// Pick the decode kernel shape for one linear, from MI355X sweeps of every
+// variant at the Llama-8B decode shapes.
 //
 // M <= 16: one workgroup covers all of K for 16 weight rows (no exchange
-// between workgroups), choosing the variant whose K coverage fits K with the
-// least waste; on the measured MI355X sweep this beat every split-K variant at
-// the Llama-8B decode shapes (an exchange costs three serialized memory round
-// trips at the end of the kernel). Otherwise a cost model counts HBM bytes
+// between workgroups) with the variant whose K coverage fits K with the least
+// waste, except when the weight has too few 16-row tiles to fill the GPU,
+// where K is split 4 ways (an exchange costs a few serialized memory round
+// trips at the end of the kernel, worth it only then). M in (32, 64]: the
+// measured winners per K and N. Otherwise a cost model counts HBM bytes
 // (the weight once, the fp32 partial round trip when K is split across
 // workgroups, a quarter weight for X re-reads from L2) divided by how well the
 // grid fills the 256 CUs.
 SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
     const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    struct Rule { int64_t kmax; int ks, nwn, nwk, xd; };
+    auto first_fit = [&](const Rule* rules, int n, SkinnyPlan* out) {
+        for (int i = 0; i < n; ++i) {
+            const Rule& r = rules[i];
+            if (K > r.kmax) continue;
+            SkinnyPlan p{mt, r.ks, r.nwn, r.nwk, r.xd, 1, 1};
+            const int idx = find_skinny(p);
+            if (idx < 0 || !skinny_plan_fits(p, M)) continue;
+            p = make_plan(kSkinnyTable[idx], N, K);
+            if (p.splits > 1 && (p.splits * M * N > kSkinnyWsFloats || p.ntiles > kSkinnyWsCounters)) continue;
+            *out = p;
+            return true;
+        }
+        return false;
+    };
+    SkinnyPlan chosen;
     if (mt == 1) {
-        struct Rule { int64_t kmax; int ks, nwn, nwk, xd; };
+        // Few 16-row tiles (qkv-sized N): split K 4 ways over 1024-wide
+        // groups; otherwise cover K in one workgroup.
+        static const Rule few_tiles[] = {{1 << 30, 8, 1, 4, 1}};
         static const Rule rules[] = {
-            {512, 4, 1, 4, 1}, {1024, 8, 1, 4, 1}, {2048, 4, 1, 16, 0}, {4096, 8, 1, 16, 0},
+            {512, 4, 1, 4, 1}, {1024, 8, 1, 4, 1}, {2048, 8, 1, 8, 0}, {4096, 16, 1, 8, 0},
             {5120, 20, 1, 8, 0},
         };
-        for (const Rule& r : rules) {
-            if (K > r.kmax) continue;
-            SkinnyPlan p{1, r.ks, r.nwn, r.nwk, r.xd, 1, 1};
-            const int idx = find_skinny(p);
-            if (idx >= 0 && skinny_plan_fits(p, M)) return make_plan(kSkinnyTable[idx], N, K);
-        }
+        if ((N + 15) / 16 < 128 && K >= 2048 && first_fit(few_tiles, 1, &chosen)) return chosen;
+        if (first_fit(rules, 5, &chosen)) return chosen;
+    } else if (mt == 4) {
+        // M in (32, 64]: measured winners at the Llama-8B t=16 shard shapes.
+        static const Rule rules_small_n[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 4, 1, 4, 1}};
+        static const Rule rules[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 8, 2, 2, 0}};
+        if (first_fit(N <= 1024 ? rules_small_n : rules, 3, &chosen)) return chosen;
     }
     SkinnyPlan best{mt, 8, 4, 2, 0, 1, 1};
     double best_cost = -1.0;
