@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--eager", action="store_true", help="time eager launches instead of the captured step")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--counters", action="store_true",
+                   help="run under rocprofv3 --pmc: a plain copy of known size, then W+K eager steps; "
+                        "prints what --summarize-counters needs and times nothing")
     return p.parse_args()
 
 
@@ -276,6 +279,109 @@ def cpu_baseline(w, seconds):
 
 # ------------------------------------------------------------------- main
 
+GEMM_SOURCES = ("gemm_skinny.hip", "gemm_tiled.hip", "common.h", "kernels.h")
+
+
+def gemm_source_sha256():
+    """Hash of the GEMM kernels' sources: a stored counter summary speaks for
+    the kernels only while this is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "megatron_sharded_linears_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}.json")
+
+
+def stored_traffic(workload):
+    """HBM bytes per step of the GEMM launches, from the committed counter
+    summary of this workload, or None when there is none or the kernels'
+    sources have changed since it was taken."""
+    try:
+        with open(traffic_file(workload)) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256") != gemm_source_sha256():
+        return None
+    return d
+
+
+def is_gemm_kernel(name):
+    return "skinny_kernel" in name or "tiled_dma_kernel" in name or "tiled_reg_kernel" in name
+
+
+def summarize_counters(fetch_csv, write_csv, run_json, out=None):
+    """HBM traffic of the step's GEMM launches from two rocprofv3 --pmc runs
+    of `bench.py --counters` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
+    Each counter is scaled by what it reads for the plain copy of known size
+    (shard_copy_kernel at t = 1: reads and writes exactly `copy_bytes`)."""
+    import csv
+    import re
+    with open(run_json) as f:
+        run = json.loads([ln for ln in f if ln.startswith("{")][-1])
+
+    def load(path, counter):
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                m = re.search(r"(\w+_kernel)(<[^>]*>)?", r["Kernel_Name"])
+                short = (m.group(1) + (m.group(2) or "")) if m else r["Kernel_Name"][:60]
+                if r.get("Grid_Size"):
+                    short += f" grid={r['Grid_Size']}"
+                per.setdefault(short, []).append(float(r["Counter_Value"]) * 1024.0)
+        return per
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    nb = run["copy_bytes"]
+    cf = [v for k, vs in fetch.items() if k.startswith("shard_copy_kernel") for v in vs]
+    cw = [v for k, vs in write.items() if k.startswith("shard_copy_kernel") for v in vs]
+    if len(cf) != run["copy_launches"] or len(cw) != run["copy_launches"]:
+        raise SystemExit(f"expected {run['copy_launches']} copy dispatches, found {len(cf)} / {len(cw)}")
+    f_fetch = nb / (sum(cf) / len(cf))
+    f_write = nb / (sum(cw) / len(cw))
+    steps = run["steps"]
+    rows, fetch_step, write_step, launches = [], 0.0, 0.0, 0
+    for k in sorted(set(fetch) | set(write)):
+        if not is_gemm_kernel(k):
+            continue
+        fv, wv = fetch.get(k, []), write.get(k, [])
+        if len(fv) != len(wv) or len(fv) % steps:
+            raise SystemExit(f"{k}: {len(fv)} fetch / {len(wv)} write dispatches over {steps} steps")
+        fetch_step += sum(fv) * f_fetch / steps
+        write_step += sum(wv) * f_write / steps
+        launches += len(fv) // steps
+        rows.append((k, len(fv) // steps, sum(fv) / len(fv) * f_fetch, sum(wv) / len(wv) * f_write))
+    if launches != run["gemm_launches_per_step"]:
+        raise SystemExit(f"found {launches} GEMM launches per step, expected {run['gemm_launches_per_step']}")
+    alg = run["gemm_algorithmic_bytes_per_step"]
+    d = {"workload": run["workload"], "source_sha256": run["source_sha256"],
+         "copy_bytes": nb, "fetch_scale": round(f_fetch, 5), "write_scale": round(f_write, 5),
+         "gemm_launches_per_step": launches, "fetch_bytes_per_step": round(fetch_step),
+         "write_bytes_per_step": round(write_step), "traffic_bytes_per_step": round(fetch_step + write_step),
+         "algorithmic_bytes_per_step": alg, "traffic_over_algorithmic": round((fetch_step + write_step) / alg, 4),
+         "per_kernel": [{"kernel": k, "launches_per_step": n, "fetch_bytes_per_launch": round(fb),
+                         "write_bytes_per_launch": round(wb)} for k, n, fb, wb in rows]}
+    print(f"copy of {nb} B: FETCH_SIZE scale {f_fetch:.4f}, WRITE_SIZE scale {f_write:.4f}")
+    print(f"{'kernel':56s} {'launches/step':>13s} {'fetch_MiB/launch':>16s} {'write_MiB/launch':>16s}")
+    for k, n, fb, wb in rows:
+        print(f"{k[:56]:56s} {n:13d} {fb / 2**20:16.3f} {wb / 2**20:16.3f}")
+    print(f"per step: traffic {(fetch_step + write_step) / 2**20:.2f} MiB, algorithmic {alg / 2**20:.2f} MiB, "
+          f"ratio {(fetch_step + write_step) / alg:.4f}")
+    if out:
+        with open(out, "w") as f:
+            json.dump(d, f, indent=1)
+            f.write("\n")
+    return d
+
+
+
 def summarize_trace(path, top=30):
     """Per (kernel, workgroups) duration stats from a rocprofv3
     --kernel-trace --output-format csv trace: a row per distinct launch shape,
@@ -303,6 +409,9 @@ def main():
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2])
         return
+    if len(sys.argv) in (5, 6) and sys.argv[1] == "--summarize-counters":
+        summarize_counters(*sys.argv[2:])
+        return
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: every shard of the t-way split is computed on that one "
@@ -325,6 +434,29 @@ def main():
     for n, _, _ in ops:
         if n not in names:
             names.append(n)
+
+    gemm_ops = [k for k in ("qkv", "o", "gate_up", "down", "lm_head") if k in work]
+    if args.counters:
+        # A plain copy of known size (the counters' scale), then W+K eager steps.
+        cfg = w.cfg()
+        full = lib.tp_full_shape(cfg, "gate_up")
+        src = I.device_normal_bf16(full, 1.0, 5, "cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            lib.tp_shard_weights(cfg, 1, 0, "gate_up", src, dst)
+        torch.cuda.synchronize()
+        if not torch.equal(src, dst):
+            raise SystemExit("calibration copy mismatch")
+        del src, dst
+        for _ in range(args.warmup + args.steps):
+            run_ops(ops)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": w.name, "copy_bytes": full[0] * full[1] * 2, "copy_launches": 3,
+                          "steps": args.warmup + args.steps,
+                          "gemm_launches_per_step": sum(work[k][0] for k in gemm_ops),
+                          "gemm_algorithmic_bytes_per_step": sum(work[k][0] * work[k][2] for k in gemm_ops),
+                          "source_sha256": gemm_source_sha256()}), flush=True)
+        return
 
     # --- eager: the same calls issued one by one from Python
     for _ in range(args.warmup):
@@ -369,24 +501,30 @@ def main():
                         "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2) if flops else None,
                         "bytes_per_launch": byts}
 
-    gemm_ops = [k for k in ("qkv", "o", "gate_up", "down", "lm_head") if k in work]
     flops_step = sum(work[k][0] * work[k][1] for k in gemm_ops)
     value = flops_step / (ms_step * 1e-3) / 1e12
     gemm_us = sum(per_op[k]["us_per_launch"] * work[k][0] for k in gemm_ops)
     gemm_bytes_step = sum(work[k][0] * work[k][2] for k in gemm_ops)
     achieved = gemm_bytes_step / (gemm_us * 1e-6) / 1e9
     red = per_op["reduce"]
+    st = stored_traffic(w.name)
+    traffic = st["traffic_bytes_per_step"] if st else None
     if w.tokens <= 64:
         roofline = {"bound": "hbm", "kernel": "decode linear (skinny_kernel), all launches of a step",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                     "launches_per_step": sum(work[k][0] for k in gemm_ops), "us_per_step": round(gemm_us, 2)}
     else:
         tflops = flops_step / (gemm_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "kernel": "prefill linear (tiled_kernel), all launches of a step",
                     "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                     "launches_per_step": sum(work[k][0] for k in gemm_ops), "us_per_step": round(gemm_us, 2)}
+    roofline["algorithmic_bytes_per_step"] = gemm_bytes_step
+    roofline["traffic_unit"] = "HBM bytes over the launches of one step (rocprofv3 FETCH_SIZE + WRITE_SIZE, " \
+                               "scaled by a plain copy of known size)"
+    if st:
+        roofline["traffic_over_algorithmic"] = st["traffic_over_algorithmic"]
 
     line = {
         "metric": METRIC,
