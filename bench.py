@@ -7,10 +7,16 @@ A step is one pass of the whole path over one batch of synthetic tokens, for
 one rank r = 0 of a t-way split, with every input already resident in HBM:
 
     embedding   tp_vocab_embed (rank r) + tp_reduce_partials over t shards
-    per layer   tp_column_linear (qkv) ; tp_row_linear_partial (o) ;
-                tp_reduce_partials ; tp_column_linear (gate_up) ; tp_swiglu ;
-                tp_row_linear_partial (down) ; tp_reduce_partials
+    per layer   tp_column_linear (qkv) ;
+                tp_row_linear_reduce (o, then the sum over ranks) ;
+                tp_column_linear_swiglu (gate_up, then SwiGLU) ;
+                tp_row_linear_reduce (down, then the sum over ranks)
     LM head     tp_lm_head_shard (rank r) + tp_concat_logits over t shards
+
+At prefill sizes (more than 64 tokens) the row-parallel linears and the sums
+are separate calls (tp_row_linear_partial + tp_reduce_partials). With
+--separate every step is separate calls: gate_up, SwiGLU, o, reduce, down,
+reduce; the other variant's step time is always reported as `alt_path`.
 
 The other t-1 ranks' partial sums and logits (which would arrive over the
 interconnect) are seeded synthetic buffers resident in HBM. Attention is not
@@ -54,6 +60,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llama8b_t8_decode_m16")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of the captured step")
+    p.add_argument("--separate", action="store_true",
+                   help="time the step through the separate calls (no fused SwiGLU / reduce epilogues)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--counters", action="store_true",
@@ -142,6 +150,10 @@ class Rank:
             "down": (w.layers, gemm_flops(M, d[0], d[1]), gemm_bytes(M, d[0], d[1])),
             "swiglu": (w.layers, 0, 6 * M * (g[0] // 2)),
             "reduce": (2 * w.layers, 0, (2 * t + 2) * M * H),
+            # fused calls: the linear reads the other ranks' partials / writes SwiGLU's output
+            "o_reduce": (w.layers, gemm_flops(M, o[0], o[1]), gemm_bytes(M, o[0], o[1]) + 2 * (t - 1) * M * H),
+            "gate_up_swiglu": (w.layers, gemm_flops(M, g[0], g[1]), 2 * g[0] * g[1] + 2 * M * g[1] + M * g[0]),
+            "down_reduce": (w.layers, gemm_flops(M, d[0], d[1]), gemm_bytes(M, d[0], d[1]) + 2 * (t - 1) * M * H),
         }
         if self.vocab:
             Ms, vs = self.hs_rows, self.vs
@@ -154,8 +166,9 @@ class Rank:
         return ops
 
 
-def build_ops(R, lib):
-    """The step as a list of (name, fn, args): every launch of one pass."""
+def build_ops(R, lib, fused_swiglu=True, fused_reduce=True):
+    """The step as a list of (name, fn, args): every call of one pass. Fused
+    calls replace gate_up + SwiGLU and a row-parallel linear + its reduce."""
     w = R.w
     t = w.t
     ops = []
@@ -166,18 +179,48 @@ def build_ops(R, lib):
         h = R.h
     for L in R.layers:
         ops.append(("qkv", lib.tp_column_linear, (h, L["qkv"], R.qkv)))
-        ops.append(("o", lib.tp_row_linear_partial, (L["ctx"], L["o"], R.po)))
-        ops.append(("reduce", lib.tp_reduce_partials, ([R.po] + L["peers_o"], R.y1)))
-        ops.append(("gate_up", lib.tp_column_linear, (R.y1, L["gate_up"], R.gu)))
-        ops.append(("swiglu", lib.tp_swiglu, (R.gu, R.act)))
-        ops.append(("down", lib.tp_row_linear_partial, (R.act, L["down"], R.pd)))
-        ops.append(("reduce", lib.tp_reduce_partials, ([R.pd] + L["peers_d"], R.h)))
+        if fused_reduce:
+            ops.append(("o_reduce", lib.tp_row_linear_reduce, (L["ctx"], L["o"], [None] + L["peers_o"], 0, R.y1)))
+        else:
+            ops.append(("o", lib.tp_row_linear_partial, (L["ctx"], L["o"], R.po)))
+            ops.append(("reduce", lib.tp_reduce_partials, ([R.po] + L["peers_o"], R.y1)))
+        if fused_swiglu:
+            ops.append(("gate_up_swiglu", lib.tp_column_linear_swiglu, (R.y1, L["gate_up"], R.act)))
+        else:
+            ops.append(("gate_up", lib.tp_column_linear, (R.y1, L["gate_up"], R.gu)))
+            ops.append(("swiglu", lib.tp_swiglu, (R.gu, R.act)))
+        if fused_reduce:
+            ops.append(("down_reduce", lib.tp_row_linear_reduce, (R.act, L["down"], [None] + L["peers_d"], 0, R.h)))
+        else:
+            ops.append(("down", lib.tp_row_linear_partial, (R.act, L["down"], R.pd)))
+            ops.append(("reduce", lib.tp_reduce_partials, ([R.pd] + L["peers_d"], R.h)))
         h = R.h
     if R.vocab:
         hs = h[h.shape[0] - R.hs_rows:]
         ops.append(("lm_head", lib.tp_lm_head_shard, (hs, R.lm, R.logits)))
         ops.append(("concat", lib.tp_concat_logits, ([R.logits] + R.peer_logits, w.vocab, R.full_logits)))
     return ops
+
+
+GEMM_OPS = ("qkv", "o", "gate_up", "down", "lm_head", "o_reduce", "gate_up_swiglu", "down_reduce")
+
+
+def time_step(torch, ops, steps, warmup):
+    """K replays of the captured step between HIP events: (ms per step, wall s)."""
+    g_step = capture(torch, ops)
+    for _ in range(warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        g_step.replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall0
+    del g_step
+    return start.elapsed_time(end) / steps, wall_s
 
 
 def run_ops(ops, only=None):
@@ -429,13 +472,18 @@ def main():
     torch.cuda.synchronize()
     work = R.work()
 
-    ops = build_ops(R, lib)
+    # The step: fused calls where they are one launch (SwiGLU always; the
+    # reduce at decode sizes, where the linear's epilogue sums the partials).
+    fused = not args.separate
+    fused_reduce = fused and w.tokens <= 64
+    ops = build_ops(R, lib, fused_swiglu=fused, fused_reduce=fused_reduce)
+    alt_ops = build_ops(R, lib, fused_swiglu=not fused, fused_reduce=(not fused) and w.tokens <= 64)
     names = []
     for n, _, _ in ops:
         if n not in names:
             names.append(n)
 
-    gemm_ops = [k for k in ("qkv", "o", "gate_up", "down", "lm_head") if k in work]
+    gemm_ops = [k for k in GEMM_OPS if k in names]
     if args.counters:
         # A plain copy of known size (the counters' scale), then W+K eager steps.
         cfg = w.cfg()
@@ -471,28 +519,19 @@ def main():
     ms_eager = a.elapsed_time(b) / args.steps
 
     # --- timed region: exactly K steps, each the replay of the captured step
-    g_step = capture(torch, ops)
-    for _ in range(args.warmup):
-        g_step.replay()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        g_step.replay()
-    end.record()
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t_wall0
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_step, wall_s = time_step(torch, ops, args.steps, args.warmup)
     if args.eager:
         ms_step = ms_eager
+    # the same step through the other set of calls, for comparison
+    ms_alt, _ = time_step(torch, alt_ops, args.steps, args.warmup)
 
     # --- per kernel: each op's launches of one step, captured and replayed K times
     per_op = {}
-    for name in names:
+    op_names = names + [n for n in ("reduce",) if n not in names]
+    for name in op_names:
         n_per_step, flops, byts = work[name]
         repeat = max(1, -(-32 // n_per_step))   # at least 32 launches per replay
-        g = capture(torch, ops, only=name, repeat=repeat)
+        g = capture(torch, ops if name in names else alt_ops, only=name, repeat=repeat)
         ms = time_graph(torch, g, args.steps, 2)
         del g
         us = ms * 1e3 / (n_per_step * repeat)
@@ -510,13 +549,13 @@ def main():
     st = stored_traffic(w.name)
     traffic = st["traffic_bytes_per_step"] if st else None
     if w.tokens <= 64:
-        roofline = {"bound": "hbm", "kernel": "decode linear (skinny_kernel), all launches of a step",
+        roofline = {"bound": "hbm", "kernel": "decode linear (skinny_kernel), all GEMM launches of a step",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                     "launches_per_step": sum(work[k][0] for k in gemm_ops), "us_per_step": round(gemm_us, 2)}
     else:
         tflops = flops_step / (gemm_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "kernel": "prefill linear (tiled_kernel), all launches of a step",
+        roofline = {"bound": "mfma", "kernel": "prefill linear (tiled_dma_kernel), all GEMM launches of a step",
                     "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                     "launches_per_step": sum(work[k][0] for k in gemm_ops), "us_per_step": round(gemm_us, 2)}
@@ -544,14 +583,18 @@ def main():
                    "head_dim": w.head_dim, "intermediate": w.intermediate,
                    "vocab": w.vocab if w.has_vocab else None, "lm_positions": w.lm_positions if w.has_vocab else 0,
                    "parallelism": f"tp{w.t} rank share on 1 GPU",
-                   "execution": "eager launches" if args.eager else "HIP graph of the step"},
+                   "execution": "eager launches" if args.eager else "HIP graph of the step",
+                   "calls": ("fused SwiGLU and reduce epilogues" if fused_reduce else
+                             "fused SwiGLU epilogue" if fused else "separate calls")},
         "roofline": roofline,
         "reduce": {"GBps": red["GBps"], "frac": round(red["GBps"] / HBM_PEAK_GBPS, 4),
                    "us_per_call": red["us_per_launch"], "calls_per_step": work["reduce"][0],
                    "bytes_per_call": work["reduce"][2]},
         "eager_ms_per_step": round(ms_eager, 4),
         "gemm_only_TFLOPs": round(flops_step / (gemm_us * 1e-6) / 1e12, 2),
-        "step_GBps": round(sum(n * b for n, _, b in work.values()) / (ms_step * 1e-3) / 1e9, 1),
+        "step_GBps": round(sum(work[k][0] * work[k][2] for k in names) / (ms_step * 1e-3) / 1e9, 1),
+        "alt_path": {"calls": "separate" if fused else "fused", "ms_per_step": round(ms_alt, 4),
+                     "value": round(flops_step / (ms_alt * 1e-3) / 1e12, 3)},
         "per_op": per_op,
         "wall_s_timed": round(wall_s, 3),
         "pages_context": pages_context(w),

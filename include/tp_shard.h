@@ -158,6 +158,32 @@ int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_shard, const
 int tp_reduce_partials(const void* const* partials, int t, int64_t numel, int in_dtype,
                        void* out, int out_dtype, void* stream);
 
+/* S3 + S4 in one call: act[m, j] = silu(g) * u with g = bf16(x[m, :] . w[j, :])
+ * and u = bf16(x[m, :] . w[i_shard + j, :]), silu as in tp_swiglu, computed in
+ * fp32 and rounded once ([P1 3.2] SwiGLU MLP; [P3 线性层怎么切]: gate_up
+ * column-parallel, then SiLU x up on the rank's slice with no exchange).
+ * w_gate_up: the rank's [2 i_shard, K] bf16 shard, rows [gate | up] as
+ * tp_shard_weights lays them out; act: [M, i_shard] bf16. Gives the same bits
+ * as tp_column_linear (no bias) followed by tp_swiglu, without writing the
+ * [M, 2 i_shard] intermediate. K % 8 == 0; any i_shard >= 1. */
+int tp_column_linear_swiglu(const void* x, int64_t M, int64_t K, const void* w_gate_up, int64_t i_shard,
+                            void* act, void* stream);
+
+/* S5 + S6 / S7 + S8 in one call: the row-parallel linear of rank `rank`
+ * followed by the sum over ranks ([P1 3.2] Row Parallel then [P1 3.1]
+ * All-Reduce): out = bf16(sum_{i=0}^{t-1} P_i) accumulated in fp32 in the
+ * order i = 0..t-1 from P_0, where P_rank = bf16(x_shard w_shard^T) (the
+ * rank's own partial, rounded as a bf16 partial buffer holds it) and P_i
+ * (i != rank) = partials[i]. `partials` is a HOST array of t pointers; entry
+ * `rank` is ignored (may be NULL), the others are device [M, N] bf16 buffers
+ * that must not be `out` (TP_ERR_SHAPE). out: [M, N] bf16. Gives the same bits
+ * as tp_row_linear_partial (bf16) into partials[rank] followed by
+ * tp_reduce_partials. M <= 64 with t <= 16 and N % 4 == 0 is one launch (the
+ * sum is the linear's epilogue); otherwise the own partial is written to
+ * `out` and summed in place. */
+int tp_row_linear_reduce(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
+                         const void* const* partials, int t, int rank, void* out, void* stream);
+
 /* S9a. Vocab-parallel embedding, one shard's contribution: for each token m,
  * out[m, :] = e_shard[ids[m] - rank Vs, :] when rank Vs <= ids[m] <
  * min((rank+1) Vs, vocab), else a row of -0.0 (Vs = ceil(vocab / t)). Ids

@@ -94,18 +94,10 @@ int get_workspace(hipStream_t s, tpk::Workspace* out) {
 // tests that exercise every variant. Zero means automatic.
 int g_force_ksteps = 0, g_force_nwn = 0, g_force_nwk = 0, g_force_xd = 0;
 
-int run_linear(const void* x, int64_t M, int64_t K, const void* w, int64_t N, const void* bias,
-               void* y, int out_dtype, void* stream) {
-    if (x == nullptr || w == nullptr || y == nullptr) return TP_ERR_NULL;
-    if (M < 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return TP_ERR_SHAPE;
-    if (!dtype_ok(out_dtype)) return TP_ERR_DTYPE;
-    if (K % 8 != 0) return TP_ERR_ALIGNMENT;
-    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return TP_ERR_ALIGNMENT;
-    if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TP_ERR_ALIGNMENT;
-    if (M == 0) return TP_OK;
-
-    tpk::GemmArgs a{x, w, bias, y, M, N, K, out_dtype};
-    hipStream_t s = static_cast<hipStream_t>(stream);
+// Launch one validated linear. a.N is the kernel's row space (for EPI_SWIGLU
+// on the decode kernel: 16-row blocks of 8 gate and 8 up rows).
+int launch_linear(const tpk::GemmArgs& a, hipStream_t s) {
+    const int64_t M = a.M, N = a.N, K = a.K;
     hipError_t e;
     if (M <= kSkinnyMaxM) {
         tpk::SkinnyPlan p = tpk::plan_skinny(M, N, K);
@@ -136,6 +128,29 @@ int run_linear(const void* x, int64_t M, int64_t K, const void* w, int64_t N, co
         e = tpk::launch_tiled(a, s);
     }
     return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+}
+
+int check_linear(const void* x, int64_t M, int64_t K, const void* w, int64_t N, const void* y) {
+    if (x == nullptr || w == nullptr || y == nullptr) return TP_ERR_NULL;
+    if (M < 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return TP_ERR_SHAPE;
+    if (K % 8 != 0) return TP_ERR_ALIGNMENT;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return TP_ERR_ALIGNMENT;
+    return TP_OK;
+}
+
+int run_linear(const void* x, int64_t M, int64_t K, const void* w, int64_t N, const void* bias,
+               void* y, int out_dtype, void* stream) {
+    const int st = check_linear(x, M, K, w, N, y);
+    if (st != TP_OK) return st;
+    if (!dtype_ok(out_dtype)) return TP_ERR_DTYPE;
+    if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TP_ERR_ALIGNMENT;
+    if (M == 0) return TP_OK;
+    tpk::GemmArgs a{};
+    a.x = x; a.w = w; a.bias = bias; a.y = y;
+    a.M = M; a.N = N; a.K = K;
+    a.out_dtype = out_dtype;
+    a.epi = tpk::EPI_STORE;
+    return launch_linear(a, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -284,6 +299,69 @@ int tp_lm_head_shard(const void* h, int64_t M, int64_t K, const void* w_lm_shard
                      void* logits_shard, int out_dtype, void* stream) {
     try {
         return run_linear(h, M, K, w_lm_shard, v_shard, nullptr, logits_shard, out_dtype, stream);
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_column_linear_swiglu(const void* x, int64_t M, int64_t K, const void* w_gate_up, int64_t i_shard,
+                            void* act, void* stream) {
+    try {
+        if (i_shard <= 0 || i_shard >= kMaxDim / 2) return TP_ERR_SHAPE;
+        const int st = check_linear(x, M, K, w_gate_up, 2 * i_shard, act);
+        if (st != TP_OK) return st;
+        if (M == 0) return TP_OK;
+        tpk::GemmArgs a{};
+        a.x = x; a.w = w_gate_up; a.y = act;
+        a.M = M; a.K = K;
+        a.out_dtype = TP_BF16;
+        a.epi = tpk::EPI_SWIGLU;
+        a.i_half = i_shard;
+        // decode kernel: 16-row blocks of 8 gate + 8 up rows; tiled kernel:
+        // 2 i_shard here, whole tiles of paired rows inside the launcher
+        a.N = M <= kSkinnyMaxM ? 16 * ((i_shard + 7) / 8) : 2 * i_shard;
+        return launch_linear(a, static_cast<hipStream_t>(stream));
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_row_linear_reduce(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
+                         const void* const* partials, int t, int rank, void* out, void* stream) {
+    try {
+        const int st = check_linear(x_shard, M, K_shard, w_shard, N, out);
+        if (st != TP_OK) return st;
+        if (partials == nullptr) return TP_ERR_NULL;
+        if (t < 1 || t > TP_MAX_SHARDS || rank < 0 || rank >= t) return TP_ERR_RANGE;
+        for (int i = 0; i < t; ++i) {
+            if (i == rank) continue;
+            if (partials[i] == nullptr) return TP_ERR_NULL;
+            if (!aligned16(partials[i])) return TP_ERR_ALIGNMENT;
+            if (partials[i] == out) return TP_ERR_SHAPE;
+        }
+        if (M == 0) return TP_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        tpk::GemmArgs a{};
+        a.x = x_shard; a.w = w_shard; a.y = out;
+        a.M = M; a.N = N; a.K = K_shard;
+        a.out_dtype = TP_BF16;
+        if (M <= kSkinnyMaxM && t <= tpk::kMaxFusedPeers && N % 4 == 0) {
+            a.epi = tpk::EPI_REDUCE;
+            a.t = t;
+            a.rank = rank;
+            for (int i = 0; i < t; ++i) a.peers[i] = i == rank ? nullptr : partials[i];
+            return launch_linear(a, s);
+        }
+        // Two launches with the same arithmetic: the rank's bf16 partial is
+        // written to `out`, then summed in place with the others in rank order.
+        a.epi = tpk::EPI_STORE;
+        const int st2 = launch_linear(a, s);
+        if (st2 != TP_OK) return st2;
+        tpk::PartialPtrs ptrs;
+        std::memset(&ptrs, 0, sizeof(ptrs));
+        for (int i = 0; i < t; ++i) ptrs.p[i] = i == rank ? out : partials[i];
+        const hipError_t e = tpk::launch_reduce(ptrs, t, M * N, TP_BF16, out, TP_BF16, s);
+        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
     } catch (...) {
         return TP_ERR_HIP;
     }

@@ -53,6 +53,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return u >> 16;
 }
 
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// SiLU of [P1 3.2]'s SwiGLU MLP: g / (1 + e^-g). For very negative g, e^-g
+// overflows to +inf and the quotient is -0, the limit; for large positive g
+// it is g. Shared by the SwiGLU kernel and the fused GEMM epilogue so both
+// give the same bits.
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
 // Pack two fp32 values as bf16 into one 32-bit word (lo in bits 0..15).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);

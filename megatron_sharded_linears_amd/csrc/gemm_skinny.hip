@@ -20,6 +20,12 @@
 //     arrive on a tile (one atomic counter per tile) sums the partials in
 //     split order, so the result does not depend on arrival order. Partials
 //     travel through relaxed device-scope atomic stores and loads.
+//   * Fused epilogues. SwiGLU: each 16-row MFMA block holds 8 gate rows and
+//     the same 8 up rows, so lanes 0-31 own gate outputs whose up partners
+//     sit 32 lanes higher; one cross-lane swap pairs them and the block
+//     writes 8 SwiGLU outputs per token. Reduce: the rank's rounded partial is
+//     summed with the other ranks' partials in rank order and rounded once.
+//     Both give the same bits as the separate kernels.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,19 +49,19 @@ struct SkinnyCfg {
     static constexpr int kGroupK = kWaveK * NWK;       // K per workgroup
     static constexpr int kTokens = 16 * MT;
     static constexpr int kXStride = kGroupK + 8;       // LDS row stride (elements), 16 B pad
-    static constexpr int kRedBytes = NWK > 1 ? (NWK - 1) * NWN * MT * 4 * 64 * 4 : 0;
+    static constexpr int kOwn = (MT + NWK - 1) / NWK;   // token tiles each wave finishes
+    static constexpr int kRedBytes = NWK > 1 ? NWK * NWN * MT * 4 * 64 * 4 : 0;
     // LDS for xrows staged token rows plus the cross-wave reduction buffer
     static int lds_bytes(int xrows) { return (XD ? 0 : xrows * kXStride * 2) + kRedBytes; }
 };
 
 __device__ __forceinline__ void store_out4(const GemmArgs& a, int64_t m, int64_t n, const float* v) {
     // 4 consecutive outputs y[m, n..n+3] (+ bias), bf16 or fp32.
-    float o[4];
+    float o[4] = {v[0], v[1], v[2], v[3]};
+    if (a.bias != nullptr) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float b = 0.f;
-        if (a.bias != nullptr && n + i < a.N) b = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[n + i]);
-        o[i] = v[i] + b;
+        for (int i = 0; i < 4; ++i)
+            if (n + i < a.N) o[i] += bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[n + i]);
     }
     const int64_t base = m * a.N + n;
     const bool full = (n + 3 < a.N) && (a.N % 4 == 0);
@@ -76,7 +82,95 @@ __device__ __forceinline__ void store_out4(const GemmArgs& a, int64_t m, int64_t
     }
 }
 
-template <int MT, int KSTEPS, int NWN, int NWK, int XD>
+// Weight row of kernel row v, or -1 past the end. EPI_SWIGLU pairs gate and
+// up rows in 16-row blocks: rows 8 b + r (r < 8) of gate and of up form block b.
+template <int EPI>
+__device__ __forceinline__ int64_t weight_row(const GemmArgs& a, int64_t v) {
+    if constexpr (EPI != EPI_SWIGLU) return v < a.N ? v : -1;
+    const int64_t j = (v >> 4) * 8 + (v & 7);
+    if (j >= a.i_half) return -1;
+    return (v & 8) ? a.i_half + j : j;
+}
+
+// Other ranks' values of one lane's 4 outputs, bf16 pairs indexed by rank
+// (the own slot unused). Loaded before they are needed: at the start of a
+// tile when the lane finishes one token tile, else just before the sum.
+// EPI_REDUCE launches have N % 4 == 0, so a lane's 4 outputs are one 8-byte
+// load per rank. The guards are uniform and one-sided (a branch that merged
+// two values would make each load wait for the one before); lanes past the
+// edge read the start of the peer's buffer instead and discard it.
+struct PeerVals { uint2 v[kMaxFusedPeers]; };
+
+__device__ __forceinline__ void load_peers(const GemmArgs& a, int64_t m, int64_t n, PeerVals& p) {
+    const bool ok = m < a.M && n < a.N;
+    const int64_t base = ok ? m * a.N + n : 0;
+#pragma unroll
+    for (int r = 0; r < kMaxFusedPeers; ++r) {
+        if (r < a.t && r != a.rank)
+            p.v[r] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.peers[r]) + base);
+    }
+}
+
+// EPI_REDUCE: out[m, n..n+3] = bf16(sum over ranks in order from rank 0),
+// the own partial rounded as a bf16 partial buffer holds it.
+__device__ __forceinline__ void reduce_out4(const GemmArgs& a, int64_t m, int64_t n, const float* v,
+                                            const PeerVals& p) {
+    // Unrolled with constant indices (the values stay in registers); the
+    // guards are uniform, so only the t ranks' iterations execute.
+    float own[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) own[i] = round_bf16(v[i]);
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < kMaxFusedPeers; ++r) {
+        if (r < a.t) {
+            float q[4];
+            if (r == a.rank) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) q[i] = own[i];
+            } else {
+                q[0] = bf16_to_f32(p.v[r].x & 0xFFFFu);
+                q[1] = bf16_to_f32(p.v[r].x >> 16);
+                q[2] = bf16_to_f32(p.v[r].y & 0xFFFFu);
+                q[3] = bf16_to_f32(p.v[r].y >> 16);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = r == 0 ? q[i] : o[i] + q[i];
+        }
+    }
+    uint16_t* y = reinterpret_cast<uint16_t*>(a.y) + m * a.N + n;
+    *reinterpret_cast<uint2*>(y) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+}
+
+// Final values of one lane: D rows n..n+3 (kernel row space) of token m.
+// Every lane of the wave must call it (the SwiGLU pairing swaps lanes).
+template <int EPI>
+__device__ __forceinline__ void finish4(const GemmArgs& a, int64_t m, int64_t n, const float* v, int lane,
+                                        const PeerVals& peers) {
+    if constexpr (EPI == EPI_SWIGLU) {
+        float u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(v[i], 32);
+        const int64_t j = (n >> 4) * 8 + (n & 7);      // first of the 4 gate columns
+        if (lane < 32 && m < a.M && j < a.i_half) {
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = silu_f32(round_bf16(v[i])) * round_bf16(u[i]);
+            uint16_t* y = reinterpret_cast<uint16_t*>(a.y) + m * a.i_half + j;
+            if (j + 3 < a.i_half && a.i_half % 4 == 0) {
+                *reinterpret_cast<uint2*>(y) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            } else {
+                for (int i = 0; i < 4; ++i) if (j + i < a.i_half) y[i] = (uint16_t)f32_to_bf16(o[i]);
+            }
+        }
+        return;
+    }
+    if (m >= a.M || n >= a.N) return;
+    if constexpr (EPI == EPI_REDUCE) reduce_out4(a, m, n, v, peers);
+    else store_out4(a, m, n, v);
+}
+
+template <int MT, int KSTEPS, int NWN, int NWK, int XD, int EPI>
 __global__ void __launch_bounds__(64 * NWN * NWK)
 skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restrict__ ws,
               unsigned* __restrict__ counters) {
@@ -94,10 +188,27 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     const int64_t M = a.M, N = a.N, K = a.K;
     const int split = blockIdx.y;
     const int64_t k_group = (int64_t)split * C::kGroupK;
+    // Neighbouring row tiles share the 128-byte lines of the output (and of
+    // the other ranks' partials). Workgroup b runs on XCD b mod 8, so an
+    // unsplit grid hands each XCD a contiguous range of tiles (a permutation
+    // of [0, grid) per round; later rounds add the grid size).
     int64_t tile = blockIdx.x;
+    if (splits == 1 && gridDim.x % 8 == 0) tile = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
 
     const bf16_t* __restrict__ X = reinterpret_cast<const bf16_t*>(a.x);
     const bf16_t* __restrict__ W = reinterpret_cast<const bf16_t*>(a.w);
+
+    // 0. EPI_REDUCE with one token tile per wave: the other ranks' values for
+    //    the first tile are loaded before anything else, so they arrive while
+    //    the weights stream (later tiles of a persistent loop load theirs
+    //    just before the sum).
+    constexpr bool kPrefetchPeers = EPI == EPI_REDUCE && C::kOwn == 1;
+    PeerVals peers;
+    const int64_t m_own0 = 16 * wk + (lane & 15);          // token of the first owned tile
+    if constexpr (kPrefetchPeers) {
+        if (splits == 1 && wk < MT) load_peers(a, m_own0, tile * C::kRows + wn * 16 + 4 * (lane >> 4), peers);
+    }
+    bool first_tile = true;
 
     // 1. Stage X[0:xrows, k_group : k_group + kGroupK] into registers (issued
     //    first so that waiting for it does not wait for the weight stream).
@@ -123,16 +234,16 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     const int64_t k_wave = k_group + (int64_t)wk * C::kWaveK + 8 * (lane >> 4);
     uint4 wr[KSTEPS];
     auto load_w = [&](int64_t t, uint4* dst) {
-        const int64_t n_lane = t * C::kRows + wn * 16 + (lane & 15);
+        const int64_t row = weight_row<EPI>(a, t * C::kRows + wn * 16 + (lane & 15));
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             const int64_t k = k_wave + 32 * s;
             dst[s] = make_uint4(0u, 0u, 0u, 0u);
-            if (n_lane < N && k < K) {
+            if (row >= 0 && k < K) {
 #if TP_SKINNY_W_NT
-                dst[s] = ld_nt16(W + n_lane * K + k);
+                dst[s] = ld_nt16(W + row * K + k);
 #else
-                dst[s] = *reinterpret_cast<const uint4*>(W + n_lane * K + k);
+                dst[s] = *reinterpret_cast<const uint4*>(W + row * K + k);
 #endif
             }
         }
@@ -168,7 +279,13 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
 
     const int xcol = wk * C::kWaveK + 8 * (lane >> 4);
     f32x4_t acc[MT];
+    // Wave (wn, wk) finishes token tiles mt = wk + NWK o (o < kOwn): its own
+    // accumulators when NWK == 1, else the in-order sum of the NWK waves'
+    // accumulators read back from LDS.
+    float fin[C::kOwn][4];
     for (;;) {
+        const int64_t n_out = tile * C::kRows + wn * 16 + 4 * (lane >> 4);   // first of this lane's 4 rows
+
         // Prefetch the next tile's weights (unsplit grids loop over tiles).
         const int64_t next = tile + gridDim.x;
         const bool has_next = splits == 1 && next < ntiles;
@@ -196,43 +313,51 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
         }
 
         // 5. Sum the NWK waves that share rows, in wave order, through LDS.
-        if (NWK > 1) {
-            if (wk > 0) {
+        if constexpr (NWK > 1) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        red[((((wk - 1) * NWN + wn) * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
-            }
+                for (int i = 0; i < 4; ++i)
+                    red[(((wk * NWN + wn) * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
             __syncthreads();
-            if (wk == 0) {
 #pragma unroll
-                for (int w = 1; w < NWK; ++w)
+            for (int o = 0; o < C::kOwn; ++o) {
+                const int mt = wk + NWK * o;
+                if (mt < MT) {
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
+                    for (int i = 0; i < 4; ++i) {
+                        float v = red[(((0 * NWN + wn) * MT + mt) * 4 + i) * 64 + lane];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[mt][i] += red[((((w - 1) * NWN + wn) * MT + mt) * 4 + i) * 64 + lane];
+                        for (int w = 1; w < NWK; ++w) v += red[(((w * NWN + wn) * MT + mt) * 4 + i) * 64 + lane];
+                        fin[o][i] = v;
+                    }
+                }
             }
             __syncthreads();   // the buffer is rewritten for the next tile
+        } else {
+#pragma unroll
+            for (int o = 0; o < C::kOwn; ++o)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fin[o][i] = acc[o][i];
         }
         if (splits > 1) break;
 
-        const int64_t n_out = tile * C::kRows + wn * 16 + 4 * (lane >> 4);
-        if (wk == 0) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
+        for (int o = 0; o < C::kOwn; ++o) {
+            const int mt = wk + NWK * o;
+            if (mt < MT) {                       // wave-uniform: every lane calls finish4
                 const int64_t m = 16 * mt + (lane & 15);
-                if (m < M && n_out < N) {
-                    float v[4] = {acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]};
-                    store_out4(a, m, n_out, v);
+                if constexpr (EPI == EPI_REDUCE) {
+                    if (!kPrefetchPeers || !first_tile) load_peers(a, m, n_out, peers);
                 }
+                finish4<EPI>(a, m, n_out, fin[o], lane, peers);
             }
         }
         if (!has_next) return;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) wr[s] = wnext[s];
         tile = next;
+        first_tile = false;
     }
 
     const int64_t n_out = tile * C::kRows + wn * 16 + 4 * (lane >> 4);   // first of this lane's 4 outputs
@@ -248,23 +373,22 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     //    invalidates the whole L2 of the XCD, once per workgroup.
     // 4 consecutive floats per lane: two 64-bit stores when 8-byte aligned.
     const bool pair = (N % 2 == 0) && (n_out + 3 < N);
-    if (wk == 0) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int64_t m = 16 * mt + (lane & 15);
-            if (m < M) {
-                float* p = ws + ((int64_t)split * M + m) * N + n_out;
-                if (pair) {
-                    const uint64_t lo = (uint64_t)__float_as_uint(acc[mt][0]) | ((uint64_t)__float_as_uint(acc[mt][1]) << 32);
-                    const uint64_t hi = (uint64_t)__float_as_uint(acc[mt][2]) | ((uint64_t)__float_as_uint(acc[mt][3]) << 32);
-                    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(reinterpret_cast<uint64_t*>(p) + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                } else {
+    for (int o = 0; o < C::kOwn; ++o) {
+        const int mt = wk + NWK * o;
+        const int64_t m = 16 * mt + (lane & 15);
+        if (mt < MT && m < M) {
+            float* p = ws + ((int64_t)split * M + m) * N + n_out;
+            if (pair) {
+                const uint64_t lo = (uint64_t)__float_as_uint(fin[o][0]) | ((uint64_t)__float_as_uint(fin[o][1]) << 32);
+                const uint64_t hi = (uint64_t)__float_as_uint(fin[o][2]) | ((uint64_t)__float_as_uint(fin[o][3]) << 32);
+                __hip_atomic_store(reinterpret_cast<uint64_t*>(p), lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(reinterpret_cast<uint64_t*>(p) + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (n_out + i < N)
-                            __hip_atomic_store(p + i, acc[mt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+                for (int i = 0; i < 4; ++i)
+                    if (n_out + i < N)
+                        __hip_atomic_store(p + i, fin[o][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -280,12 +404,14 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     // 7. Last workgroup on this tile: sum the partials in split order. The
     //    loads of up to 8 splits are issued back to back before any is used,
     //    so they cost one memory round trip, not one each.
-    if (wk == 0) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+    for (int o = 0; o < C::kOwn; ++o) {
+        const int mt = wk + NWK * o;
+        if (mt < MT) {                           // wave-uniform: every lane calls finish4
             const int64_t m = 16 * mt + (lane & 15);
+            if constexpr (EPI == EPI_REDUCE) load_peers(a, m, n_out, peers);
+            float v[4] = {0.f, 0.f, 0.f, 0.f};
             if (m < M && n_out < N) {
-                float v[4] = {0.f, 0.f, 0.f, 0.f};
                 for (int sp0 = 0; sp0 < splits; sp0 += 8) {
                     float t[8][4];
 #pragma unroll
@@ -314,8 +440,8 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
 #pragma unroll
                             for (int i = 0; i < 4; ++i) v[i] += t[j][i];
                 }
-                store_out4(a, m, n_out, v);
             }
+            finish4<EPI>(a, m, n_out, v, lane, peers);
         }
     }
     if (tid == 0) atomicExch(&counters[tile], 0u);
@@ -326,14 +452,17 @@ typedef int (*SkinnyLdsFn)(int);
 
 struct SkinnyEntry {
     int mt, ksteps, nwn, nwk, xd;
-    SkinnyFn fn;
+    SkinnyFn fn[3];   // by epilogue: EPI_STORE, EPI_SWIGLU, EPI_REDUCE
     int threads;
     SkinnyLdsFn lds;
     int group_k;
 };
 
-#define TP_SK(MT, KS, NN, NK, XD)                                                          \
-    {MT, KS, NN, NK, XD, skinny_kernel<MT, KS, NN, NK, XD>, SkinnyCfg<MT, KS, NN, NK, XD>::kThreads, \
+#define TP_SK(MT, KS, NN, NK, XD)                                                                  \
+    {MT, KS, NN, NK, XD,                                                                           \
+     {skinny_kernel<MT, KS, NN, NK, XD, EPI_STORE>, skinny_kernel<MT, KS, NN, NK, XD, EPI_SWIGLU>,    \
+      skinny_kernel<MT, KS, NN, NK, XD, EPI_REDUCE>},                                               \
+     SkinnyCfg<MT, KS, NN, NK, XD>::kThreads,                                                       \
      SkinnyCfg<MT, KS, NN, NK, XD>::lds_bytes, SkinnyCfg<MT, KS, NN, NK, XD>::kGroupK}
 // M <= 16: every variant. M in (16, 64]: the ones that fit in registers.
 #define TP_SK_MT1                                                                                    \
@@ -356,8 +485,8 @@ const SkinnyEntry kSkinnyTable[] = {TP_SK_MT1, TP_SK_MTN(2), TP_SK_MTN(4)};
 
 constexpr int kMaxLds = 160 * 1024 - 1024;   // dynamic LDS; the rest is the kernel's static LDS
 constexpr int kNumSkinny = sizeof(kSkinnyTable) / sizeof(kSkinnyTable[0]);
-int g_lds_attr[kNumSkinny] = {};            // dynamic LDS limit set so far per kernel
-int g_occupancy[kNumSkinny][2] = {};     // cached (lds bytes, workgroups per CU)
+int g_lds_attr[kNumSkinny][3] = {};         // dynamic LDS limit set so far per kernel
+int g_occupancy[kNumSkinny][3][2] = {};     // cached (lds bytes, workgroups per CU)
 int g_num_cus[16] = {};
 
 int find_skinny(const SkinnyPlan& p) {
@@ -464,14 +593,17 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
     const int idx = find_skinny(p);
     if (idx < 0) return hipErrorInvalidValue;
     const SkinnyEntry* e = &kSkinnyTable[idx];
+    const int epi = a.epi;
+    if (epi < 0 || epi > 2) return hipErrorInvalidValue;
+    const SkinnyFn fn = e->fn[epi];
     const int xrows = xrows_for(*e, a.M);
     const int lds = e->lds(xrows);
     if (lds > kMaxLds) return hipErrorInvalidValue;
-    if (lds > 65536 && lds > g_lds_attr[idx]) {
-        const hipError_t ae = hipFuncSetAttribute(reinterpret_cast<const void*>(e->fn),
+    if (lds > 65536 && lds > g_lds_attr[idx][epi]) {
+        const hipError_t ae = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (ae != hipSuccess) return ae;
-        g_lds_attr[idx] = lds;
+        g_lds_attr[idx][epi] = lds;
     }
     int64_t grid_x = p.ntiles;
     if (p.splits == 1) {
@@ -485,19 +617,20 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
             he = hipDeviceGetAttribute(&g_num_cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
             if (he != hipSuccess) return he;
         }
-        if (g_occupancy[idx][0] != lds || g_occupancy[idx][1] == 0) {
+        int* occ = g_occupancy[idx][epi];
+        if (occ[0] != lds || occ[1] == 0) {
             int per_cu = 0;
-            he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(e->fn),
+            he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn),
                                                               e->threads, lds);
             if (he != hipSuccess) return he;
-            g_occupancy[idx][0] = lds;
-            g_occupancy[idx][1] = per_cu > 0 ? per_cu : 1;
+            occ[0] = lds;
+            occ[1] = per_cu > 0 ? per_cu : 1;
         }
-        const int64_t cap = (int64_t)g_occupancy[idx][1] * g_num_cus[dev];
+        const int64_t cap = (int64_t)occ[1] * g_num_cus[dev];
         if (grid_x > cap) grid_x = cap;
     }
     dim3 grid((unsigned)grid_x, (unsigned)p.splits);
-    hipLaunchKernelGGL(e->fn, grid, dim3(e->threads), lds, s, a, p.splits, p.ntiles, xrows, ws.partials,
+    hipLaunchKernelGGL(fn, grid, dim3(e->threads), lds, s, a, p.splits, p.ntiles, xrows, ws.partials,
                        ws.counters);
     return hipGetLastError();
 }

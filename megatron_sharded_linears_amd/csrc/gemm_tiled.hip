@@ -15,6 +15,9 @@
 //     k-slices of a range stay in that XCD's L2 while its CUs reuse them.
 //   * Epilogue: accumulators go through LDS one block row at a time, then all
 //     threads write rows of Y in 16-byte runs (bias added there).
+//   * SwiGLU epilogue: a tile's first BN/2 rows are gate rows and its last
+//     BN/2 the same up rows, i.e. the two wave rows' halves of the LDS slab,
+//     so a thread reads a gate run and its up run and writes 4 outputs.
 //
 // tiled_dma_kernel (K % 32 == 0): k-tiles of 32 land in LDS by direct
 // global -> LDS loads in a 4-stage ring (details below). tiled_reg_kernel
@@ -43,18 +46,42 @@ struct TileCfg {
     static constexpr int kLdsBytes = 2 * kStageElems * 2;
 };
 
+// Weight row of kernel row v for tiles of BN rows, or -1 past the end.
+// EPI_SWIGLU: tile b holds gate rows [b BN/2, (b+1) BN/2), then the same up rows.
+template <int BN>
+__device__ __forceinline__ int64_t tile_w_row(const GemmArgs& a, int64_t v) {
+    if (a.epi != EPI_SWIGLU) return v < a.N ? v : -1;
+    const int64_t j = (v / BN) * (BN / 2) + (v % (BN / 2));
+    if (j >= a.i_half) return -1;
+    return (v % BN) >= BN / 2 ? a.i_half + j : j;
+}
+
+// SwiGLU of 4 gate values and their up values: y[m, j..j+3], bf16, with the
+// gate_up outputs rounded to bf16 first as the unfused path stores them.
+__device__ __forceinline__ void swiglu_out4(const GemmArgs& a, int64_t m, int64_t j, float4 g, float4 u) {
+    const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = silu_f32(round_bf16(gv[i])) * round_bf16(uv[i]);
+    uint16_t* y = reinterpret_cast<uint16_t*>(a.y) + m * a.i_half + j;
+    if (j + 3 < a.i_half && a.i_half % 4 == 0) {
+        *reinterpret_cast<uint2*>(y) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    } else {
+        for (int i = 0; i < 4; ++i) if (j + i < a.i_half) y[i] = (uint16_t)f32_to_bf16(o[i]);
+    }
+}
+
 // Element offset of (row, 16-byte chunk c) in a [rows][64] bf16 LDS tile.
 __device__ __forceinline__ int swz(int row, int c) {
     return row * kBK + ((c ^ ((row >> 1) & 7)) << 3);
 }
 
 __device__ __forceinline__ void store_out4(const GemmArgs& a, int64_t m, int64_t n, const float* v) {
-    float o[4];
+    float o[4] = {v[0], v[1], v[2], v[3]};
+    if (a.bias != nullptr) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float b = 0.f;
-        if (a.bias != nullptr && n + i < a.N) b = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[n + i]);
-        o[i] = v[i] + b;
+        for (int i = 0; i < 4; ++i)
+            if (n + i < a.N) o[i] += bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[n + i]);
     }
     const int64_t base = m * a.N + n;
     const bool full = (n + 3 < a.N) && (a.N % 4 == 0);
@@ -106,9 +133,9 @@ tiled_reg_kernel(GemmArgs a, int tiles_n, int tiles_m) {
         const int64_t k_ = (K0) + cchunk * 8;                                               \
         const bool kin_ = k_ < K;                                                           \
         _Pragma("unroll") for (int j = 0; j < C::kWChunks; ++j) {                           \
-            const int64_t r_ = n0 + crow + 32 * j;                                          \
+            const int64_t r_ = tile_w_row<BN>(a, n0 + crow + 32 * j);                        \
             wr[j] = u32x4_t{0u, 0u, 0u, 0u};                                                \
-            if (kin_ && r_ < N) wr[j] = *reinterpret_cast<const u32x4_t*>(W + r_ * K + k_); \
+            if (kin_ && r_ >= 0) wr[j] = *reinterpret_cast<const u32x4_t*>(W + r_ * K + k_); \
         }                                                                                   \
         _Pragma("unroll") for (int j = 0; j < C::kXChunks; ++j) {                           \
             const int64_t r_ = m0 + crow + 32 * j;                                          \
@@ -198,6 +225,20 @@ tiled_reg_kernel(GemmArgs a, int tiles_n, int tiles_m) {
         // 2 slabs x BM tokens x 8 runs of 4 rows
         constexpr int kRuns = 2 * BM * 8;
         static_assert(kRuns % kThreads == 0, "store loop must divide evenly");
+        static_assert((kRuns / 2) % kThreads == 0, "SwiGLU store loop must divide evenly");
+        if (a.epi == EPI_SWIGLU) {
+#pragma unroll
+            for (int it = 0; it < kRuns / 2 / kThreads; ++it) {
+                const int q = tid + it * kThreads;
+                const int mt = q >> 3;
+                const int run = q & 7;
+                const int64_t m = m0 + mt;
+                const int64_t j = (int64_t)tile_n * C::kWN + i * 32 + 4 * run;
+                if (m < M && j < a.i_half)
+                    swiglu_out4(a, m, j, *reinterpret_cast<const float4*>(slab + mt * kSlabStride + 4 * run),
+                                *reinterpret_cast<const float4*>(slab + (BM + mt) * kSlabStride + 4 * run));
+            }
+        } else
 #pragma unroll
         for (int it = 0; it < kRuns / kThreads; ++it) {
             const int q = tid + it * kThreads;
@@ -295,9 +336,14 @@ tiled_dma_kernel(GemmArgs a, int tiles_n, int tiles_m) {
         const int rbase = (is_w ? instr : instr - C::kInstrW) * 16;
         const int r = rbase + (lane >> 2);
         const int c = (lane & 3) ^ ((r >> 2) & 3);
-        int64_t g = is_w ? n0 + r : m0 + r;
-        const int64_t lim = is_w ? N : M;
-        if (g > lim - 1) g = lim - 1;
+        int64_t g;
+        if (is_w) {
+            g = tile_w_row<BN>(a, n0 + r);
+            if (g < 0) g = 0;
+        } else {
+            g = m0 + r;
+            if (g > M - 1) g = M - 1;
+        }
         src[q] = (is_w ? W : X) + g * K + 8 * c;
         dst_off[q] = (is_w ? 0 : BN * 64) + rbase * 64;
     });
@@ -387,6 +433,20 @@ tiled_dma_kernel(GemmArgs a, int tiles_n, int tiles_m) {
         __syncthreads();
         constexpr int kRuns = 2 * BM * 8;
         static_assert(kRuns % C::kThreadsWG == 0, "store loop must divide evenly");
+        static_assert((kRuns / 2) % C::kThreadsWG == 0, "SwiGLU store loop must divide evenly");
+        if (a.epi == EPI_SWIGLU) {
+#pragma unroll
+            for (int it = 0; it < kRuns / 2 / C::kThreadsWG; ++it) {
+                const int q = tid + it * C::kThreadsWG;
+                const int mt = q >> 3;
+                const int run = q & 7;
+                const int64_t m = m0 + mt;
+                const int64_t j = (int64_t)tile_n * C::kWN + i * 32 + 4 * run;
+                if (m < M && j < a.i_half)
+                    swiglu_out4(a, m, j, *reinterpret_cast<const float4*>(slab + mt * kSlabStride + 4 * run),
+                                *reinterpret_cast<const float4*>(slab + (BM + mt) * kSlabStride + 4 * run));
+            }
+        } else
 #pragma unroll
         for (int it = 0; it < kRuns / C::kThreadsWG; ++it) {
             const int q = tid + it * C::kThreadsWG;
@@ -436,6 +496,8 @@ int g_tiled_force = -1;
 int tiled_variant_count() { return kNumTiled; }
 void tiled_force_variant(int idx) { g_tiled_force = idx; }
 
+// EPI_SWIGLU: a.N is 2 * i_half on entry (used to pick the tile shape); the
+// kernel's row space is then whole tiles of paired gate and up rows.
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     // Kernel choice, from MI355X measurements at the Llama-8B and Qwen-32B
     // prefill shard shapes: 256 x 256 tiles on 8 waves when they give at
@@ -458,11 +520,13 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
         if (ae != hipSuccess) return ae;
         g_tiled_attr[best] = true;
     }
-    const int tn = (int)((a.N + e.bn - 1) / e.bn);
-    const int tm = (int)((a.M + e.bm - 1) / e.bm);
+    GemmArgs b = a;
+    if (a.epi == EPI_SWIGLU) b.N = (int64_t)e.bn * ((a.i_half + e.bn / 2 - 1) / (e.bn / 2));
+    const int tn = (int)((b.N + e.bn - 1) / e.bn);
+    const int tm = (int)((b.M + e.bm - 1) / e.bm);
     const int ntiles = tn * tm;
     const int grid = ((ntiles + kXcds - 1) / kXcds) * kXcds;
-    hipLaunchKernelGGL(e.fn, dim3(grid), dim3(e.threads), e.lds, s, a, tn, tm);
+    hipLaunchKernelGGL(e.fn, dim3(grid), dim3(e.threads), e.lds, s, b, tn, tm);
     return hipGetLastError();
 }
 

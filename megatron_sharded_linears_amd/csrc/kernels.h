@@ -39,7 +39,21 @@ hipError_t launch_vocab_embed(const int32_t* ids, int64_t M, const void* table, 
 hipError_t launch_concat(const PartialPtrs& ptrs, int t, int64_t M, int64_t v_shard,
                          int64_t vocab, int dtype, void* out, hipStream_t s);
 
+// Epilogue of a linear.
+enum Epilogue : int {
+    EPI_STORE = 0,    // y = acc (+ bias), out_dtype
+    EPI_SWIGLU = 1,   // weight rows [gate (i_half); up (i_half)]; y[m, j] = silu(bf16(g)) * bf16(u), bf16
+    EPI_REDUCE = 2,   // y = bf16(sum over t partials in order), own = bf16(acc) at position `rank`
+};
+
+constexpr int kMaxFusedPeers = 16;   // t limit of the fused reduce epilogue
+
 // Linear Y[M, N] = X[M, K] W[N, K]^T (+ bias[N]); out_dtype TP_BF16 / TP_F32.
+// With EPI_SWIGLU, N is the kernel's row space (groups of gate rows paired
+// with the same up rows, see the kernels), the weight holds 2 * i_half rows
+// and y is [M, i_half]. With EPI_REDUCE (decode kernel only, N % 4 == 0), y
+// is [M, N] bf16 and peers[i] (bf16 [M, N], i != rank) are the other ranks'
+// partials.
 struct GemmArgs {
     const void* x;
     const void* w;
@@ -47,6 +61,10 @@ struct GemmArgs {
     void* y;
     int64_t M, N, K;
     int out_dtype;
+    int epi;
+    int64_t i_half;     // EPI_SWIGLU
+    int t, rank;        // EPI_REDUCE
+    const void* peers[kMaxFusedPeers];
 };
 
 // Scratch for K split across workgroups: fp32 partial tiles and one arrival
@@ -80,7 +98,7 @@ bool skinny_plan_fits(const SkinnyPlan& p, int64_t M);   // LDS need for M token
 int64_t skinny_workspace_floats(const SkinnyPlan& p, int64_t M, int64_t N);
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace& ws, hipStream_t s);
 
-hipError_t launch_tiled(const GemmArgs& a, hipStream_t s);
+hipError_t launch_tiled(const GemmArgs& a, hipStream_t s);   // EPI_STORE or EPI_SWIGLU (a.N = 2 i_half)
 int tiled_variant_count();
 void tiled_force_variant(int idx);   // -1: automatic
 

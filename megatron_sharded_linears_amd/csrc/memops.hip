@@ -66,12 +66,6 @@ shard_copy_kernel(ShardMap m, const uint4* __restrict__ src, uint4* __restrict__
 
 // --------------------------------------------------------------------- swiglu
 
-__device__ __forceinline__ float silu_f32(float g) {
-    // g / (1 + e^-g). For very negative g, e^-g overflows to +inf and the
-    // quotient is -0, the limit; for large positive g it is g.
-    return g / (1.0f + __expf(-g));
-}
-
 __global__ void __launch_bounds__(kThreads)
 swiglu_kernel(const uint4* __restrict__ gu, int64_t M, int64_t i_vec, uint4* __restrict__ out) {
     const int64_t total = M * i_vec;

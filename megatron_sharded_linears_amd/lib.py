@@ -71,6 +71,8 @@ _PROTOS = {
     "tp_shard_weights": (_int, [_cfgp, _int, _int, _int, _vp, _vp, _vp]),
     "tp_column_linear": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
     "tp_swiglu": (_int, [_vp, _i64, _i64, _vp, _vp]),
+    "tp_column_linear_swiglu": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "tp_row_linear_reduce": (_int, [_vp, _i64, _i64, _vp, _i64, _ptr_array, _int, _int, _vp, _vp]),
     "tp_row_linear_partial": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp]),
     "tp_reduce_partials": (_int, [_ptr_array, _int, _i64, _int, _vp, _int, _vp]),
     "tp_vocab_embed": (_int, [_vp, _i64, _vp, _i64, _int, _int, _i64, _vp, _vp]),
@@ -226,6 +228,43 @@ def tp_swiglu(gu, out, stream=None):
         raise ValueError("tp_swiglu: out must be [M, gu.shape[1] / 2]")
     _check(_lib.tp_swiglu(_dev(gu, "gu", torch.bfloat16, 2), M, two_i // 2, _dev(out, "out", torch.bfloat16, 2),
                           _stream(stream)), "tp_swiglu")
+    return out
+
+
+def tp_column_linear_swiglu(x, w_gate_up, act, stream=None):
+    M, K = x.shape
+    two_i, K2 = w_gate_up.shape
+    if K != K2 or two_i % 2 or tuple(act.shape) != (M, two_i // 2):
+        raise ValueError("tp_column_linear_swiglu: need x [M, K], w_gate_up [2 I, K], act [M, I]")
+    _check(_lib.tp_column_linear_swiglu(_dev(x, "x", torch.bfloat16, 2), M, K,
+                                        _dev(w_gate_up, "w_gate_up", torch.bfloat16, 2), two_i // 2,
+                                        _dev(act, "act", torch.bfloat16, 2), _stream(stream)),
+           "tp_column_linear_swiglu")
+    return act
+
+
+def tp_row_linear_reduce(x_shard, w_shard, partials, rank, out, stream=None):
+    """`partials`: t entries; entry `rank` is ignored (None allowed), the others
+    are the other ranks' bf16 [M, N] partials."""
+    M, K, N = _linear_shapes(x_shard, w_shard, out, "tp_row_linear_reduce")
+    t = len(partials)
+    if t < 1 or t > TP_MAX_SHARDS:
+        raise ValueError("need 1..64 partials")
+    ptrs = []
+    for i, p in enumerate(partials):
+        if i == rank:
+            ptrs.append(0)
+            continue
+        _dev(p, f"partials[{i}]", torch.bfloat16, 2)
+        if tuple(p.shape) != (M, N):
+            raise ValueError(f"partials[{i}] must be [M, N]")
+        ptrs.append(p.data_ptr())
+    arr = (ctypes.c_void_p * t)(*ptrs)
+    _check(_lib.tp_row_linear_reduce(_dev(x_shard, "x_shard", torch.bfloat16, 2), M, K,
+                                     _dev(w_shard, "w_shard", torch.bfloat16, 2), N,
+                                     ctypes.cast(arr, _ptr_array), t, rank,
+                                     _dev(out, "out", torch.bfloat16, 2), _stream(stream)),
+           "tp_row_linear_reduce")
     return out
 
 

@@ -151,6 +151,28 @@ def test_elementwise_validation_before_any_hip_call():
     assert C.tp_shard_weights(ctypes.byref(cfg), 2, 0, 9, A, B, S) == -5
 
 
+def test_fused_calls_validate_before_any_hip_call():
+    f = C.tp_column_linear_swiglu
+    assert f(NULL, 16, 64, B, 32, Y, S) == -1
+    assert f(A, 16, 64, B, 0, Y, S) == -2                    # i_shard 0
+    assert f(A, 16, 60, B, 32, Y, S) == -4                   # K % 8
+    assert f(A, 16, 64, MIS, 32, Y, S) == -4
+    assert f(A, 0, 64, B, 12, Y, S) == 0                     # any i_shard; M == 0 no-op
+    g = C.tp_row_linear_reduce
+    arr = (ctypes.c_void_p * 4)(0x50000, 0, 0x60000, 0x70000)   # entry 1 is the calling rank
+    pp = ctypes.cast(arr, lib._ptr_array)
+    assert g(A, 0, 64, B, 32, pp, 4, 1, Y, S) == 0             # own entry may be NULL
+    assert g(A, 0, 64, B, 32, pp, 4, 2, Y, S) == -1            # another rank's entry NULL
+    assert g(A, 0, 64, B, 32, pp, 4, 4, Y, S) == -6            # rank == t
+    assert g(A, 0, 64, B, 32, pp, 0, 0, Y, S) == -6
+    assert g(A, 0, 64, B, 32, pp, 65, 0, Y, S) == -6
+    assert g(A, 0, 64, B, 32, None, 4, 1, Y, S) == -1
+    assert g(A, 16, 60, B, 32, pp, 4, 1, Y, S) == -4           # K % 8
+    assert g(A, 0, 64, B, 32, pp, 4, 1, ctypes.c_void_p(0x60000), S) == -2   # out is a peer's partial
+    mis = (ctypes.c_void_p * 2)(0, 0x60008)
+    assert g(A, 0, 64, B, 32, ctypes.cast(mis, lib._ptr_array), 2, 0, Y, S) == -4
+
+
 def test_tune_rejects_unbuilt_variants():
     assert C.tp_tune_skinny(3, 4, 2, 0) == -2
     assert C.tp_tune_skinny(8, 4, 2, 0) == 0

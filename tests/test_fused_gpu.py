@@ -1,0 +1,163 @@
+"""The fused calls: tp_column_linear_swiglu (gate_up linear with SwiGLU as
+its epilogue) and tp_row_linear_reduce (row-parallel linear with the sum over
+ranks as its epilogue). Each must give the same bits as the two separate
+calls it replaces — for every decode-kernel variant, both tiled shapes, split
+and unsplit K — and match the oracle on exact-integer and random inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from megatron_sharded_linears_amd import inputs as I
+from parity import assert_close, assert_within_bf16_ulps, bits, f64
+
+pytestmark = pytest.mark.gpu
+
+from megatron_sharded_linears_amd import lib  # noqa: E402
+from test_parity_gpu import SKINNY_VARIANTS  # noqa: E402
+
+DEV = "cuda"
+SEED = 9100
+
+
+def dev(t):
+    return t.to(DEV)
+
+
+def empty(shape, dtype=torch.bfloat16):
+    return torch.empty(shape, dtype=dtype, device=DEV)
+
+
+def separate_swiglu(x, w, i_s):
+    gu = empty((x.shape[0], 2 * i_s))
+    lib.tp_column_linear(x, w, gu)
+    act = empty((x.shape[0], i_s))
+    lib.tp_swiglu(gu, act)
+    return act
+
+
+def fused_swiglu(x, w, i_s):
+    act = empty((x.shape[0], i_s))
+    act.fill_(float("nan"))                      # every element must be written
+    lib.tp_column_linear_swiglu(x, w, act)
+    return act
+
+
+# (M, I_shard, K): Llama-8B t=8 decode (16, 1792, 4096) and t=16 (64, 896,
+# 4096), ragged tails, the tiled path (M > 64) with 256- and 128-row tiles
+SWIGLU_SHAPES = [(16, 1792, 4096), (64, 896, 4096), (1, 8, 64), (7, 904, 520), (33, 96, 1032),
+                 (65, 136, 200), (300, 520, 256), (256, 1024, 2048), (130, 64, 4104)]
+
+
+@pytest.mark.parametrize("M,Is,K", SWIGLU_SHAPES)
+def test_column_linear_swiglu_same_bits_as_separate_calls(M, Is, K):
+    x = dev(I.normal_bf16((SEED, 1, M, Is, K), (M, K)))
+    w = dev(I.normal_bf16((SEED, 2, M, Is, K), (2 * Is, K), 0.05))
+    got = fused_swiglu(x, w, Is)
+    assert np.array_equal(bits(got), bits(separate_swiglu(x, w, Is))), (M, Is, K)
+    # and the oracle's gate_up -> bf16 -> SwiGLU chain
+    gu = oracle.round_bf16(oracle.linear(f64(x.cpu()), f64(w.cpu())))
+    assert_close(f64(got), oracle.swiglu(gu[:, :Is], gu[:, Is:]), f"fused swiglu {(M, Is, K)}")
+
+
+@pytest.mark.parametrize("M,Is,K", [(16, 100, 256), (3, 13, 72), (64, 1, 8), (100, 37, 136)])
+def test_column_linear_swiglu_ragged_width_exact_integer(M, Is, K):
+    """I_shard not a multiple of 8 (no separate tp_swiglu to compare with):
+    inputs in {-1, 0, 1} with K <= 256 make gate and up exact in bf16, so the
+    only rounding is SwiGLU's own: within 1 bf16 ulp of the oracle."""
+    x = I.small_int_bf16((SEED, 3, M, Is, K), (M, K))
+    w = I.small_int_bf16((SEED, 4, M, Is, K), (2 * Is, K))
+    got = fused_swiglu(dev(x), dev(w), Is)
+    gu = oracle.linear(f64(x), f64(w))
+    assert np.array_equal(gu, oracle.round_bf16(gu))
+    assert_within_bf16_ulps(f64(got), oracle.swiglu(gu[:, :Is], gu[:, Is:]), 1, "ragged fused swiglu")
+
+
+@pytest.mark.parametrize("ks,nn,nk,xd", SKINNY_VARIANTS)
+def test_every_decode_variant_fused_epilogues(ks, nn, nk, xd):
+    lib.tp_tune_skinny(ks, nn, nk, xd)
+    try:
+        for (M, Is, K) in [(16, 136, 1032), (40, 48, 4104)]:
+            x = dev(I.normal_bf16((SEED, 5, M, Is, K), (M, K)))
+            w = dev(I.normal_bf16((SEED, 6, M, Is, K), (2 * Is, K), 0.05))
+            assert np.array_equal(bits(fused_swiglu(x, w, Is)), bits(separate_swiglu(x, w, Is))), (M, Is, K)
+        for (M, N, K, t, rank) in [(16, 200, 1032, 8, 3), (33, 64, 4104, 3, 0)]:
+            x = dev(I.normal_bf16((SEED, 7, M, N, K), (M, K)))
+            w = dev(I.normal_bf16((SEED, 8, M, N, K), (N, K), 0.05))
+            peers = [dev(I.normal_bf16((SEED, 9, M, N, i), (M, N))) for i in range(t)]
+            assert np.array_equal(bits(fused_reduce(x, w, peers, rank)), bits(separate_reduce(x, w, peers, rank)))
+    finally:
+        lib.tp_tune_skinny(0, 0, 0, 0)
+
+
+def separate_reduce(x, w, peers, rank):
+    parts = list(peers)
+    parts[rank] = empty((x.shape[0], w.shape[0]))
+    lib.tp_row_linear_partial(x, w, parts[rank])
+    out = empty((x.shape[0], w.shape[0]))
+    lib.tp_reduce_partials(parts, out)
+    return out
+
+
+def fused_reduce(x, w, peers, rank):
+    out = empty((x.shape[0], w.shape[0]))
+    out.fill_(float("nan"))
+    parts = list(peers)
+    parts[rank] = None
+    lib.tp_row_linear_reduce(x, w, parts, rank, out)
+    return out
+
+
+# (M, N, K_shard): Llama-8B t=8 o and down, t=16 o; ragged; tiled (M > 64)
+REDUCE_SHAPES = [(16, 4096, 512), (16, 4096, 1792), (64, 4096, 256), (5, 100, 40), (33, 130, 264),
+                 (100, 256, 128), (300, 72, 520)]
+
+
+@pytest.mark.parametrize("M,N,K", REDUCE_SHAPES)
+@pytest.mark.parametrize("t", [1, 2, 3, 8, 16, 17])
+def test_row_linear_reduce_same_bits_as_separate_calls(M, N, K, t):
+    x = dev(I.normal_bf16((SEED, 10, M, N, K), (M, K)))
+    w = dev(I.normal_bf16((SEED, 11, M, N, K), (N, K), 0.05))
+    peers = [dev(I.normal_bf16((SEED, 12, M, N, t, i), (M, N), 0.5)) for i in range(t)]
+    for rank in sorted({0, t // 2, t - 1}):
+        got = fused_reduce(x, w, peers, rank)
+        assert np.array_equal(bits(got), bits(separate_reduce(x, w, peers, rank))), (M, N, K, t, rank)
+    # the oracle: own partial rounded to bf16, then the in-order sum
+    own = oracle.round_bf16(oracle.linear(f64(x.cpu()), f64(w.cpu())))
+    ps = [f64(p) for p in peers]
+    ps[t - 1] = own
+    assert_close(f64(got), oracle.all_reduce_sum(ps), f"fused reduce {(M, N, K, t)}")
+
+
+@pytest.mark.parametrize("M,N,K,t", [(16, 4096, 192, 8), (64, 300, 72, 16), (90, 128, 200, 4), (1, 8, 8, 2)])
+def test_row_linear_reduce_exact_integer(M, N, K, t):
+    """Small integers everywhere, sized so that the own partial (|p| <= K)
+    and the sum (|s| <= K + 8 (t - 1)) stay within 256, where every integer
+    is a bf16 value: the result equals the oracle exactly."""
+    x = I.small_int_bf16((SEED, 13, M, N, K), (M, K))
+    w = I.small_int_bf16((SEED, 14, M, N, K), (N, K))
+    peers = [I.small_int_bf16((SEED, 15, M, N, i), (M, N), -8, 8) for i in range(t)]
+    rank = t // 2
+    got = fused_reduce(dev(x), dev(w), [dev(p) for p in peers], rank)
+    ps = [f64(p) for p in peers]
+    ps[rank] = oracle.linear(f64(x), f64(w))
+    ref = oracle.all_reduce_sum(ps)
+    assert np.all(np.abs(ref) <= 256)
+    assert np.array_equal(f64(got), ref)
+
+
+def test_row_linear_reduce_skipping_a_rank_fails_the_tolerance():
+    """A planted mistake (one rank's partial left out of the sum, as a
+    dropped all-reduce contribution would) is caught by the parity bar."""
+    M, N, K, t, rank = 16, 512, 256, 4, 1
+    x = dev(I.normal_bf16((SEED, 16), (M, K)))
+    w = dev(I.normal_bf16((SEED, 17), (N, K), 0.05))
+    peers = [dev(I.normal_bf16((SEED, 18, i), (M, N), 0.5)) for i in range(t)]
+    got = f64(fused_reduce(x, w, peers, rank))
+    own = oracle.round_bf16(oracle.linear(f64(x.cpu()), f64(w.cpu())))
+    ps = [f64(p) for p in peers]
+    ps[rank] = own
+    assert_close(got, oracle.all_reduce_sum(ps), "fused reduce")
+    with pytest.raises(AssertionError):
+        assert_close(got, oracle.all_reduce_sum(ps[:2] + ps[3:]), "missing rank")
