@@ -53,6 +53,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return u >> 16;
 }
 
+// Workgroup barrier for data exchanged through LDS only. It waits for this
+// wave's LDS accesses but not for its outstanding global loads; a plain
+// __syncthreads() is a release of all memory and, since global loads and
+// stores share one counter on this GPU, waits for every load in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
 // SiLU of [P1 3.2]'s SwiGLU MLP: g / (1 + e^-g). For very negative g, e^-g

@@ -215,6 +215,10 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     //    Only the xrows = min(M, 16 MT) real token rows are staged.
     constexpr int kXPerThread = XD ? 1 : (C::kTokens * (C::kGroupK / 8) + C::kThreads - 1) / C::kThreads;
     const int x_chunks = XD ? 0 : xrows * (C::kGroupK / 8);
+    // Every load in this kernel is unconditional (out-of-range lanes read a
+    // clamped in-bounds address and their values are replaced by zeros where
+    // used), so the compiler can wait for exactly the loads it needs instead
+    // of for all of them.
     uint4 xr[kXPerThread];
     if (!XD) {
 #pragma unroll
@@ -223,29 +227,28 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
             const int m = c / (C::kGroupK / 8);
             const int kc = c % (C::kGroupK / 8);
             const int64_t k = k_group + kc * 8;
-            xr[j] = make_uint4(0u, 0u, 0u, 0u);
-            if (c < x_chunks && k < K)
-                xr[j] = *reinterpret_cast<const uint4*>(X + (int64_t)m * K + k);
+            const bool ok = c < x_chunks && k < K;
+            xr[j] = *reinterpret_cast<const uint4*>(X + (ok ? (int64_t)m * K + k : 0));
         }
     }
 
     // 2. Issue the first tile's weight loads (and, with XD, the wave's X
     //    fragments, which are the same for every tile).
+    // Weight rows past the end read row 0 (their outputs are never stored);
+    // k past K reads column 0 and is zeroed at the MFMA (k_ok).
     const int64_t k_wave = k_group + (int64_t)wk * C::kWaveK + 8 * (lane >> 4);
     uint4 wr[KSTEPS];
     auto load_w = [&](int64_t t, uint4* dst) {
         const int64_t row = weight_row<EPI>(a, t * C::kRows + wn * 16 + (lane & 15));
+        const bf16_t* wrow = W + (row >= 0 ? row : 0) * K;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             const int64_t k = k_wave + 32 * s;
-            dst[s] = make_uint4(0u, 0u, 0u, 0u);
-            if (row >= 0 && k < K) {
 #if TP_SKINNY_W_NT
-                dst[s] = ld_nt16(W + row * K + k);
+            dst[s] = ld_nt16(wrow + (k < K ? k : 0));
 #else
-                dst[s] = *reinterpret_cast<const uint4*>(W + row * K + k);
+            dst[s] = *reinterpret_cast<const uint4*>(wrow + (k < K ? k : 0));
 #endif
-            }
         }
     };
     load_w(tile, wr);
@@ -255,15 +258,15 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
         for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
+                // token rows past M feed outputs that are never stored
                 const int64_t m = 16 * mt + (lane & 15);
                 const int64_t k = k_wave + 32 * s;
-                xd[XD ? s : 0][XD ? mt : 0] = make_uint4(0u, 0u, 0u, 0u);
-                if (m < M && k < K)
-                    xd[XD ? s : 0][XD ? mt : 0] = *reinterpret_cast<const uint4*>(X + m * K + k);
+                xd[XD ? s : 0][XD ? mt : 0] =
+                    *reinterpret_cast<const uint4*>(X + (m < M ? m : 0) * K + (k < K ? k : 0));
             }
     }
 
-    // 3. X chunk -> LDS.
+    // 3. X chunk -> LDS (zeros past K).
     if (!XD) {
 #pragma unroll
         for (int j = 0; j < kXPerThread; ++j) {
@@ -271,10 +274,11 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
             if (c < x_chunks) {
                 const int m = c / (C::kGroupK / 8);
                 const int kc = c % (C::kGroupK / 8);
-                *reinterpret_cast<uint4*>(xs + m * C::kXStride + kc * 8) = xr[j];
+                const bool ok = k_group + kc * 8 < K;
+                *reinterpret_cast<uint4*>(xs + m * C::kXStride + kc * 8) = ok ? xr[j] : make_uint4(0u, 0u, 0u, 0u);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     const int xcol = wk * C::kWaveK + 8 * (lane >> 4);
@@ -297,7 +301,8 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
         for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, wr[s]);
+            const bool k_ok = k_wave + 32 * s < K;
+            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, k_ok ? wr[s] : make_uint4(0u, 0u, 0u, 0u));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 uint4 xv;
@@ -319,7 +324,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     red[(((wk * NWN + wn) * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int o = 0; o < C::kOwn; ++o) {
                 const int mt = wk + NWK * o;
@@ -333,7 +338,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
                     }
                 }
             }
-            __syncthreads();   // the buffer is rewritten for the next tile
+            lds_barrier();     // the buffer is rewritten for the next tile
         } else {
 #pragma unroll
             for (int o = 0; o < C::kOwn; ++o)
