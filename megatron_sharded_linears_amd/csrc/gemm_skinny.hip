@@ -555,7 +555,7 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
     if (mt == 1) {
         // Few 16-row tiles (qkv-sized N): split K 4 ways over 1024-wide
         // groups; otherwise cover K in one workgroup.
-        static const Rule few_tiles[] = {{1 << 30, 8, 1, 4, 1}};
+        static const Rule few_tiles[] = {{1 << 30, 8, 1, 4, 0}};
         static const Rule rules[] = {
             {512, 4, 1, 4, 1}, {1024, 8, 1, 4, 1}, {2048, 8, 1, 8, 0}, {4096, 16, 1, 8, 0},
             {5120, 20, 1, 8, 0},
@@ -565,8 +565,9 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
     } else if (mt == 4) {
         // M in (32, 64]: measured winners at the Llama-8B t=16 shard shapes.
         static const Rule rules_small_n[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 4, 1, 4, 1}};
-        static const Rule rules[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 8, 2, 2, 0}};
-        if (first_fit(N <= 1024 ? rules_small_n : rules, 3, &chosen)) return chosen;
+        static const Rule rules_mid_n[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 8, 1, 4, 0}};
+        static const Rule rules[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 8, 4, 2, 0}};
+        if (first_fit(N <= 1024 ? rules_small_n : N <= 2048 ? rules_mid_n : rules, 3, &chosen)) return chosen;
     }
     SkinnyPlan best{mt, 8, 4, 2, 0, 1, 1};
     double best_cost = -1.0;
