@@ -192,22 +192,25 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     // the other ranks' partials). Workgroup b runs on XCD b mod 8, so an
     // unsplit grid hands each XCD a contiguous range of tiles (a permutation
     // of [0, grid) per round; later rounds add the grid size).
-    int64_t tile = blockIdx.x;
-    if (splits == 1 && gridDim.x % 8 == 0) tile = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+    // (Read without branching, so that every kernel argument the first loads
+    // depend on arrives in one batch of scalar loads.)
+    const unsigned gx = gridDim.x;
+    // an empty asm that needs them: the compiler cannot defer these loads
+    // past the first branch
+    asm volatile("" ::"s"(splits), "s"(xrows), "s"(gx), "s"(a.t), "s"(a.rank));
+    const bool remap = splits == 1 && gx % 8 == 0;
+    int64_t tile = remap ? (int64_t)(blockIdx.x % 8) * (gx / 8) + blockIdx.x / 8 : (int64_t)blockIdx.x;
 
     const bf16_t* __restrict__ X = reinterpret_cast<const bf16_t*>(a.x);
     const bf16_t* __restrict__ W = reinterpret_cast<const bf16_t*>(a.w);
 
-    // 0. EPI_REDUCE with one token tile per wave: the other ranks' values for
-    //    the first tile are loaded before anything else, so they arrive while
-    //    the weights stream (later tiles of a persistent loop load theirs
-    //    just before the sum).
+    // EPI_REDUCE with one token tile per wave: the owner waves load the other
+    // ranks' values for the first tile right after its weights (step 2), so
+    // they arrive while the weights stream; later tiles of a persistent loop
+    // load theirs just before the sum.
     constexpr bool kPrefetchPeers = EPI == EPI_REDUCE && C::kOwn == 1;
     PeerVals peers;
     const int64_t m_own0 = 16 * wk + (lane & 15);          // token of the first owned tile
-    if constexpr (kPrefetchPeers) {
-        if (splits == 1 && wk < MT) load_peers(a, m_own0, tile * C::kRows + wn * 16 + 4 * (lane >> 4), peers);
-    }
     bool first_tile = true;
 
     // 1. Stage X[0:xrows, k_group : k_group + kGroupK] into registers (issued
@@ -251,19 +254,29 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
 #endif
         }
     };
-    load_w(tile, wr);
+    // XD: each step's weight and X fragments are issued together, so the
+    //     MFMA of step s waits only for loads 0..s (the load counter is in
+    //     order) and X never holds back the weight stream.
     uint4 xd[XD ? KSTEPS : 1][XD ? MT : 1];
-    if (XD) {
+    if constexpr (XD) {
+        const int64_t row = weight_row<EPI>(a, tile * C::kRows + wn * 16 + (lane & 15));
+        const bf16_t* wrow = W + (row >= 0 ? row : 0) * K;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
+        for (int s = 0; s < KSTEPS; ++s) {
+            const int64_t k = k_wave + 32 * s;
+            wr[s] = *reinterpret_cast<const uint4*>(wrow + (k < K ? k : 0));
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 // token rows past M feed outputs that are never stored
                 const int64_t m = 16 * mt + (lane & 15);
-                const int64_t k = k_wave + 32 * s;
-                xd[XD ? s : 0][XD ? mt : 0] =
-                    *reinterpret_cast<const uint4*>(X + (m < M ? m : 0) * K + (k < K ? k : 0));
+                xd[s][mt] = *reinterpret_cast<const uint4*>(X + (m < M ? m : 0) * K + (k < K ? k : 0));
             }
+        }
+    } else {
+        load_w(tile, wr);
+    }
+    if constexpr (kPrefetchPeers) {
+        if (splits == 1 && wk < MT) load_peers(a, m_own0, tile * C::kRows + wn * 16 + 4 * (lane >> 4), peers);
     }
 
     // 3. X chunk -> LDS (zeros past K).
@@ -290,11 +303,14 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     for (;;) {
         const int64_t n_out = tile * C::kRows + wn * 16 + 4 * (lane >> 4);   // first of this lane's 4 rows
 
-        // Prefetch the next tile's weights (unsplit grids loop over tiles).
+        // Prefetch the next tile's weights (unsplit grids with X staged in
+        // LDS loop over tiles; XD grids have one workgroup per tile).
         const int64_t next = tile + gridDim.x;
-        const bool has_next = splits == 1 && next < ntiles;
-        uint4 wnext[KSTEPS];
-        if (has_next) load_w(next, wnext);
+        const bool has_next = !XD && splits == 1 && next < ntiles;
+        uint4 wnext[XD ? 1 : KSTEPS];
+        if constexpr (!XD) {
+            if (has_next) load_w(next, wnext);
+        }
 
         // 4. MFMAs: acc[mt] holds D[n = 4*(lane/16) + i][m = 16*mt + lane%16].
 #pragma unroll
@@ -360,7 +376,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
         }
         if (!has_next) return;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) wr[s] = wnext[s];
+        for (int s = 0; s < KSTEPS; ++s) wr[s] = wnext[XD ? 0 : s];
         tile = next;
         first_tile = false;
     }
@@ -612,7 +628,7 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
         g_lds_attr[idx][epi] = lds;
     }
     int64_t grid_x = p.ntiles;
-    if (p.splits == 1) {
+    if (p.splits == 1 && !p.xd) {
         // Unsplit: as many workgroups as fit on the GPU at once, each looping
         // over row tiles (X is staged once per workgroup).
         int dev = 0;
