@@ -115,6 +115,19 @@ def test_every_decode_kernel_variant_exact_and_deterministic(ks, nn, nk, xd):
         lib.tp_tune_skinny(0, 0, 0, 0)
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 6000, 4096), (3, 8008, 4104)])
+def test_persistent_decode_grid_with_xcd_tile_order(M, N, K):
+    """More 16-row tiles than resident workgroups (K = 4096 keeps one
+    LDS-staged workgroup per CU): workgroups loop over tiles in the XCD-
+    contiguous order, the last round partly filled. Exact on integers."""
+    x = I.small_int_bf16((SEED, 40, M, N, K), (M, K))
+    w = I.small_int_bf16((SEED, 41, M, N, K), (N, K))
+    y = empty((M, N), torch.float32)
+    y.fill_(float("nan"))
+    lib.tp_row_linear_partial(dev(x), dev(w), y)
+    assert np.array_equal(f64(y), oracle.linear(f64(x), f64(w)))
+
+
 def test_split_k_partials_are_never_stale():
     """Heavily split variants reuse one workspace call after call: every call
     gets new inputs, so a partial read before its writer's store was visible
