@@ -231,8 +231,8 @@ int tp_tune_skinny(int ksteps, int nwn, int nwk, int x_direct);
  * call (-1 restores the automatic choice; TP_ERR_RANGE for an unknown index):
  * 0, 1, 2 = direct-to-LDS kernels with 256 x 256, 256 x 128, 128 x 128 tiles
  * (weight rows x tokens) on 4 waves; 4, 5, 6 = the same tiles on 8 waves;
- * 3 = register-staged 128 x 128 tiles, the only one that takes K % 32 != 0
- * (the direct-to-LDS kernels fall back to it). */
+ * 7 = 192 x 128 tiles on 4 waves; 3 = register-staged 128 x 128 tiles, the
+ * only one that takes K % 32 != 0 (the direct-to-LDS kernels fall back to it). */
 int tp_tune_tiled(int variant);
 
 #ifdef __cplusplus

@@ -483,6 +483,7 @@ const TiledEntry kTiled[] = {
     TP_DMA(256, 256, 4, 4),
     TP_DMA(256, 128, 4, 4),
     TP_DMA(128, 128, 4, 4),
+    TP_DMA(192, 128, 4, 2),
 };
 #undef TP_DMA
 constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);

@@ -61,6 +61,20 @@ def test_column_linear_swiglu_same_bits_as_separate_calls(M, Is, K):
     assert_close(f64(got), oracle.swiglu(gu[:, :Is], gu[:, Is:]), f"fused swiglu {(M, Is, K)}")
 
 
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 6, 7])
+def test_every_prefill_tile_shape_fused_swiglu(variant):
+    """The SwiGLU epilogue pairs gate and up rows inside each tile (first
+    and second half of its rows): every tile shape, ragged widths."""
+    lib.tp_tune_tiled(variant)
+    try:
+        for (M, Is, K) in [(300, 520, 256), (130, 200, 1024), (257, 96, 64)]:
+            x = dev(I.normal_bf16((SEED, 20, M, Is, K), (M, K)))
+            w = dev(I.normal_bf16((SEED, 21, M, Is, K), (2 * Is, K), 0.05))
+            assert np.array_equal(bits(fused_swiglu(x, w, Is)), bits(separate_swiglu(x, w, Is))), (variant, M, Is, K)
+    finally:
+        lib.tp_tune_tiled(-1)
+
+
 @pytest.mark.parametrize("M,Is,K", [(16, 100, 256), (3, 13, 72), (64, 1, 8), (100, 37, 136)])
 def test_column_linear_swiglu_ragged_width_exact_integer(M, Is, K):
     """I_shard not a multiple of 8 (no separate tp_swiglu to compare with):
