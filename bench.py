@@ -325,15 +325,24 @@ def cpu_baseline(w, seconds):
 GEMM_SOURCES = ("gemm_skinny.hip", "gemm_tiled.hip", "common.h", "kernels.h")
 
 
-def gemm_source_sha256():
-    """Hash of the GEMM kernels' sources: a stored counter summary speaks for
-    the kernels only while this is unchanged."""
+def code_digest(text):
+    """SHA-256 of C++ source text with comments removed and whitespace
+    collapsed: changes to comments or layout do not change it."""
     import hashlib
-    h = hashlib.sha256()
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
+def gemm_source_sha256():
+    """Digest of the GEMM kernels' code: a stored counter summary speaks for
+    the kernels only while this is unchanged."""
+    texts = []
     for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "megatron_sharded_linears_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+        with open(os.path.join(ROOT, "megatron_sharded_linears_amd", "csrc", f)) as fh:
+            texts.append(fh.read())
+    return code_digest("\n".join(texts))
 
 
 def traffic_file(workload):

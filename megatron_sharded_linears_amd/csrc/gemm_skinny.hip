@@ -11,20 +11,30 @@
 //     token row.
 //   * W goes global -> VGPR directly, each lane fetching 16 contiguous bytes
 //     of one row; all of a wave's k-steps are issued before the first MFMA so
-//     that many loads are in flight per CU.
-//   * X's K-chunk is loaded once per workgroup into LDS (padded rows) and
-//     shared by the waves that cover different weight rows.
-//   * K is split across the waves of a workgroup (summed through LDS) and, if
-//     the weight has too few rows to fill 256 CUs, across workgroups: each
-//     writes an fp32 partial tile to the workspace and the last workgroup to
-//     arrive on a tile (one atomic counter per tile) sums the partials in
-//     split order, so the result does not depend on arrival order. Partials
-//     travel through relaxed device-scope atomic stores and loads.
+//     that many loads are in flight per CU. Every load is unconditional
+//     (out-of-range lanes read a clamped in-bounds address and are zeroed or
+//     discarded at use) and LDS exchanges use LDS-only barriers, so each
+//     s_waitcnt covers just the loads it needs (a load in a branch, or a full
+//     __syncthreads(), would make it wait for all of them).
+//   * X is staged once per workgroup in LDS (padded rows) and shared by the
+//     waves that cover different weight rows, or, with one 16-row block per
+//     workgroup, loaded per wave step by step together with the weights.
+//   * K is split across the waves of a workgroup, summed through LDS in wave
+//     order; each wave then finishes the token tiles it owns (mt = wk mod NWK).
+//     If the weight has too few rows to fill 256 CUs, K is also split across
+//     workgroups: each writes an fp32 partial tile to the workspace and the
+//     last workgroup to arrive on a tile (one atomic counter per tile) sums
+//     the partials in split order, so the result does not depend on arrival
+//     order. Partials travel through relaxed device-scope atomic stores and
+//     loads.
+//   * Consecutive row tiles run on the same XCD (they share output lines),
+//     and the kernel arguments the first loads need arrive in one batch.
 //   * Fused epilogues. SwiGLU: each 16-row MFMA block holds 8 gate rows and
 //     the same 8 up rows, so lanes 0-31 own gate outputs whose up partners
 //     sit 32 lanes higher; one cross-lane swap pairs them and the block
 //     writes 8 SwiGLU outputs per token. Reduce: the rank's rounded partial is
-//     summed with the other ranks' partials in rank order and rounded once.
+//     summed with the other ranks' partials in rank order and rounded once;
+//     the owner waves load those partials right after the first weights.
 //     Both give the same bits as the separate kernels.
 #include "common.h"
 #include "kernels.h"
@@ -93,8 +103,9 @@ __device__ __forceinline__ int64_t weight_row(const GemmArgs& a, int64_t v) {
 }
 
 // Other ranks' values of one lane's 4 outputs, bf16 pairs indexed by rank
-// (the own slot unused). Loaded before they are needed: at the start of a
-// tile when the lane finishes one token tile, else just before the sum.
+// (the own slot unused). When a wave finishes one token tile, the first
+// tile's values are loaded right after its weights; otherwise (and for later
+// tiles of a persistent loop, and in the last split) just before the sum.
 // EPI_REDUCE launches have N % 4 == 0, so a lane's 4 outputs are one 8-byte
 // load per rank. The guards are uniform and one-sided (a branch that merged
 // two values would make each load wait for the one before); lanes past the

@@ -41,6 +41,14 @@ def test_summarize_counters_scales_by_the_copy(tmp_path):
     assert json.load(open(tmp_path / "out.json"))["traffic_bytes_per_step"] == 420 * 1024
 
 
+def test_code_digest_ignores_comments_and_layout_only():
+    a = "int f(int x) {  // doubles\n  return 2 * x; /* plain */ }"
+    b = "int f(int x)\n{\n    return 2 * x;\n}"
+    c = "int f(int x) { return 3 * x; }"
+    assert bench.code_digest(a) == bench.code_digest(b)
+    assert bench.code_digest(a) != bench.code_digest(c)
+
+
 def test_stored_traffic_needs_unchanged_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "traffic_file", lambda w: str(tmp_path / f"{w}.json"))
     (tmp_path / "a.json").write_text(json.dumps({"source_sha256": bench.gemm_source_sha256(),
