@@ -229,10 +229,13 @@ int tp_tune_skinny(int ksteps, int nwn, int nwk, int x_direct);
 
 /* Force the kernel of the prefill-sized (M > 64) linear for every later
  * call (-1 restores the automatic choice; TP_ERR_RANGE for an unknown index):
- * 0, 1, 2 = direct-to-LDS kernels with 256 x 256, 256 x 128, 128 x 128 tiles
- * (weight rows x tokens) on 4 waves; 4, 5, 6 = the same tiles on 8 waves;
- * 7 = 192 x 128 tiles on 4 waves; 3 = register-staged 128 x 128 tiles, the
- * only one that takes K % 32 != 0 (the direct-to-LDS kernels fall back to it). */
+ * 0, 1, 2 = direct-to-LDS kernels with 32-wide k-tiles and 256 x 256,
+ * 256 x 128, 128 x 128 tiles (weight rows x tokens) on 4 waves; 4, 5, 6 = the
+ * same tiles on 8 waves; 7 = 192 x 128 tiles on 4 waves; 8, 9, 10 = 256 x 256,
+ * 256 x 128, 128 x 128 tiles on 8 waves with 64-wide k-tiles (K % 64 == 0);
+ * 3 = register-staged 128 x 128 tiles, the only one that takes K % 32 != 0.
+ * A forced kernel whose K multiple a call does not meet keeps the automatic
+ * choice for that call. */
 int tp_tune_tiled(int variant);
 
 #ifdef __cplusplus

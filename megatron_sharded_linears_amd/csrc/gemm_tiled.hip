@@ -270,7 +270,8 @@ tiled_reg_kernel(GemmArgs a, int tiles_n, int tiles_m) {
 // memory would wait for every outstanding DMA). Each iteration reads the step-1 fragments, runs the
 // step-0 MFMAs, crosses the barrier for the next stage, issues the DMA three
 // stages ahead into the slot freed by the previous iteration, reads the next
-// stage's step-0 fragments and runs the step-1 MFMAs.
+// stage's step-0 fragments and runs the step-1 MFMAs; the last k-tile runs
+// after the loop (K >= 32: the launcher only sees validated shapes).
 // LDS stage: W tile [BN][32] then X tile [BM][32], 64-byte rows, 16-byte
 // chunks XOR-swizzled by (row / 4) mod 4; a lane's DMA destination is fixed
 // (wave base + 16 * lane), so the swizzle is realized by choosing which
@@ -399,21 +400,26 @@ tiled_dma_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     lds_barrier();
     read_frags(std::integral_constant<int, kF0>{}, 0, 0);
 
-    // (No scheduling barriers here: letting the compiler interleave the LDS
-    // reads with the MFMAs measured 3-6 % faster than pinning the order.)
-    for (int kt = 0; kt < ktiles; ++kt) {
+    // The last k-tile is peeled off so that the loop body has no branch
+    // around the next stage's fragment reads: at such a join the compiler
+    // waits for every LDS read in flight, so the step-1 MFMAs would wait for
+    // the next stage's reads as well (3-5 % slower). (No scheduling barriers:
+    // the compiler's interleaving of reads and MFMAs measured as fast as a
+    // pinned one.)
+    for (int kt = 0; kt + 1 < ktiles; ++kt) {
         read_frags(std::integral_constant<int, kF1>{}, kt, 1);
         mfmas(std::integral_constant<int, kF0>{});
-        if (kt + 1 < ktiles) {
-            // stages issued after kt + 1: up to kt + NS - 2
-            const int last = kt + NS - 2 < ktiles - 1 ? kt + NS - 2 : ktiles - 1;
-            wait_stage(last - (kt + 1));
-            lds_barrier();   // every wave's part of stage kt + 1 has landed; stage kt - 1 is free
-            if (kt + NS - 1 < ktiles) issue(kt + NS - 1);
-            read_frags(std::integral_constant<int, kF0>{}, kt + 1, 0);
-        }
+        // stages issued after kt + 1: up to kt + NS - 2
+        const int last = kt + NS - 2 < ktiles - 1 ? kt + NS - 2 : ktiles - 1;
+        wait_stage(last - (kt + 1));
+        lds_barrier();   // every wave's part of stage kt + 1 has landed; stage kt - 1 is free
+        if (kt + NS - 1 < ktiles) issue(kt + NS - 1);
+        read_frags(std::integral_constant<int, kF0>{}, kt + 1, 0);
         mfmas(std::integral_constant<int, kF1>{});
     }
+    read_frags(std::integral_constant<int, kF1>{}, ktiles - 1, 1);
+    mfmas(std::integral_constant<int, kF0>{});
+    mfmas(std::integral_constant<int, kF1>{});
     wait_vmcnt<0>();
     __syncthreads();
 
@@ -464,28 +470,256 @@ tiled_dma_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     });
 }
 
+// ---------------------------------------------------------------------------
+// 64-wide k-tiles (K % 64 == 0): every DMA row segment is a whole 128-byte
+// line (8 lanes x 16 B), where 32-wide k-tiles fetch each line in two halves
+// a k-tile apart; and there is one barrier per 64 of K. On the prefill shard
+// shapes it runs 3-10 % faster than the 32-wide kernel with the same tile. LDS stage: W tile [BN][64] then X tile [BM][64], 128-byte rows,
+// 16-byte chunks XOR-swizzled by row mod 8 (8 consecutive rows read by 8
+// lanes hit 8 different bank groups). After the barrier of k-tile kt every
+// wave has finished reading stage kt, so the DMA of k-tile kt + NS goes into
+// its slot: NS stages are in flight from the prologue on.
+template <int BN, int BM, int NS, int WGM>
+struct Dma64Cfg {
+    static constexpr int kBK = 64;
+    static constexpr int kWaves = 2 * WGM;
+    static constexpr int kThreadsWG = 64 * kWaves;
+    static constexpr int kWN = BN / 2, kWM = BM / WGM;
+    static constexpr int kBlkN = kWN / 32, kBlkM = kWM / 32;
+    static constexpr int kStageBytes = (BN + BM) * 128;
+    static constexpr int kInstrW = BN / 8, kInstrX = BM / 8;
+    static constexpr int kInstrPerWave = (kInstrW + kInstrX) / kWaves;
+    static constexpr int kSlabBytes = 2 * BM * 36 * 4;
+    static constexpr int kLdsBytes = NS * kStageBytes > kSlabBytes ? NS * kStageBytes : kSlabBytes;
+    static_assert((kInstrW + kInstrX) % kWaves == 0, "DMA instructions must split evenly over the waves");
+    static_assert(kBlkM >= 1, "at least one 32-token block per wave");
+    static_assert(NS >= 2 && NS * kInstrPerWave <= 63, "stages in flight must fit the load counter");
+};
+
+__device__ __forceinline__ int swz128(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+
+template <int BN, int BM, int NS, int WGM>
+__global__ void __launch_bounds__(128 * WGM, 1)
+tiled_dma64_kernel(GemmArgs a, int tiles_n, int tiles_m) {
+    using C = Dma64Cfg<BN, BM, NS, WGM>;
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    unsigned char* lds8 = lds_raw;
+
+    const int ntiles = tiles_n * tiles_m;
+    const int per_xcd = (ntiles + kXcds - 1) / kXcds;
+    const int t = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (t >= ntiles) return;
+    const int tile_n = t / tiles_m;
+    const int tile_m = t % tiles_m;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wn = wave / WGM;
+    const int wm = wave % WGM;
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t n0 = (int64_t)tile_n * BN;
+    const int64_t m0 = (int64_t)tile_m * BM;
+    const bf16_t* __restrict__ X = reinterpret_cast<const bf16_t*>(a.x);
+    const bf16_t* __restrict__ W = reinterpret_cast<const bf16_t*>(a.w);
+    const int ktiles = (int)(K / C::kBK);
+
+    // Per-lane DMA source rows (clamped: rows past the end only feed outputs
+    // that are never stored); lane l of an instruction fills LDS chunk l % 8
+    // of row l / 8 with the global chunk that the swizzle puts there.
+    const bf16_t* src[C::kInstrPerWave];
+    int dst_off[C::kInstrPerWave];
+    static_for<C::kInstrPerWave>([&](auto q) {
+        const int instr = wave + C::kWaves * q;
+        const bool is_w = instr < C::kInstrW;
+        const int rbase = (is_w ? instr : instr - C::kInstrW) * 8;
+        const int r = rbase + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        int64_t g;
+        if (is_w) {
+            g = tile_w_row<BN>(a, n0 + r);
+            if (g < 0) g = 0;
+        } else {
+            g = m0 + r;
+            if (g > M - 1) g = M - 1;
+        }
+        src[q] = (is_w ? W : X) + g * K + 8 * c;
+        dst_off[q] = (is_w ? 0 : BN * 128) + rbase * 128;
+    });
+    auto issue = [&](int kt) {
+        unsigned char* base = lds8 + (kt % NS) * C::kStageBytes;
+        const int64_t k0 = (int64_t)kt * C::kBK;
+        static_for<C::kInstrPerWave>([&](auto q) {
+            __builtin_amdgcn_global_load_lds(src[q] + k0, base + dst_off[q], 16, 0, 0);
+        });
+    };
+
+    f32x16_t acc[C::kBlkN][C::kBlkM];
+    static_for<C::kBlkN>([&](auto i) {
+        static_for<C::kBlkM>([&](auto j) { acc[i][j] = f32x16_t{}; });
+    });
+
+    const int orow = lane & 31;
+    const int ohalf = lane >> 5;
+    bf16x8_t fa[2][C::kBlkN], fb[2][C::kBlkM];
+    auto read_frags = [&](auto buf, int kt, int s) {
+        const unsigned char* ws = lds8 + (kt % NS) * C::kStageBytes;
+        const unsigned char* xs = ws + BN * 128;
+        const int c = 2 * s + ohalf;
+        static_for<C::kBlkN>([&](auto i) {
+            fa[buf][i] = __builtin_bit_cast(bf16x8_t,
+                *reinterpret_cast<const u32x4_t*>(ws + swz128(wn * C::kWN + i * 32 + orow, c)));
+        });
+        static_for<C::kBlkM>([&](auto j) {
+            fb[buf][j] = __builtin_bit_cast(bf16x8_t,
+                *reinterpret_cast<const u32x4_t*>(xs + swz128(wm * C::kWM + j * 32 + orow, c)));
+        });
+    };
+    auto mfmas = [&](auto buf) {
+        static_for<C::kBlkN>([&](auto i) {
+            static_for<C::kBlkM>([&](auto j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+            });
+        });
+    };
+    // wait until at most `pending` of this wave's most recent stages are in flight
+    auto wait_stage = [&](int pending) {
+        if (pending <= 0) wait_vmcnt<0>();
+        static_for<NS - 1>([&](auto p) {
+            if (pending == decltype(p)::value + 1) wait_vmcnt<(decltype(p)::value + 1) * C::kInstrPerWave>();
+        });
+    };
+    // Order of the reads and MFMAs that follow one another in the loop:
+    // MFMA, read, MFMA, read, ..., then the rest. An MFMA goes first, so the
+    // group's first MFMA waits only for the previous group's reads; left to
+    // itself the compiler clusters reads behind waits here (9 % slower).
+    auto pin_group = [&]() {
+        constexpr int R = C::kBlkN + C::kBlkM, F = C::kBlkN * C::kBlkM;
+        constexpr int P = R < F ? R : F;
+        static_for<P>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        });
+        if constexpr (R > P) __builtin_amdgcn_sched_group_barrier(0x100, R - P, 0);
+        if constexpr (F > P) __builtin_amdgcn_sched_group_barrier(0x008, F - P, 0);
+    };
+    constexpr int kF0 = 0, kF1 = 1;
+    using F0 = std::integral_constant<int, kF0>;
+    using F1 = std::integral_constant<int, kF1>;
+
+    const int pro = ktiles < NS ? ktiles : NS;
+    for (int kt = 0; kt < pro; ++kt) issue(kt);
+    wait_stage(pro - 1);
+    lds_barrier();
+    read_frags(F0{}, 0, 0);
+
+    // The last k-tile runs after the loop, so the loop body has no branch
+    // around fragment reads (see the 32-wide kernel).
+    for (int kt = 0; kt + 1 < ktiles; ++kt) {
+        read_frags(F1{}, kt, 1);
+        mfmas(F0{});
+        pin_group();
+        read_frags(F0{}, kt, 2);
+        mfmas(F1{});
+        pin_group();
+        read_frags(F1{}, kt, 3);
+        mfmas(F0{});
+        pin_group();
+        // stages issued after kt + 1: up to kt + NS - 1
+        const int last = kt + NS - 1 < ktiles - 1 ? kt + NS - 1 : ktiles - 1;
+        wait_stage(last - (kt + 1));
+        lds_barrier();   // stage kt + 1 has landed; every wave is done with stage kt
+        if (kt + NS < ktiles) issue(kt + NS);
+        read_frags(F0{}, kt + 1, 0);
+        mfmas(F1{});
+        pin_group();
+    }
+    read_frags(F1{}, ktiles - 1, 1);
+    mfmas(F0{});
+    read_frags(F0{}, ktiles - 1, 2);
+    mfmas(F1{});
+    read_frags(F1{}, ktiles - 1, 3);
+    mfmas(F0{});
+    mfmas(F1{});
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    // Epilogue: as in the 32-wide kernel.
+    float* slab = reinterpret_cast<float*>(lds8);
+    constexpr int kSlabStride = 36;
+    static_for<C::kBlkN>([&](auto i) {
+        static_for<C::kBlkM>([&](auto j) {
+            const int mt = wm * C::kWM + j * 32 + (lane & 31);
+            static_for<4>([&](auto g) {
+                const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                *reinterpret_cast<f32x4_t*>(slab + (wn * BM + mt) * kSlabStride + 8 * g + 4 * (lane >> 5)) = v;
+            });
+        });
+        __syncthreads();
+        constexpr int kRuns = 2 * BM * 8;
+        static_assert(kRuns % C::kThreadsWG == 0, "store loop must divide evenly");
+        static_assert((kRuns / 2) % C::kThreadsWG == 0, "SwiGLU store loop must divide evenly");
+        if (a.epi == EPI_SWIGLU) {
+#pragma unroll
+            for (int it = 0; it < kRuns / 2 / C::kThreadsWG; ++it) {
+                const int q = tid + it * C::kThreadsWG;
+                const int mt = q >> 3;
+                const int run = q & 7;
+                const int64_t m = m0 + mt;
+                const int64_t j = (int64_t)tile_n * C::kWN + i * 32 + 4 * run;
+                if (m < M && j < a.i_half)
+                    swiglu_out4(a, m, j, *reinterpret_cast<const float4*>(slab + mt * kSlabStride + 4 * run),
+                                *reinterpret_cast<const float4*>(slab + (BM + mt) * kSlabStride + 4 * run));
+            }
+        } else
+#pragma unroll
+        for (int it = 0; it < kRuns / C::kThreadsWG; ++it) {
+            const int q = tid + it * C::kThreadsWG;
+            const int half = q / (BM * 8);
+            const int rem = q - half * (BM * 8);
+            const int mt = rem >> 3;
+            const int run = rem & 7;
+            const int64_t m = m0 + mt;
+            const int64_t n = n0 + half * C::kWN + i * 32 + 4 * run;
+            if (m < M && n < N) {
+                const float4 v = *reinterpret_cast<const float4*>(slab + (half * BM + mt) * kSlabStride + 4 * run);
+                float o[4] = {v.x, v.y, v.z, v.w};
+                store_out4(a, m, n, o);
+            }
+        }
+        __syncthreads();
+    });
+}
+
 typedef void (*TiledFn)(GemmArgs, int, int);
 struct TiledEntry {
     int bn, bm;
-    bool dma;          // needs K % 32 == 0
+    int kmul;          // K must be a multiple of this
     TiledFn fn;
     int lds;
     int threads;
 };
 
 #define TP_DMA(BN, BM, NS, WGM) \
-    {BN, BM, true, tiled_dma_kernel<BN, BM, NS, WGM>, DmaCfg<BN, BM, NS, WGM>::kLdsBytes, DmaCfg<BN, BM, NS, WGM>::kThreadsWG}
+    {BN, BM, 32, tiled_dma_kernel<BN, BM, NS, WGM>, DmaCfg<BN, BM, NS, WGM>::kLdsBytes, DmaCfg<BN, BM, NS, WGM>::kThreadsWG}
+#define TP_DMA64(BN, BM, NS, WGM) \
+    {BN, BM, 64, tiled_dma64_kernel<BN, BM, NS, WGM>, Dma64Cfg<BN, BM, NS, WGM>::kLdsBytes, \
+     Dma64Cfg<BN, BM, NS, WGM>::kThreadsWG}
 const TiledEntry kTiled[] = {
     TP_DMA(256, 256, 4, 2),
     TP_DMA(256, 128, 4, 2),
     TP_DMA(128, 128, 4, 2),
-    {128, 128, false, tiled_reg_kernel<128, 128>, TileCfg<128, 128>::kLdsBytes, kThreads},
+    {128, 128, 8, tiled_reg_kernel<128, 128>, TileCfg<128, 128>::kLdsBytes, kThreads},
     TP_DMA(256, 256, 4, 4),
     TP_DMA(256, 128, 4, 4),
     TP_DMA(128, 128, 4, 4),
     TP_DMA(192, 128, 4, 2),
+    TP_DMA64(256, 256, 2, 4),
+    TP_DMA64(256, 128, 3, 4),
+    TP_DMA64(128, 128, 3, 4),
 };
 #undef TP_DMA
+#undef TP_DMA64
 constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);
 bool g_tiled_attr[kNumTiled] = {};
 int g_tiled_force = -1;
@@ -499,18 +733,20 @@ void tiled_force_variant(int idx) { g_tiled_force = idx; }
 // kernel's row space is then whole tiles of paired gate and up rows.
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     // Kernel choice, from MI355X measurements at the Llama-8B and Qwen-32B
-    // prefill shard shapes: 256 x 256 tiles on 8 waves when they give at
-    // least 192 tiles; else 256 x 128 tiles on 8 waves when those do; else
-    // (few tiles, or K <= 1024 where a tile's fixed prologue/epilogue cost
-    // weighs most) 128 x 128 tiles on 8 waves. K % 32 != 0 takes the
-    // register-staged kernel.
+    // prefill shard shapes, all on 8 waves: 256 x 256 tiles when they give at
+    // least 192 tiles; else 256 x 128 tiles when those do; else 128 x 128
+    // tiles. K <= 1024 (where a tile's fixed prologue and epilogue weigh
+    // most) takes 128 x 128 tiles with 32-wide k-tiles; otherwise 64-wide
+    // k-tiles when K % 64 == 0, 32-wide ones when K % 32 == 0, and the
+    // register-staged kernel for any other K.
     auto tiles = [&](int bn, int bm) { return ((a.N + bn - 1) / bn) * ((a.M + bm - 1) / bm); };
+    const int shape = tiles(256, 256) >= 192 ? 0 : tiles(256, 128) >= 192 ? 1 : 2;
     int best;
     if (a.K % 32 != 0) best = 3;
-    else if (a.K > 1024 && tiles(256, 256) >= 192) best = 4;
-    else if (a.K > 1024 && tiles(256, 128) >= 192) best = 5;
-    else best = 6;
-    if (g_tiled_force >= 0 && g_tiled_force < kNumTiled && (!kTiled[g_tiled_force].dma || a.K % 32 == 0))
+    else if (a.K <= 1024) best = 6;
+    else if (a.K % 64 == 0) best = 8 + shape;
+    else best = 4 + shape;
+    if (g_tiled_force >= 0 && g_tiled_force < kNumTiled && a.K % kTiled[g_tiled_force].kmul == 0)
         best = g_tiled_force;
     const TiledEntry& e = kTiled[best];
     if (!g_tiled_attr[best]) {
