@@ -232,7 +232,8 @@ int tp_tune_skinny(int ksteps, int nwn, int nwk, int x_direct);
  * 0, 1, 2 = direct-to-LDS kernels with 32-wide k-tiles and 256 x 256,
  * 256 x 128, 128 x 128 tiles (weight rows x tokens) on 4 waves; 4, 5, 6 = the
  * same tiles on 8 waves; 7 = 192 x 128 tiles on 4 waves; 8, 9, 10 = 256 x 256,
- * 256 x 128, 128 x 128 tiles on 8 waves with 64-wide k-tiles (K % 64 == 0);
+ * 256 x 128, 128 x 128 tiles on 8 waves with 64-wide k-tiles (K % 64 == 0),
+ * 11 = 192 x 128 tiles likewise;
  * 3 = register-staged 128 x 128 tiles, the only one that takes K % 32 != 0.
  * A forced kernel whose K multiple a call does not meet keeps the automatic
  * choice for that call. */

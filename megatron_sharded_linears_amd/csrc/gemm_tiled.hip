@@ -33,6 +33,7 @@ namespace {
 constexpr int kBK = 64;         // K per stage
 constexpr int kThreads = 256;   // 4 waves, 2 x 2
 constexpr int kXcds = 8;
+constexpr int kCus = 256;       // MI355X compute units
 
 template <int BN, int BM>
 struct TileCfg {
@@ -717,6 +718,7 @@ const TiledEntry kTiled[] = {
     TP_DMA64(256, 256, 2, 4),
     TP_DMA64(256, 128, 3, 4),
     TP_DMA64(128, 128, 3, 4),
+    TP_DMA64(192, 128, 3, 4),
 };
 #undef TP_DMA
 #undef TP_DMA64
@@ -738,14 +740,18 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     // tiles. K <= 1024 (where a tile's fixed prologue and epilogue weigh
     // most) takes 128 x 128 tiles with 32-wide k-tiles; otherwise 64-wide
     // k-tiles when K % 64 == 0, 32-wide ones when K % 32 == 0, and the
-    // register-staged kernel for any other K.
+    // register-staged kernel for any other K. With 64-wide k-tiles, 256 x 128
+    // tiles that leave CUs idle give way to 192 x 128 tiles when those fill
+    // at most one pass of the chip (Llama-8B t = 2 qkv: 192 tiles of
+    // 256 x 128 take 70 us, 256 of 192 x 128 take 62 us).
     auto tiles = [&](int bn, int bm) { return ((a.N + bn - 1) / bn) * ((a.M + bm - 1) / bm); };
     const int shape = tiles(256, 256) >= 192 ? 0 : tiles(256, 128) >= 192 ? 1 : 2;
     int best;
     if (a.K % 32 != 0) best = 3;
     else if (a.K <= 1024) best = 6;
-    else if (a.K % 64 == 0) best = 8 + shape;
-    else best = 4 + shape;
+    else if (a.K % 64 != 0) best = 4 + shape;
+    else if (shape == 1 && tiles(256, 128) < kCus && tiles(192, 128) <= kCus) best = 11;
+    else best = 8 + shape;
     if (g_tiled_force >= 0 && g_tiled_force < kNumTiled && a.K % kTiled[g_tiled_force].kmul == 0)
         best = g_tiled_force;
     const TiledEntry& e = kTiled[best];

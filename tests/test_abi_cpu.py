@@ -178,7 +178,7 @@ def test_tune_rejects_unbuilt_variants():
     assert C.tp_tune_skinny(8, 4, 2, 0) == 0
     assert C.tp_tune_skinny(8, 1, 16, 1) == 0
     assert C.tp_tune_skinny(0, 0, 0, 0) == 0
-    assert C.tp_tune_tiled(11) == -6
+    assert C.tp_tune_tiled(12) == -6
     assert C.tp_tune_tiled(-2) == -6
     assert C.tp_tune_tiled(1) == 0
     assert C.tp_tune_tiled(-1) == 0

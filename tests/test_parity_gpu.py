@@ -146,7 +146,7 @@ def test_split_k_partials_are_never_stale():
             lib.tp_tune_skinny(0, 0, 0, 0)
 
 
-@pytest.mark.parametrize("variant", list(range(11)))
+@pytest.mark.parametrize("variant", list(range(12)))
 def test_every_prefill_tile_shape_exact(variant):
     lib.tp_tune_tiled(variant)
     try:
