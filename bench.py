@@ -363,8 +363,11 @@ def stored_traffic(workload):
     return d
 
 
+GEMM_KERNELS = ("skinny_kernel", "tiled_dma_kernel", "tiled_dma64_kernel", "tiled_reg_kernel")
+
+
 def is_gemm_kernel(name):
-    return "skinny_kernel" in name or "tiled_dma_kernel" in name or "tiled_reg_kernel" in name
+    return any(k in name for k in GEMM_KERNELS)
 
 
 def summarize_counters(fetch_csv, write_csv, run_json, out=None):
@@ -564,7 +567,7 @@ def main():
                     "launches_per_step": sum(work[k][0] for k in gemm_ops), "us_per_step": round(gemm_us, 2)}
     else:
         tflops = flops_step / (gemm_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "kernel": "prefill linear (tiled_dma_kernel), all GEMM launches of a step",
+        roofline = {"bound": "mfma", "kernel": "prefill linear (tiled_dma64_kernel / tiled_dma_kernel), all GEMM launches of a step",
                     "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                     "launches_per_step": sum(work[k][0] for k in gemm_ops), "us_per_step": round(gemm_us, 2)}
