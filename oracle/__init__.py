@@ -20,6 +20,11 @@ Parity status of each function (what pins it, in tests/test_oracle_pins.py):
   head / vocab maps     pinned: per-card KV sizes printed on the pages, the
                         GQA grouping invariant, hand-worked tiny cases in
                         tests/golden, the workload shard sizes.
+  rms_norm              pinned: closed forms (constant rows, unit-RMS rows, a
+                        hand-worked 3-4 row), invariance under positive
+                        scaling, per-row independence, eps monotonicity.
+  add_rms_norm          pinned: the add rounded once to bf16 (hand cases,
+                        torch's bf16 add), then rms_norm.
   layer_linear_path     composed of the pinned functions above.
 """
 
@@ -30,6 +35,7 @@ from .tp_ref import (
     vocab_range_of_rank, qkv_shard_rows, gate_up_shard_rows, o_shard_cols,
     down_shard_cols, vocab_shard, shard_weight, vocab_embed_shard,
     vocab_embed_from_shard, column_linear_rank, row_linear_rank_partial, layer_linear_path,
+    rms_norm, add_rms_norm,
 )
 
 __all__ = [
@@ -38,5 +44,5 @@ __all__ = [
     "kv_heads_of_rank", "gqa_group", "vocab_shard_rows", "vocab_range_of_rank",
     "qkv_shard_rows", "gate_up_shard_rows", "o_shard_cols", "down_shard_cols",
     "vocab_shard", "shard_weight", "vocab_embed_shard", "vocab_embed_from_shard", "column_linear_rank",
-    "row_linear_rank_partial", "layer_linear_path",
+    "row_linear_rank_partial", "layer_linear_path", "rms_norm", "add_rms_norm",
 ]

@@ -9,8 +9,8 @@ Pages cited (by title and section):
   [P1] "第 9 章 多进程与张量并行" (zero-to-sglang), sections 2.2, 3.1, 3.2.
   [P2] "Tensor Parallelism 执行路径" (SGLang internals), the weight-split
        diagram and "前向执行的实际流程".
-  [P3] "张量、流水线与数据并行", sections "线性层怎么切" and
-       "每 token 的通信量（估算）".
+  [P3] "张量、流水线与数据并行", sections "线性层怎么切",
+       "每 token 的通信量（估算）" and "流水线并行".
 
 Everything is plain NumPy in float64. Inputs are arrays of any float type
 (bf16 values upcast exactly); results are float64 and are not rounded unless a
@@ -22,6 +22,8 @@ Y = X W^T. [P1 3.2] calls the output dimension a "row"; the column-parallel
 split is therefore a split of the output (first) axis and the row-parallel
 split a split of the input (second) axis.
 """
+
+import math
 
 import numpy as np
 
@@ -104,6 +106,39 @@ def embedding_lookup(table, ids):
     ok = (ids >= 0) & (ids < V)
     out[ok] = table[ids[ok]]
     return out
+
+
+def rms_norm(x, gamma, eps):
+    """RMSNorm of each row, float64: y[m, j] = x[m, j] / sqrt(mean_k x[m, k]^2
+    + eps) * gamma[j].
+
+    [P1 3.2]: RMSNorm is not split; every rank keeps the whole norm and
+    applies it to the whole (replicated) hidden row. The pages name the norm
+    but do not write it out; the reading taken is the usual root-mean-square
+    definition, mean over the hidden axis, eps inside the square root, the
+    per-column weight gamma applied after the scaling."""
+    x = np.asarray(x, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    if x.ndim != 2 or gamma.shape != (x.shape[1],):
+        raise ValueError(f"rms_norm: x {x.shape} and gamma {gamma.shape} do not match")
+    if not (eps >= 0.0 and math.isfinite(eps)):
+        raise ValueError("rms_norm: eps must be finite and >= 0")
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    return x / np.sqrt(ms + eps) * gamma[None, :]
+
+
+def add_rms_norm(x, residual, gamma, eps):
+    """Residual add, then RMSNorm, as a rank applies them after the all-reduce
+    of a row-parallel output ([P1 3.2]: the norm replicated on every rank;
+    [P3 流水线并行]: the residual is carried beside hidden_states).
+
+    h = bf16(residual + x): the residual stream is a stored activation and is
+    held in bf16 like every activation on this path. Returns (h, rms_norm(h))
+    in float64, the second not rounded. ``x`` may be None (no add: h =
+    residual)."""
+    residual = np.asarray(residual, dtype=np.float64)
+    h = residual if x is None else round_bf16(residual + np.asarray(x, dtype=np.float64))
+    return h, rms_norm(h, gamma, eps)
 
 
 # ---------------------------------------------------------------------------

@@ -20,7 +20,7 @@ from oracle import (
     embedding_lookup, q_heads_of_rank, kv_heads_of_rank, gqa_group, vocab_shard_rows,
     vocab_range_of_rank, qkv_shard_rows, gate_up_shard_rows, o_shard_cols,
     down_shard_cols, shard_weight, vocab_embed_shard, vocab_embed_from_shard,
-    layer_linear_path,
+    layer_linear_path, rms_norm, add_rms_norm,
 )
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -383,3 +383,71 @@ def test_layer_linear_path_integer_case_matches_hand_chain():
     act = round_bf16(g / (1 + np.exp(-g)) * u)
     assert np.array_equal(out["act"], act)
     assert np.array_equal(out["down"], round_bf16(act @ wd.T))
+
+
+# ------------------------------------------------------- rms_norm / add_rms_norm
+
+def test_rms_norm_closed_forms():
+    # hand-worked row: mean(9, 16) = 12.5, so 3 and 4 scale by 1 / sqrt(12.5) = sqrt(2) / 5
+    out = rms_norm([[3.0, 4.0]], [1.0, 1.0], 0.0)
+    assert np.allclose(out, [[3 * math.sqrt(2) / 5, 4 * math.sqrt(2) / 5]], rtol=1e-15, atol=0)
+    # a constant row keeps only its sign (eps = 0), scaled by gamma per column
+    g = np.array([0.5, -1.0, 2.0, 3.0, 0.25, 1.0, -7.0])
+    assert np.allclose(rms_norm(np.full((1, 7), -2.5), g, 0.0), -g[None, :], rtol=1e-15, atol=0)
+    # ... and c / sqrt(c^2 + eps) with eps
+    assert np.allclose(rms_norm([[1.0, 1.0]], [1.0, 1.0], 3.0), [[0.5, 0.5]], rtol=1e-15, atol=0)
+    # a row whose mean square is 1 is only multiplied by gamma
+    x = np.array([[1.0, -1.0, 1.0, -1.0]])
+    g4 = np.array([2.0, 3.0, -4.0, 0.5])
+    assert np.array_equal(rms_norm(x, g4, 0.0), x * g4)
+
+
+def test_rms_norm_scale_invariance_rows_and_columns():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((5, 64))
+    g = rng.standard_normal(64)
+    base = rms_norm(x, g, 0.0)
+    for a in (1e-3, 0.37, 12.0, 4096.0):
+        assert np.allclose(rms_norm(a * x, g, 0.0), base, rtol=1e-13, atol=0)
+    # rows are normalised independently: rows of very different scale stacked
+    # together give the same rows as alone (a mean over the wrong axis fails)
+    y = np.vstack([x[:1] * 1e3, x[1:2] * 1e-3])
+    assert np.allclose(rms_norm(y, g, 0.0)[0], rms_norm(x[:1], g, 0.0)[0], rtol=1e-13, atol=0)
+    assert np.allclose(rms_norm(y, g, 0.0)[1], rms_norm(x[1:2], g, 0.0)[0], rtol=1e-13, atol=0)
+    # gamma multiplies columns: in a square case the transposed reading differs
+    sq = rng.standard_normal((6, 6))
+    gs = np.arange(1.0, 7.0)
+    out = rms_norm(sq, gs, 0.0)
+    assert np.allclose(out / gs[None, :], rms_norm(sq, np.ones(6), 0.0), rtol=1e-13, atol=0)
+    # every output row has mean square mean(gamma^2 * (x / rms)^2); with gamma = 1 it is 1
+    assert np.allclose(np.mean(rms_norm(x, np.ones(64), 0.0) ** 2, axis=1), 1.0, rtol=1e-13, atol=0)
+    # a larger eps shrinks every magnitude
+    assert np.all(np.abs(rms_norm(x, g, 1e-1)) <= np.abs(rms_norm(x, g, 1e-6)) + 1e-300)
+
+
+def test_rms_norm_matches_torch_in_float64():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((9, 40)) * rng.uniform(0.01, 100.0, size=(9, 1))
+    g = rng.standard_normal(40)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (40,), torch.from_numpy(g), eps=1e-5).numpy()
+    assert np.allclose(rms_norm(x, g, 1e-5), ref, rtol=1e-12, atol=1e-300)
+
+
+def test_add_rms_norm_rounds_the_add_once():
+    # 1 + 2^-8 lies halfway between bf16 neighbours 1 and 1 + 2^-7: to even, 1
+    h, _ = add_rms_norm([[2.0 ** -8]], [[1.0]], [1.0], 0.0)
+    assert h[0, 0] == 1.0
+    h, _ = add_rms_norm([[3 * 2.0 ** -8]], [[1.0]], [1.0], 0.0)
+    assert h[0, 0] == 1.0 + 2 * 2.0 ** -7                   # tie again, to even upward
+    # against torch's bf16 add (fp32 add of two bf16 values, rounded once)
+    rng = np.random.default_rng(3)
+    a = torch.from_numpy(rng.standard_normal((4, 256)).astype(np.float32)).to(torch.bfloat16)
+    b = torch.from_numpy((rng.standard_normal((4, 256)) * 3).astype(np.float32)).to(torch.bfloat16)
+    g = rng.standard_normal(256)
+    h, out = add_rms_norm(a.float().numpy(), b.float().numpy(), g, 1e-5)
+    assert np.array_equal(h, (a + b).float().numpy().astype(np.float64))
+    # the norm reads the rounded sum, not the exact one
+    assert np.array_equal(out, rms_norm(h, g, 1e-5))
+    # no add: the residual is normalised as it is
+    h0, out0 = add_rms_norm(None, b.float().numpy(), g, 1e-5)
+    assert np.array_equal(h0, b.float().numpy()) and np.array_equal(out0, rms_norm(h0, g, 1e-5))
