@@ -113,7 +113,11 @@ class Rank:
                 "ctx": dn((M, self.shapes["o"][1]), 1.0, s + 5),
                 "peers_o": peers_o if shared_peers else [dn((M, H), 0.5, s + 10 + j) for j in range(t - 1)],
                 "peers_d": peers_d if shared_peers else [dn((M, H), 0.5, s + 40 + j) for j in range(t - 1)],
+                # RMSNorm weights (around 1) before attention and before the MLP
+                "g_in": (1.0 + dn((H,), 0.1, s + 6).float()).to(bf),
+                "g_post": (1.0 + dn((H,), 0.1, s + 7).float()).to(bf),
             })
+        self.g_final = (1.0 + dn((H,), 0.1, 8).float()).to(bf)
         self.x = dn((M, H), 1.0, 7)
         self.qkv = torch.empty((M, self.shapes["qkv"][0]), dtype=bf, device=dev)
         self.po = torch.empty((M, H), dtype=bf, device=dev)
@@ -122,6 +126,7 @@ class Rank:
         self.act = torch.empty((M, self.shapes["gate_up"][0] // 2), dtype=bf, device=dev)
         self.pd = torch.empty((M, H), dtype=bf, device=dev)
         self.h = torch.empty((M, H), dtype=bf, device=dev)
+        self.xn = torch.empty((M, H), dtype=bf, device=dev)     # normalised activations
         self.vocab = w.has_vocab
         if self.vocab:
             vs = self.shapes["embed"][0]
@@ -154,6 +159,10 @@ class Rank:
             "o_reduce": (w.layers, gemm_flops(M, o[0], o[1]), gemm_bytes(M, o[0], o[1]) + 2 * (t - 1) * M * H),
             "gate_up_swiglu": (w.layers, gemm_flops(M, g[0], g[1]), 2 * g[0] * g[1] + 2 * M * g[1] + M * g[0]),
             "down_reduce": (w.layers, gemm_flops(M, d[0], d[1]), gemm_bytes(M, d[0], d[1]) + 2 * (t - 1) * M * H),
+            # sum over ranks + residual add + RMSNorm: t partials and the residual
+            # read, the residual and the normalised row written, gamma read
+            "reduce_norm": (2 * w.layers, 0, (2 * t + 6) * M * H + 2 * H),
+            "input_norm": (1, 0, 4 * M * H + 2 * H),
         }
         if self.vocab:
             Ms, vs = self.hs_rows, self.vs
@@ -197,6 +206,35 @@ def build_ops(R, lib, fused_swiglu=True, fused_reduce=True):
         h = R.h
     if R.vocab:
         hs = h[h.shape[0] - R.hs_rows:]
+        ops.append(("lm_head", lib.tp_lm_head_shard, (hs, R.lm, R.logits)))
+        ops.append(("concat", lib.tp_concat_logits, ([R.logits] + R.peer_logits, w.vocab, R.full_logits)))
+    return ops
+
+
+def build_norm_ops(R, lib, eps=1e-5):
+    """The step with the residual stream and the replicated RMSNorms of a
+    Llama layer: input norm; qkv; o partial, then the sum over ranks fused with
+    the residual add and the post-attention norm; gate_up + SwiGLU; down
+    partial, then the sum, the add and the next norm (the next layer's input
+    norm, or the final norm before the LM head)."""
+    w = R.w
+    ops = []
+    res = R.x
+    if R.vocab:
+        ops.append(("embed", lib.tp_vocab_embed, (R.ids, R.embed, w.vocab, w.t, 0, R.ze)))
+        ops.append(("embed_reduce", lib.tp_reduce_partials, ([R.ze] + R.peers_e, R.h)))
+        res = R.h
+    ops.append(("input_norm", lib.tp_add_rmsnorm, (None, res, R.layers[0]["g_in"], eps, R.xn)))
+    for i, L in enumerate(R.layers):
+        g_next = R.layers[i + 1]["g_in"] if i + 1 < len(R.layers) else R.g_final
+        ops.append(("qkv", lib.tp_column_linear, (R.xn, L["qkv"], R.qkv)))
+        ops.append(("o", lib.tp_row_linear_partial, (L["ctx"], L["o"], R.po)))
+        ops.append(("reduce_norm", lib.tp_reduce_add_rmsnorm, ([R.po] + L["peers_o"], res, L["g_post"], eps, R.xn)))
+        ops.append(("gate_up_swiglu", lib.tp_column_linear_swiglu, (R.xn, L["gate_up"], R.act)))
+        ops.append(("down", lib.tp_row_linear_partial, (R.act, L["down"], R.pd)))
+        ops.append(("reduce_norm", lib.tp_reduce_add_rmsnorm, ([R.pd] + L["peers_d"], res, g_next, eps, R.xn)))
+    if R.vocab:
+        hs = R.xn[R.xn.shape[0] - R.hs_rows:]
         ops.append(("lm_head", lib.tp_lm_head_shard, (hs, R.lm, R.logits)))
         ops.append(("concat", lib.tp_concat_logits, ([R.logits] + R.peer_logits, w.vocab, R.full_logits)))
     return ops
@@ -536,6 +574,9 @@ def main():
         ms_step = ms_eager
     # the same step through the other set of calls, for comparison
     ms_alt, _ = time_step(torch, alt_ops, args.steps, args.warmup)
+    # and with the residual stream and the RMSNorms of a real layer
+    norm_ops = build_norm_ops(R, lib)
+    ms_norm, _ = time_step(torch, norm_ops, args.steps, args.warmup)
 
     # --- per kernel: each op's launches of one step, captured and replayed K times
     per_op = {}
@@ -551,6 +592,11 @@ def main():
                         "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                         "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2) if flops else None,
                         "bytes_per_launch": byts}
+
+    n_norm = work["reduce_norm"][0]
+    g = capture(torch, norm_ops, only="reduce_norm", repeat=max(1, -(-32 // n_norm)))
+    us_norm = time_graph(torch, g, args.steps, 2) * 1e3 / (n_norm * max(1, -(-32 // n_norm)))
+    del g
 
     flops_step = sum(work[k][0] * work[k][1] for k in gemm_ops)
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -607,6 +653,11 @@ def main():
         "step_GBps": round(sum(work[k][0] * work[k][2] for k in names) / (ms_step * 1e-3) / 1e9, 1),
         "alt_path": {"calls": "separate" if fused else "fused", "ms_per_step": round(ms_alt, 4),
                      "value": round(flops_step / (ms_alt * 1e-3) / 1e12, 3)},
+        "with_norms": {"calls": "input norm; per layer qkv, o partial, sum + residual add + RMSNorm "
+                                "(tp_reduce_add_rmsnorm), gate_up + SwiGLU, down partial, sum + add + norm",
+                       "ms_per_step": round(ms_norm, 4), "value": round(flops_step / (ms_norm * 1e-3) / 1e12, 3),
+                       "reduce_norm_us_per_call": round(us_norm, 3),
+                       "reduce_norm_GBps": round(work["reduce_norm"][2] / (us_norm * 1e-6) / 1e9, 1)},
         "per_op": per_op,
         "wall_s_timed": round(wall_s, 3),
         "pages_context": pages_context(w),

@@ -184,6 +184,30 @@ int tp_column_linear_swiglu(const void* x, int64_t M, int64_t K, const void* w_g
 int tp_row_linear_reduce(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
                          const void* const* partials, int t, int rank, void* out, void* stream);
 
+/* Residual add and RMSNorm, replicated on every rank ([P1 3.2]: the norm is
+ * not split; every rank applies the whole norm to the whole hidden row;
+ * [P3 流水线并行]: the residual travels beside hidden_states). In place on
+ * the residual stream: residual[m, :] = bf16(residual[m, :] + x[m, :]) (x may
+ * be NULL: no add, residual unchanged), then
+ *   out[m, j] = bf16(h[m, j] * r_m * gamma[j]),  r_m = 1 / sqrt(mean_j h[m, j]^2 + eps)
+ * with h the new residual, all in fp32 (the mean is a fixed-order sum, the
+ * same run to run). x, residual, out: [M, H] bf16; gamma: [H] bf16; eps finite
+ * and >= 0 (TP_ERR_RANGE otherwise); H % 8 == 0, H <= 32768 (TP_ERR_SHAPE:
+ * one workgroup holds a row in registers). out, residual, gamma and x
+ * must not overlap (TP_ERR_SHAPE). */
+int tp_add_rmsnorm(const void* x_or_null, int64_t M, int64_t H, void* residual, const void* gamma, float eps,
+                   void* out, void* stream);
+
+/* S6 / S8 + residual add + RMSNorm in one call: the sum over ranks of a
+ * row-parallel output ([P1 3.1] All-Reduce, as tp_reduce_partials: fp32 in
+ * the order i = 0..t-1 from partials[0], rounded to bf16), added to the
+ * residual and normalised as tp_add_rmsnorm does. `partials` is a HOST array
+ * of t >= 1 device pointers to [M, H] buffers of `partial_dtype`; none may
+ * overlap residual or out. Gives the same bits as tp_reduce_partials (bf16
+ * out) followed by tp_add_rmsnorm. */
+int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype, int64_t M, int64_t H,
+                          void* residual, const void* gamma, float eps, void* out, void* stream);
+
 /* S9a. Vocab-parallel embedding, one shard's contribution: for each token m,
  * out[m, :] = e_shard[ids[m] - rank Vs, :] when rank Vs <= ids[m] <
  * min((rank+1) Vs, vocab), else a row of -0.0 (Vs = ceil(vocab / t)). Ids

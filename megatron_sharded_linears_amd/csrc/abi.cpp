@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -445,6 +446,67 @@ int tp_concat_logits(const void* const* shard_logits, int t, int64_t M, int64_t 
         const hipError_t e = tpk::launch_concat(ptrs, t, M, v_shard, vocab, dtype, out,
                                                 static_cast<hipStream_t>(stream));
         return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+namespace {
+
+constexpr int64_t kMaxNormWidth = 32768;   // one workgroup holds a whole row in registers
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+// Shared validation of the two add + RMSNorm calls; `inputs` are t buffers
+// of M x H elements of in_dtype (t may be 0).
+int add_rmsnorm_call(const void* const* inputs, int t, int in_dtype, int64_t M, int64_t H, void* residual,
+                     const void* gamma, float eps, void* out, void* stream) {
+    if (residual == nullptr || gamma == nullptr || out == nullptr) return TP_ERR_NULL;
+    if (t < 0 || t > TP_MAX_SHARDS) return TP_ERR_RANGE;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return TP_ERR_RANGE;
+    if (!dtype_ok(in_dtype)) return TP_ERR_DTYPE;
+    if (M < 0 || H <= 0 || M >= kMaxDim || H > kMaxNormWidth) return TP_ERR_SHAPE;
+    if (H % 8 != 0 || !aligned16(residual) || !aligned16(gamma) || !aligned16(out)) return TP_ERR_ALIGNMENT;
+    const int64_t act_bytes = M * H * 2, in_bytes = M * H * (in_dtype == TP_F32 ? 4 : 2);
+    if (overlap(out, act_bytes, residual, act_bytes) || overlap(out, act_bytes, gamma, H * 2) ||
+        overlap(residual, act_bytes, gamma, H * 2))
+        return TP_ERR_SHAPE;
+    tpk::PartialPtrs ptrs;
+    std::memset(&ptrs, 0, sizeof(ptrs));
+    for (int i = 0; i < t; ++i) {
+        if (inputs[i] == nullptr) return TP_ERR_NULL;
+        if (!aligned16(inputs[i])) return TP_ERR_ALIGNMENT;
+        if (overlap(inputs[i], in_bytes, out, act_bytes) || overlap(inputs[i], in_bytes, residual, act_bytes))
+            return TP_ERR_SHAPE;
+        ptrs.p[i] = inputs[i];
+    }
+    if (M == 0) return TP_OK;
+    const hipError_t e = tpk::launch_add_rmsnorm(ptrs, t, in_dtype, M, H, residual, gamma, eps, out,
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+}
+
+}  // namespace
+
+int tp_add_rmsnorm(const void* x_or_null, int64_t M, int64_t H, void* residual, const void* gamma, float eps,
+                   void* out, void* stream) {
+    try {
+        const void* in[1] = {x_or_null};
+        return add_rmsnorm_call(in, x_or_null != nullptr ? 1 : 0, TP_BF16, M, H, residual, gamma, eps, out, stream);
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype, int64_t M, int64_t H,
+                          void* residual, const void* gamma, float eps, void* out, void* stream) {
+    try {
+        if (partials == nullptr) return TP_ERR_NULL;
+        if (t < 1) return TP_ERR_RANGE;
+        return add_rmsnorm_call(partials, t, partial_dtype, M, H, residual, gamma, eps, out, stream);
     } catch (...) {
         return TP_ERR_HIP;
     }

@@ -179,6 +179,145 @@ hipError_t reduce_dispatch(const PartialPtrs& ptrs, int t, int64_t numel, void* 
     return hipGetLastError();
 }
 
+// ------------------------------------------------ residual add + RMSNorm
+
+// One workgroup per token row (the norm needs the whole row), 512 threads,
+// each owning VPT vectors of 8 values, v = thread + 512 j. Every load of the
+// row (the residual, gamma and, with T >= 0, all T partials) is issued before
+// any is used, so a row costs one memory round trip, then one LDS reduction:
+// at decode sizes (16 rows) the latency is the cost. The partials are summed
+// in rank order from partial 0 and rounded to bf16 as the reducer stores them
+// (T = 0: no add), added to the residual and rounded again; the new residual
+// is written back. The squares are summed in a fixed tree (per thread in
+// vector order, lane butterflies, then the waves in order), so results are
+// the same run to run. out = bf16(h * r * gamma), r = 1 / sqrt(sum / H + eps).
+// T = -1: runtime t, partials read in a loop (t not in 0, 1, 2, 4, 8, 16).
+constexpr int kNormThreads = 512;
+
+template <int IN_F32, int T, int VPT>
+__global__ void __launch_bounds__(kNormThreads)
+add_rmsnorm_kernel(PartialPtrs ptrs, int t_rt, uint16_t* __restrict__ residual, const uint16_t* __restrict__ gamma,
+                   float eps, int64_t H, uint16_t* __restrict__ out) {
+    constexpr int kInVec = IN_F32 ? 2 : 1;        // 16-byte loads per 8 values of a partial
+    const int64_t m = blockIdx.x;
+    const int64_t nvec = H / 8;
+    uint4* res = reinterpret_cast<uint4*>(residual + m * H);
+    const uint4* g4 = reinterpret_cast<const uint4*>(gamma);
+    const int64_t row_vec = m * nvec * kInVec;     // first 16-byte vector of row m in a partial
+    const int t = T >= 0 ? T : t_rt;
+
+    int64_t vv[VPT];
+    bool ok[VPT];
+    uint4 rraw[VPT], graw[VPT];
+    uint4 praw[VPT][(T > 0 ? T : 1) * kInVec];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int64_t v = threadIdx.x + (int64_t)kNormThreads * j;
+        ok[j] = v < nvec;
+        vv[j] = ok[j] ? v : 0;                     // clamped: loads stay in bounds and unconditional
+        rraw[j] = res[vv[j]];
+        graw[j] = g4[vv[j]];
+        if constexpr (T > 0) {
+#pragma unroll
+            for (int i = 0; i < T; ++i)
+#pragma unroll
+                for (int q = 0; q < kInVec; ++q)
+                    praw[j][i * kInVec + q] = reinterpret_cast<const uint4*>(ptrs.p[i])[row_vec + vv[j] * kInVec + q];
+        }
+    }
+
+    float h[VPT][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        unpack_bf16x8(rraw[j], h[j]);
+        if (t > 0) {
+            float acc[8];
+            auto part = [&](int i, float* f) {
+                if constexpr (T > 0) {
+                    if (IN_F32) {
+                        const uint4 a = praw[j][i * kInVec], b = praw[j][i * kInVec + kInVec - 1];
+                        f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y);
+                        f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+                        f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y);
+                        f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
+                    } else {
+                        unpack_bf16x8(praw[j][i], f);
+                    }
+                } else {
+                    load8<IN_F32>(reinterpret_cast<const char*>(ptrs.p[i]) + row_vec * 16, vv[j], f);
+                }
+            };
+            part(0, acc);
+#pragma unroll
+            for (int i = 1; i < t; ++i) {
+                float f[8];
+                part(i, f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += f[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[j][e] = round_bf16(h[j][e] + round_bf16(acc[e]));
+            if (ok[j]) res[vv[j]] = pack_bf16x8(h[j]);
+        }
+        if (ok[j]) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += h[j][e] * h[j][e];
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    __shared__ float wave_ss[kNormThreads / 64];
+    if ((threadIdx.x & 63) == 0) wave_ss[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = wave_ss[0];
+#pragma unroll
+    for (int w = 1; w < kNormThreads / 64; ++w) tot += wave_ss[w];
+    const float r = 1.0f / sqrtf(tot / (float)H + eps);
+    uint4* o4 = reinterpret_cast<uint4*>(out + m * H);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        float g[8], y[8];
+        unpack_bf16x8(graw[j], g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = h[j][e] * r * g[e];
+        if (ok[j]) o4[vv[j]] = pack_bf16x8(y);
+    }
+}
+
+template <int IN_F32, int T>
+hipError_t add_rmsnorm_vpt(const PartialPtrs& ptrs, int t, int64_t M, int64_t H, uint16_t* res,
+                           const uint16_t* g, float eps, uint16_t* o, hipStream_t s) {
+    const int64_t nvec = H / 8;
+    const dim3 grid((unsigned)M), block(kNormThreads);
+    if (nvec <= kNormThreads)
+        hipLaunchKernelGGL((add_rmsnorm_kernel<IN_F32, T, 1>), grid, block, 0, s, ptrs, t, res, g, eps, H, o);
+    else if (nvec <= 2 * kNormThreads)   // 16 fp32 partials of 2 vectors would spill: loop instead
+        hipLaunchKernelGGL((add_rmsnorm_kernel<IN_F32, (IN_F32 && T > 8 ? -1 : T), 2>), grid, block, 0, s, ptrs, t,
+                           res, g, eps, H, o);
+    // wider rows: partials read in a loop (all T partials of 4 or 8 vectors
+    // per thread would not fit in registers)
+    else if (nvec <= 4 * kNormThreads)
+        hipLaunchKernelGGL((add_rmsnorm_kernel<IN_F32, -1, 4>), grid, block, 0, s, ptrs, t, res, g, eps, H, o);
+    else
+        hipLaunchKernelGGL((add_rmsnorm_kernel<IN_F32, -1, 8>), grid, block, 0, s, ptrs, t, res, g, eps, H, o);
+    return hipGetLastError();
+}
+
+template <int IN_F32>
+hipError_t add_rmsnorm_t(const PartialPtrs& ptrs, int t, int64_t M, int64_t H, uint16_t* res,
+                         const uint16_t* g, float eps, uint16_t* o, hipStream_t s) {
+    switch (t) {
+    case 0: return add_rmsnorm_vpt<IN_F32, 0>(ptrs, t, M, H, res, g, eps, o, s);
+    case 1: return add_rmsnorm_vpt<IN_F32, 1>(ptrs, t, M, H, res, g, eps, o, s);
+    case 2: return add_rmsnorm_vpt<IN_F32, 2>(ptrs, t, M, H, res, g, eps, o, s);
+    case 4: return add_rmsnorm_vpt<IN_F32, 4>(ptrs, t, M, H, res, g, eps, o, s);
+    case 8: return add_rmsnorm_vpt<IN_F32, 8>(ptrs, t, M, H, res, g, eps, o, s);
+    case 16: return add_rmsnorm_vpt<IN_F32, 16>(ptrs, t, M, H, res, g, eps, o, s);
+    default: return add_rmsnorm_vpt<IN_F32, -1>(ptrs, t, M, H, res, g, eps, o, s);
+    }
+}
+
 // ---------------------------------------------------------------- vocab embed
 
 // One contribution of a vocab-parallel embedding: row ids[m] - lo of this
@@ -289,6 +428,16 @@ hipError_t launch_concat(const PartialPtrs& ptrs, int t, int64_t M, int64_t v_sh
         else hipLaunchKernelGGL(concat_elem_kernel<0>, dim3(g), dim3(kThreads), 0, s, ptrs, M, v_shard, vocab, out);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_add_rmsnorm(const PartialPtrs& ptrs, int t, int in_dtype, int64_t M, int64_t H,
+                              void* residual, const void* gamma, float eps, void* out, hipStream_t s) {
+    if (H / 8 > 8 * kNormThreads) return hipErrorInvalidValue;   // H > 32768: rejected by the ABI
+    uint16_t* res = reinterpret_cast<uint16_t*>(residual);
+    const uint16_t* g = reinterpret_cast<const uint16_t*>(gamma);
+    uint16_t* o = reinterpret_cast<uint16_t*>(out);
+    return in_dtype == TP_F32 ? add_rmsnorm_t<1>(ptrs, t, M, H, res, g, eps, o, s)
+                              : add_rmsnorm_t<0>(ptrs, t, M, H, res, g, eps, o, s);
 }
 
 }  // namespace tpk

@@ -78,6 +78,8 @@ _PROTOS = {
     "tp_vocab_embed": (_int, [_vp, _i64, _vp, _i64, _int, _int, _i64, _vp, _vp]),
     "tp_lm_head_shard": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp]),
     "tp_concat_logits": (_int, [_ptr_array, _int, _i64, _i64, _i64, _int, _vp, _vp]),
+    "tp_add_rmsnorm": (_int, [_vp, _i64, _i64, _vp, _vp, ctypes.c_float, _vp, _vp]),
+    "tp_reduce_add_rmsnorm": (_int, [_ptr_array, _int, _int, _i64, _i64, _vp, _vp, ctypes.c_float, _vp, _vp]),
     "tp_tune_skinny": (_int, [_int, _int, _int, _int]),
     "tp_tune_tiled": (_int, [_int]),
 }
@@ -293,6 +295,52 @@ def tp_reduce_partials(partials, out, stream=None):
     arr, keep = _ptrs(partials)
     _check(_lib.tp_reduce_partials(arr, t, numel, _dtype_code(in_dt), ctypes.c_void_p(out.data_ptr()),
                                    _dtype_code(out.dtype), _stream(stream)), "tp_reduce_partials")
+    del keep
+    return out
+
+
+def _norm_operands(residual, gamma, out):
+    _dev(residual, "residual", torch.bfloat16, 2)
+    M, H = residual.shape
+    _dev(gamma, "gamma", torch.bfloat16, 1)
+    if gamma.shape[0] != H:
+        raise ValueError("gamma length != hidden size")
+    _dev(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, H):
+        raise ValueError("out shape != residual shape")
+    return M, H
+
+
+def tp_add_rmsnorm(x, residual, gamma, eps, out, stream=None):
+    """residual <- bf16(residual + x) (x None: unchanged); out <- RMSNorm of
+    the new residual times gamma."""
+    M, H = _norm_operands(residual, gamma, out)
+    if x is not None:
+        _dev(x, "x", torch.bfloat16, 2)
+        if tuple(x.shape) != (M, H):
+            raise ValueError("x shape != residual shape")
+    _check(_lib.tp_add_rmsnorm(None if x is None else ctypes.c_void_p(x.data_ptr()), M, H,
+                               ctypes.c_void_p(residual.data_ptr()), ctypes.c_void_p(gamma.data_ptr()),
+                               float(eps), ctypes.c_void_p(out.data_ptr()), _stream(stream)), "tp_add_rmsnorm")
+    return out
+
+
+def tp_reduce_add_rmsnorm(partials, residual, gamma, eps, out, stream=None):
+    """residual <- bf16(residual + bf16(sum of partials in rank order)); out <-
+    RMSNorm of the new residual times gamma."""
+    M, H = _norm_operands(residual, gamma, out)
+    t = len(partials)
+    if t < 1 or t > TP_MAX_SHARDS:
+        raise ValueError("need 1..64 partials")
+    in_dt = partials[0].dtype
+    for i, p in enumerate(partials):
+        _dev(p, f"partials[{i}]", in_dt, 2)
+        if tuple(p.shape) != (M, H):
+            raise ValueError("partial shape != residual shape")
+    arr, keep = _ptrs(partials)
+    _check(_lib.tp_reduce_add_rmsnorm(arr, t, _dtype_code(in_dt), M, H, ctypes.c_void_p(residual.data_ptr()),
+                                      ctypes.c_void_p(gamma.data_ptr()), float(eps),
+                                      ctypes.c_void_p(out.data_ptr()), _stream(stream)), "tp_reduce_add_rmsnorm")
     del keep
     return out
 

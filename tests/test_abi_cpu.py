@@ -182,3 +182,36 @@ def test_tune_rejects_unbuilt_variants():
     assert C.tp_tune_tiled(-2) == -6
     assert C.tp_tune_tiled(1) == 0
     assert C.tp_tune_tiled(-1) == 0
+
+
+def test_norm_calls_validate_before_any_hip_call():
+    f = C.tp_add_rmsnorm
+    R, G = ctypes.c_void_p(0x90000), ctypes.c_void_p(0xA0000)
+    eps = ctypes.c_float(1e-5)
+    assert f(A, 4, 64, NULL, G, eps, Y, S) == -1                      # residual NULL
+    assert f(A, 4, 64, R, NULL, eps, Y, S) == -1
+    assert f(A, 4, 60, R, G, eps, Y, S) == -4                         # H % 8
+    assert f(A, 4, 64, R, G, ctypes.c_float(-1.0), Y, S) == -6        # eps < 0
+    assert f(A, 4, 64, R, G, ctypes.c_float(float("nan")), Y, S) == -6
+    assert f(A, 4, 64, R, G, ctypes.c_float(float("inf")), Y, S) == -6
+    assert f(A, -1, 64, R, G, eps, Y, S) == -2
+    assert f(A, 4, 0, R, G, eps, Y, S) == -2
+    assert f(A, 4, 32776, R, G, eps, Y, S) == -2                      # H > 32768
+    assert f(A, 0, 32768, R, G, eps, Y, S) == 0
+    assert f(MIS, 4, 64, R, G, eps, Y, S) == -4
+    assert f(A, 4, 64, R, G, eps, ctypes.c_void_p(0x90000 + 64), S) == -2   # out overlaps residual
+    assert f(ctypes.c_void_p(0x90000 + 128), 4, 64, R, G, eps, Y, S) == -2  # x overlaps residual
+    assert f(A, 0, 64, R, G, eps, Y, S) == 0                          # M == 0: no-op
+    assert f(NULL, 0, 64, R, G, eps, Y, S) == 0                       # x may be NULL
+    g = C.tp_reduce_add_rmsnorm
+    arr = (ctypes.c_void_p * 3)(0x10000, 0x20000, 0x30000)
+    pp = ctypes.cast(arr, lib._ptr_array)
+    assert g(pp, 0, 0, 0, 64, R, G, eps, Y, S) == -6                  # t >= 1
+    assert g(pp, 65, 0, 0, 64, R, G, eps, Y, S) == -6
+    assert g(None, 3, 0, 0, 64, R, G, eps, Y, S) == -1
+    assert g(pp, 3, 7, 0, 64, R, G, eps, Y, S) == -5                  # dtype
+    bad = (ctypes.c_void_p * 2)(0x10000, 0x30008)
+    assert g(ctypes.cast(bad, lib._ptr_array), 2, 0, 4, 64, R, G, eps, Y, S) == -4
+    same = (ctypes.c_void_p * 2)(0x10000, 0x90000)
+    assert g(ctypes.cast(same, lib._ptr_array), 2, 0, 4, 64, R, G, eps, Y, S) == -2   # partial is residual
+    assert g(pp, 3, 1, 0, 64, R, G, eps, Y, S) == 0                   # fp32 partials, M == 0
