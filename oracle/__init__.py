@@ -25,6 +25,11 @@ Parity status of each function (what pins it, in tests/test_oracle_pins.py):
                         scaling, per-row independence, eps monotonicity.
   add_rms_norm          pinned: the add rounded once to bf16 (hand cases,
                         torch's bf16 add), then rms_norm.
+  gqa_decode_attention  pinned: uniform scores give the mean of V, one
+                        dominant score selects its V row, invariance under a
+                        joint permutation of positions, GQA head grouping,
+                        torch's float64 scaled_dot_product_attention.
+  append_kv             pinned: hand-placed rows.
   layer_linear_path     composed of the pinned functions above.
 """
 
@@ -35,7 +40,7 @@ from .tp_ref import (
     vocab_range_of_rank, qkv_shard_rows, gate_up_shard_rows, o_shard_cols,
     down_shard_cols, vocab_shard, shard_weight, vocab_embed_shard,
     vocab_embed_from_shard, column_linear_rank, row_linear_rank_partial, layer_linear_path,
-    rms_norm, add_rms_norm,
+    rms_norm, add_rms_norm, gqa_decode_attention, append_kv,
 )
 
 __all__ = [
@@ -45,4 +50,5 @@ __all__ = [
     "qkv_shard_rows", "gate_up_shard_rows", "o_shard_cols", "down_shard_cols",
     "vocab_shard", "shard_weight", "vocab_embed_shard", "vocab_embed_from_shard", "column_linear_rank",
     "row_linear_rank_partial", "layer_linear_path", "rms_norm", "add_rms_norm",
+    "gqa_decode_attention", "append_kv",
 ]

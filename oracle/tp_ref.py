@@ -8,7 +8,7 @@ module imports nothing from the product package.
 Pages cited (by title and section):
   [P1] "第 9 章 多进程与张量并行" (zero-to-sglang), sections 2.2, 3.1, 3.2.
   [P2] "Tensor Parallelism 执行路径" (SGLang internals), the weight-split
-       diagram and "前向执行的实际流程".
+       diagram, "前向执行的实际流程" and "KV Cache 在 TP 下怎样分布".
   [P3] "张量、流水线与数据并行", sections "线性层怎么切",
        "每 token 的通信量（估算）" and "流水线并行".
 
@@ -139,6 +139,55 @@ def add_rms_norm(x, residual, gamma, eps):
     residual = np.asarray(residual, dtype=np.float64)
     h = residual if x is None else round_bf16(residual + np.asarray(x, dtype=np.float64))
     return h, rms_norm(h, gamma, eps)
+
+
+def gqa_decode_attention(q, k_cache, v_cache, lens, num_q_heads, num_kv_heads):
+    """One decode step of grouped-query attention for the heads a rank holds,
+    float64.
+
+    [P2 前向执行的实际流程] Step 2 and [P2 KV Cache 在 TP 下怎样分布]: a rank
+    computes attention for its own Q heads against the K and V of its own KV
+    heads, with no exchange; [P3 线性层怎么切]: with fewer KV heads than ranks a
+    KV head is replicated, so the rank's Q heads all read it. The pages do not
+    write the attention itself; the reading taken is scaled dot-product
+    attention, softmax over positions of q . k / sqrt(d), no rotary
+    embedding, no mask beyond the sequence's length.
+
+    q: [B, num_q_heads, d]; k_cache, v_cache: [B, num_kv_heads, L, d]; lens:
+    [B] — sequence b attends to positions 0 .. lens[b] - 1 (lens[b] >= 1).
+    Q head h reads KV head h // (num_q_heads // num_kv_heads).
+    Returns [B, num_q_heads, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    k_cache = np.asarray(k_cache, dtype=np.float64)
+    v_cache = np.asarray(v_cache, dtype=np.float64)
+    B, nq, d = q.shape
+    if nq != num_q_heads or num_q_heads % num_kv_heads != 0 or k_cache.shape[1] != num_kv_heads:
+        raise ValueError("gqa_decode_attention: head counts do not match")
+    group = num_q_heads // num_kv_heads
+    out = np.zeros((B, nq, d))
+    for b in range(B):
+        n = int(lens[b])
+        if n < 1 or n > k_cache.shape[2]:
+            raise ValueError("gqa_decode_attention: lens[b] outside [1, L]")
+        for h in range(nq):
+            kv = h // group
+            s = k_cache[b, kv, :n] @ q[b, h] / math.sqrt(d)
+            p = np.exp(s - s.max())
+            out[b, h] = (p / p.sum()) @ v_cache[b, kv, :n]
+    return out
+
+
+def append_kv(k_cache, v_cache, k_new, v_new, lens):
+    """The decode step's cache write: the new token's K and V of sequence b go
+    to position lens[b] (the cache grows by one; [P2 KV Cache 在 TP 下怎样分布]:
+    each rank writes only its own KV heads). Returns new arrays.
+    k_new, v_new: [B, num_kv_heads, d]."""
+    k = np.array(np.asarray(k_cache, dtype=np.float64), copy=True)
+    v = np.array(np.asarray(v_cache, dtype=np.float64), copy=True)
+    for b in range(k.shape[0]):
+        k[b, :, int(lens[b])] = np.asarray(k_new, dtype=np.float64)[b]
+        v[b, :, int(lens[b])] = np.asarray(v_new, dtype=np.float64)[b]
+    return k, v
 
 
 # ---------------------------------------------------------------------------

@@ -20,7 +20,7 @@ from oracle import (
     embedding_lookup, q_heads_of_rank, kv_heads_of_rank, gqa_group, vocab_shard_rows,
     vocab_range_of_rank, qkv_shard_rows, gate_up_shard_rows, o_shard_cols,
     down_shard_cols, shard_weight, vocab_embed_shard, vocab_embed_from_shard,
-    layer_linear_path, rms_norm, add_rms_norm,
+    layer_linear_path, rms_norm, add_rms_norm, gqa_decode_attention, append_kv,
 )
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -451,3 +451,80 @@ def test_add_rms_norm_rounds_the_add_once():
     # no add: the residual is normalised as it is
     h0, out0 = add_rms_norm(None, b.float().numpy(), g, 1e-5)
     assert np.array_equal(h0, b.float().numpy()) and np.array_equal(out0, rms_norm(h0, g, 1e-5))
+
+
+# ------------------------------------------------- gqa_decode_attention / append_kv
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(21)
+    B, nq, nkv, L, d = 2, 4, 2, 9, 16
+    q = rng.standard_normal((B, nq, d))
+    v = rng.standard_normal((B, nkv, L, d))
+    # identical keys: every position scores the same, the output is the mean of V
+    k = np.broadcast_to(rng.standard_normal((1, 1, 1, d)), (B, nkv, L, d)).copy()
+    lens = [9, 5]
+    out = gqa_decode_attention(q, k, v, lens, nq, nkv)
+    for b in range(B):
+        for h in range(nq):
+            assert np.allclose(out[b, h], v[b, h // 2, :lens[b]].mean(axis=0), rtol=1e-13, atol=1e-15)
+    # one key aligned with q and far larger than the others selects its V row
+    k = rng.standard_normal((B, nkv, L, d)) * 1e-3
+    k[0, 0, 3] = 1e4 * q[0, 0] / np.linalg.norm(q[0, 0])
+    out = gqa_decode_attention(q, k, v, [9, 9], nq, nkv)
+    assert np.allclose(out[0, 0], v[0, 0, 3], rtol=0, atol=1e-12)
+    # a single position: the output is that V row whatever the scores
+    out = gqa_decode_attention(q, rng.standard_normal((B, nkv, L, d)), v, [1, 1], nq, nkv)
+    assert np.array_equal(out[:, 0], v[:, 0, 0]) and np.array_equal(out[:, 3], v[:, 1, 0])
+
+
+def test_attention_invariances_and_grouping():
+    rng = np.random.default_rng(22)
+    B, nq, nkv, L, d = 3, 8, 2, 12, 32
+    q = rng.standard_normal((B, nq, d))
+    k = rng.standard_normal((B, nkv, L, d))
+    v = rng.standard_normal((B, nkv, L, d))
+    lens = [12, 7, 1]
+    out = gqa_decode_attention(q, k, v, lens, nq, nkv)
+    # a joint permutation of the valid positions changes nothing
+    perm = rng.permutation(7)
+    k2, v2 = k.copy(), v.copy()
+    k2[1, :, :7], v2[1, :, :7] = k[1][:, perm], v[1][:, perm]
+    assert np.allclose(gqa_decode_attention(q, k2, v2, lens, nq, nkv)[1], out[1], rtol=1e-13, atol=1e-15)
+    # positions at or past lens[b] are never read
+    k3, v3 = k.copy(), v.copy()
+    k3[1, :, 7:], v3[1, :, 7:] = np.nan, np.nan
+    assert np.array_equal(gqa_decode_attention(q, k3, v3, lens, nq, nkv), out)
+    # Q heads 0-3 read KV head 0, heads 4-7 KV head 1 (not h mod n_kv)
+    for h in range(nq):
+        one = gqa_decode_attention(q[:, h:h + 1], k[:, h // 4:h // 4 + 1], v[:, h // 4:h // 4 + 1], lens, 1, 1)
+        assert np.allclose(one[:, 0], out[:, h], rtol=1e-14, atol=1e-15)
+    assert not np.allclose(out[:, 1], gqa_decode_attention(q[:, 1:2], k[:, 1:2], v[:, 1:2], lens, 1, 1)[:, 0])
+
+
+def test_attention_matches_torch_sdpa_in_float64():
+    rng = np.random.default_rng(23)
+    B, nq, nkv, L, d = 4, 4, 1, 40, 64
+    q = rng.standard_normal((B, nq, d))
+    k = rng.standard_normal((B, nkv, L, d))
+    v = rng.standard_normal((B, nkv, L, d))
+    lens = [40, 17, 2, 33]
+    out = gqa_decode_attention(q, k, v, lens, nq, nkv)
+    F = torch.nn.functional
+    for b in range(B):
+        n = lens[b]
+        qt = torch.from_numpy(q[b:b + 1, :, None, :])
+        kt = torch.from_numpy(k[b:b + 1, :, :n]).repeat_interleave(nq // nkv, dim=1)
+        vt = torch.from_numpy(v[b:b + 1, :, :n]).repeat_interleave(nq // nkv, dim=1)
+        ref = F.scaled_dot_product_attention(qt, kt, vt)[0, :, 0].numpy()
+        assert np.allclose(out[b], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_append_kv_places_rows():
+    k = np.zeros((2, 1, 4, 3))
+    v = np.zeros((2, 1, 4, 3))
+    kn = np.arange(6.0).reshape(2, 1, 3) + 1
+    vn = -kn
+    k2, v2 = append_kv(k, v, kn, vn, [0, 3])
+    assert np.array_equal(k2[0, 0, 0], [1, 2, 3]) and np.array_equal(k2[1, 0, 3], [4, 5, 6])
+    assert np.array_equal(v2[1, 0, 3], [-4, -5, -6]) and np.count_nonzero(k2) == 6
+    assert np.count_nonzero(k) == 0                    # inputs untouched
