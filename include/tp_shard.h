@@ -208,6 +208,26 @@ int tp_add_rmsnorm(const void* x_or_null, int64_t M, int64_t H, void* residual, 
 int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype, int64_t M, int64_t H,
                           void* residual, const void* gamma, float eps, void* out, void* stream);
 
+/* One decode step of the rank's grouped-query attention, with the KV-cache
+ * append ([P2 前向执行的实际流程] Step 2: each rank computes attention for its
+ * own heads with no exchange; [P2 KV Cache 在 TP 下怎样分布]: each rank holds
+ * and writes only its own KV heads; [P3 线性层怎么切]: a KV head shared by
+ * several ranks is replicated in each). Sequence b's new token (its K and V
+ * in the qkv row) is written to position lens[b] of the cache, then
+ *   ctx[b, h d + j] = sum_{p <= lens[b]} softmax_p(q_h . k_p / sqrt(d)) v_p[j]
+ * with Q head h reading KV head h / (nq / nkv); fp32 math, one rounding.
+ * No rotary embedding is applied. qkv: [B, (nq + 2 nkv) d] bf16, rows
+ * [Q heads | K heads | V heads] (tp_column_linear's output with the
+ * tp_shard_weights QKV layout); k_cache, v_cache: [B, nkv, L, d] bf16 (read,
+ * and written at lens[b]); lens: DEVICE [B] int32, read on the device: a
+ * sequence with lens[b] outside [0, L) gets a zero ctx row and no cache
+ * write; ctx: [B, nq d] bf16, head h in columns [h d, (h+1) d) — the rank's
+ * o_proj input. d in {32, 64, 128, 256}, nq % nkv == 0, nq / nkv <= 8,
+ * L <= 32768, B <= 65535 (TP_ERR_SHAPE otherwise). Uses the stream's
+ * workspace (allocated on the first call on a stream). */
+int tp_decode_attention(const void* qkv, int64_t B, int nq, int nkv, int head_dim, void* k_cache, void* v_cache,
+                        int64_t L, const int32_t* lens, void* ctx, void* stream);
+
 /* S9a. Vocab-parallel embedding, one shard's contribution: for each token m,
  * out[m, :] = e_shard[ids[m] - rank Vs, :] when rank Vs <= ids[m] <
  * min((rank+1) Vs, vocab), else a row of -0.0 (Vs = ceil(vocab / t)). Ids

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
 
-SOURCES = ["abi.cpp", "memops.hip", "gemm_skinny.hip", "gemm_tiled.hip"]
+SOURCES = ["abi.cpp", "memops.hip", "gemm_skinny.hip", "gemm_tiled.hip", "attention.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -13,6 +13,7 @@
 #include <utility>
 
 #include "kernels.h"
+#include "layer_ops.h"
 #include "tp_shard.h"
 
 namespace {
@@ -507,6 +508,52 @@ int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype,
         if (partials == nullptr) return TP_ERR_NULL;
         if (t < 1) return TP_ERR_RANGE;
         return add_rmsnorm_call(partials, t, partial_dtype, M, H, residual, gamma, eps, out, stream);
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_decode_attention(const void* qkv, int64_t B, int nq, int nkv, int head_dim, void* k_cache, void* v_cache,
+                        int64_t L, const int32_t* lens, void* ctx, void* stream) {
+    try {
+        if (qkv == nullptr || k_cache == nullptr || v_cache == nullptr || lens == nullptr || ctx == nullptr)
+            return TP_ERR_NULL;
+        if (B < 0 || B > 65535 || L < 1 || L > (int64_t)tpk::kAttnMaxChunks * tpk::kAttnChunk) return TP_ERR_SHAPE;
+        if (nq < 1 || nkv < 1 || nkv > 65535 || nq % nkv != 0 || nq / nkv > 8) return TP_ERR_SHAPE;
+        if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256) return TP_ERR_SHAPE;
+        if (!aligned16(qkv) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(ctx) ||
+            (reinterpret_cast<uintptr_t>(lens) & 3u))
+            return TP_ERR_ALIGNMENT;
+        const int64_t qkv_row = (int64_t)(nq + 2 * nkv) * head_dim;
+        const int64_t qkv_bytes = B * qkv_row * 2, cache_bytes = B * nkv * L * head_dim * 2,
+                      ctx_bytes = B * nq * head_dim * 2;
+        if (overlap(ctx, ctx_bytes, qkv, qkv_bytes) || overlap(ctx, ctx_bytes, k_cache, cache_bytes) ||
+            overlap(ctx, ctx_bytes, v_cache, cache_bytes) || overlap(k_cache, cache_bytes, v_cache, cache_bytes) ||
+            overlap(qkv, qkv_bytes, k_cache, cache_bytes) || overlap(qkv, qkv_bytes, v_cache, cache_bytes) ||
+            overlap(lens, B * 4, ctx, ctx_bytes) || overlap(lens, B * 4, k_cache, cache_bytes) ||
+            overlap(lens, B * 4, v_cache, cache_bytes))
+            return TP_ERR_SHAPE;
+        if (B == 0) return TP_OK;
+        tpk::AttnArgs a;
+        a.qkv = static_cast<const uint16_t*>(qkv);
+        a.k_cache = static_cast<uint16_t*>(k_cache);
+        a.v_cache = static_cast<uint16_t*>(v_cache);
+        a.lens = lens;
+        a.ctx = static_cast<uint16_t*>(ctx);
+        a.B = B;
+        a.L = L;
+        a.nq = nq;
+        a.nkv = nkv;
+        a.head_dim = head_dim;
+        a.qkv_stride = qkv_row;
+        a.scale = 1.0f / std::sqrt((float)head_dim);
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        tpk::Workspace ws{nullptr, 0, nullptr, 0};
+        const int st = get_workspace(s, &ws);
+        if (st != TP_OK) return st;
+        if (tpk::attention_workspace_floats(a) > ws.partial_floats || B * nkv > ws.num_counters) return TP_ERR_SHAPE;
+        const hipError_t e = tpk::launch_decode_attention(a, ws, s);
+        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
     } catch (...) {
         return TP_ERR_HIP;
     }

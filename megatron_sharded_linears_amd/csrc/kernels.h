@@ -39,12 +39,6 @@ hipError_t launch_vocab_embed(const int32_t* ids, int64_t M, const void* table, 
 hipError_t launch_concat(const PartialPtrs& ptrs, int t, int64_t M, int64_t v_shard,
                          int64_t vocab, int dtype, void* out, hipStream_t s);
 
-// residual[m] = bf16(residual[m] + bf16(sum of the t partials' row m)) (t = 0:
-// unchanged), out[m] = bf16(residual[m] * rsqrt-scale * gamma); one workgroup
-// per row, M <= 2^31 - 1, H % 8 == 0, H <= 32768.
-hipError_t launch_add_rmsnorm(const PartialPtrs& ptrs, int t, int in_dtype, int64_t M, int64_t H,
-                              void* residual, const void* gamma, float eps, void* out, hipStream_t s);
-
 // Epilogue of a linear.
 enum Epilogue : int {
     EPI_STORE = 0,    // y = acc (+ bias), out_dtype

@@ -5,6 +5,7 @@
 // contraction, so none of them uses the matrix cores.
 #include "common.h"
 #include "kernels.h"
+#include "layer_ops.h"
 
 namespace tpk {
 

@@ -80,6 +80,7 @@ _PROTOS = {
     "tp_concat_logits": (_int, [_ptr_array, _int, _i64, _i64, _i64, _int, _vp, _vp]),
     "tp_add_rmsnorm": (_int, [_vp, _i64, _i64, _vp, _vp, ctypes.c_float, _vp, _vp]),
     "tp_reduce_add_rmsnorm": (_int, [_ptr_array, _int, _int, _i64, _i64, _vp, _vp, ctypes.c_float, _vp, _vp]),
+    "tp_decode_attention": (_int, [_vp, _i64, _int, _int, _int, _vp, _vp, _i64, _vp, _vp, _vp]),
     "tp_tune_skinny": (_int, [_int, _int, _int, _int]),
     "tp_tune_tiled": (_int, [_int]),
 }
@@ -343,6 +344,31 @@ def tp_reduce_add_rmsnorm(partials, residual, gamma, eps, out, stream=None):
                                       ctypes.c_void_p(out.data_ptr()), _stream(stream)), "tp_reduce_add_rmsnorm")
     del keep
     return out
+
+
+def tp_decode_attention(qkv, k_cache, v_cache, lens, nq, ctx, stream=None):
+    """One decode step of the rank's GQA attention: the new K, V of each
+    sequence go to position lens[b] of the caches, then ctx = attention of
+    its nq query heads over positions 0..lens[b]. Caches [B, nkv, L, d]."""
+    _dev(k_cache, "k_cache", torch.bfloat16, 4)
+    _dev(v_cache, "v_cache", torch.bfloat16, 4)
+    B, nkv, L, d = k_cache.shape
+    if tuple(v_cache.shape) != (B, nkv, L, d):
+        raise ValueError("v_cache shape != k_cache shape")
+    _dev(qkv, "qkv", torch.bfloat16, 2)
+    if tuple(qkv.shape) != (B, (nq + 2 * nkv) * d):
+        raise ValueError("qkv must be [B, (nq + 2 nkv) d]")
+    _dev(lens, "lens", torch.int32, 1)
+    if lens.shape[0] != B:
+        raise ValueError("lens must have B entries")
+    _dev(ctx, "ctx", torch.bfloat16, 2)
+    if tuple(ctx.shape) != (B, nq * d):
+        raise ValueError("ctx must be [B, nq d]")
+    _check(_lib.tp_decode_attention(ctypes.c_void_p(qkv.data_ptr()), B, nq, nkv, d,
+                                    ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()), L,
+                                    ctypes.c_void_p(lens.data_ptr()), ctypes.c_void_p(ctx.data_ptr()),
+                                    _stream(stream)), "tp_decode_attention")
+    return ctx
 
 
 def tp_vocab_embed(ids, e_shard, vocab, t, rank, out_partial, stream=None):

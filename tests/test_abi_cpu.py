@@ -215,3 +215,23 @@ def test_norm_calls_validate_before_any_hip_call():
     same = (ctypes.c_void_p * 2)(0x10000, 0x90000)
     assert g(ctypes.cast(same, lib._ptr_array), 2, 0, 4, 64, R, G, eps, Y, S) == -2   # partial is residual
     assert g(pp, 3, 1, 0, 64, R, G, eps, Y, S) == 0                   # fp32 partials, M == 0
+
+
+def test_attention_validates_before_any_hip_call():
+    f = C.tp_decode_attention
+    KC, VC, LN, CT = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000), \
+        ctypes.c_void_p(0x400000)
+    assert f(NULL, 4, 4, 1, 128, KC, VC, 64, LN, CT, S) == -1
+    assert f(A, 4, 4, 1, 128, KC, VC, 64, NULL, CT, S) == -1
+    assert f(A, 4, 4, 1, 96, KC, VC, 64, LN, CT, S) == -2            # head_dim not 32/64/128/256
+    assert f(A, 4, 6, 4, 128, KC, VC, 64, LN, CT, S) == -2           # nq % nkv
+    assert f(A, 4, 18, 2, 128, KC, VC, 64, LN, CT, S) == -2          # group of 9 > 8
+    assert f(A, 4, 4, 1, 128, KC, VC, 0, LN, CT, S) == -2            # L >= 1
+    assert f(A, 4, 4, 1, 128, KC, VC, 32769, LN, CT, S) == -2        # L <= 32768
+    assert f(A, -1, 4, 1, 128, KC, VC, 64, LN, CT, S) == -2
+    assert f(A, 65536, 4, 1, 128, KC, VC, 64, LN, CT, S) == -2
+    assert f(MIS, 4, 4, 1, 128, KC, VC, 64, LN, CT, S) == -4
+    assert f(A, 4, 4, 1, 128, KC, VC, 64, ctypes.c_void_p(0x300002), CT, S) == -4   # lens 4-byte aligned
+    assert f(A, 4, 4, 1, 128, KC, KC, 64, LN, CT, S) == -2           # caches overlap
+    assert f(A, 4, 4, 1, 128, KC, VC, 64, LN, ctypes.c_void_p(0x100000 + 256), S) == -2   # ctx in the K cache
+    assert f(A, 0, 4, 1, 128, KC, VC, 64, LN, CT, S) == 0            # B == 0: no-op
