@@ -118,6 +118,20 @@ class Rank:
                 "g_post": (1.0 + dn((H,), 0.1, s + 7).float()).to(bf),
             })
         self.g_final = (1.0 + dn((H,), 0.1, 8).float()).to(bf)
+        # Decode: the rank's KV caches (its query heads' KV heads, replicated
+        # when there are fewer KV heads than ranks), KV_LEN tokens cached per
+        # sequence, room for KV_CAP; the step appends one token at KV_LEN.
+        d = w.head_dim
+        self.nq_r = self.shapes["o"][1] // d
+        self.nkv_r = (self.shapes["qkv"][0] // d - self.nq_r) // 2
+        self.attn = M <= 64
+        if self.attn:
+            for l, Ld in enumerate(self.layers):
+                s = 100 * (l + 1)
+                Ld["k_cache"] = dn((M, self.nkv_r, KV_CAP, d), 1.0, s + 8)
+                Ld["v_cache"] = dn((M, self.nkv_r, KV_CAP, d), 1.0, s + 9)
+            self.kv_lens = torch.full((M,), KV_LEN, dtype=torch.int32, device=dev)
+            self.ctx_attn = torch.empty((M, self.nq_r * d), dtype=bf, device=dev)
         self.x = dn((M, H), 1.0, 7)
         self.qkv = torch.empty((M, self.shapes["qkv"][0]), dtype=bf, device=dev)
         self.po = torch.empty((M, H), dtype=bf, device=dev)
@@ -163,6 +177,11 @@ class Rank:
             # read, the residual and the normalised row written, gamma read
             "reduce_norm": (2 * w.layers, 0, (2 * t + 6) * M * H + 2 * H),
             "input_norm": (1, 0, 4 * M * H + 2 * H),
+            # K and V of KV_LEN + 1 positions per (sequence, KV head), the qkv
+            # rows read, the context written, the new K and V written
+            "attention": (w.layers, 4 * M * self.nq_r * w.head_dim * (KV_LEN + 1),
+                          2 * 2 * M * self.nkv_r * (KV_LEN + 1) * w.head_dim + 2 * M * q[0]
+                          + 2 * M * self.nq_r * w.head_dim + 2 * 2 * M * self.nkv_r * w.head_dim),
         }
         if self.vocab:
             Ms, vs = self.hs_rows, self.vs
@@ -240,7 +259,26 @@ def build_norm_ops(R, lib, eps=1e-5):
     return ops
 
 
+def build_layer_ops(R, lib, eps=1e-5):
+    """The decode step of whole layers minus the rotary embedding: the norm
+    step (build_norm_ops) with o_proj reading the rank's attention over its
+    KV caches (tp_decode_attention, which also appends the new token)
+    instead of a synthetic context."""
+    ops = []
+    for name, fn, args in build_norm_ops(R, lib, eps):
+        if name == "o":
+            L = next(Ld for Ld in R.layers if Ld["o"] is args[1])
+            ops.append(("attention", lib.tp_decode_attention,
+                        (R.qkv, L["k_cache"], L["v_cache"], R.kv_lens, R.nq_r, R.ctx_attn)))
+            ops.append(("o", fn, (R.ctx_attn, args[1], args[2])))
+        else:
+            ops.append((name, fn, args))
+    return ops
+
+
 GEMM_OPS = ("qkv", "o", "gate_up", "down", "lm_head", "o_reduce", "gate_up_swiglu", "down_reduce")
+KV_LEN = 2048      # tokens cached per sequence before the decode step (the pages' prefill chunk)
+KV_CAP = 2304      # cache capacity per sequence
 
 
 def time_step(torch, ops, steps, warmup):
@@ -577,6 +615,9 @@ def main():
     # and with the residual stream and the RMSNorms of a real layer
     norm_ops = build_norm_ops(R, lib)
     ms_norm, _ = time_step(torch, norm_ops, args.steps, args.warmup)
+    # and (decode) whole layers: norms and the rank's attention over its KV caches
+    layer_ops = build_layer_ops(R, lib) if R.attn else None
+    ms_layer = time_step(torch, layer_ops, args.steps, args.warmup)[0] if layer_ops else None
 
     # --- per kernel: each op's launches of one step, captured and replayed K times
     per_op = {}
@@ -593,6 +634,16 @@ def main():
                         "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2) if flops else None,
                         "bytes_per_launch": byts}
 
+    attn = None
+    if layer_ops:
+        n_at = work["attention"][0]
+        g = capture(torch, layer_ops, only="attention", repeat=1)
+        us_at = time_graph(torch, g, args.steps, 2) * 1e3 / n_at
+        del g
+        attn = {"us_per_call": round(us_at, 3), "GBps": round(work["attention"][2] / (us_at * 1e-6) / 1e9, 1),
+                "frac_of_hbm": round(work["attention"][2] / (us_at * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                "bytes_per_call": work["attention"][2], "kv_len": KV_LEN, "kv_capacity": KV_CAP,
+                "q_heads": R.nq_r, "kv_heads": R.nkv_r}
     n_norm = work["reduce_norm"][0]
     g = capture(torch, norm_ops, only="reduce_norm", repeat=max(1, -(-32 // n_norm)))
     us_norm = time_graph(torch, g, args.steps, 2) * 1e3 / (n_norm * max(1, -(-32 // n_norm)))
@@ -658,6 +709,10 @@ def main():
                        "ms_per_step": round(ms_norm, 4), "value": round(flops_step / (ms_norm * 1e-3) / 1e12, 3),
                        "reduce_norm_us_per_call": round(us_norm, 3),
                        "reduce_norm_GBps": round(work["reduce_norm"][2] / (us_norm * 1e-6) / 1e9, 1)},
+        "full_layer": None if not layer_ops else {
+            "calls": "with_norms plus tp_decode_attention (KV append + attention) feeding o_proj; no rotary embedding",
+            "ms_per_step": round(ms_layer, 4), "value": round(flops_step / (ms_layer * 1e-3) / 1e12, 3),
+            "attention": attn},
         "per_op": per_op,
         "wall_s_timed": round(wall_s, 3),
         "pages_context": pages_context(w),

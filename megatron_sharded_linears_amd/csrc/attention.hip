@@ -192,13 +192,28 @@ decode_attention_kernel(AttnArgs a, float* __restrict__ ws, unsigned* __restrict
 
     // Last workgroup on (b, kvh): merge the chunks that hold positions, in
     // chunk order. A sequence with lens[b] outside [0, L) gets a zero row.
-    // The chunks' max and sum go to LDS in one batch of loads; each head's
-    // weights w_c = e^(m_c - M) / sum_c' l_c' e^(m_c' - M) follow; then every
-    // output sums w_c o_c over the chunks, 8 loads issued before their use.
+    // One memory round: each thread issues the loads of its outputs' partial
+    // values for up to BATCH chunks and of the chunks' max and sum before any
+    // is used; the weights w_c = e^(m_c - M) / sum_c' l_c' e^(m_c' - M) are
+    // formed in LDS; each output sums w_c o_c in chunk order.
+    constexpr int OPT = (G * D + kAttnThreads - 1) / kAttnThreads;   // outputs per thread
+    constexpr int BATCH = OPT >= 8 ? 8 : 64 / OPT;                   // chunks per round of loads
     __shared__ float s_w[G][kAttnMaxChunks];
     __shared__ float s_m[G][kAttnMaxChunks];
     const int nvalid = (n + kAttnChunk - 1) / kAttnChunk;
     const float* base = ws + ((b * a.nkv + kvh) * nchunks) * (int64_t)REC;
+    const int last_c = nvalid > 0 ? nvalid - 1 : 0;
+    float part[OPT][BATCH];
+#pragma unroll
+    for (int q = 0; q < OPT; ++q) {
+        const int i = tid + q * kAttnThreads < G * D ? tid + q * kAttnThreads : 0;
+        const int g = i / D, j = i % D;
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const int c = k < last_c ? k : last_c;
+            part[q][k] = __hip_atomic_load(base + c * REC + g * (D + 2) + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
     for (int i = tid; i < G * nvalid; i += kAttnThreads) {
         const int g = i / nvalid, c = i % nvalid;
         const float* r = base + c * REC + g * (D + 2) + D;
@@ -214,21 +229,20 @@ decode_attention_kernel(AttnArgs a, float* __restrict__ ws, unsigned* __restrict
         for (int c = 0; c < nvalid; ++c) s_w[tid][c] = __expf(s_m[tid][c] - mx) / l;
     }
     __syncthreads();
-    for (int i = tid; i < G * D; i += kAttnThreads) {
-        const int g = i / D, j = i % D;
-        float o = 0.f;
-        for (int c0 = 0; c0 < nvalid; c0 += 8) {
-            float part[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int c = c0 + k < nvalid ? c0 + k : nvalid - 1;
-                part[k] = __hip_atomic_load(base + c * REC + g * (D + 2) + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+    for (int q = 0; q < OPT; ++q) {
+        const int i = tid + q * kAttnThreads;
+        if (i < G * D) {
+            const int g = i / D, j = i % D;
+            float o = 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (c0 + k < nvalid) o += s_w[g][c0 + k] * part[k];
+            for (int k = 0; k < BATCH; ++k)
+                if (k < nvalid) o += s_w[g][k] * part[q][k];
+            for (int c = BATCH; c < nvalid; ++c)   // more than BATCH chunks: one load each
+                o += s_w[g][c] * __hip_atomic_load(base + c * REC + g * (D + 2) + j, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            a.ctx[b * (int64_t)a.nq * D + (int64_t)(kvh * G + g) * D + j] = (uint16_t)f32_to_bf16(o);
         }
-        a.ctx[b * (int64_t)a.nq * D + (int64_t)(kvh * G + g) * D + j] = (uint16_t)f32_to_bf16(o);
     }
     if (tid == 0) atomicExch(ctr, 0u);
 }
