@@ -518,7 +518,7 @@ int tp_decode_attention(const void* qkv, int64_t B, int nq, int nkv, int head_di
     try {
         if (qkv == nullptr || k_cache == nullptr || v_cache == nullptr || lens == nullptr || ctx == nullptr)
             return TP_ERR_NULL;
-        if (B < 0 || B > 65535 || L < 1 || L > (int64_t)tpk::kAttnMaxChunks * tpk::kAttnChunk) return TP_ERR_SHAPE;
+        if (B < 0 || B > 65535 || L < 1 || L > tpk::kAttnMaxLen) return TP_ERR_SHAPE;
         if (nq < 1 || nkv < 1 || nkv > 65535 || nq % nkv != 0 || nq / nkv > 8) return TP_ERR_SHAPE;
         if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256) return TP_ERR_SHAPE;
         if (!aligned16(qkv) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(ctx) ||
@@ -551,7 +551,7 @@ int tp_decode_attention(const void* qkv, int64_t B, int nq, int nkv, int head_di
         tpk::Workspace ws{nullptr, 0, nullptr, 0};
         const int st = get_workspace(s, &ws);
         if (st != TP_OK) return st;
-        if (tpk::attention_workspace_floats(a) > ws.partial_floats || B * nkv > ws.num_counters) return TP_ERR_SHAPE;
+        if (tpk::attention_workspace_floats(a) > ws.partial_floats) return TP_ERR_SHAPE;
         const hipError_t e = tpk::launch_decode_attention(a, ws, s);
         return e == hipSuccess ? TP_OK : TP_ERR_HIP;
     } catch (...) {

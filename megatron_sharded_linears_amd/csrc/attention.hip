@@ -3,26 +3,32 @@
 //
 // A rank holds nq query heads and nkv KV heads (its share, KV heads possibly
 // replicated); the G = nq / nkv query heads of a group read the same K and V.
-// Decode attention is bound by reading the cache once: per (sequence, KV head)
-// 2 (n) D bytes of bf16 K and V against 4 G (n) D flops, far below what the
-// vector ALU sustains, so there are no MFMAs here. Design:
-//   * Workgroups split the sequence: one per (chunk of 128 positions, KV
-//     head, sequence). Each reads its K and V rows once for all G heads of the
-//     group. D / 8 lanes hold one position (16 bytes each), so a wave covers
-//     64 / (D / 8) positions per step; every K and V load of the chunk is
-//     issued before the first is used (clamped addresses, masked results).
-//   * The new token's K and V are read from the qkv output (its position is
-//     lens[b]); the workgroup whose chunk holds that position also writes
-//     them into the cache. No other workgroup of the launch reads that cache
-//     row, so the append needs no ordering.
-//   * Per chunk: scores in LDS, each wave takes whole heads for the max, the
-//     exponentials and their sum; the weighted V rows are summed across the
-//     position slots of a wave by lane swaps, then across the waves in order.
-//   * Chunks are merged by the last workgroup to arrive on (sequence, KV
-//     head) (one counter each, reset by that workgroup): partial results
-//     travel through relaxed device-scope stores and loads and are combined
-//     in chunk order with the usual max-rescaling, so the result does not
-//     depend on arrival order.
+// Decode attention is bound by reading the cache once: per (sequence, KV
+// head) 2 (n) D bytes of bf16 K and V. Two launches:
+//
+//   1. attn_chunk_kernel, one workgroup of 4 waves per (chunk of positions,
+//      KV head, sequence). Every cache load of the chunk, the queries and the
+//      new token's K and V are issued at the start, before the sequence length
+//      arrives (addresses are clamped inside the cache; rows past the length
+//      are masked once it is known), so the loads cost one memory round trip.
+//        * Scores on the matrix cores: v_mfma_f32_16x16x32_bf16 with 16 cache
+//          rows as the A operand and the group's query heads (padded to 16)
+//          as the B operand, so every lane ends with 4 whole dot products and
+//          no cross-lane reduction is needed.
+//        * Softmax statistics per wave (max and sum of its positions, per
+//          head); the probabilities go through a wave-private LDS slab to the
+//          layout of the V loads, where each lane owns 8 consecutive columns
+//          of V and sums p * v over its positions.
+//        * The waves' sums are rescaled to the chunk's max and written, with
+//          that max and the chunk's sum of exponentials, as one record per
+//          (chunk, head) to the workspace (plain stores: the kernel boundary
+//          makes them visible to the merge).
+//      The workgroup whose chunk holds the new token's position replaces the
+//      stale cache row in registers and writes the new K and V into the caches
+//      (the append); no other workgroup reads that row.
+//   2. attn_merge_kernel, one thread per output column: the records of the
+//      chunks in use are combined in chunk order with the usual max
+//      rescaling, so the result does not depend on scheduling.
 #include "common.h"
 #include "layer_ops.h"
 
@@ -35,246 +41,294 @@ constexpr int kAttnWaves = kAttnThreads / 64;
 
 template <int D, int G>
 __global__ void __launch_bounds__(kAttnThreads)
-decode_attention_kernel(AttnArgs a, float* __restrict__ ws, unsigned* __restrict__ counters) {
-    constexpr int LP = D / 8;                        // lanes per position
-    constexpr int PW = 64 / LP;                      // positions per wave step
-    constexpr int STEPS = kAttnChunk / (kAttnWaves * PW);
-    constexpr int REC = G * (D + 2);                 // floats of one chunk's partial: G x (o[D], m, l)
-    static_assert(kAttnChunk % (kAttnWaves * PW) == 0, "chunk must split evenly over the waves");
+attn_chunk_kernel(AttnArgs a, float* __restrict__ ws) {
+    constexpr int WP = attn_chunk(D) / kAttnWaves;   // positions per wave (16 per MFMA block)
+    constexpr int NB = WP / 16;                      // MFMA blocks per wave
+    constexpr int KS = D / 32;                       // MFMA k-steps per block
+    constexpr int LPR = D / 8;                       // lanes per V row (16 bytes each)
+    constexpr int RPI = 64 / LPR;                    // V rows per wave load
+    constexpr int VSTEPS = WP / RPI;                 // V loads per lane
+    constexpr int GP = G <= 4 ? 4 : 8;               // heads, padded, per LDS probability row
+    constexpr int RED = G > 4 ? 2 : 1;               // row groups folded by a lane swap first
+    constexpr int RG = RPI / RED;                    // row groups per wave kept in LDS
+    constexpr int REC = G * (D + 2);                 // floats of one chunk's record
+    static_assert(WP % 16 == 0 && WP % RPI == 0, "wave positions must split into blocks and V steps");
 
-    __shared__ float s_score[G][kAttnChunk];
-    __shared__ float s_ml[G][2];
-    __shared__ float s_acc[kAttnWaves][G][D];
-    __shared__ unsigned s_last;
+    __shared__ __align__(16) float s_p[kAttnWaves][WP][GP];         // probabilities (wave-private)
+    __shared__ float s_ml[kAttnWaves][2][GP];                      // per wave and head: max, sum
+    __shared__ __align__(16) float s_o[kAttnWaves * RG][G][D];     // per row group: sum of p v
 
     const int ci = blockIdx.x, kvh = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sub = lane / LP, piece = lane % LP;
-    const int nchunks = gridDim.x;
-    const int32_t len = a.lens[b];
-    const bool valid_seq = len >= 0 && len < a.L;
-    const int n = valid_seq ? len + 1 : 0;           // keys: the cached ones and the new one
-    const int p0 = ci * kAttnChunk;
-    const int cnt = n - p0 < kAttnChunk ? n - p0 : kAttnChunk;   // positions of this chunk (<= 0: none)
+    const int p0 = ci * attn_chunk(D);
+    const int pw = p0 + wave * WP;                   // first position of this wave
+    const int last = (int)(a.L - 1);
 
     const uint16_t* qrow = a.qkv + b * a.qkv_stride;
-    const uint16_t* k_new = qrow + (int64_t)(a.nq + kvh) * D + piece * 8;
-    const uint16_t* v_new = qrow + (int64_t)(a.nq + a.nkv + kvh) * D + piece * 8;
-    const int64_t cache_base = ((b * a.nkv + kvh) * a.L) * D + piece * 8;
-    float* rec = ws + ((b * a.nkv + kvh) * nchunks + ci) * (int64_t)REC;
+    const uint16_t* k_new = qrow + (int64_t)(a.nq + kvh) * D;
+    const uint16_t* v_new = qrow + (int64_t)(a.nq + a.nkv + kvh) * D;
+    const int64_t cache0 = (b * a.nkv + kvh) * a.L * D;
 
-    if (cnt > 0) {
-        // every K and V piece of the chunk, then the queries (pre-scaled)
-        uint4 kr[STEPS], vr[STEPS];
+    // 1. Loads. MFMA operand lanes: row (cache position or head) lane & 15,
+    //    8-element group lane >> 4 of each 32-wide k-step. V lanes: row
+    //    lane / LPR of each step, columns vd .. vd + 7.
+    const int32_t len = a.lens[b];
+    const int kr = lane & 15, kq = lane >> 4;
+    const int vr = lane / LPR, vd = 8 * (lane % LPR);
+    uint4 kf[NB][KS];
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            const int idx = (st * kAttnWaves + wave) * PW + sub;
-            const int pos = p0 + (idx < cnt ? idx : cnt - 1);
-            const bool is_new = pos == n - 1;
-            const uint16_t* kp = is_new ? k_new : a.k_cache + cache_base + (int64_t)pos * D;
-            const uint16_t* vp = is_new ? v_new : a.v_cache + cache_base + (int64_t)pos * D;
-            kr[st] = *reinterpret_cast<const uint4*>(kp);
-            vr[st] = *reinterpret_cast<const uint4*>(vp);
+    for (int bl = 0; bl < NB; ++bl) {
+        const int pos = pw + 16 * bl + kr;
+        const int64_t row = cache0 + (int64_t)(pos < last ? pos : last) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kf[bl][ks] = *reinterpret_cast<const uint4*>(a.k_cache + row + 32 * ks + 8 * kq);
+    }
+    uint4 vf[VSTEPS];
+#pragma unroll
+    for (int st = 0; st < VSTEPS; ++st) {
+        const int pos = pw + st * RPI + vr;
+        vf[st] = *reinterpret_cast<const uint4*>(a.v_cache + cache0 + (int64_t)(pos < last ? pos : last) * D + vd);
+    }
+    // query head kr of the group (lanes past G read head 0; their columns of
+    // the scores are never used) and the new token's K in the same layout
+    const int qh = kr < G ? kr : 0;
+    uint4 qf[KS], knf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = *reinterpret_cast<const uint4*>(qrow + (int64_t)(kvh * G + qh) * D + 32 * ks + 8 * kq);
+        knf[ks] = *reinterpret_cast<const uint4*>(k_new + 32 * ks + 8 * kq);
+    }
+    const uint4 vn = *reinterpret_cast<const uint4*>(v_new + vd);
+
+    // 2. Positions 0 .. n-1 are in use: the cached ones and the new token at
+    //    n - 1 = lens[b] (none when lens[b] is outside [0, L)). The new row
+    //    replaces the stale cache row and is appended by the lanes holding it.
+    const bool valid = len >= 0 && (int64_t)len < a.L;
+    const int n = valid ? len + 1 : 0;
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl) {
+        const int pos = pw + 16 * bl + kr;
+        if (pos == n - 1) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                kf[bl][ks] = knf[ks];
+                *reinterpret_cast<uint4*>(a.k_cache + cache0 + (int64_t)pos * D + 32 * ks + 8 * kq) = knf[ks];
+            }
         }
-        float qf[G][8];
+    }
+#pragma unroll
+    for (int st = 0; st < VSTEPS; ++st) {
+        const int pos = pw + st * RPI + vr;
+        if (pos == n - 1) {
+            vf[st] = vn;
+            *reinterpret_cast<uint4*>(a.v_cache + cache0 + (int64_t)pos * D + vd) = vn;
+        }
+        // rows past the end may hold anything (NaN included): their weight is 0
+        if (pos >= n) vf[st] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // 3. Scores: sc[bl][r] = K[pw + 16 bl + 4 kq + r] . Q[head kr].
+    f32x4_t sc[NB];
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl) {
+        sc[bl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            sc[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[bl][ks]),
+                                                             __builtin_bit_cast(bf16x8_t, qf[ks]), sc[bl], 0, 0, 0);
+    }
+
+    // 4. Per-wave softmax statistics of each head: the 4 lanes of a head
+    //    (kq = 0..3) hold its WP scores. A wave with no position in use keeps
+    //    max -inf and sum 0 and contributes nothing.
+    float s[NB][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int pos = pw + 16 * bl + 4 * kq + r;
+            s[bl][r] = pos < n ? sc[bl][r] * a.scale : -INFINITY;
+            mx = fmaxf(mx, s[bl][r]);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mref = mx == -INFINITY ? 0.f : mx;
+    float l = 0.f;
+#pragma unroll
+    for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[bl][r] = __expf(s[bl][r] - mref);
+            l += s[bl][r];
+        }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (kr < G) {
+#pragma unroll
+        for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_p[wave][16 * bl + 4 * kq + r][kr] = s[bl][r];
+        if (kq == 0) {
+            s_ml[wave][0][kr] = mx;
+            s_ml[wave][1][kr] = l;
+        }
+    }
+    lds_barrier();
+
+    // 5. Weighted V rows: each lane over its VSTEPS positions, for every head.
+    float acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+#pragma unroll
+    for (int st = 0; st < VSTEPS; ++st) {
+        float p[GP];
+#pragma unroll
+        for (int q = 0; q < GP / 4; ++q) {
+            const float4 p4 = *reinterpret_cast<const float4*>(&s_p[wave][st * RPI + vr][4 * q]);
+            p[4 * q] = p4.x;
+            p[4 * q + 1] = p4.y;
+            p[4 * q + 2] = p4.z;
+            p[4 * q + 3] = p4.w;
+        }
+        float v[8];
+        unpack_bf16x8(vf[st], v);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] += p[g] * v[e];
+    }
+    if constexpr (RED == 2) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] += __shfl_xor(acc[g][e], 32);
+    }
+    if (RED == 1 || lane < 32) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            unpack_bf16x8(*reinterpret_cast<const uint4*>(qrow + (int64_t)(kvh * G + g) * D + piece * 8), qf[g]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qf[g][e] *= a.scale;
-        }
-        // the append: the lanes that hold the new row write it to the cache
-        if (n - 1 >= p0 && n - 1 < p0 + kAttnChunk) {
-#pragma unroll
-            for (int st = 0; st < STEPS; ++st) {
-                const int idx = (st * kAttnWaves + wave) * PW + sub;
-                if (p0 + idx == n - 1) {
-                    *reinterpret_cast<uint4*>(a.k_cache + cache_base + (int64_t)(n - 1) * D) = kr[st];
-                    *reinterpret_cast<uint4*>(a.v_cache + cache_base + (int64_t)(n - 1) * D) = vr[st];
-                }
-            }
-        }
-        // scores
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            const int idx = (st * kAttnWaves + wave) * PW + sub;
-            float kf[8];
-            unpack_bf16x8(kr[st], kf);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float d = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) d += qf[g][e] * kf[e];
-#pragma unroll
-                for (int o = 1; o < LP; o <<= 1) d += __shfl_xor(d, o);
-                if (piece == 0 && idx < cnt) s_score[g][idx] = d;
-            }
-        }
-        __syncthreads();
-        // softmax statistics: wave w takes heads w, w + 4, ...
-        for (int g = wave; g < G; g += kAttnWaves) {
-            float m = -INFINITY;
-            for (int i = lane; i < cnt; i += 64) m = fmaxf(m, s_score[g][i]);
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-            float l = 0.f;
-            for (int i = lane; i < cnt; i += 64) {
-                const float p = __expf(s_score[g][i] - m);
-                s_score[g][i] = p;
-                l += p;
-            }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
-            if (lane == 0) {
-                s_ml[g][0] = m;
-                s_ml[g][1] = l;
-            }
-        }
-        __syncthreads();
-        // weighted V rows: per lane over its positions, then over the
-        // position slots of the wave, then over the waves
-        float acc[G][8];
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            const int idx = (st * kAttnWaves + wave) * PW + sub;
-            float vf[8];
-            unpack_bf16x8(vr[st], vf);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float p = idx < cnt ? s_score[g][idx] : 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[g][e] += p * vf[e];
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float v = acc[g][e];
-#pragma unroll
-                for (int o = LP; o < 64; o <<= 1) v += __shfl_xor(v, o);
-                acc[g][e] = v;
-            }
-        if (sub == 0) {
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s_acc[wave][g][piece * 8 + e] = acc[g][e];
-        }
-        __syncthreads();
-        // publish this chunk's partial: o[G][D], then m and l per head
-        for (int i = tid; i < G * D; i += kAttnThreads) {
-            const int g = i / D, j = i % D;
-            float v = s_acc[0][g][j];
-#pragma unroll
-            for (int w = 1; w < kAttnWaves; ++w) v += s_acc[w][g][j];
-            __hip_atomic_store(rec + g * (D + 2) + j, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (tid < G) {
-            __hip_atomic_store(rec + tid * (D + 2) + D, s_ml[tid][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(rec + tid * (D + 2) + D + 1, s_ml[tid][1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            float* dst = &s_o[wave * RG + vr][g][vd];
+            *reinterpret_cast<float4*>(dst) = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    unsigned* ctr = counters + b * a.nkv + kvh;
-    if (tid == 0) {
-        const unsigned prev = atomicAdd(ctr, 1u);
-        s_last = prev == (unsigned)(nchunks - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (s_last != 1u) return;
+    lds_barrier();
 
-    // Last workgroup on (b, kvh): merge the chunks that hold positions, in
-    // chunk order. A sequence with lens[b] outside [0, L) gets a zero row.
-    // One memory round: each thread issues the loads of its outputs' partial
-    // values for up to BATCH chunks and of the chunks' max and sum before any
-    // is used; the weights w_c = e^(m_c - M) / sum_c' l_c' e^(m_c' - M) are
-    // formed in LDS; each output sums w_c o_c in chunk order.
-    constexpr int OPT = (G * D + kAttnThreads - 1) / kAttnThreads;   // outputs per thread
-    constexpr int BATCH = OPT >= 8 ? 8 : 64 / OPT;                   // chunks per round of loads
-    __shared__ float s_w[G][kAttnMaxChunks];
-    __shared__ float s_m[G][kAttnMaxChunks];
-    const int nvalid = (n + kAttnChunk - 1) / kAttnChunk;
-    const float* base = ws + ((b * a.nkv + kvh) * nchunks) * (int64_t)REC;
-    const int last_c = nvalid > 0 ? nvalid - 1 : 0;
-    float part[OPT][BATCH];
+    // 6. The chunk's record per head: sum over waves of e^(m_w - m) o_w (row
+    //    groups and waves in order), then m = max_w m_w and sum_w e^(m_w - m) l_w.
+    if (n <= p0) return;                              // no position of this chunk in use
+    float* rec = ws + ((b * a.nkv + kvh) * gridDim.x + ci) * (int64_t)REC;
+    for (int i = tid; i < G * D; i += kAttnThreads) {
+        const int g = i / D, j = i - g * D;
+        float m = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < OPT; ++q) {
-        const int i = tid + q * kAttnThreads < G * D ? tid + q * kAttnThreads : 0;
-        const int g = i / D, j = i % D;
+        for (int w = 0; w < kAttnWaves; ++w) m = fmaxf(m, s_ml[w][0][g]);
+        float o = 0.f, lc = 0.f;
 #pragma unroll
-        for (int k = 0; k < BATCH; ++k) {
-            const int c = k < last_c ? k : last_c;
-            part[q][k] = __hip_atomic_load(base + c * REC + g * (D + 2) + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int w = 0; w < kAttnWaves; ++w) {
+            const float f = __expf(s_ml[w][0][g] - m);
+            float ow = 0.f;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) ow += s_o[w * RG + r][g][j];
+            o += f * ow;
+            lc += f * s_ml[w][1][g];
+        }
+        rec[g * (D + 2) + j] = o;
+        if (j == 0) {
+            rec[g * (D + 2) + D] = m;
+            rec[g * (D + 2) + D + 1] = lc;
         }
     }
-    for (int i = tid; i < G * nvalid; i += kAttnThreads) {
-        const int g = i / nvalid, c = i % nvalid;
-        const float* r = base + c * REC + g * (D + 2) + D;
-        s_m[g][c] = __hip_atomic_load(r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_w[g][c] = __hip_atomic_load(r + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (tid < G) {
-        float mx = -INFINITY;
-        for (int c = 0; c < nvalid; ++c) mx = fmaxf(mx, s_m[tid][c]);
-        float l = 0.f;
-        for (int c = 0; c < nvalid; ++c) l += s_w[tid][c] * __expf(s_m[tid][c] - mx);
-        for (int c = 0; c < nvalid; ++c) s_w[tid][c] = __expf(s_m[tid][c] - mx) / l;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < OPT; ++q) {
-        const int i = tid + q * kAttnThreads;
-        if (i < G * D) {
-            const int g = i / D, j = i % D;
-            float o = 0.f;
-#pragma unroll
-            for (int k = 0; k < BATCH; ++k)
-                if (k < nvalid) o += s_w[g][k] * part[q][k];
-            for (int c = BATCH; c < nvalid; ++c)   // more than BATCH chunks: one load each
-                o += s_w[g][c] * __hip_atomic_load(base + c * REC + g * (D + 2) + j, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            a.ctx[b * (int64_t)a.nq * D + (int64_t)(kvh * G + g) * D + j] = (uint16_t)f32_to_bf16(o);
-        }
-    }
-    if (tid == 0) atomicExch(ctr, 0u);
 }
 
-typedef void (*AttnFn)(AttnArgs, float*, unsigned*);
+// Records of the chunks 0 .. ceil(n / chunk) - 1 of (sequence, KV head),
+// combined in chunk order, MB chunks per round of loads:
+// ctx = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c with M the running max.
+template <int D, int G>
+__global__ void __launch_bounds__(D)
+attn_merge_kernel(AttnArgs a, const float* __restrict__ ws, int nchunks) {
+    constexpr int REC = G * (D + 2);
+    constexpr int MB = 32;
+    const int g = blockIdx.x, kvh = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int j = threadIdx.x;
+    const int32_t len = a.lens[b];
+    const bool valid = len >= 0 && (int64_t)len < a.L;
+    const int n = valid ? len + 1 : 0;
+    const int nvalid = (n + attn_chunk(D) - 1) / attn_chunk(D);
+    const float* base = ws + (b * a.nkv + kvh) * (int64_t)nchunks * REC + g * (D + 2);
+    float M = -INFINITY, lsum = 0.f, o = 0.f;
+    for (int c0 = 0; c0 < nvalid; c0 += MB) {
+        float mc[MB], lc[MB], oc[MB];
+#pragma unroll
+        for (int k = 0; k < MB; ++k) {
+            const int c = c0 + k < nvalid ? c0 + k : nvalid - 1;
+            mc[k] = base[(int64_t)c * REC + D];
+            lc[k] = base[(int64_t)c * REC + D + 1];
+            oc[k] = base[(int64_t)c * REC + j];
+        }
+        float Mn = M;
+#pragma unroll
+        for (int k = 0; k < MB; ++k)
+            if (c0 + k < nvalid) Mn = fmaxf(Mn, mc[k]);
+        const float f = __expf(M - Mn);               // 0 on the first round (M = -inf)
+        lsum *= f;
+        o *= f;
+#pragma unroll
+        for (int k = 0; k < MB; ++k)
+            if (c0 + k < nvalid) {
+                const float e = __expf(mc[k] - Mn);
+                lsum += e * lc[k];
+                o += e * oc[k];
+            }
+        M = Mn;
+    }
+    // a sequence with no position in use gets a zero row
+    a.ctx[b * (int64_t)a.nq * D + (int64_t)(kvh * G + g) * D + j] =
+        (uint16_t)f32_to_bf16(nvalid > 0 ? o / lsum : 0.f);
+}
+
+struct AttnFns {
+    void (*chunk)(AttnArgs, float*);
+    void (*merge)(AttnArgs, const float*, int);
+};
+
+template <int D, int G>
+AttnFns attn_fns() {
+    return AttnFns{attn_chunk_kernel<D, G>, attn_merge_kernel<D, G>};
+}
 
 template <int D>
-AttnFn attn_for_group(int g) {
+AttnFns attn_for_group(int g) {
     switch (g) {
-    case 1: return decode_attention_kernel<D, 1>;
-    case 2: return decode_attention_kernel<D, 2>;
-    case 3: return decode_attention_kernel<D, 3>;
-    case 4: return decode_attention_kernel<D, 4>;
-    case 5: return decode_attention_kernel<D, 5>;
-    case 6: return decode_attention_kernel<D, 6>;
-    case 7: return decode_attention_kernel<D, 7>;
-    case 8: return decode_attention_kernel<D, 8>;
-    default: return nullptr;
+    case 1: return attn_fns<D, 1>();
+    case 2: return attn_fns<D, 2>();
+    case 3: return attn_fns<D, 3>();
+    case 4: return attn_fns<D, 4>();
+    case 5: return attn_fns<D, 5>();
+    case 6: return attn_fns<D, 6>();
+    case 7: return attn_fns<D, 7>();
+    case 8: return attn_fns<D, 8>();
+    default: return AttnFns{nullptr, nullptr};
     }
 }
 
 }  // namespace
 
 int64_t attention_workspace_floats(const AttnArgs& a) {
-    const int64_t nchunks = (a.L + kAttnChunk - 1) / kAttnChunk;
+    const int64_t ch = attn_chunk(a.head_dim);
+    const int64_t nchunks = (a.L + ch - 1) / ch;
     const int64_t g = a.nq / a.nkv;
     return a.B * a.nkv * nchunks * g * (a.head_dim + 2);
 }
 
 hipError_t launch_decode_attention(const AttnArgs& a, const Workspace& ws, hipStream_t s) {
     const int g = a.nq / a.nkv;
-    AttnFn fn = nullptr;
+    AttnFns fn{nullptr, nullptr};
     switch (a.head_dim) {
     case 32: fn = attn_for_group<32>(g); break;
     case 64: fn = attn_for_group<64>(g); break;
@@ -282,10 +336,15 @@ hipError_t launch_decode_attention(const AttnArgs& a, const Workspace& ws, hipSt
     case 256: fn = attn_for_group<256>(g); break;
     default: break;
     }
-    if (fn == nullptr) return hipErrorInvalidValue;
-    const unsigned nchunks = (unsigned)((a.L + kAttnChunk - 1) / kAttnChunk);
-    hipLaunchKernelGGL(fn, dim3(nchunks, (unsigned)a.nkv, (unsigned)a.B), dim3(kAttnThreads), 0, s, a,
-                       ws.partials, ws.counters);
+    if (fn.chunk == nullptr) return hipErrorInvalidValue;
+    const int64_t ch = attn_chunk(a.head_dim);
+    const int nchunks = (int)((a.L + ch - 1) / ch);
+    hipLaunchKernelGGL(fn.chunk, dim3((unsigned)nchunks, (unsigned)a.nkv, (unsigned)a.B), dim3(kAttnThreads), 0, s,
+                       a, ws.partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn.merge, dim3((unsigned)g, (unsigned)a.nkv, (unsigned)a.B), dim3((unsigned)a.head_dim), 0, s,
+                       a, static_cast<const float*>(ws.partials), nchunks);
     return hipGetLastError();
 }
 
