@@ -248,6 +248,9 @@ attn_chunk_kernel(AttnArgs a, float* __restrict__ ws) {
 // Records of the chunks 0 .. ceil(n / chunk) - 1 of (sequence, KV head),
 // combined in chunk order, MB chunks per round of loads:
 // ctx = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c with M the running max.
+// The first round's loads do not wait for the sequence length (they cover
+// the first MB chunks of the cache; records past the ones in use are left
+// over from other calls and are never used).
 template <int D, int G>
 __global__ void __launch_bounds__(D)
 attn_merge_kernel(AttnArgs a, const float* __restrict__ ws, int nchunks) {
@@ -256,21 +259,25 @@ attn_merge_kernel(AttnArgs a, const float* __restrict__ ws, int nchunks) {
     const int g = blockIdx.x, kvh = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int j = threadIdx.x;
-    const int32_t len = a.lens[b];
-    const bool valid = len >= 0 && (int64_t)len < a.L;
-    const int n = valid ? len + 1 : 0;
-    const int nvalid = (n + attn_chunk(D) - 1) / attn_chunk(D);
     const float* base = ws + (b * a.nkv + kvh) * (int64_t)nchunks * REC + g * (D + 2);
-    float M = -INFINITY, lsum = 0.f, o = 0.f;
-    for (int c0 = 0; c0 < nvalid; c0 += MB) {
-        float mc[MB], lc[MB], oc[MB];
+    const int32_t len = a.lens[b];
+    float mc[MB], lc[MB], oc[MB];
+    auto load = [&](int c0, int cmax) {
 #pragma unroll
         for (int k = 0; k < MB; ++k) {
-            const int c = c0 + k < nvalid ? c0 + k : nvalid - 1;
+            const int c = c0 + k < cmax ? c0 + k : cmax - 1;
             mc[k] = base[(int64_t)c * REC + D];
             lc[k] = base[(int64_t)c * REC + D + 1];
             oc[k] = base[(int64_t)c * REC + j];
         }
+    };
+    load(0, nchunks);
+    const bool valid = len >= 0 && (int64_t)len < a.L;
+    const int n = valid ? len + 1 : 0;
+    const int nvalid = (n + attn_chunk(D) - 1) / attn_chunk(D);
+    float M = -INFINITY, lsum = 0.f, o = 0.f;
+    for (int c0 = 0; c0 < nvalid; c0 += MB) {
+        if (c0 > 0) load(c0, nvalid);
         float Mn = M;
 #pragma unroll
         for (int k = 0; k < MB; ++k)
