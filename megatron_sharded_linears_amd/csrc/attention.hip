@@ -7,7 +7,11 @@
 // head) 2 (n) D bytes of bf16 K and V. Two launches:
 //
 //   1. attn_chunk_kernel, one workgroup of 4 waves per (chunk of positions,
-//      KV head, sequence). Every cache load of the chunk, the queries and the
+//      KV head, sequence). A chunk is 192 positions (64 at d = 256, where a
+//      second 16-row block per wave would not fit in registers): at the
+//      decode workloads' shapes it leaves the busiest CU the fewest cache
+//      rows to stream (128 and 256 were slower), and being fixed, a
+//      sequence's result does not depend on the batch around it. Every cache load of the chunk, the queries and the
 //      new token's K and V are issued at the start, before the sequence length
 //      arrives (addresses are clamped inside the cache; rows past the length
 //      are masked once it is known), so the loads cost one memory round trip.
@@ -39,11 +43,11 @@ namespace {
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / 64;
 
-template <int D, int G>
+template <int D, int G, int NB>
 __global__ void __launch_bounds__(kAttnThreads)
 attn_chunk_kernel(AttnArgs a, float* __restrict__ ws) {
-    constexpr int WP = attn_chunk(D) / kAttnWaves;   // positions per wave (16 per MFMA block)
-    constexpr int NB = WP / 16;                      // MFMA blocks per wave
+    constexpr int WP = 16 * NB;                      // positions per wave (NB MFMA blocks of 16)
+    constexpr int CH = WP * kAttnWaves;              // positions per workgroup
     constexpr int KS = D / 32;                       // MFMA k-steps per block
     constexpr int LPR = D / 8;                       // lanes per V row (16 bytes each)
     constexpr int RPI = 64 / LPR;                    // V rows per wave load
@@ -61,7 +65,7 @@ attn_chunk_kernel(AttnArgs a, float* __restrict__ ws) {
     const int ci = blockIdx.x, kvh = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int p0 = ci * attn_chunk(D);
+    const int p0 = ci * CH;
     const int pw = p0 + wave * WP;                   // first position of this wave
     const int last = (int)(a.L - 1);
 
@@ -253,7 +257,7 @@ attn_chunk_kernel(AttnArgs a, float* __restrict__ ws) {
 // over from other calls and are never used).
 template <int D, int G>
 __global__ void __launch_bounds__(D)
-attn_merge_kernel(AttnArgs a, const float* __restrict__ ws, int nchunks) {
+attn_merge_kernel(AttnArgs a, const float* __restrict__ ws, int nchunks, int chunk) {
     constexpr int REC = G * (D + 2);
     constexpr int MB = 32;
     const int g = blockIdx.x, kvh = blockIdx.y;
@@ -274,7 +278,7 @@ attn_merge_kernel(AttnArgs a, const float* __restrict__ ws, int nchunks) {
     load(0, nchunks);
     const bool valid = len >= 0 && (int64_t)len < a.L;
     const int n = valid ? len + 1 : 0;
-    const int nvalid = (n + attn_chunk(D) - 1) / attn_chunk(D);
+    const int nvalid = (n + chunk - 1) / chunk;
     float M = -INFINITY, lsum = 0.f, o = 0.f;
     for (int c0 = 0; c0 < nvalid; c0 += MB) {
         if (c0 > 0) load(c0, nvalid);
@@ -299,14 +303,18 @@ attn_merge_kernel(AttnArgs a, const float* __restrict__ ws, int nchunks) {
         (uint16_t)f32_to_bf16(nvalid > 0 ? o / lsum : 0.f);
 }
 
+// MFMA blocks of 16 positions per wave (a chunk is 64 NB positions)
+template <int D>
+constexpr int attn_nb() { return D > 128 ? 1 : 3; }
+
 struct AttnFns {
     void (*chunk)(AttnArgs, float*);
-    void (*merge)(AttnArgs, const float*, int);
+    void (*merge)(AttnArgs, const float*, int, int);
 };
 
 template <int D, int G>
 AttnFns attn_fns() {
-    return AttnFns{attn_chunk_kernel<D, G>, attn_merge_kernel<D, G>};
+    return AttnFns{attn_chunk_kernel<D, G, attn_nb<D>()>, attn_merge_kernel<D, G>};
 }
 
 template <int D>
@@ -323,6 +331,8 @@ AttnFns attn_for_group(int g) {
     default: return AttnFns{nullptr, nullptr};
     }
 }
+
+int attn_chunk(int head_dim) { return head_dim > 128 ? 64 * attn_nb<256>() : 64 * attn_nb<128>(); }
 
 }  // namespace
 
@@ -344,14 +354,14 @@ hipError_t launch_decode_attention(const AttnArgs& a, const Workspace& ws, hipSt
     default: break;
     }
     if (fn.chunk == nullptr) return hipErrorInvalidValue;
-    const int64_t ch = attn_chunk(a.head_dim);
-    const int nchunks = (int)((a.L + ch - 1) / ch);
+    const int chunk = attn_chunk(a.head_dim);
+    const int nchunks = (int)((a.L + chunk - 1) / chunk);
     hipLaunchKernelGGL(fn.chunk, dim3((unsigned)nchunks, (unsigned)a.nkv, (unsigned)a.B), dim3(kAttnThreads), 0, s,
                        a, ws.partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn.merge, dim3((unsigned)g, (unsigned)a.nkv, (unsigned)a.B), dim3((unsigned)a.head_dim), 0, s,
-                       a, static_cast<const float*>(ws.partials), nchunks);
+                       a, static_cast<const float*>(ws.partials), nchunks, chunk);
     return hipGetLastError();
 }
 

@@ -29,8 +29,6 @@ struct AttnArgs {
     float scale;          // 1 / sqrt(head_dim)
 };
 constexpr int64_t kAttnMaxLen = 32768;   // cache positions per sequence
-// cache positions per workgroup of the chunk kernel
-__host__ __device__ constexpr int attn_chunk(int head_dim) { return head_dim > 128 ? 64 : 128; }
 // floats of the per-chunk records (the chunk kernel writes, the merge reads)
 int64_t attention_workspace_floats(const AttnArgs& a);
 hipError_t launch_decode_attention(const AttnArgs& a, const Workspace& ws, hipStream_t s);

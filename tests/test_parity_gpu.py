@@ -198,6 +198,38 @@ def test_lm_head_fp32_logits_and_zero_padded_rows():
     assert np.all(f64(shards[1])[:, 500] == 0.0)       # the padded row of the last shard
 
 
+@pytest.mark.parametrize("V,t", [(1000, 2), (1001, 4), (7, 4)])
+def test_tied_embedding_and_lm_head_share_one_shard(V, t):
+    """Tied input embedding and LM head (one [V, H] table): the vocab split
+    gives both the same rows, so one shard buffer serves tp_vocab_embed and
+    tp_lm_head_shard. The embed and lm_head shard copies are bit-identical,
+    the summed lookups equal E[ids] and the concatenated logits equal h E^T."""
+    H, M = 64, 16
+    cfg = {"hidden": H, "num_q_heads": t, "num_kv_heads": 1, "head_dim": 8, "intermediate": 8 * t, "vocab": V}
+    E = I.normal_bf16((SEED, 40, V, t), (V, H), 0.02)
+    ids = I.uniform_ids((SEED, 41, V, t), M, V)
+    h = I.normal_bf16((SEED, 42, V, t), (M, H))
+    parts, logits = [], []
+    for r in range(t):
+        es = empty(lib.tp_shard_shape(cfg, t, "embed"))
+        lib.tp_shard_weights(cfg, t, r, "embed", dev(E), es)
+        ls = empty(lib.tp_shard_shape(cfg, t, "lm_head"))
+        lib.tp_shard_weights(cfg, t, r, "lm_head", dev(E), ls)
+        assert np.array_equal(bits(es), bits(ls)), r
+        z = empty((M, H))
+        lib.tp_vocab_embed(dev(ids), es, V, t, r, z)
+        parts.append(z)
+        lg = empty((M, es.shape[0]))
+        lib.tp_lm_head_shard(dev(h), es, lg)
+        logits.append(lg)
+    total = empty((M, H))
+    lib.tp_reduce_partials(parts, total)
+    assert np.array_equal(bits(total), oracle.bf16_bits(oracle.embedding_lookup(f64(E), ids.numpy())))
+    out = empty((M, V))
+    lib.tp_concat_logits(logits, V, out)
+    assert_close(f64(out), oracle.linear(f64(h), f64(E)), "tied lm_head")
+
+
 # ------------------------------------------------------------------ S4 swiglu
 
 @pytest.mark.parametrize("M,Is", [(16, 512), (3, 8), (64, 896), (2048, 1792)])
