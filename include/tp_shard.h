@@ -208,6 +208,40 @@ int tp_add_rmsnorm(const void* x_or_null, int64_t M, int64_t H, void* residual, 
 int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype, int64_t M, int64_t H,
                           void* residual, const void* gamma, float eps, void* out, void* stream);
 
+/* The decode layer's norm folded into its neighbours, so that the per-layer
+ * step is four launches, not six ([P1 3.2]: the norm is replicated on every
+ * rank; [P3 流水线并行]: the residual travels beside hidden_states).
+ *
+ * tp_row_linear_reduce_add: tp_row_linear_reduce's sum over ranks (the
+ * rank's partial x_shard W^T rounded to bf16, summed in fp32 from rank 0 in
+ * order, rounded once) added to the residual stream in place:
+ *   residual[m, n] = bf16(residual[m, n] + that sum)
+ * — the same bits as tp_row_linear_reduce into a buffer followed by
+ * tp_reduce_add_rmsnorm's residual update. `partials` as in
+ * tp_row_linear_reduce (host array of t device pointers, slot `rank`
+ * ignored); none may overlap residual ([M, N] bf16). One launch when
+ * M <= 64, t <= 16 and N % 4 == 0; otherwise two (the rank's partial is
+ * staged in the stream's 16 MiB workspace; then N % 8 == 0, N <= 32768
+ * and M N 2 bytes <= 16 MiB, TP_ERR_SHAPE otherwise).
+ *
+ * tp_rmsnorm_column_linear / tp_rmsnorm_column_linear_swiglu: the column
+ * linear (tp_column_linear, tp_column_linear_swiglu) of the normalised rows
+ *   x[m, k] = bf16(h[m, k] * r_m * gamma[k]),  r_m = 1 / sqrt(mean_k h[m, k]^2 + eps)
+ * without writing x. h: [M, K] bf16 (the residual stream, read only);
+ * gamma: [K] bf16; eps finite and >= 0 (TP_ERR_RANGE); K <= 32768. One
+ * launch when M <= 16 and a decode kernel holds whole rows of K in LDS
+ * (K <= 5120): the norm's sum of squares runs in another order than
+ * tp_add_rmsnorm's, so x may differ from its output by the rounding of r_m.
+ * Otherwise two: tp_add_rmsnorm's kernel writes x into the stream's
+ * 16 MiB workspace (M K 2 bytes must fit, TP_ERR_SHAPE otherwise), then the plain
+ * linear reads it. y / act must not overlap h or gamma (TP_ERR_SHAPE). */
+int tp_row_linear_reduce_add(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
+                             const void* const* partials, int t, int rank, void* residual, void* stream);
+int tp_rmsnorm_column_linear(const void* h, const void* gamma, float eps, int64_t M, int64_t K, const void* w_shard,
+                             int64_t N, const void* bias_or_null, void* y, void* stream);
+int tp_rmsnorm_column_linear_swiglu(const void* h, const void* gamma, float eps, int64_t M, int64_t K,
+                                    const void* w_gate_up, int64_t i_shard, void* act, void* stream);
+
 /* One decode step of the rank's grouped-query attention, with the KV-cache
  * append ([P2 前向执行的实际流程] Step 2: each rank computes attention for its
  * own heads with no exchange; [P2 KV Cache 在 TP 下怎样分布]: each rank holds

@@ -5,6 +5,7 @@
 // everything and maps it to a tp_status.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cmath>
 #include <cstring>
@@ -98,7 +99,9 @@ int g_force_ksteps = 0, g_force_nwn = 0, g_force_nwk = 0, g_force_xd = 0;
 
 // Launch one validated linear. a.N is the kernel's row space (for EPI_SWIGLU
 // on the decode kernel: 16-row blocks of 8 gate and 8 up rows).
-int launch_linear(const tpk::GemmArgs& a, hipStream_t s) {
+// ws_limit: floats of the stream workspace's front a split-K plan may use
+// (the rest may hold an operand the caller staged at the back).
+int launch_linear(const tpk::GemmArgs& a, hipStream_t s, int64_t ws_limit = kWsFloats) {
     const int64_t M = a.M, N = a.N, K = a.K;
     hipError_t e;
     if (M <= kSkinnyMaxM) {
@@ -114,7 +117,7 @@ int launch_linear(const tpk::GemmArgs& a, hipStream_t s) {
             f.splits = (int)((K + gk - 1) / gk);
             // a forced shape that does not fit this M (LDS) or the workspace
             // keeps the automatic plan
-            const bool fits = f.splits == 1 || (tpk::skinny_workspace_floats(f, M, N) <= kWsFloats &&
+            const bool fits = f.splits == 1 || (tpk::skinny_workspace_floats(f, M, N) <= ws_limit &&
                                                 f.ntiles <= kWsCounters && f.splits <= 65535);
             if (tpk::skinny_variant_exists(f) && tpk::skinny_plan_fits(f, M) && fits) p = f;
         }
@@ -122,7 +125,8 @@ int launch_linear(const tpk::GemmArgs& a, hipStream_t s) {
         if (p.splits > 1) {
             const int st = get_workspace(s, &ws);
             if (st != TP_OK) return st;
-            if (tpk::skinny_workspace_floats(p, M, N) > ws.partial_floats || p.ntiles > ws.num_counters)
+            if (tpk::skinny_workspace_floats(p, M, N) > std::min(ws.partial_floats, ws_limit) ||
+                p.ntiles > ws.num_counters)
                 return TP_ERR_SHAPE;
         }
         e = tpk::launch_skinny(a, p, ws, s);
@@ -508,6 +512,157 @@ int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype,
         if (partials == nullptr) return TP_ERR_NULL;
         if (t < 1) return TP_ERR_RANGE;
         return add_rmsnorm_call(partials, t, partial_dtype, M, H, residual, gamma, eps, out, stream);
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+namespace {
+
+// The back `bytes` of the stream workspace (whole 256-byte units) for an
+// operand a fused call's two-launch path stages; *front is what stays free
+// for the linear's own split-K partials.
+int workspace_back(hipStream_t s, int64_t bytes, void** out, int64_t* front) {
+    tpk::Workspace ws{nullptr, 0, nullptr, 0};
+    const int st = get_workspace(s, &ws);
+    if (st != TP_OK) return st;
+    const int64_t need = (bytes + 255) / 256 * 256;
+    if (need > ws.partial_floats * 4) return TP_ERR_SHAPE;
+    *out = reinterpret_cast<char*>(ws.partials) + (ws.partial_floats * 4 - need);
+    *front = ws.partial_floats - need / 4;
+    return TP_OK;
+}
+
+// x = RMSNorm(a.x) (a.gamma, a.eps) feeding the linear a describes. One
+// launch when the decode kernel can stage whole rows; otherwise the norm
+// writes the normalised rows to the workspace and the plain linear reads them.
+int run_norm_linear(tpk::GemmArgs a, hipStream_t s) {
+    if (a.M <= kSkinnyMaxM) {
+        const tpk::SkinnyPlan p = tpk::plan_skinny_norm(a.M, a.N, a.K);
+        if (p.splits == 1) {
+            const tpk::Workspace ws{nullptr, 0, nullptr, 0};
+            const hipError_t e = tpk::launch_skinny(a, p, ws, s);
+            return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+        }
+    }
+    void* xn = nullptr;
+    int64_t front = 0;
+    const int st = workspace_back(s, a.M * a.K * 2, &xn, &front);
+    if (st != TP_OK) return st;
+    tpk::PartialPtrs none;
+    std::memset(&none, 0, sizeof(none));
+    const hipError_t e = tpk::launch_add_rmsnorm(none, 0, TP_BF16, a.M, a.K, const_cast<void*>(a.x), a.gamma, a.eps,
+                                                 xn, s);
+    if (e != hipSuccess) return TP_ERR_HIP;
+    a.x = xn;
+    a.gamma = nullptr;
+    return launch_linear(a, s, front);
+}
+
+int check_norm_input(const void* h, int64_t K, const void* gamma, float eps, const void* y,
+                     int64_t M, int64_t n_bytes) {
+    if (gamma == nullptr) return TP_ERR_NULL;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return TP_ERR_RANGE;
+    if (K > kMaxNormWidth) return TP_ERR_SHAPE;
+    if (!aligned16(gamma)) return TP_ERR_ALIGNMENT;
+    if (overlap(y, n_bytes, h, M * K * 2) || overlap(y, n_bytes, gamma, K * 2))
+        return TP_ERR_SHAPE;
+    return TP_OK;
+}
+
+}  // namespace
+
+int tp_rmsnorm_column_linear(const void* h, const void* gamma, float eps, int64_t M, int64_t K, const void* w_shard,
+                             int64_t N, const void* bias_or_null, void* y, void* stream) {
+    try {
+        int st = check_linear(h, M, K, w_shard, N, y);
+        if (st != TP_OK) return st;
+        st = check_norm_input(h, K, gamma, eps, y, M, M * N * 2);
+        if (st != TP_OK) return st;
+        if (bias_or_null != nullptr && (reinterpret_cast<uintptr_t>(bias_or_null) & 1u)) return TP_ERR_ALIGNMENT;
+        if (M == 0) return TP_OK;
+        tpk::GemmArgs a{};
+        a.x = h; a.w = w_shard; a.bias = bias_or_null; a.y = y;
+        a.M = M; a.N = N; a.K = K;
+        a.out_dtype = TP_BF16;
+        a.epi = tpk::EPI_STORE;
+        a.gamma = gamma;
+        a.eps = eps;
+        return run_norm_linear(a, static_cast<hipStream_t>(stream));
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_rmsnorm_column_linear_swiglu(const void* h, const void* gamma, float eps, int64_t M, int64_t K,
+                                    const void* w_gate_up, int64_t i_shard, void* act, void* stream) {
+    try {
+        if (i_shard <= 0 || i_shard >= kMaxDim / 2) return TP_ERR_SHAPE;
+        int st = check_linear(h, M, K, w_gate_up, 2 * i_shard, act);
+        if (st != TP_OK) return st;
+        st = check_norm_input(h, K, gamma, eps, act, M, M * i_shard * 2);
+        if (st != TP_OK) return st;
+        if (M == 0) return TP_OK;
+        tpk::GemmArgs a{};
+        a.x = h; a.w = w_gate_up; a.y = act;
+        a.M = M; a.K = K;
+        a.out_dtype = TP_BF16;
+        a.epi = tpk::EPI_SWIGLU;
+        a.i_half = i_shard;
+        a.N = M <= kSkinnyMaxM ? 16 * ((i_shard + 7) / 8) : 2 * i_shard;
+        a.gamma = gamma;
+        a.eps = eps;
+        return run_norm_linear(a, static_cast<hipStream_t>(stream));
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_row_linear_reduce_add(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
+                             const void* const* partials, int t, int rank, void* residual, void* stream) {
+    try {
+        const int st = check_linear(x_shard, M, K_shard, w_shard, N, residual);
+        if (st != TP_OK) return st;
+        if (partials == nullptr) return TP_ERR_NULL;
+        if (t < 1 || t > TP_MAX_SHARDS || rank < 0 || rank >= t) return TP_ERR_RANGE;
+        const int64_t bytes = M * N * 2;
+        for (int i = 0; i < t; ++i) {
+            if (i == rank) continue;
+            if (partials[i] == nullptr) return TP_ERR_NULL;
+            if (!aligned16(partials[i])) return TP_ERR_ALIGNMENT;
+            if (overlap(partials[i], bytes, residual, bytes)) return TP_ERR_SHAPE;
+        }
+        if (overlap(x_shard, M * K_shard * 2, residual, bytes)) return TP_ERR_SHAPE;
+        if (M == 0) return TP_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        tpk::GemmArgs a{};
+        a.x = x_shard; a.w = w_shard; a.y = residual;
+        a.M = M; a.N = N; a.K = K_shard;
+        a.out_dtype = TP_BF16;
+        if (M <= kSkinnyMaxM && t <= tpk::kMaxFusedPeers && N % 4 == 0) {
+            a.epi = tpk::EPI_REDUCE_ADD;
+            a.t = t;
+            a.rank = rank;
+            for (int i = 0; i < t; ++i) a.peers[i] = i == rank ? nullptr : partials[i];
+            return launch_linear(a, s);
+        }
+        // Two launches with the same arithmetic: the rank's bf16 partial goes
+        // to the back of the workspace, then the sum over ranks in order is
+        // added to the residual (the add + norm kernel without its norm).
+        if (N % 8 != 0 || N > kMaxNormWidth) return TP_ERR_SHAPE;
+        void* own = nullptr;
+        int64_t front = 0;
+        const int st2 = workspace_back(s, bytes, &own, &front);
+        if (st2 != TP_OK) return st2;
+        a.y = own;
+        a.epi = tpk::EPI_STORE;
+        const int st3 = launch_linear(a, s, front);
+        if (st3 != TP_OK) return st3;
+        tpk::PartialPtrs ptrs;
+        std::memset(&ptrs, 0, sizeof(ptrs));
+        for (int i = 0; i < t; ++i) ptrs.p[i] = i == rank ? own : partials[i];
+        const hipError_t e = tpk::launch_add_rmsnorm(ptrs, t, TP_BF16, M, N, residual, nullptr, 0.0f, nullptr, s);
+        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
     } catch (...) {
         return TP_ERR_HIP;
     }

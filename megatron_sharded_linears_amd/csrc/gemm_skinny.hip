@@ -110,8 +110,10 @@ __device__ __forceinline__ int64_t weight_row(const GemmArgs& a, int64_t v) {
 // load per rank. The guards are uniform and one-sided (a branch that merged
 // two values would make each load wait for the one before); lanes past the
 // edge read the start of the peer's buffer instead and discard it.
-struct PeerVals { uint2 v[kMaxFusedPeers]; };
+// EPI_REDUCE_ADD also holds the lane's 4 residual values (read from y).
+struct PeerVals { uint2 v[kMaxFusedPeers]; uint2 res; };
 
+template <int EPI>
 __device__ __forceinline__ void load_peers(const GemmArgs& a, int64_t m, int64_t n, PeerVals& p) {
     const bool ok = m < a.M && n < a.N;
     const int64_t base = ok ? m * a.N + n : 0;
@@ -120,10 +122,14 @@ __device__ __forceinline__ void load_peers(const GemmArgs& a, int64_t m, int64_t
         if (r < a.t && r != a.rank)
             p.v[r] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.peers[r]) + base);
     }
+    if constexpr (EPI == EPI_REDUCE_ADD)
+        p.res = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.y) + base);
 }
 
 // EPI_REDUCE: out[m, n..n+3] = bf16(sum over ranks in order from rank 0),
 // the own partial rounded as a bf16 partial buffer holds it.
+// EPI_REDUCE_ADD: y[m, n..n+3] = bf16(y + that bf16 sum) (the residual stream).
+template <int EPI>
 __device__ __forceinline__ void reduce_out4(const GemmArgs& a, int64_t m, int64_t n, const float* v,
                                             const PeerVals& p) {
     // Unrolled with constant indices (the values stay in registers); the
@@ -148,6 +154,12 @@ __device__ __forceinline__ void reduce_out4(const GemmArgs& a, int64_t m, int64_
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = r == 0 ? q[i] : o[i] + q[i];
         }
+    }
+    if constexpr (EPI == EPI_REDUCE_ADD) {
+        const float res[4] = {bf16_to_f32(p.res.x & 0xFFFFu), bf16_to_f32(p.res.x >> 16),
+                              bf16_to_f32(p.res.y & 0xFFFFu), bf16_to_f32(p.res.y >> 16)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = res[i] + round_bf16(o[i]);
     }
     uint16_t* y = reinterpret_cast<uint16_t*>(a.y) + m * a.N + n;
     *reinterpret_cast<uint2*>(y) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
@@ -177,15 +189,18 @@ __device__ __forceinline__ void finish4(const GemmArgs& a, int64_t m, int64_t n,
         return;
     }
     if (m >= a.M || n >= a.N) return;
-    if constexpr (EPI == EPI_REDUCE) reduce_out4(a, m, n, v, peers);
+    if constexpr (EPI == EPI_REDUCE || EPI == EPI_REDUCE_ADD) reduce_out4<EPI>(a, m, n, v, peers);
     else store_out4(a, m, n, v);
 }
 
-template <int MT, int KSTEPS, int NWN, int NWK, int XD, int EPI>
+// NORM = 1 (XD = 0, K not split, so a workgroup stages whole rows of X):
+// X's rows are RMS-normalised in LDS before the MFMAs (a.gamma, a.eps).
+template <int MT, int KSTEPS, int NWN, int NWK, int XD, int EPI, int NORM = 0>
 __global__ void __launch_bounds__(64 * NWN * NWK)
 skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restrict__ ws,
               unsigned* __restrict__ counters) {
     using C = SkinnyCfg<MT, KSTEPS, NWN, NWK, XD>;
+    static_assert(!NORM || !XD, "the norm needs X staged in LDS");
     extern __shared__ __align__(16) unsigned char smem[];
     bf16_t* xs = reinterpret_cast<bf16_t*>(smem);                       // [xrows][kXStride]
     float* red = reinterpret_cast<float*>(smem + (XD ? 0 : (size_t)xrows * C::kXStride * 2));
@@ -219,7 +234,8 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     // ranks' values for the first tile right after its weights (step 2), so
     // they arrive while the weights stream; later tiles of a persistent loop
     // load theirs just before the sum.
-    constexpr bool kPrefetchPeers = EPI == EPI_REDUCE && C::kOwn == 1;
+    constexpr bool kReduce = EPI == EPI_REDUCE || EPI == EPI_REDUCE_ADD;
+    constexpr bool kPrefetchPeers = kReduce && C::kOwn == 1;
     PeerVals peers;
     const int64_t m_own0 = 16 * wk + (lane & 15);          // token of the first owned tile
     bool first_tile = true;
@@ -243,6 +259,19 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
             const int64_t k = k_group + kc * 8;
             const bool ok = c < x_chunks && k < K;
             xr[j] = *reinterpret_cast<const uint4*>(X + (ok ? (int64_t)m * K + k : 0));
+        }
+    }
+    // NORM: gamma's K values, 16 bytes per thread and chunk, bound for LDS
+    constexpr int kGPerThread = NORM ? (C::kGroupK / 8 + C::kThreads - 1) / C::kThreads : 1;
+    __shared__ __align__(16) bf16_t s_gamma[NORM ? C::kGroupK : 8];
+    __shared__ float s_rinv[NORM ? 16 * MT : 1];
+    uint4 gr[kGPerThread];
+    if constexpr (NORM) {
+        const bf16_t* __restrict__ G = reinterpret_cast<const bf16_t*>(a.gamma);
+#pragma unroll
+        for (int j = 0; j < kGPerThread; ++j) {
+            const int kc = tid + j * C::kThreads;
+            gr[j] = *reinterpret_cast<const uint4*>(G + (kc * 8 < K ? kc * 8 : 0));
         }
     }
 
@@ -287,7 +316,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
         load_w(tile, wr);
     }
     if constexpr (kPrefetchPeers) {
-        if (splits == 1 && wk < MT) load_peers(a, m_own0, tile * C::kRows + wn * 16 + 4 * (lane >> 4), peers);
+        if (splits == 1 && wk < MT) load_peers<EPI>(a, m_own0, tile * C::kRows + wn * 16 + 4 * (lane >> 4), peers);
     }
 
     // 3. X chunk -> LDS (zeros past K).
@@ -300,6 +329,49 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
                 const int kc = c % (C::kGroupK / 8);
                 const bool ok = k_group + kc * 8 < K;
                 *reinterpret_cast<uint4*>(xs + m * C::kXStride + kc * 8) = ok ? xr[j] : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+        if constexpr (NORM) {
+#pragma unroll
+            for (int j = 0; j < kGPerThread; ++j) {
+                const int kc = tid + j * C::kThreads;
+                if (kc < C::kGroupK / 8) *reinterpret_cast<uint4*>(s_gamma + kc * 8) = gr[j];
+            }
+        }
+        lds_barrier();
+    }
+
+    // 3b. NORM: x = bf16(x / sqrt(sum_k x^2 / K + eps) * gamma), per staged row
+    //     (the zeros past K add nothing to the sum). Wave w sums rows w, w +
+    //     waves, ... in a fixed order; the rows are then scaled in place.
+    if constexpr (NORM) {
+        constexpr int kWaves = NWN * NWK;
+        for (int m = wave; m < xrows; m += kWaves) {
+            float ss = 0.f;
+            for (int c8 = lane; c8 < C::kGroupK / 8; c8 += 64) {
+                float f[8];
+                unpack_bf16x8(*reinterpret_cast<const uint4*>(xs + m * C::kXStride + c8 * 8), f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+            if (lane == 0) s_rinv[m] = 1.0f / sqrtf(ss / (float)K + a.eps);
+        }
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < kXPerThread; ++j) {
+            const int c = tid + j * C::kThreads;
+            const int m = c / (C::kGroupK / 8);
+            const int kc = c % (C::kGroupK / 8);
+            if (c < x_chunks && kc * 8 < K) {
+                float h[8], g[8], y[8];
+                unpack_bf16x8(xr[j], h);
+                unpack_bf16x8(*reinterpret_cast<const uint4*>(s_gamma + kc * 8), g);
+                const float r = s_rinv[m];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = h[e] * r * g[e];
+                *reinterpret_cast<uint4*>(xs + m * C::kXStride + kc * 8) = pack_bf16x8(y);
             }
         }
         lds_barrier();
@@ -379,8 +451,8 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
             const int mt = wk + NWK * o;
             if (mt < MT) {                       // wave-uniform: every lane calls finish4
                 const int64_t m = 16 * mt + (lane & 15);
-                if constexpr (EPI == EPI_REDUCE) {
-                    if (!kPrefetchPeers || !first_tile) load_peers(a, m, n_out, peers);
+                if constexpr (kReduce) {
+                    if (!kPrefetchPeers || !first_tile) load_peers<EPI>(a, m, n_out, peers);
                 }
                 finish4<EPI>(a, m, n_out, fin[o], lane, peers);
             }
@@ -441,7 +513,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
         const int mt = wk + NWK * o;
         if (mt < MT) {                           // wave-uniform: every lane calls finish4
             const int64_t m = 16 * mt + (lane & 15);
-            if constexpr (EPI == EPI_REDUCE) load_peers(a, m, n_out, peers);
+            if constexpr (kReduce) load_peers<EPI>(a, m, n_out, peers);
             float v[4] = {0.f, 0.f, 0.f, 0.f};
             if (m < M && n_out < N) {
                 for (int sp0 = 0; sp0 < splits; sp0 += 8) {
@@ -482,9 +554,20 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
 typedef void (*SkinnyFn)(GemmArgs, int, int64_t, int, float*, unsigned*);
 typedef int (*SkinnyLdsFn)(int);
 
+// The norm-prologue kernel of a shape, for the column linears (EPI_STORE,
+// EPI_SWIGLU), built only for one 16-token tile, X in LDS, one row group.
+template <int MT, int KS, int NN, int NK, int XD, int EPI>
+constexpr SkinnyFn skinny_norm_fn() {
+    if constexpr (MT == 1 && XD == 0 && NN == 1 && EPI <= EPI_SWIGLU)
+        return skinny_kernel<MT, KS, NN, NK, XD, EPI, 1>;
+    else
+        return nullptr;
+}
+
 struct SkinnyEntry {
     int mt, ksteps, nwn, nwk, xd;
-    SkinnyFn fn[3];   // by epilogue: EPI_STORE, EPI_SWIGLU, EPI_REDUCE
+    SkinnyFn fn[4];   // by epilogue: EPI_STORE, EPI_SWIGLU, EPI_REDUCE, EPI_REDUCE_ADD
+    SkinnyFn fn_norm[2];   // with the norm prologue: EPI_STORE, EPI_SWIGLU (or nullptr)
     int threads;
     SkinnyLdsFn lds;
     int group_k;
@@ -493,7 +576,8 @@ struct SkinnyEntry {
 #define TP_SK(MT, KS, NN, NK, XD)                                                                  \
     {MT, KS, NN, NK, XD,                                                                           \
      {skinny_kernel<MT, KS, NN, NK, XD, EPI_STORE>, skinny_kernel<MT, KS, NN, NK, XD, EPI_SWIGLU>,    \
-      skinny_kernel<MT, KS, NN, NK, XD, EPI_REDUCE>},                                               \
+      skinny_kernel<MT, KS, NN, NK, XD, EPI_REDUCE>, skinny_kernel<MT, KS, NN, NK, XD, EPI_REDUCE_ADD>}, \
+     {skinny_norm_fn<MT, KS, NN, NK, XD, EPI_STORE>(), skinny_norm_fn<MT, KS, NN, NK, XD, EPI_SWIGLU>()}, \
      SkinnyCfg<MT, KS, NN, NK, XD>::kThreads,                                                       \
      SkinnyCfg<MT, KS, NN, NK, XD>::lds_bytes, SkinnyCfg<MT, KS, NN, NK, XD>::kGroupK}
 // M <= 16: every variant. M in (16, 64]: the ones that fit in registers.
@@ -517,8 +601,8 @@ const SkinnyEntry kSkinnyTable[] = {TP_SK_MT1, TP_SK_MTN(2), TP_SK_MTN(4)};
 
 constexpr int kMaxLds = 160 * 1024 - 1024;   // dynamic LDS; the rest is the kernel's static LDS
 constexpr int kNumSkinny = sizeof(kSkinnyTable) / sizeof(kSkinnyTable[0]);
-int g_lds_attr[kNumSkinny][3] = {};         // dynamic LDS limit set so far per kernel
-int g_occupancy[kNumSkinny][3][2] = {};     // cached (lds bytes, workgroups per CU)
+int g_lds_attr[kNumSkinny][6] = {};         // dynamic LDS limit set so far per kernel
+int g_occupancy[kNumSkinny][6][2] = {};     // cached (lds bytes, workgroups per CU)
 int g_num_cus[16] = {};
 
 int find_skinny(const SkinnyPlan& p) {
@@ -547,6 +631,36 @@ bool skinny_plan_fits(const SkinnyPlan& p, int64_t M) {
     if (idx < 0) return false;
     const SkinnyEntry& e = kSkinnyTable[idx];
     return e.lds(xrows_for(e, M)) <= kMaxLds;
+}
+
+// With the norm prologue: one 16-token tile whose whole rows (K <= the
+// variant's K coverage) sit in LDS next to gamma's K values.
+bool skinny_norm_plan_fits(const SkinnyPlan& p, int64_t M, int64_t K) {
+    const int idx = find_skinny(p);
+    if (idx < 0) return false;
+    const SkinnyEntry& e = kSkinnyTable[idx];
+    if (e.fn_norm[0] == nullptr || M > 16 || K > e.group_k) return false;
+    // dynamic LDS (staged rows, reduction buffer) + static (gamma, row scales, flags)
+    return e.lds(xrows_for(e, M)) + 2 * e.group_k + 512 <= 160 * 1024;
+}
+
+// Decode shape for a linear with the norm prologue: the variant covering K
+// in one workgroup with the least waste (as plan_skinny does for M <= 16
+// when K is not split), or splits = 0 when none fits (the caller then
+// normalises separately).
+SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K) {
+    struct Rule { int64_t kmax; int ks, nwn, nwk; };
+    static const Rule rules[] = {{512, 4, 1, 4}, {1024, 8, 1, 4}, {2048, 8, 1, 8}, {4096, 16, 1, 8}, {5120, 20, 1, 8}};
+    for (const Rule& r : rules) {
+        if (K > r.kmax) continue;
+        SkinnyPlan p{1, r.ks, r.nwn, r.nwk, 0, 1, 1};
+        const int idx = find_skinny(p);
+        if (idx < 0) continue;
+        p = make_plan(kSkinnyTable[idx], N, K);
+        if (p.splits == 1 && skinny_norm_plan_fits(p, M, K)) return p;
+    }
+    SkinnyPlan none{1, 0, 0, 0, 0, 0, 0};
+    return none;
 }
 
 // Pick the decode kernel shape for one linear, from MI355X sweeps of every
@@ -627,16 +741,21 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
     if (idx < 0) return hipErrorInvalidValue;
     const SkinnyEntry* e = &kSkinnyTable[idx];
     const int epi = a.epi;
-    if (epi < 0 || epi > 2) return hipErrorInvalidValue;
-    const SkinnyFn fn = e->fn[epi];
+    if (epi < 0 || epi > 3) return hipErrorInvalidValue;
+    const bool norm = a.gamma != nullptr;
+    if (norm && (epi > EPI_SWIGLU || p.splits != 1 || !skinny_norm_plan_fits(p, a.M, a.K)))
+        return hipErrorInvalidValue;
+    const SkinnyFn fn = norm ? e->fn_norm[epi] : e->fn[epi];
+    if (fn == nullptr) return hipErrorInvalidValue;
+    const int slot = norm ? 4 + epi : epi;      // kernel state below is per function
     const int xrows = xrows_for(*e, a.M);
     const int lds = e->lds(xrows);
     if (lds > kMaxLds) return hipErrorInvalidValue;
-    if (lds > 65536 && lds > g_lds_attr[idx][epi]) {
+    if (lds > 65536 && lds > g_lds_attr[idx][slot]) {
         const hipError_t ae = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                                   hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (ae != hipSuccess) return ae;
-        g_lds_attr[idx][epi] = lds;
+        g_lds_attr[idx][slot] = lds;
     }
     int64_t grid_x = p.ntiles;
     if (p.splits == 1 && !p.xd) {
@@ -650,7 +769,7 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
             he = hipDeviceGetAttribute(&g_num_cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
             if (he != hipSuccess) return he;
         }
-        int* occ = g_occupancy[idx][epi];
+        int* occ = g_occupancy[idx][slot];
         if (occ[0] != lds || occ[1] == 0) {
             int per_cu = 0;
             he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn),

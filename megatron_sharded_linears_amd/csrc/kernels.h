@@ -44,6 +44,7 @@ enum Epilogue : int {
     EPI_STORE = 0,    // y = acc (+ bias), out_dtype
     EPI_SWIGLU = 1,   // weight rows [gate (i_half); up (i_half)]; y[m, j] = silu(bf16(g)) * bf16(u), bf16
     EPI_REDUCE = 2,   // y = bf16(sum over t partials in order), own = bf16(acc) at position `rank`
+    EPI_REDUCE_ADD = 3,   // as EPI_REDUCE, then y = bf16(y + that sum): y is the residual, in place
 };
 
 constexpr int kMaxFusedPeers = 16;   // t limit of the fused reduce epilogue
@@ -63,7 +64,11 @@ struct GemmArgs {
     int out_dtype;
     int epi;
     int64_t i_half;     // EPI_SWIGLU
-    int t, rank;        // EPI_REDUCE
+    int t, rank;        // EPI_REDUCE, EPI_REDUCE_ADD
+    // RMSNorm of X's rows before the product (decode kernel, X staged in LDS,
+    // K not split): x = bf16(x / sqrt(mean(x^2) + eps) * gamma). nullptr: none.
+    const void* gamma;
+    float eps;
     const void* peers[kMaxFusedPeers];
 };
 
@@ -95,6 +100,10 @@ constexpr int64_t kSkinnyWsCounters = 65536;
 SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K);
 bool skinny_variant_exists(const SkinnyPlan& p);
 bool skinny_plan_fits(const SkinnyPlan& p, int64_t M);   // LDS need for M tokens within limits
+// The norm prologue's plan (splits == 0: no variant stages whole rows of K
+// for M tokens; normalise separately) and its fit test.
+SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K);
+bool skinny_norm_plan_fits(const SkinnyPlan& p, int64_t M, int64_t K);
 int64_t skinny_workspace_floats(const SkinnyPlan& p, int64_t M, int64_t N);
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace& ws, hipStream_t s);
 

@@ -10,7 +10,8 @@ namespace tpk {
 
 // residual[m] = bf16(residual[m] + bf16(sum of the t partials' row m)) (t = 0:
 // unchanged), out[m] = bf16(residual[m] * rsqrt-scale * gamma); one workgroup
-// per row, M <= 2^31 - 1, H % 8 == 0, H <= 32768.
+// per row, M <= 2^31 - 1, H % 8 == 0, H <= 32768. out == nullptr: the
+// residual update only (gamma unused).
 hipError_t launch_add_rmsnorm(const PartialPtrs& ptrs, int t, int in_dtype, int64_t M, int64_t H,
                               void* residual, const void* gamma, float eps, void* out, hipStream_t s);
 

@@ -266,6 +266,7 @@ add_rmsnorm_kernel(PartialPtrs ptrs, int t_rt, uint16_t* __restrict__ residual, 
             for (int e = 0; e < 8; ++e) ss += h[j][e] * h[j][e];
         }
     }
+    if (out == nullptr) return;      // the sum and the residual add only (uniform)
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
     __shared__ float wave_ss[kNormThreads / 64];
@@ -435,7 +436,8 @@ hipError_t launch_add_rmsnorm(const PartialPtrs& ptrs, int t, int in_dtype, int6
                               void* residual, const void* gamma, float eps, void* out, hipStream_t s) {
     if (H / 8 > 8 * kNormThreads) return hipErrorInvalidValue;   // H > 32768: rejected by the ABI
     uint16_t* res = reinterpret_cast<uint16_t*>(residual);
-    const uint16_t* g = reinterpret_cast<const uint16_t*>(gamma);
+    // out == nullptr: no norm; gamma's loads then read the residual instead
+    const uint16_t* g = reinterpret_cast<const uint16_t*>(out != nullptr ? gamma : residual);
     uint16_t* o = reinterpret_cast<uint16_t*>(out);
     return in_dtype == TP_F32 ? add_rmsnorm_t<1>(ptrs, t, M, H, res, g, eps, o, s)
                               : add_rmsnorm_t<0>(ptrs, t, M, H, res, g, eps, o, s);

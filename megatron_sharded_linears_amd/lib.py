@@ -73,6 +73,9 @@ _PROTOS = {
     "tp_swiglu": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "tp_column_linear_swiglu": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
     "tp_row_linear_reduce": (_int, [_vp, _i64, _i64, _vp, _i64, _ptr_array, _int, _int, _vp, _vp]),
+    "tp_row_linear_reduce_add": (_int, [_vp, _i64, _i64, _vp, _i64, _ptr_array, _int, _int, _vp, _vp]),
+    "tp_rmsnorm_column_linear": (_int, [_vp, _vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "tp_rmsnorm_column_linear_swiglu": (_int, [_vp, _vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp]),
     "tp_row_linear_partial": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp]),
     "tp_reduce_partials": (_int, [_ptr_array, _int, _i64, _int, _vp, _int, _vp]),
     "tp_vocab_embed": (_int, [_vp, _i64, _vp, _i64, _int, _int, _i64, _vp, _vp]),
@@ -269,6 +272,65 @@ def tp_row_linear_reduce(x_shard, w_shard, partials, rank, out, stream=None):
                                      _dev(out, "out", torch.bfloat16, 2), _stream(stream)),
            "tp_row_linear_reduce")
     return out
+
+
+def tp_row_linear_reduce_add(x_shard, w_shard, partials, rank, residual, stream=None):
+    """residual <- bf16(residual + bf16(sum over ranks in order)), the rank's
+    own partial being x_shard W^T; `partials` as in tp_row_linear_reduce."""
+    M, K, N = _linear_shapes(x_shard, w_shard, residual, "tp_row_linear_reduce_add")
+    t = len(partials)
+    if t < 1 or t > TP_MAX_SHARDS:
+        raise ValueError("need 1..64 partials")
+    ptrs = []
+    for i, p in enumerate(partials):
+        if i == rank:
+            ptrs.append(0)
+            continue
+        _dev(p, f"partials[{i}]", torch.bfloat16, 2)
+        if tuple(p.shape) != (M, N):
+            raise ValueError(f"partials[{i}] must be [M, N]")
+        ptrs.append(p.data_ptr())
+    arr = (ctypes.c_void_p * t)(*ptrs)
+    _check(_lib.tp_row_linear_reduce_add(_dev(x_shard, "x_shard", torch.bfloat16, 2), M, K,
+                                         _dev(w_shard, "w_shard", torch.bfloat16, 2), N,
+                                         ctypes.cast(arr, _ptr_array), t, rank,
+                                         _dev(residual, "residual", torch.bfloat16, 2), _stream(stream)),
+           "tp_row_linear_reduce_add")
+    return residual
+
+
+def tp_rmsnorm_column_linear(h, gamma, eps, w_shard, y, bias=None, stream=None):
+    """y = RMSNorm(h) gamma W^T (+ bias), the normalised rows not written."""
+    M, K, N = _linear_shapes(h, w_shard, y, "tp_rmsnorm_column_linear")
+    _dev(gamma, "gamma", torch.bfloat16, 1)
+    if gamma.shape[0] != K:
+        raise ValueError("gamma length != K")
+    b = None
+    if bias is not None:
+        b = _dev(bias, "bias", torch.bfloat16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias length != N")
+    _check(_lib.tp_rmsnorm_column_linear(_dev(h, "h", torch.bfloat16, 2), gamma.data_ptr(), float(eps), M, K,
+                                         _dev(w_shard, "w_shard", torch.bfloat16, 2), N, b,
+                                         _dev(y, "y", torch.bfloat16, 2), _stream(stream)),
+           "tp_rmsnorm_column_linear")
+    return y
+
+
+def tp_rmsnorm_column_linear_swiglu(h, gamma, eps, w_gate_up, act, stream=None):
+    """act = SwiGLU of RMSNorm(h) gamma W_gate_up^T."""
+    M, K = h.shape
+    two_i, K2 = w_gate_up.shape
+    if K != K2 or two_i % 2 or tuple(act.shape) != (M, two_i // 2):
+        raise ValueError("tp_rmsnorm_column_linear_swiglu: need h [M, K], w_gate_up [2 I, K], act [M, I]")
+    _dev(gamma, "gamma", torch.bfloat16, 1)
+    if gamma.shape[0] != K:
+        raise ValueError("gamma length != K")
+    _check(_lib.tp_rmsnorm_column_linear_swiglu(_dev(h, "h", torch.bfloat16, 2), gamma.data_ptr(), float(eps), M, K,
+                                                _dev(w_gate_up, "w_gate_up", torch.bfloat16, 2), two_i // 2,
+                                                _dev(act, "act", torch.bfloat16, 2), _stream(stream)),
+           "tp_rmsnorm_column_linear_swiglu")
+    return act
 
 
 def tp_row_linear_partial(x_shard, w_shard, partial, stream=None):
