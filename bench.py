@@ -259,18 +259,62 @@ def build_norm_ops(R, lib, eps=1e-5):
     return ops
 
 
-def build_layer_ops(R, lib, eps=1e-5):
-    """The decode step of whole layers minus the rotary embedding: the norm
-    step (build_norm_ops) with o_proj reading the rank's attention over its
-    KV caches (tp_decode_attention, which also appends the new token)
-    instead of a synthetic context."""
+def fold_norm_weights(R, lib):
+    """Load-time copies of the weights that follow a norm with its gamma
+    folded in (tp_fold_norm_weight): qkv (input norm), gate_up (post-attention
+    norm), the LM head (final norm)."""
+    if R.layers and "qkv_f" in R.layers[0]:
+        return
+    for L in R.layers:
+        L["qkv_f"] = lib.tp_fold_norm_weight(L["qkv"], L["g_in"], torch_empty_like(L["qkv"]))
+        L["gate_up_f"] = lib.tp_fold_norm_weight(L["gate_up"], L["g_post"], torch_empty_like(L["gate_up"]))
+    if R.vocab:
+        R.lm_f = lib.tp_fold_norm_weight(R.lm, R.g_final, torch_empty_like(R.lm))
+
+
+def torch_empty_like(t):
+    import torch
+    return torch.empty_like(t)
+
+
+def build_fused_norm_ops(R, lib, eps=1e-5):
+    """The norm step (build_norm_ops, same arithmetic) in four launches per
+    layer: each norm runs inside the next column linear's staging of X
+    (tp_rmsnorm_column_linear, _swiglu) and each sum over ranks adds into the
+    residual as the row-parallel linear's epilogue (tp_row_linear_reduce_add);
+    the final norm feeds the LM head the same way."""
+    w = R.w
     ops = []
-    for name, fn, args in build_norm_ops(R, lib, eps):
+    res = R.x
+    if R.vocab:
+        ops.append(("embed", lib.tp_vocab_embed, (R.ids, R.embed, w.vocab, w.t, 0, R.ze)))
+        ops.append(("embed_reduce", lib.tp_reduce_partials, ([R.ze] + R.peers_e, R.h)))
+        res = R.h
+    fold_norm_weights(R, lib)
+    for L in R.layers:
+        ops.append(("qkv", lib.tp_rmsnorm_column_linear, (res, eps, L["qkv_f"], R.qkv)))
+        ops.append(("o", lib.tp_row_linear_reduce_add, (L["ctx"], L["o"], [None] + L["peers_o"], 0, res)))
+        ops.append(("gate_up_swiglu", lib.tp_rmsnorm_column_linear_swiglu, (res, eps, L["gate_up_f"], R.act)))
+        ops.append(("down", lib.tp_row_linear_reduce_add, (R.act, L["down"], [None] + L["peers_d"], 0, res)))
+    if R.vocab:
+        hs = res[res.shape[0] - R.hs_rows:]
+        ops.append(("lm_head", lib.tp_rmsnorm_column_linear, (hs, eps, R.lm_f, R.logits)))
+        ops.append(("concat", lib.tp_concat_logits, ([R.logits] + R.peer_logits, w.vocab, R.full_logits)))
+    return ops
+
+
+def build_layer_ops(R, lib, fused_norm, eps=1e-5):
+    """The decode step of whole layers minus the rotary embedding: the norm
+    step (build_fused_norm_ops or build_norm_ops) with o_proj reading the
+    rank's attention over its KV caches (tp_decode_attention, which also
+    appends the new token) instead of a synthetic context."""
+    ops = []
+    for name, fn, args in (build_fused_norm_ops if fused_norm else build_norm_ops)(R, lib, eps):
         if name == "o":
             L = next(Ld for Ld in R.layers if Ld["o"] is args[1])
             ops.append(("attention", lib.tp_decode_attention,
                         (R.qkv, L["k_cache"], L["v_cache"], R.kv_lens, R.nq_r, R.ctx_attn)))
-            ops.append(("o", fn, (R.ctx_attn, args[1], args[2])))
+            ops.append(("o", fn, (R.ctx_attn,) + tuple(args[1:])))
         else:
             ops.append((name, fn, args))
     return ops
@@ -615,8 +659,12 @@ def main():
     # and with the residual stream and the RMSNorms of a real layer
     norm_ops = build_norm_ops(R, lib)
     ms_norm, _ = time_step(torch, norm_ops, args.steps, args.warmup)
-    # and (decode) whole layers: norms and the rank's attention over its KV caches
-    layer_ops = build_layer_ops(R, lib) if R.attn else None
+    # decode: the same step with the norms folded into the linears
+    ms_norm_fused = time_step(torch, build_fused_norm_ops(R, lib), args.steps, args.warmup)[0] if R.attn else None
+    # and (decode) whole layers: norms and the rank's attention over its KV
+    # caches, on whichever norm step measured faster
+    fused_norm = ms_norm_fused is not None and ms_norm_fused < ms_norm
+    layer_ops = build_layer_ops(R, lib, fused_norm) if R.attn else None
     ms_layer = time_step(torch, layer_ops, args.steps, args.warmup)[0] if layer_ops else None
 
     # --- per kernel: each op's launches of one step, captured and replayed K times
@@ -708,9 +756,16 @@ def main():
                                 "(tp_reduce_add_rmsnorm), gate_up + SwiGLU, down partial, sum + add + norm",
                        "ms_per_step": round(ms_norm, 4), "value": round(flops_step / (ms_norm * 1e-3) / 1e12, 3),
                        "reduce_norm_us_per_call": round(us_norm, 3),
-                       "reduce_norm_GBps": round(work["reduce_norm"][2] / (us_norm * 1e-6) / 1e9, 1)},
+                       "reduce_norm_GBps": round(work["reduce_norm"][2] / (us_norm * 1e-6) / 1e9, 1),
+                       "fused": None if ms_norm_fused is None else {
+                           "calls": "per layer tp_rmsnorm_column_linear (qkv), tp_row_linear_reduce_add (o), "
+                                    "tp_rmsnorm_column_linear_swiglu (gate_up), tp_row_linear_reduce_add (down); "
+                                    "the final norm inside the LM head's linear",
+                           "ms_per_step": round(ms_norm_fused, 4),
+                           "value": round(flops_step / (ms_norm_fused * 1e-3) / 1e12, 3)}},
         "full_layer": None if not layer_ops else {
-            "calls": "with_norms plus tp_decode_attention (KV append + attention) feeding o_proj; no rotary embedding",
+            "calls": ("with_norms' fused calls" if fused_norm else "with_norms' calls") +
+                     " plus tp_decode_attention (KV append + attention) feeding o_proj; no rotary embedding",
             "ms_per_step": round(ms_layer, 4), "value": round(flops_step / (ms_layer * 1e-3) / 1e12, 3),
             "attention": attn},
         "per_op": per_op,

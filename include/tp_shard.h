@@ -224,23 +224,31 @@ int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype,
  * staged in the stream's 16 MiB workspace; then N % 8 == 0, N <= 32768
  * and M N 2 bytes <= 16 MiB, TP_ERR_SHAPE otherwise).
  *
+ * tp_fold_norm_weight (load time, like tp_shard_weights): the norm's gamma
+ * folded into the next linear's weight, w_folded[n, k] = bf16(w[n, k] *
+ * gamma[k]) ([N, K] bf16, K % 8 == 0; w_folded may equal w, no other
+ * overlap), so that RMSNorm(h) W^T = r (h w_folded^T) with a per-row r.
+ *
  * tp_rmsnorm_column_linear / tp_rmsnorm_column_linear_swiglu: the column
- * linear (tp_column_linear, tp_column_linear_swiglu) of the normalised rows
- *   x[m, k] = bf16(h[m, k] * r_m * gamma[k]),  r_m = 1 / sqrt(mean_k h[m, k]^2 + eps)
- * without writing x. h: [M, K] bf16 (the residual stream, read only);
- * gamma: [K] bf16; eps finite and >= 0 (TP_ERR_RANGE); K <= 32768. One
- * launch when M <= 16 and a decode kernel holds whole rows of K in LDS
- * (K <= 5120): the norm's sum of squares runs in another order than
- * tp_add_rmsnorm's, so x may differ from its output by the rounding of r_m.
- * Otherwise two: tp_add_rmsnorm's kernel writes x into the stream's
- * 16 MiB workspace (M K 2 bytes must fit, TP_ERR_SHAPE otherwise), then the plain
- * linear reads it. y / act must not overlap h or gamma (TP_ERR_SHAPE). */
+ * linear (tp_column_linear, tp_column_linear_swiglu) of RMS-normalised rows,
+ * given the folded weight:
+ *   y[m, n] = r_m sum_k h[m, k] w_folded[n, k],  r_m = 1 / sqrt(mean_k h[m, k]^2 + eps)
+ * (= RMSNorm(h) gamma W^T up to the rounding of the folded weight), the
+ * normalised rows never written. h: [M, K] bf16 (the residual stream, read
+ * only); eps finite and >= 0 (TP_ERR_RANGE); K <= 32768. One launch when
+ * M <= 16 and a decode kernel holds whole rows of K in LDS (K <= 5120): the
+ * sums of squares come from the diagonal of h h^T on the matrix cores and r
+ * scales the outputs. Otherwise two: tp_add_rmsnorm's kernel (unit weights)
+ * writes bf16(h r) into the stream's 16 MiB workspace (M K 2 bytes must fit,
+ * TP_ERR_SHAPE otherwise), then the plain linear reads it. y / act must not
+ * overlap h (TP_ERR_SHAPE). */
+int tp_fold_norm_weight(const void* w, int64_t N, int64_t K, const void* gamma, void* w_folded, void* stream);
 int tp_row_linear_reduce_add(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
                              const void* const* partials, int t, int rank, void* residual, void* stream);
-int tp_rmsnorm_column_linear(const void* h, const void* gamma, float eps, int64_t M, int64_t K, const void* w_shard,
-                             int64_t N, const void* bias_or_null, void* y, void* stream);
-int tp_rmsnorm_column_linear_swiglu(const void* h, const void* gamma, float eps, int64_t M, int64_t K,
-                                    const void* w_gate_up, int64_t i_shard, void* act, void* stream);
+int tp_rmsnorm_column_linear(const void* h, float eps, int64_t M, int64_t K, const void* w_folded, int64_t N,
+                             const void* bias_or_null, void* y, void* stream);
+int tp_rmsnorm_column_linear_swiglu(const void* h, float eps, int64_t M, int64_t K, const void* w_gate_up_folded,
+                                    int64_t i_shard, void* act, void* stream);
 
 /* One decode step of the rank's grouped-query attention, with the KV-cache
  * append ([P2 前向执行的实际流程] Step 2: each rank computes attention for its

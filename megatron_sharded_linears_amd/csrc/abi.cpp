@@ -533,9 +533,10 @@ int workspace_back(hipStream_t s, int64_t bytes, void** out, int64_t* front) {
     return TP_OK;
 }
 
-// x = RMSNorm(a.x) (a.gamma, a.eps) feeding the linear a describes. One
-// launch when the decode kernel can stage whole rows; otherwise the norm
-// writes the normalised rows to the workspace and the plain linear reads them.
+// The linear a describes on RMS-normalised rows of a.x (unit weights: the
+// norm's gamma is folded into a.w). One launch when the decode kernel can
+// stage whole rows; otherwise the norm writes the normalised rows to the
+// workspace and the plain linear reads them.
 int run_norm_linear(tpk::GemmArgs a, hipStream_t s) {
     if (a.M <= kSkinnyMaxM) {
         const tpk::SkinnyPlan p = tpk::plan_skinny_norm(a.M, a.N, a.K);
@@ -551,33 +552,45 @@ int run_norm_linear(tpk::GemmArgs a, hipStream_t s) {
     if (st != TP_OK) return st;
     tpk::PartialPtrs none;
     std::memset(&none, 0, sizeof(none));
-    const hipError_t e = tpk::launch_add_rmsnorm(none, 0, TP_BF16, a.M, a.K, const_cast<void*>(a.x), a.gamma, a.eps,
+    const hipError_t e = tpk::launch_add_rmsnorm(none, 0, TP_BF16, a.M, a.K, const_cast<void*>(a.x), nullptr, a.eps,
                                                  xn, s);
     if (e != hipSuccess) return TP_ERR_HIP;
     a.x = xn;
-    a.gamma = nullptr;
+    a.norm = 0;
     return launch_linear(a, s, front);
 }
 
-int check_norm_input(const void* h, int64_t K, const void* gamma, float eps, const void* y,
-                     int64_t M, int64_t n_bytes) {
-    if (gamma == nullptr) return TP_ERR_NULL;
+int check_norm_input(const void* h, int64_t K, float eps, const void* y, int64_t M, int64_t n_bytes) {
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return TP_ERR_RANGE;
     if (K > kMaxNormWidth) return TP_ERR_SHAPE;
-    if (!aligned16(gamma)) return TP_ERR_ALIGNMENT;
-    if (overlap(y, n_bytes, h, M * K * 2) || overlap(y, n_bytes, gamma, K * 2))
-        return TP_ERR_SHAPE;
+    if (overlap(y, n_bytes, h, M * K * 2)) return TP_ERR_SHAPE;
     return TP_OK;
 }
 
 }  // namespace
 
-int tp_rmsnorm_column_linear(const void* h, const void* gamma, float eps, int64_t M, int64_t K, const void* w_shard,
-                             int64_t N, const void* bias_or_null, void* y, void* stream) {
+int tp_fold_norm_weight(const void* w, int64_t N, int64_t K, const void* gamma, void* w_folded, void* stream) {
     try {
+        if (w == nullptr || gamma == nullptr || w_folded == nullptr) return TP_ERR_NULL;
+        if (N <= 0 || K <= 0 || N >= kMaxDim || K >= kMaxDim) return TP_ERR_SHAPE;
+        if (K % 8 != 0 || !aligned16(w) || !aligned16(gamma) || !aligned16(w_folded)) return TP_ERR_ALIGNMENT;
+        const int64_t bytes = N * K * 2;
+        if ((w_folded != w && overlap(w_folded, bytes, w, bytes)) || overlap(w_folded, bytes, gamma, K * 2))
+            return TP_ERR_SHAPE;
+        const hipError_t e = tpk::launch_fold_norm_weight(w, N, K, gamma, w_folded, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_rmsnorm_column_linear(const void* h, float eps, int64_t M, int64_t K, const void* w_folded, int64_t N,
+                             const void* bias_or_null, void* y, void* stream) {
+    try {
+        const void* w_shard = w_folded;
         int st = check_linear(h, M, K, w_shard, N, y);
         if (st != TP_OK) return st;
-        st = check_norm_input(h, K, gamma, eps, y, M, M * N * 2);
+        st = check_norm_input(h, K, eps, y, M, M * N * 2);
         if (st != TP_OK) return st;
         if (bias_or_null != nullptr && (reinterpret_cast<uintptr_t>(bias_or_null) & 1u)) return TP_ERR_ALIGNMENT;
         if (M == 0) return TP_OK;
@@ -586,7 +599,7 @@ int tp_rmsnorm_column_linear(const void* h, const void* gamma, float eps, int64_
         a.M = M; a.N = N; a.K = K;
         a.out_dtype = TP_BF16;
         a.epi = tpk::EPI_STORE;
-        a.gamma = gamma;
+        a.norm = 1;
         a.eps = eps;
         return run_norm_linear(a, static_cast<hipStream_t>(stream));
     } catch (...) {
@@ -594,13 +607,14 @@ int tp_rmsnorm_column_linear(const void* h, const void* gamma, float eps, int64_
     }
 }
 
-int tp_rmsnorm_column_linear_swiglu(const void* h, const void* gamma, float eps, int64_t M, int64_t K,
-                                    const void* w_gate_up, int64_t i_shard, void* act, void* stream) {
+int tp_rmsnorm_column_linear_swiglu(const void* h, float eps, int64_t M, int64_t K, const void* w_gate_up_folded,
+                                    int64_t i_shard, void* act, void* stream) {
     try {
+        const void* w_gate_up = w_gate_up_folded;
         if (i_shard <= 0 || i_shard >= kMaxDim / 2) return TP_ERR_SHAPE;
         int st = check_linear(h, M, K, w_gate_up, 2 * i_shard, act);
         if (st != TP_OK) return st;
-        st = check_norm_input(h, K, gamma, eps, act, M, M * i_shard * 2);
+        st = check_norm_input(h, K, eps, act, M, M * i_shard * 2);
         if (st != TP_OK) return st;
         if (M == 0) return TP_OK;
         tpk::GemmArgs a{};
@@ -610,7 +624,7 @@ int tp_rmsnorm_column_linear_swiglu(const void* h, const void* gamma, float eps,
         a.epi = tpk::EPI_SWIGLU;
         a.i_half = i_shard;
         a.N = M <= kSkinnyMaxM ? 16 * ((i_shard + 7) / 8) : 2 * i_shard;
-        a.gamma = gamma;
+        a.norm = 1;
         a.eps = eps;
         return run_norm_linear(a, static_cast<hipStream_t>(stream));
     } catch (...) {

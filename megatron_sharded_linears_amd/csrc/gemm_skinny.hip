@@ -193,14 +193,19 @@ __device__ __forceinline__ void finish4(const GemmArgs& a, int64_t m, int64_t n,
     else store_out4(a, m, n, v);
 }
 
-// NORM = 1 (XD = 0, K not split, so a workgroup stages whole rows of X):
-// X's rows are RMS-normalised in LDS before the MFMAs (a.gamma, a.eps).
+// NORM = 1 (one 16-token tile, X staged in LDS, K not split across
+// workgroups): the RMSNorm of X's rows with gamma already folded into W
+// (tp_fold_norm_weight): y = r_m (x_m . w'_n), r_m = 1 / sqrt(sum_k x_mk^2 / K
+// + eps). sum_k x_mk^2 is the diagonal of X X^T, one more MFMA per k-step on
+// the X fragments already in registers (the matrix cores idle otherwise), so
+// the norm adds no per-element work.
 template <int MT, int KSTEPS, int NWN, int NWK, int XD, int EPI, int NORM = 0>
 __global__ void __launch_bounds__(64 * NWN * NWK)
 skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restrict__ ws,
               unsigned* __restrict__ counters) {
     using C = SkinnyCfg<MT, KSTEPS, NWN, NWK, XD>;
-    static_assert(!NORM || !XD, "the norm needs X staged in LDS");
+    static_assert(!NORM || (!XD && MT == 1 && NWN == 1 && NWK > 1), "the norm needs one tile of X in LDS");
+    __shared__ float s_gram[NORM ? NWK * 4 * 64 : 1];    // NORM: each wave's X X^T fragment
     extern __shared__ __align__(16) unsigned char smem[];
     bf16_t* xs = reinterpret_cast<bf16_t*>(smem);                       // [xrows][kXStride]
     float* red = reinterpret_cast<float*>(smem + (XD ? 0 : (size_t)xrows * C::kXStride * 2));
@@ -261,19 +266,6 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
             xr[j] = *reinterpret_cast<const uint4*>(X + (ok ? (int64_t)m * K + k : 0));
         }
     }
-    // NORM: gamma's K values, 16 bytes per thread and chunk, bound for LDS
-    constexpr int kGPerThread = NORM ? (C::kGroupK / 8 + C::kThreads - 1) / C::kThreads : 1;
-    __shared__ __align__(16) bf16_t s_gamma[NORM ? C::kGroupK : 8];
-    __shared__ float s_rinv[NORM ? 16 * MT : 1];
-    uint4 gr[kGPerThread];
-    if constexpr (NORM) {
-        const bf16_t* __restrict__ G = reinterpret_cast<const bf16_t*>(a.gamma);
-#pragma unroll
-        for (int j = 0; j < kGPerThread; ++j) {
-            const int kc = tid + j * C::kThreads;
-            gr[j] = *reinterpret_cast<const uint4*>(G + (kc * 8 < K ? kc * 8 : 0));
-        }
-    }
 
     // 2. Issue the first tile's weight loads (and, with XD, the wave's X
     //    fragments, which are the same for every tile).
@@ -331,51 +323,9 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
                 *reinterpret_cast<uint4*>(xs + m * C::kXStride + kc * 8) = ok ? xr[j] : make_uint4(0u, 0u, 0u, 0u);
             }
         }
-        if constexpr (NORM) {
-#pragma unroll
-            for (int j = 0; j < kGPerThread; ++j) {
-                const int kc = tid + j * C::kThreads;
-                if (kc < C::kGroupK / 8) *reinterpret_cast<uint4*>(s_gamma + kc * 8) = gr[j];
-            }
-        }
         lds_barrier();
     }
 
-    // 3b. NORM: x = bf16(x / sqrt(sum_k x^2 / K + eps) * gamma), per staged row
-    //     (the zeros past K add nothing to the sum). Wave w sums rows w, w +
-    //     waves, ... in a fixed order; the rows are then scaled in place.
-    if constexpr (NORM) {
-        constexpr int kWaves = NWN * NWK;
-        for (int m = wave; m < xrows; m += kWaves) {
-            float ss = 0.f;
-            for (int c8 = lane; c8 < C::kGroupK / 8; c8 += 64) {
-                float f[8];
-                unpack_bf16x8(*reinterpret_cast<const uint4*>(xs + m * C::kXStride + c8 * 8), f);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
-            }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-            if (lane == 0) s_rinv[m] = 1.0f / sqrtf(ss / (float)K + a.eps);
-        }
-        lds_barrier();
-#pragma unroll
-        for (int j = 0; j < kXPerThread; ++j) {
-            const int c = tid + j * C::kThreads;
-            const int m = c / (C::kGroupK / 8);
-            const int kc = c % (C::kGroupK / 8);
-            if (c < x_chunks && kc * 8 < K) {
-                float h[8], g[8], y[8];
-                unpack_bf16x8(xr[j], h);
-                unpack_bf16x8(*reinterpret_cast<const uint4*>(s_gamma + kc * 8), g);
-                const float r = s_rinv[m];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = h[e] * r * g[e];
-                *reinterpret_cast<uint4*>(xs + m * C::kXStride + kc * 8) = pack_bf16x8(y);
-            }
-        }
-        lds_barrier();
-    }
 
     const int xcol = wk * C::kWaveK + 8 * (lane >> 4);
     f32x4_t acc[MT];
@@ -398,6 +348,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
         // 4. MFMAs: acc[mt] holds D[n = 4*(lane/16) + i][m = 16*mt + lane%16].
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t gram = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             const bool k_ok = k_wave + 32 * s < K;
@@ -413,6 +364,9 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
                                    : make_uint4(0u, 0u, 0u, 0u);
                 }
                 acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, xv), acc[mt], 0, 0, 0);
+                if constexpr (NORM)
+                    gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
+                                                                   __builtin_bit_cast(bf16x8_t, xv), gram, 0, 0, 0);
             }
         }
 
@@ -423,6 +377,10 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     red[(((wk * NWN + wn) * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
+            if constexpr (NORM) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s_gram[(wk * 4 + i) * 64 + lane] = gram[i];
+            }
             lds_barrier();
 #pragma unroll
             for (int o = 0; o < C::kOwn; ++o) {
@@ -436,6 +394,20 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
                         fin[o][i] = v;
                     }
                 }
+            }
+            if constexpr (NORM) {
+                // X X^T[m][m] sits in lane m + 16 (m / 4), element m % 4, of
+                // each wave's fragment; summed over the waves in order.
+                const int m = lane & 15;
+                const int src = (m % 4) * 64 + m + 16 * (m / 4);
+                float ss = s_gram[src];
+#pragma unroll
+                for (int w = 1; w < NWK; ++w) ss += s_gram[w * 4 * 64 + src];
+                const float r = 1.0f / sqrtf(ss / (float)K + a.eps);
+#pragma unroll
+                for (int o = 0; o < C::kOwn; ++o)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) fin[o][i] *= r;
             }
             lds_barrier();     // the buffer is rewritten for the next tile
         } else {
@@ -558,7 +530,7 @@ typedef int (*SkinnyLdsFn)(int);
 // EPI_SWIGLU), built only for one 16-token tile, X in LDS, one row group.
 template <int MT, int KS, int NN, int NK, int XD, int EPI>
 constexpr SkinnyFn skinny_norm_fn() {
-    if constexpr (MT == 1 && XD == 0 && NN == 1 && EPI <= EPI_SWIGLU)
+    if constexpr (MT == 1 && XD == 0 && NN == 1 && NK > 1 && EPI <= EPI_SWIGLU)
         return skinny_kernel<MT, KS, NN, NK, XD, EPI, 1>;
     else
         return nullptr;
@@ -633,15 +605,15 @@ bool skinny_plan_fits(const SkinnyPlan& p, int64_t M) {
     return e.lds(xrows_for(e, M)) <= kMaxLds;
 }
 
-// With the norm prologue: one 16-token tile whose whole rows (K <= the
-// variant's K coverage) sit in LDS next to gamma's K values.
+// With the norm: one 16-token tile whose whole rows (K <= the variant's K
+// coverage) sit in LDS.
 bool skinny_norm_plan_fits(const SkinnyPlan& p, int64_t M, int64_t K) {
     const int idx = find_skinny(p);
     if (idx < 0) return false;
     const SkinnyEntry& e = kSkinnyTable[idx];
     if (e.fn_norm[0] == nullptr || M > 16 || K > e.group_k) return false;
-    // dynamic LDS (staged rows, reduction buffer) + static (gamma, row scales, flags)
-    return e.lds(xrows_for(e, M)) + 2 * e.group_k + 512 <= 160 * 1024;
+    // dynamic LDS (staged rows, reduction buffer) + static (X X^T fragments, flags)
+    return e.lds(xrows_for(e, M)) + e.nwk * 4 * 64 * 4 + 512 <= 160 * 1024;
 }
 
 // Decode shape for a linear with the norm prologue: the variant covering K
@@ -742,7 +714,7 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
     const SkinnyEntry* e = &kSkinnyTable[idx];
     const int epi = a.epi;
     if (epi < 0 || epi > 3) return hipErrorInvalidValue;
-    const bool norm = a.gamma != nullptr;
+    const bool norm = a.norm != 0;
     if (norm && (epi > EPI_SWIGLU || p.splits != 1 || !skinny_norm_plan_fits(p, a.M, a.K)))
         return hipErrorInvalidValue;
     const SkinnyFn fn = norm ? e->fn_norm[epi] : e->fn[epi];

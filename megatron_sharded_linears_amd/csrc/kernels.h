@@ -65,9 +65,9 @@ struct GemmArgs {
     int epi;
     int64_t i_half;     // EPI_SWIGLU
     int t, rank;        // EPI_REDUCE, EPI_REDUCE_ADD
-    // RMSNorm of X's rows before the product (decode kernel, X staged in LDS,
-    // K not split): x = bf16(x / sqrt(mean(x^2) + eps) * gamma). nullptr: none.
-    const void* gamma;
+    // norm != 0: the RMSNorm of X's rows with gamma folded into W (decode
+    // kernel, one tile of X in LDS, K not split): y = acc / sqrt(mean_k x^2 + eps).
+    int norm;
     float eps;
     const void* peers[kMaxFusedPeers];
 };

@@ -11,7 +11,10 @@ namespace tpk {
 // residual[m] = bf16(residual[m] + bf16(sum of the t partials' row m)) (t = 0:
 // unchanged), out[m] = bf16(residual[m] * rsqrt-scale * gamma); one workgroup
 // per row, M <= 2^31 - 1, H % 8 == 0, H <= 32768. out == nullptr: the
-// residual update only (gamma unused).
+// residual update only; gamma == nullptr: unit weights.
+// w_out[n, k] = bf16(w[n, k] * gamma[k]) for [N, K] bf16 (K % 8 == 0; may be in place).
+hipError_t launch_fold_norm_weight(const void* w, int64_t N, int64_t K, const void* gamma, void* out, hipStream_t s);
+
 hipError_t launch_add_rmsnorm(const PartialPtrs& ptrs, int t, int in_dtype, int64_t M, int64_t H,
                               void* residual, const void* gamma, float eps, void* out, hipStream_t s);
 

@@ -203,7 +203,10 @@ add_rmsnorm_kernel(PartialPtrs ptrs, int t_rt, uint16_t* __restrict__ residual, 
     const int64_t m = blockIdx.x;
     const int64_t nvec = H / 8;
     uint4* res = reinterpret_cast<uint4*>(residual + m * H);
-    const uint4* g4 = reinterpret_cast<const uint4*>(gamma);
+    // gamma == nullptr: unit weights (the loads then read the residual row
+    // instead and their values are not used)
+    const bool unit = gamma == nullptr;
+    const uint4* g4 = reinterpret_cast<const uint4*>(unit ? residual + m * H : gamma);
     const int64_t row_vec = m * nvec * kInVec;     // first 16-byte vector of row m in a partial
     const int t = T >= 0 ? T : t_rt;
 
@@ -282,7 +285,7 @@ add_rmsnorm_kernel(PartialPtrs ptrs, int t_rt, uint16_t* __restrict__ residual, 
         float g[8], y[8];
         unpack_bf16x8(graw[j], g);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = h[j][e] * r * g[e];
+        for (int e = 0; e < 8; ++e) y[e] = unit ? h[j][e] * r : h[j][e] * r * g[e];
         if (ok[j]) o4[vv[j]] = pack_bf16x8(y);
     }
 }
@@ -319,6 +322,23 @@ hipError_t add_rmsnorm_t(const PartialPtrs& ptrs, int t, int64_t M, int64_t H, u
     default: return add_rmsnorm_vpt<IN_F32, -1>(ptrs, t, M, H, res, g, eps, o, s);
     }
 }
+
+// --------------------------------------------------------- norm weight folding
+
+// w_out[n, k] = bf16(w[n, k] * gamma[k]), 8 elements per thread (K % 8 == 0).
+__global__ void __launch_bounds__(kThreads)
+fold_norm_weight_kernel(const uint4* __restrict__ w, const uint4* __restrict__ gamma, int64_t k_vec, int64_t total,
+                        uint4* __restrict__ out) {
+    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < total; v += (int64_t)gridDim.x * kThreads) {
+        float x[8], g[8];
+        unpack_bf16x8(w[v], x);
+        unpack_bf16x8(gamma[v % k_vec], g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= g[e];
+        out[v] = pack_bf16x8(x);
+    }
+}
+
 
 // ---------------------------------------------------------------- vocab embed
 
@@ -436,11 +456,20 @@ hipError_t launch_add_rmsnorm(const PartialPtrs& ptrs, int t, int in_dtype, int6
                               void* residual, const void* gamma, float eps, void* out, hipStream_t s) {
     if (H / 8 > 8 * kNormThreads) return hipErrorInvalidValue;   // H > 32768: rejected by the ABI
     uint16_t* res = reinterpret_cast<uint16_t*>(residual);
-    // out == nullptr: no norm; gamma's loads then read the residual instead
-    const uint16_t* g = reinterpret_cast<const uint16_t*>(out != nullptr ? gamma : residual);
+    const uint16_t* g = reinterpret_cast<const uint16_t*>(gamma);
     uint16_t* o = reinterpret_cast<uint16_t*>(out);
     return in_dtype == TP_F32 ? add_rmsnorm_t<1>(ptrs, t, M, H, res, g, eps, o, s)
                               : add_rmsnorm_t<0>(ptrs, t, M, H, res, g, eps, o, s);
+}
+
+hipError_t launch_fold_norm_weight(const void* w, int64_t N, int64_t K, const void* gamma, void* out, hipStream_t s) {
+    const int64_t total = N * (K / 8);
+    int64_t blocks = (total + kThreads - 1) / kThreads;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fold_norm_weight_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(w), static_cast<const uint4*>(gamma), K / 8, total,
+                       static_cast<uint4*>(out));
+    return hipGetLastError();
 }
 
 }  // namespace tpk

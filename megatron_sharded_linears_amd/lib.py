@@ -74,8 +74,9 @@ _PROTOS = {
     "tp_column_linear_swiglu": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
     "tp_row_linear_reduce": (_int, [_vp, _i64, _i64, _vp, _i64, _ptr_array, _int, _int, _vp, _vp]),
     "tp_row_linear_reduce_add": (_int, [_vp, _i64, _i64, _vp, _i64, _ptr_array, _int, _int, _vp, _vp]),
-    "tp_rmsnorm_column_linear": (_int, [_vp, _vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
-    "tp_rmsnorm_column_linear_swiglu": (_int, [_vp, _vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "tp_fold_norm_weight": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "tp_rmsnorm_column_linear": (_int, [_vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "tp_rmsnorm_column_linear_swiglu": (_int, [_vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp]),
     "tp_row_linear_partial": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp]),
     "tp_reduce_partials": (_int, [_ptr_array, _int, _i64, _int, _vp, _int, _vp]),
     "tp_vocab_embed": (_int, [_vp, _i64, _vp, _i64, _int, _int, _i64, _vp, _vp]),
@@ -299,36 +300,44 @@ def tp_row_linear_reduce_add(x_shard, w_shard, partials, rank, residual, stream=
     return residual
 
 
-def tp_rmsnorm_column_linear(h, gamma, eps, w_shard, y, bias=None, stream=None):
-    """y = RMSNorm(h) gamma W^T (+ bias), the normalised rows not written."""
-    M, K, N = _linear_shapes(h, w_shard, y, "tp_rmsnorm_column_linear")
+def tp_fold_norm_weight(w, gamma, w_folded, stream=None):
+    """w_folded = bf16(w * gamma) column by column: the RMSNorm weight folded
+    into the next linear (load time). w_folded may be w."""
+    N, K = w.shape
     _dev(gamma, "gamma", torch.bfloat16, 1)
-    if gamma.shape[0] != K:
-        raise ValueError("gamma length != K")
+    if gamma.shape[0] != K or tuple(w_folded.shape) != (N, K):
+        raise ValueError("tp_fold_norm_weight: need w [N, K], gamma [K], w_folded [N, K]")
+    _check(_lib.tp_fold_norm_weight(_dev(w, "w", torch.bfloat16, 2), N, K, gamma.data_ptr(),
+                                    _dev(w_folded, "w_folded", torch.bfloat16, 2), _stream(stream)),
+           "tp_fold_norm_weight")
+    return w_folded
+
+
+def tp_rmsnorm_column_linear(h, eps, w_folded, y, bias=None, stream=None):
+    """y = RMSNorm(h) W^T (+ bias) with the norm's gamma folded into w_folded
+    (tp_fold_norm_weight); the normalised rows are not written."""
+    M, K, N = _linear_shapes(h, w_folded, y, "tp_rmsnorm_column_linear")
     b = None
     if bias is not None:
         b = _dev(bias, "bias", torch.bfloat16, 1)
         if bias.shape[0] != N:
             raise ValueError("bias length != N")
-    _check(_lib.tp_rmsnorm_column_linear(_dev(h, "h", torch.bfloat16, 2), gamma.data_ptr(), float(eps), M, K,
-                                         _dev(w_shard, "w_shard", torch.bfloat16, 2), N, b,
+    _check(_lib.tp_rmsnorm_column_linear(_dev(h, "h", torch.bfloat16, 2), float(eps), M, K,
+                                         _dev(w_folded, "w_folded", torch.bfloat16, 2), N, b,
                                          _dev(y, "y", torch.bfloat16, 2), _stream(stream)),
            "tp_rmsnorm_column_linear")
     return y
 
 
-def tp_rmsnorm_column_linear_swiglu(h, gamma, eps, w_gate_up, act, stream=None):
-    """act = SwiGLU of RMSNorm(h) gamma W_gate_up^T."""
+def tp_rmsnorm_column_linear_swiglu(h, eps, w_gate_up_folded, act, stream=None):
+    """act = SwiGLU of RMSNorm(h) W_gate_up^T, gamma folded into the weight."""
     M, K = h.shape
-    two_i, K2 = w_gate_up.shape
+    two_i, K2 = w_gate_up_folded.shape
     if K != K2 or two_i % 2 or tuple(act.shape) != (M, two_i // 2):
         raise ValueError("tp_rmsnorm_column_linear_swiglu: need h [M, K], w_gate_up [2 I, K], act [M, I]")
-    _dev(gamma, "gamma", torch.bfloat16, 1)
-    if gamma.shape[0] != K:
-        raise ValueError("gamma length != K")
-    _check(_lib.tp_rmsnorm_column_linear_swiglu(_dev(h, "h", torch.bfloat16, 2), gamma.data_ptr(), float(eps), M, K,
-                                                _dev(w_gate_up, "w_gate_up", torch.bfloat16, 2), two_i // 2,
-                                                _dev(act, "act", torch.bfloat16, 2), _stream(stream)),
+    _check(_lib.tp_rmsnorm_column_linear_swiglu(_dev(h, "h", torch.bfloat16, 2), float(eps), M, K,
+                                                _dev(w_gate_up_folded, "w_gate_up_folded", torch.bfloat16, 2),
+                                                two_i // 2, _dev(act, "act", torch.bfloat16, 2), _stream(stream)),
            "tp_rmsnorm_column_linear_swiglu")
     return act
 

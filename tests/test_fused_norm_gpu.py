@@ -5,9 +5,12 @@ oracle and against the separate calls:
   tp_row_linear_reduce's sum plus one bf16 rounding of residual + sum (the
   update tp_reduce_add_rmsnorm makes), and within the linear bar of the
   float64 residual + sum of the ranks' products;
-* tp_rmsnorm_column_linear(_swiglu): within the linear bar of the oracle's
-  RMSNorm (rounded to bf16, as the stored normalised row would be) followed
-  by the linear (and SwiGLU), and of the separate calls.
+* tp_fold_norm_weight: bit for bit against bf16(w * gamma) on the host;
+* tp_rmsnorm_column_linear(_swiglu): within the linear bar of the call's
+  definition, the oracle's RMSNorm with unit weights followed by the linear
+  (and SwiGLU) on the folded weight the call receives; the plain linear also
+  within the bar of the unfolded chain (RMSNorm with gamma, then W) and of
+  the separate calls.
 
 Shapes: the decode workloads' (one launch: M <= 16, whole rows of K in LDS)
 and the two-launch paths (M in (16, 64] and M > 64; t > 16)."""
@@ -78,6 +81,29 @@ def gamma(key, K):
     return (1.0 + I.normal_bf16(key, (K,), 0.1).float()).to(torch.bfloat16)
 
 
+def folded(w, g):
+    out = empty(tuple(w.shape))
+    lib.tp_fold_norm_weight(dev(w), dev(g), out)
+    return out
+
+
+def unit_normed(h):
+    """The oracle's RMSNorm of h with unit weights (gamma is in the folded weight)."""
+    return oracle.rms_norm(f64(h), np.ones(h.shape[1]), EPS)
+
+
+@pytest.mark.parametrize("N,K", [(768, 4096), (7, 8), (1000, 256)])
+def test_fold_norm_weight_bitexact(N, K):
+    key = (SEED, 6, N, K)
+    w = I.normal_bf16(key + (0,), (N, K), 0.02)
+    g = gamma(key + (1,), K)
+    want = (w.float() * g.float()[None, :]).to(torch.bfloat16)   # one product, rounded to nearest even
+    assert np.array_equal(bits(folded(w, g)), bits(want))
+    inplace = dev(w)
+    lib.tp_fold_norm_weight(inplace, dev(g), inplace)
+    assert np.array_equal(bits(inplace), bits(want))
+
+
 @pytest.mark.parametrize("M,K,N", NORM_LINEAR_CASES)
 def test_rmsnorm_column_linear(M, K, N):
     key = (SEED, 2, M, K, N)
@@ -87,10 +113,12 @@ def test_rmsnorm_column_linear(M, K, N):
     b = I.normal_bf16(key + (3,), (N,))
     y = empty((M, N))
     hd = dev(h)
-    lib.tp_rmsnorm_column_linear(hd, dev(g), EPS, dev(w), y, bias=dev(b))
+    wf = folded(w, g)
+    lib.tp_rmsnorm_column_linear(hd, EPS, wf, y, bias=dev(b))
     assert np.array_equal(bits(hd), bits(h)), "h is read only"
+    assert_close(f64(y), oracle.linear(unit_normed(h), f64(wf), f64(b)), f"rmsnorm_column_linear {(M, K, N)}")
     ref = oracle.linear(normed(h, g), f64(w), f64(b))
-    assert_close(f64(y), ref, f"rmsnorm_column_linear {(M, K, N)}")
+    assert_close(f64(y), ref, f"rmsnorm_column_linear vs unfolded chain {(M, K, N)}")
     # against the separate calls: the norm, then the plain linear
     xn, res = empty((M, K)), dev(h)
     lib.tp_add_rmsnorm(None, res, dev(g), EPS, xn)
@@ -107,10 +135,11 @@ def test_rmsnorm_column_linear_swiglu(M, K, Is):
     g = gamma(key + (1,), K)
     w = I.normal_bf16(key + (2,), (2 * Is, K), 0.02)
     act = empty((M, Is))
-    lib.tp_rmsnorm_column_linear_swiglu(dev(h), dev(g), EPS, dev(w), act)
-    x = normed(h, g)
-    gate = oracle.round_bf16(oracle.linear(x, f64(w[:Is])))
-    up = oracle.round_bf16(oracle.linear(x, f64(w[Is:])))
+    wf = folded(w, g)
+    lib.tp_rmsnorm_column_linear_swiglu(dev(h), EPS, wf, act)
+    x = unit_normed(h)
+    gate = oracle.round_bf16(oracle.linear(x, f64(wf[:Is])))
+    up = oracle.round_bf16(oracle.linear(x, f64(wf[Is:])))
     assert_close(f64(act), oracle.swiglu(gate, up), f"rmsnorm_column_linear_swiglu {(M, K, Is)}")
 
 
@@ -122,12 +151,12 @@ def test_norm_linear_scale_invariance_and_per_row():
     key = (SEED, 4)
     h = I.normal_bf16(key + (0,), (M, K))
     g = gamma(key + (1,), K)
-    w = dev(I.normal_bf16(key + (2,), (N, K), 0.02))
+    w = folded(I.normal_bf16(key + (2,), (N, K), 0.02), g)
     y1, y2 = empty((M, N)), empty((M, N))
-    lib.tp_rmsnorm_column_linear(dev(h), dev(g), EPS, w, y1)
+    lib.tp_rmsnorm_column_linear(dev(h), EPS, w, y1)
     h2 = h.clone()
     h2[3] = h2[3] * 8.0
-    lib.tp_rmsnorm_column_linear(dev(h2), dev(g), EPS, w, y2)
+    lib.tp_rmsnorm_column_linear(dev(h2), EPS, w, y2)
     other = [m for m in range(M) if m != 3]
     assert np.array_equal(bits(y1[other]), bits(y2[other]))
     assert_close(f64(y2[3:4]), f64(y1[3:4]), "scaled row")
@@ -136,7 +165,8 @@ def test_norm_linear_scale_invariance_and_per_row():
 def test_fused_norm_step_matches_oracle_chain():
     """One decode layer through the four fused calls against the oracle's
     chain (input norm, qkv; o + sum + residual add; post norm, gate_up,
-    SwiGLU; down + sum + residual add), at the tiny workload's rank shapes."""
+    SwiGLU; down + sum + residual add) on the same (folded) weights, at the
+    tiny workload's rank shapes."""
     t, rank, M, H, Is, nq = 2, 0, 16, 256, 512, 128
     key = (SEED, 5)
     h = I.normal_bf16(key + (0,), (M, H))
@@ -150,18 +180,20 @@ def test_fused_norm_step_matches_oracle_chain():
     peer_d = I.normal_bf16(key + (9,), (M, H), 0.5)
     res = dev(h)
     qkv, act = empty((M, 192)), empty((M, Is))
-    lib.tp_rmsnorm_column_linear(res, dev(g_in), EPS, dev(w_qkv), qkv)
+    wq_f, wgu_f = folded(w_qkv, g_in), folded(w_gu, g_post)
+    lib.tp_rmsnorm_column_linear(res, EPS, wq_f, qkv)
     lib.tp_row_linear_reduce_add(dev(ctx), dev(w_o), [None, dev(peer_o)], rank, res)
-    lib.tp_rmsnorm_column_linear_swiglu(res, dev(g_post), EPS, dev(w_gu), act)
+    lib.tp_rmsnorm_column_linear_swiglu(res, EPS, wgu_f, act)
     lib.tp_row_linear_reduce_add(act, dev(w_d), [None, dev(peer_d)], rank, res)
-    # the oracle's chain, every stored activation rounded to bf16
+    # the oracle's chain on the weights the calls receive (gamma folded into
+    # qkv and gate_up), every stored activation rounded to bf16
     r64 = f64(h)
-    q_ref = oracle.linear(normed(h, g_in), f64(w_qkv))
+    q_ref = oracle.linear(unit_normed(h), f64(wq_f))
     assert_close(f64(qkv), q_ref, "qkv")
     r64 = oracle.round_bf16(r64 + oracle.round_bf16(oracle.linear(f64(ctx), f64(w_o)) + f64(peer_o)))
-    x = oracle.round_bf16(oracle.rms_norm(r64, f64(g_post), EPS))
-    a = oracle.swiglu(oracle.round_bf16(oracle.linear(x, f64(w_gu[:Is]))),
-                      oracle.round_bf16(oracle.linear(x, f64(w_gu[Is:]))))
+    x = oracle.rms_norm(r64, np.ones(H), EPS)
+    a = oracle.swiglu(oracle.round_bf16(oracle.linear(x, f64(wgu_f[:Is]))),
+                      oracle.round_bf16(oracle.linear(x, f64(wgu_f[Is:]))))
     assert_close(f64(act), a, "act")
     r64 = r64 + oracle.linear(f64(act), f64(w_d)) + f64(peer_d)
     assert_close(f64(res), r64, "residual after the layer")
