@@ -333,6 +333,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     // accumulators when NWK == 1, else the in-order sum of the NWK waves'
     // accumulators read back from LDS.
     float fin[C::kOwn][4];
+    float rnorm = 1.0f;      // NORM: this lane's row scale, from the first tile (X is the same for all)
     for (;;) {
         const int64_t n_out = tile * C::kRows + wn * 16 + 4 * (lane >> 4);   // first of this lane's 4 rows
 
@@ -364,7 +365,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
                                    : make_uint4(0u, 0u, 0u, 0u);
                 }
                 acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, xv), acc[mt], 0, 0, 0);
-                if constexpr (NORM)
+                if (NORM && first_tile)
                     gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
                                                                    __builtin_bit_cast(bf16x8_t, xv), gram, 0, 0, 0);
             }
@@ -377,7 +378,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     red[(((wk * NWN + wn) * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
-            if constexpr (NORM) {
+            if (NORM && first_tile) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) s_gram[(wk * 4 + i) * 64 + lane] = gram[i];
             }
@@ -398,16 +399,18 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
             if constexpr (NORM) {
                 // X X^T[m][m] sits in lane m + 16 (m / 4), element m % 4, of
                 // each wave's fragment; summed over the waves in order.
-                const int m = lane & 15;
-                const int src = (m % 4) * 64 + m + 16 * (m / 4);
-                float ss = s_gram[src];
+                if (first_tile) {
+                    const int m = lane & 15;
+                    const int src = (m % 4) * 64 + m + 16 * (m / 4);
+                    float ss = s_gram[src];
 #pragma unroll
-                for (int w = 1; w < NWK; ++w) ss += s_gram[w * 4 * 64 + src];
-                const float r = 1.0f / sqrtf(ss / (float)K + a.eps);
+                    for (int w = 1; w < NWK; ++w) ss += s_gram[w * 4 * 64 + src];
+                    rnorm = 1.0f / sqrtf(ss / (float)K + a.eps);
+                }
 #pragma unroll
                 for (int o = 0; o < C::kOwn; ++o)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) fin[o][i] *= r;
+                    for (int i = 0; i < 4; ++i) fin[o][i] *= rnorm;
             }
             lds_barrier();     // the buffer is rewritten for the next tile
         } else {
