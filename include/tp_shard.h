@@ -236,9 +236,9 @@ int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype,
  * (= RMSNorm(h) gamma W^T up to the rounding of the folded weight), the
  * normalised rows never written. h: [M, K] bf16 (the residual stream, read
  * only); eps finite and >= 0 (TP_ERR_RANGE); K <= 32768. One launch when
- * M <= 16 and a decode kernel holds whole rows of K in LDS (K <= 5120): the
- * sums of squares come from the diagonal of h h^T on the matrix cores and r
- * scales the outputs. Otherwise two: tp_add_rmsnorm's kernel (unit weights)
+ * M <= 16 (the decode kernel, K split across workgroups as the plain linear
+ * would be, or whole rows of K <= 5120 in one): the sums of squares come
+ * from the diagonal of h h^T on the matrix cores and r scales the outputs. Otherwise two: tp_add_rmsnorm's kernel (unit weights)
  * writes bf16(h r) into the stream's 16 MiB workspace (M K 2 bytes must fit,
  * TP_ERR_SHAPE otherwise), then the plain linear reads it. y / act must not
  * overlap h (TP_ERR_SHAPE). */

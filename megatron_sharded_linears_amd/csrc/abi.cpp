@@ -540,8 +540,16 @@ int workspace_back(hipStream_t s, int64_t bytes, void** out, int64_t* front) {
 int run_norm_linear(tpk::GemmArgs a, hipStream_t s) {
     if (a.M <= kSkinnyMaxM) {
         const tpk::SkinnyPlan p = tpk::plan_skinny_norm(a.M, a.N, a.K);
-        if (p.splits == 1) {
-            const tpk::Workspace ws{nullptr, 0, nullptr, 0};
+        if (p.splits >= 1) {
+            tpk::Workspace ws{nullptr, 0, nullptr, 0};
+            if (p.splits > 1) {
+                // partial tiles, then each split's share of the rows' sums of squares
+                const int st = get_workspace(s, &ws);
+                if (st != TP_OK) return st;
+                if (tpk::skinny_workspace_floats(p, a.M, a.N) + (int64_t)p.splits * p.ntiles * 16 > ws.partial_floats ||
+                    p.ntiles > ws.num_counters)
+                    return TP_ERR_SHAPE;
+            }
             const hipError_t e = tpk::launch_skinny(a, p, ws, s);
             return e == hipSuccess ? TP_OK : TP_ERR_HIP;
         }

@@ -193,12 +193,13 @@ __device__ __forceinline__ void finish4(const GemmArgs& a, int64_t m, int64_t n,
     else store_out4(a, m, n, v);
 }
 
-// NORM = 1 (one 16-token tile, X staged in LDS, K not split across
-// workgroups): the RMSNorm of X's rows with gamma already folded into W
-// (tp_fold_norm_weight): y = r_m (x_m . w'_n), r_m = 1 / sqrt(sum_k x_mk^2 / K
-// + eps). sum_k x_mk^2 is the diagonal of X X^T, one more MFMA per k-step on
-// the X fragments already in registers (the matrix cores idle otherwise), so
-// the norm adds no per-element work.
+// NORM = 1 (one 16-token tile, X staged in LDS): the RMSNorm of X's rows
+// with gamma already folded into W (tp_fold_norm_weight): y = r_m (x_m .
+// w'_n), r_m = 1 / sqrt(sum_k x_mk^2 / K + eps). sum_k x_mk^2 is the diagonal
+// of X X^T, one more MFMA per k-step on the X fragments already in registers
+// (the matrix cores idle otherwise), so the norm adds no per-element work.
+// With K split across workgroups each publishes its share of the sums next
+// to its partial tile and the last to arrive adds them in split order.
 template <int MT, int KSTEPS, int NWN, int NWK, int XD, int EPI, int NORM = 0>
 __global__ void __launch_bounds__(64 * NWN * NWK)
 skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restrict__ ws,
@@ -334,6 +335,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     // accumulators read back from LDS.
     float fin[C::kOwn][4];
     float rnorm = 1.0f;      // NORM: this lane's row scale, from the first tile (X is the same for all)
+    float ss_part = 0.f;     // NORM with K split: this workgroup's share of the row's sum of squares
     for (;;) {
         const int64_t n_out = tile * C::kRows + wn * 16 + 4 * (lane >> 4);   // first of this lane's 4 rows
 
@@ -405,12 +407,16 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
                     float ss = s_gram[src];
 #pragma unroll
                     for (int w = 1; w < NWK; ++w) ss += s_gram[w * 4 * 64 + src];
+                    ss_part = ss;
                     rnorm = 1.0f / sqrtf(ss / (float)K + a.eps);
                 }
+                // with K split, the row's sum is complete only in step 7
+                if (splits == 1) {
 #pragma unroll
-                for (int o = 0; o < C::kOwn; ++o)
+                    for (int o = 0; o < C::kOwn; ++o)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) fin[o][i] *= rnorm;
+                        for (int i = 0; i < 4; ++i) fin[o][i] *= rnorm;
+                }
             }
             lds_barrier();     // the buffer is rewritten for the next tile
         } else {
@@ -471,6 +477,12 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
             }
         }
     }
+    // NORM: this split's share of each row's sum of squares, after the
+    // partial tiles ([split][tile][16] floats), published the same way
+    float* const ws_ss = ws + (int64_t)splits * M * N;
+    if (NORM && wk == 0 && lane < 16)
+        __hip_atomic_store(ws_ss + ((int64_t)split * ntiles + tile) * 16 + lane, ss_part, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
@@ -483,6 +495,23 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     // 7. Last workgroup on this tile: sum the partials in split order. The
     //    loads of up to 8 splits are issued back to back before any is used,
     //    so they cost one memory round trip, not one each.
+    if constexpr (NORM) {
+        // the row's sum of squares over the splits, in split order
+        float ss = 0.f;
+        for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+            float t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int sp = sp0 + j < splits ? sp0 + j : splits - 1;
+                t[j] = __hip_atomic_load(ws_ss + ((int64_t)sp * ntiles + tile) * 16 + (lane & 15), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (sp0 + j < splits) ss += t[j];
+        }
+        rnorm = 1.0f / sqrtf(ss / (float)K + a.eps);
+    }
 #pragma unroll
     for (int o = 0; o < C::kOwn; ++o) {
         const int mt = wk + NWK * o;
@@ -519,6 +548,10 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
 #pragma unroll
                             for (int i = 0; i < 4; ++i) v[i] += t[j][i];
                 }
+            }
+            if constexpr (NORM) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] *= rnorm;
             }
             finish4<EPI>(a, m, n_out, v, lane, peers);
         }
@@ -614,17 +647,25 @@ bool skinny_norm_plan_fits(const SkinnyPlan& p, int64_t M, int64_t K) {
     const int idx = find_skinny(p);
     if (idx < 0) return false;
     const SkinnyEntry& e = kSkinnyTable[idx];
-    if (e.fn_norm[0] == nullptr || M > 16 || K > e.group_k) return false;
+    if (e.fn_norm[0] == nullptr || M > 16) return false;
     // dynamic LDS (staged rows, reduction buffer) + static (X X^T fragments, flags)
     return e.lds(xrows_for(e, M)) + e.nwk * 4 * 64 * 4 + 512 <= 160 * 1024;
 }
 
-// Decode shape for a linear with the norm prologue: the variant covering K
-// in one workgroup with the least waste (as plan_skinny does for M <= 16
-// when K is not split), or splits = 0 when none fits (the caller then
-// normalises separately).
+// Decode shape for a linear with the norm: as plan_skinny for M <= 16 (K
+// split 4 ways over 1024-wide groups for weights with few 16-row tiles,
+// otherwise the variant covering K in one workgroup with the least waste),
+// or splits = 0 when none fits (the caller then normalises separately).
 SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K) {
     struct Rule { int64_t kmax; int ks, nwn, nwk; };
+    if ((N + 15) / 16 < 128 && K >= 2048) {
+        SkinnyPlan p{1, 8, 1, 4, 0, 1, 1};
+        const int idx = find_skinny(p);
+        if (idx >= 0) {
+            p = make_plan(kSkinnyTable[idx], N, K);
+            if (skinny_norm_plan_fits(p, M, K)) return p;
+        }
+    }
     static const Rule rules[] = {{512, 4, 1, 4}, {1024, 8, 1, 4}, {2048, 8, 1, 8}, {4096, 16, 1, 8}, {5120, 20, 1, 8}};
     for (const Rule& r : rules) {
         if (K > r.kmax) continue;
@@ -718,8 +759,7 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
     const int epi = a.epi;
     if (epi < 0 || epi > 3) return hipErrorInvalidValue;
     const bool norm = a.norm != 0;
-    if (norm && (epi > EPI_SWIGLU || p.splits != 1 || !skinny_norm_plan_fits(p, a.M, a.K)))
-        return hipErrorInvalidValue;
+    if (norm && (epi > EPI_SWIGLU || !skinny_norm_plan_fits(p, a.M, a.K))) return hipErrorInvalidValue;
     const SkinnyFn fn = norm ? e->fn_norm[epi] : e->fn[epi];
     if (fn == nullptr) return hipErrorInvalidValue;
     const int slot = norm ? 4 + epi : epi;      // kernel state below is per function

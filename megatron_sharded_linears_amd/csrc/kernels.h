@@ -66,7 +66,7 @@ struct GemmArgs {
     int64_t i_half;     // EPI_SWIGLU
     int t, rank;        // EPI_REDUCE, EPI_REDUCE_ADD
     // norm != 0: the RMSNorm of X's rows with gamma folded into W (decode
-    // kernel, one tile of X in LDS, K not split): y = acc / sqrt(mean_k x^2 + eps).
+    // kernel, one tile of X in LDS): y = acc / sqrt(mean_k x^2 + eps).
     int norm;
     float eps;
     const void* peers[kMaxFusedPeers];
