@@ -235,3 +235,44 @@ def test_attention_validates_before_any_hip_call():
     assert f(A, 4, 4, 1, 128, KC, KC, 64, LN, CT, S) == -2           # caches overlap
     assert f(A, 4, 4, 1, 128, KC, VC, 64, LN, ctypes.c_void_p(0x100000 + 256), S) == -2   # ctx in the K cache
     assert f(A, 0, 4, 1, 128, KC, VC, 64, LN, CT, S) == 0            # B == 0: no-op
+
+
+def test_folded_norm_calls_validate_before_any_hip_call():
+    """The norm-folded decode calls: argument errors before any HIP call;
+    M = 0 is a no-op."""
+    eps = ctypes.c_float(1e-5)
+    f = C.tp_rmsnorm_column_linear          # h, eps, M, K, w_folded, N, bias, y, stream
+    assert f(NULL, eps, 4, 64, B, 32, NULL, Y, S) == -1
+    assert f(A, eps, 4, 60, B, 32, NULL, Y, S) == -4                          # K % 8
+    assert f(MIS, eps, 4, 64, B, 32, NULL, Y, S) == -4
+    assert f(A, ctypes.c_float(-1.0), 4, 64, B, 32, NULL, Y, S) == -6         # eps < 0
+    assert f(A, ctypes.c_float(float("nan")), 4, 64, B, 32, NULL, Y, S) == -6
+    assert f(A, eps, 4, 40000, B, 32, NULL, Y, S) == -2                       # row wider than 32768
+    assert f(A, eps, 4, 64, B, 32, NULL, ctypes.c_void_p(0x10000 + 64), S) == -2   # y overlaps h
+    assert f(A, eps, 0, 64, B, 32, NULL, Y, S) == 0
+    g = C.tp_rmsnorm_column_linear_swiglu   # h, eps, M, K, w_gate_up_folded, i_shard, act, stream
+    assert g(A, eps, 4, 64, B, 0, Y, S) == -2                                 # i_shard <= 0
+    assert g(A, ctypes.c_float(float("inf")), 4, 64, B, 16, Y, S) == -6
+    assert g(NULL, eps, 4, 64, B, 16, Y, S) == -1
+    assert g(A, eps, 0, 64, B, 16, Y, S) == 0
+    h = C.tp_fold_norm_weight               # w, N, K, gamma, w_folded, stream
+    assert h(NULL, 4, 64, B, Y, S) == -1
+    assert h(A, 4, 64, NULL, Y, S) == -1
+    assert h(A, 0, 64, B, Y, S) == -2
+    assert h(A, 4, 60, B, Y, S) == -4
+    assert h(MIS, 4, 64, B, Y, S) == -4
+    assert h(A, 4, 64, B, ctypes.c_void_p(0x10000 + 16), S) == -2             # out overlaps w partly
+    assert h(A, 4, 64, ctypes.c_void_p(0x30000 + 16), Y, S) == -2             # gamma inside out
+    r = C.tp_row_linear_reduce_add          # x, M, K, w, N, partials, t, rank, residual, stream
+    arr = (ctypes.c_void_p * 2)(0, 0x60000)
+    pp = ctypes.cast(arr, lib._ptr_array)
+    assert r(A, 4, 64, B, 32, None, 2, 0, Y, S) == -1
+    assert r(A, 4, 64, B, 32, pp, 0, 0, Y, S) == -6                           # t < 1
+    assert r(A, 4, 64, B, 32, pp, 2, 2, Y, S) == -6                           # rank >= t
+    assert r(A, 4, 64, B, 32, pp, 2, 0, ctypes.c_void_p(0x60000), S) == -2    # residual is a peer's partial
+    assert r(ctypes.c_void_p(0x30000 + 64), 4, 64, B, 32, pp, 2, 0, Y, S) == -2   # x overlaps the residual
+    mis = (ctypes.c_void_p * 2)(0, 0x60008)
+    assert r(A, 4, 64, B, 32, ctypes.cast(mis, lib._ptr_array), 2, 0, Y, S) == -4
+    null_peer = (ctypes.c_void_p * 2)(0, 0)
+    assert r(A, 4, 64, B, 32, ctypes.cast(null_peer, lib._ptr_array), 2, 0, Y, S) == -1
+    assert r(A, 0, 64, B, 32, pp, 2, 0, Y, S) == 0
