@@ -197,3 +197,26 @@ def test_fused_norm_step_matches_oracle_chain():
     assert_close(f64(act), a, "act")
     r64 = r64 + oracle.linear(f64(act), f64(w_d)) + f64(peer_d)
     assert_close(f64(res), r64, "residual after the layer")
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 16032), (16, 4096, 8016), (16, 4096, 3584)])
+def test_rmsnorm_lm_head_persistent_grid(M, K, N):
+    """The LM head with the final norm (the Llama-8B vocab shards of t = 8
+    and t = 16, and gate_up's row count): more row tiles than workgroups, so
+    each workgroup loops over tiles and reuses its first tile's row scales."""
+    key = (SEED, 7, M, K, N)
+    h = I.normal_bf16(key + (0,), (M, K), 2.0)
+    g = gamma(key + (1,), K)
+    w = I.normal_bf16(key + (2,), (N, K), 0.02)
+    wf = folded(w, g)
+    y = empty((M, N))
+    lib.tp_rmsnorm_column_linear(dev(h), EPS, wf, y)
+    assert_close(f64(y), oracle.linear(unit_normed(h), f64(wf)), f"norm + lm_head {(M, K, N)}")
+    # every row tile against the plain linear of the separately normalised rows
+    xn, res = empty((M, K)), dev(h)
+    lib.tp_add_rmsnorm(None, res, dev(g), EPS, xn)
+    y2 = empty((M, N))
+    lib.tp_column_linear(xn, dev(w), y2)
+    d = (f64(y) - f64(y2)).reshape(M, -1, 16)
+    per_tile = np.abs(d).max(axis=(0, 2)) / np.abs(f64(y2)).max()
+    assert per_tile.max() <= 2e-2, f"worst row tile {int(per_tile.argmax())}: {per_tile.max():.3g}"
