@@ -265,8 +265,13 @@ int tp_rmsnorm_column_linear_swiglu(const void* h, float eps, int64_t M, int64_t
  * sequence with lens[b] outside [0, L) gets a zero ctx row and no cache
  * write; ctx: [B, nq d] bf16, head h in columns [h d, (h+1) d) — the rank's
  * o_proj input. d in {32, 64, 128, 256}, nq % nkv == 0, nq / nkv <= 8,
- * L <= 32768, B <= 65535 (TP_ERR_SHAPE otherwise). Uses the stream's
- * workspace (allocated on the first call on a stream). */
+ * L <= 32768, B <= 65535 (TP_ERR_SHAPE otherwise). Two launches on the
+ * stream: one workgroup per (chunk of 192 cache positions, 64 at d = 256;
+ * KV head; sequence) writes a partial record, then the records of each
+ * (sequence, head) are combined in chunk order. The records live in the
+ * stream's 16 MiB workspace (allocated on the first call on a stream):
+ * B nkv ceil(L / chunk) (nq / nkv) (d + 2) floats must fit, TP_ERR_SHAPE
+ * otherwise. */
 int tp_decode_attention(const void* qkv, int64_t B, int nq, int nkv, int head_dim, void* k_cache, void* v_cache,
                         int64_t L, const int32_t* lens, void* ctx, void* stream);
 
