@@ -105,7 +105,8 @@ int launch_linear(const tpk::GemmArgs& a, hipStream_t s, int64_t ws_limit = kWsF
     const int64_t M = a.M, N = a.N, K = a.K;
     hipError_t e;
     if (M <= kSkinnyMaxM) {
-        tpk::SkinnyPlan p = tpk::plan_skinny(M, N, K);
+        tpk::SkinnyPlan p = tpk::plan_skinny(M, N, K, ws_limit);
+        if (p.splits < 1) return TP_ERR_SHAPE;        // no variant's partials fit the workspace
         if (g_force_ksteps > 0) {
             tpk::SkinnyPlan f = p;
             f.ksteps = g_force_ksteps;

@@ -691,7 +691,7 @@ SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K) {
 // (the weight once, the fp32 partial round trip when K is split across
 // workgroups, a quarter weight for X re-reads from L2) divided by how well the
 // grid fills the 256 CUs.
-SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
+SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats) {
     const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     struct Rule { int64_t kmax; int ks, nwn, nwk, xd; };
     auto first_fit = [&](const Rule* rules, int n, SkinnyPlan* out) {
@@ -702,7 +702,7 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
             const int idx = find_skinny(p);
             if (idx < 0 || !skinny_plan_fits(p, M)) continue;
             p = make_plan(kSkinnyTable[idx], N, K);
-            if (p.splits > 1 && (p.splits * M * N > kSkinnyWsFloats || p.ntiles > kSkinnyWsCounters)) continue;
+            if (p.splits > 1 && (p.splits * M * N > ws_floats || p.ntiles > kSkinnyWsCounters)) continue;
             *out = p;
             return true;
         }
@@ -726,12 +726,12 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
         static const Rule rules[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 8, 4, 2, 0}};
         if (first_fit(N <= 1024 ? rules_small_n : N <= 2048 ? rules_mid_n : rules, 3, &chosen)) return chosen;
     }
-    SkinnyPlan best{mt, 8, 4, 2, 0, 1, 1};
+    SkinnyPlan best{mt, 8, 4, 2, 0, 0, 0};   // splits = 0: nothing fits (the caller reports it)
     double best_cost = -1.0;
     for (const SkinnyEntry& e : kSkinnyTable) {
         if (e.mt != mt || e.lds(xrows_for(e, M)) > kMaxLds) continue;
         const SkinnyPlan p = make_plan(e, N, K);
-        if (p.splits > 1 && (p.splits * M * N > kSkinnyWsFloats || p.ntiles > kSkinnyWsCounters)) continue;
+        if (p.splits > 1 && (p.splits * M * N > ws_floats || p.ntiles > kSkinnyWsCounters)) continue;
         if (p.splits > 65535) continue;
         const double wgs = (double)p.ntiles * (double)p.splits;
         double bytes = 2.0 * (double)N * (double)K;

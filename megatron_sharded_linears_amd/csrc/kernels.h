@@ -97,7 +97,9 @@ struct SkinnyPlan {
 constexpr int64_t kSkinnyWsFloats = (int64_t)4 << 20;   // 16 MiB
 constexpr int64_t kSkinnyWsCounters = 65536;
 
-SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K);
+// ws_floats: the workspace floats a K split may use (less than the whole
+// workspace when the caller keeps an operand at its back).
+SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats = kSkinnyWsFloats);
 bool skinny_variant_exists(const SkinnyPlan& p);
 bool skinny_plan_fits(const SkinnyPlan& p, int64_t M);   // LDS need for M tokens within limits
 // The norm prologue's plan (splits == 0: no variant stages whole rows of K

@@ -199,11 +199,13 @@ def test_fused_norm_step_matches_oracle_chain():
     assert_close(f64(res), r64, "residual after the layer")
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 4096, 16032), (16, 4096, 8016), (16, 4096, 3584)])
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 16032), (16, 4096, 8016), (16, 4096, 3584), (64, 4096, 8016)])
 def test_rmsnorm_lm_head_persistent_grid(M, K, N):
     """The LM head with the final norm (the Llama-8B vocab shards of t = 8
     and t = 16, and gate_up's row count): more row tiles than workgroups, so
-    each workgroup loops over tiles and reuses its first tile's row scales."""
+    each workgroup loops over tiles and reuses its first tile's row scales;
+    at 64 tokens the two-launch path, whose staged rows share the workspace
+    with the linear's split-K partials."""
     key = (SEED, 7, M, K, N)
     h = I.normal_bf16(key + (0,), (M, K), 2.0)
     g = gamma(key + (1,), K)
