@@ -35,7 +35,9 @@
  *              library allocates (hipMalloc) on the first such call on that
  *              stream and keeps until the process ends; make one call per
  *              stream before capturing it into a graph. Calls on different
- *              streams never share a workspace.
+ *              streams never share a workspace. It holds 16 MiB: a decode-
+ *              sized linear picks a shape whose split partials fit (or K
+ *              unsplit), and returns TP_ERR_SHAPE if none does.
  *   Errors     Arguments are validated on the host before any HIP call; on
  *              failure a negative tp_status is returned and nothing runs.
  *              M == 0 (or numel == 0) is a valid no-op. A launch failure
