@@ -379,6 +379,26 @@ def time_graph(torch, g, reps, warmup):
     return a.elapsed_time(b) / reps
 
 
+def measure_copy(torch, lib, I, w, reps=10):
+    """HBM bandwidth of a plain streaming copy on this device: the shard copy
+    at t = 1 over the full gate_up weight, a few distinct buffers captured in
+    one graph so that no cache holds them. Context for the roofline fractions
+    (the 8 TB/s peak is the vendor's figure)."""
+    cfg = w.cfg()
+    full = lib.tp_full_shape(cfg, "gate_up")
+    nbytes = full[0] * full[1] * 2
+    n = max(2, min(8, (2 << 30) // (2 * nbytes)))
+    src = [I.device_normal_bf16(full, 1.0, 90 + i, "cuda") for i in range(n)]
+    dst = [torch.empty_like(x) for x in src]
+    ops = [("copy", lib.tp_shard_weights, (cfg, 1, 0, "gate_up", src[i], dst[i])) for i in range(n)]
+    g = capture(torch, ops)
+    ms = time_graph(torch, g, reps, 2)
+    del g, src, dst
+    gbps = 2 * nbytes * n / (ms * 1e-3) / 1e9
+    return {"kernel": "shard_copy_kernel (t = 1, 16-byte vectors)", "bytes_per_launch": 2 * nbytes,
+            "launches": n, "GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def pages_context(w):
     """The traffic the pages estimate for this workload's all-reduces and
     logits all-gather (arithmetic only; the pages measure nothing)."""
@@ -697,6 +717,8 @@ def main():
     us_norm = time_graph(torch, g, args.steps, 2) * 1e3 / (n_norm * max(1, -(-32 // n_norm)))
     del g
 
+    copy = measure_copy(torch, lib, I, w)
+
     flops_step = sum(work[k][0] * work[k][1] for k in gemm_ops)
     value = flops_step / (ms_step * 1e-3) / 1e12
     gemm_us = sum(per_op[k]["us_per_launch"] * work[k][0] for k in gemm_ops)
@@ -769,6 +791,7 @@ def main():
             "ms_per_step": round(ms_layer, 4), "value": round(flops_step / (ms_layer * 1e-3) / 1e12, 3),
             "attention": attn},
         "per_op": per_op,
+        "hbm_copy": copy,
         "wall_s_timed": round(wall_s, 3),
         "pages_context": pages_context(w),
     }
