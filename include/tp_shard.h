@@ -30,14 +30,21 @@
  *              tp_reduce_partials accepts out == partials[0] (in place).
  *   Streams    `stream` is a hipStream_t (NULL = the null stream). Every device
  *              call is asynchronous on it and does not synchronise.
- *   Workspace  The linears may split their K dimension across workgroups.
- *              They then use a per-(device, stream) fp32 workspace that the
- *              library allocates (hipMalloc) on the first such call on that
- *              stream and keeps until the process ends; make one call per
- *              stream before capturing it into a graph. Calls on different
- *              streams never share a workspace. It holds 16 MiB: a decode-
- *              sized linear picks a shape whose split partials fit (or K
- *              unsplit), and returns TP_ERR_SHAPE if none does.
+ *   Workspace  Scratch beyond a call's inputs and outputs (split-K partial
+ *              tiles and their arrival counters, the attention's per-chunk
+ *              records, an operand a fused call's two-launch path stages) is a
+ *              caller-owned device buffer passed as (workspace,
+ *              workspace_bytes); the library allocates nothing and keeps no
+ *              state between calls. Layout: the first TP_WS_COUNTER_BYTES hold
+ *              uint32 arrival counters, which must be zero before the first
+ *              call that uses the buffer (zero-fill it once); every call leaves
+ *              them zero again. The rest holds fp32 scratch and needs no
+ *              initialisation. tp_workspace_bytes() is the size the kernel
+ *              choice is tuned for. A smaller buffer (or NULL with size 0)
+ *              makes the linears keep K within one workgroup, which always
+ *              fits; calls that cannot run without scratch return
+ *              TP_ERR_SHAPE. Calls sharing one workspace must be ordered (one
+ *              stream, or synchronised): two in flight at once race.
  *   Errors     Arguments are validated on the host before any HIP call; on
  *              failure a negative tp_status is returned and nothing runs.
  *              M == 0 (or numel == 0) is a valid no-op. A launch failure
@@ -61,8 +68,7 @@ typedef enum {
     TP_ERR_ALIGNMENT = -4,     /* pointer not 16-byte aligned or a size not % 8     */
     TP_ERR_DTYPE = -5,         /* unknown tp_dtype or weight kind                   */
     TP_ERR_RANGE = -6,         /* t outside [1, 64], rank outside [0, t)            */
-    TP_ERR_HIP = -7,           /* the HIP runtime reported an error                 */
-    TP_ERR_ALLOC = -8          /* the workspace could not be allocated              */
+    TP_ERR_HIP = -7            /* the HIP runtime reported an error                 */
 } tp_status;
 
 typedef enum { TP_BF16 = 0, TP_F32 = 1 } tp_dtype;
@@ -86,6 +92,9 @@ typedef struct {
 } tp_model_cfg;
 
 #define TP_MAX_SHARDS 64
+
+/* Bytes of arrival counters at the front of a workspace (65536 uint32). */
+#define TP_WS_COUNTER_BYTES 262144
 
 /* ------------------------------------------------------------------------
  * Host-only queries. They make no HIP call and work without a GPU.
@@ -115,6 +124,12 @@ int64_t tp_vocab_shard_rows(int64_t vocab, int t);
  * num_kv_head_replicas). */
 int tp_kv_heads_of_rank(const tp_model_cfg* cfg, int t, int rank, int* first, int* count);
 
+/* Workspace size the kernel choice is tuned for: TP_WS_COUNTER_BYTES of
+ * counters plus 16 MiB of fp32 scratch (enough for every split-K plan of a
+ * decode-sized linear and for the decode attention's records at up to
+ * B nkv ceil(L / chunk) (nq / nkv) (d + 2) = 4 Mi floats). */
+int64_t tp_workspace_bytes(void);
+
 /* ------------------------------------------------------------------------
  * Device calls
  * ------------------------------------------------------------------------ */
@@ -137,7 +152,8 @@ int tp_shard_weights(const tp_model_cfg* cfg, int t, int rank, int kind,
  * the rank's slice and is not gathered ([P3 线性层怎么切]: gather_output off;
  * [P1 3.2] Column Parallel). bias_or_null: bf16 [N] or NULL. K % 8 == 0. */
 int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_shard, int64_t N,
-                     const void* bias_or_null, void* y, void* stream);
+                     const void* bias_or_null, void* y, void* workspace, int64_t workspace_bytes,
+                     void* stream);
 
 /* S4. SwiGLU on a rank's fused gate_up output: out[m, j] =
  * silu(gu[m, j]) * gu[m, i_shard + j], silu(g) = g / (1 + e^-g), computed in
@@ -150,7 +166,8 @@ int tp_swiglu(const void* gu, int64_t M, int64_t i_shard, void* out, void* strea
  * `partial_dtype` (TP_BF16 or TP_F32). The partial still needs the sum over
  * ranks ([P1 3.2] Row Parallel; [P2] output_partial). K_shard % 8 == 0. */
 int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard,
-                          int64_t N, void* partial, int partial_dtype, void* stream);
+                          int64_t N, void* partial, int partial_dtype, void* workspace,
+                          int64_t workspace_bytes, void* stream);
 
 /* S6, S8, S9b. Sum of t partial buffers: out = sum_{i=0}^{t-1} partials[i],
  * accumulated in fp32 in the fixed order i = 0, 1, ..., t-1 starting from
@@ -169,22 +186,25 @@ int tp_reduce_partials(const void* const* partials, int t, int64_t numel, int in
  * as tp_column_linear (no bias) followed by tp_swiglu, without writing the
  * [M, 2 i_shard] intermediate. K % 8 == 0; any i_shard >= 1. */
 int tp_column_linear_swiglu(const void* x, int64_t M, int64_t K, const void* w_gate_up, int64_t i_shard,
-                            void* act, void* stream);
+                            void* act, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* S5 + S6 / S7 + S8 in one call: the row-parallel linear of rank `rank`
  * followed by the sum over ranks ([P1 3.2] Row Parallel then [P1 3.1]
  * All-Reduce): out = bf16(sum_{i=0}^{t-1} P_i) accumulated in fp32 in the
- * order i = 0..t-1 from P_0, where P_rank = bf16(x_shard w_shard^T) (the
- * rank's own partial, rounded as a bf16 partial buffer holds it) and P_i
- * (i != rank) = partials[i]. `partials` is a HOST array of t pointers; entry
- * `rank` is ignored (may be NULL), the others are device [M, N] bf16 buffers
- * that must not be `out` (TP_ERR_SHAPE). out: [M, N] bf16. Gives the same bits
- * as tp_row_linear_partial (bf16) into partials[rank] followed by
- * tp_reduce_partials. M <= 64 with t <= 16 and N % 4 == 0 is one launch (the
- * sum is the linear's epilogue); otherwise the own partial is written to
- * `out` and summed in place. */
+ * order i = 0..t-1 from P_0, where P_i (i != rank) = partials[i] and P_rank =
+ * x_shard w_shard^T stored as `partial_dtype` stores it (rounded to bf16 for
+ * TP_BF16, the fp32 sum itself for TP_F32). `partials` is a HOST array of t
+ * pointers; entry `rank` is ignored (may be NULL), the others are device
+ * [M, N] buffers of `partial_dtype` that must not overlap `out`
+ * (TP_ERR_SHAPE). out: [M, N] bf16. Gives the same bits as
+ * tp_row_linear_partial (partial_dtype) into partials[rank] followed by
+ * tp_reduce_partials (bf16 out). M <= 64 with t <= 16 and N % 4 == 0 is one
+ * launch (the sum is the linear's epilogue); otherwise the own partial is
+ * staged (in `out` for TP_BF16, in the workspace for TP_F32: M N 4 bytes of
+ * scratch, TP_ERR_SHAPE if short) and the reducer sums the t buffers. */
 int tp_row_linear_reduce(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
-                         const void* const* partials, int t, int rank, void* out, void* stream);
+                         const void* const* partials, int partial_dtype, int t, int rank, void* out,
+                         void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Residual add and RMSNorm, replicated on every rank ([P1 3.2]: the norm is
  * not split; every rank applies the whole norm to the whole hidden row;
@@ -215,16 +235,17 @@ int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype,
  * rank; [P3 流水线并行]: the residual travels beside hidden_states).
  *
  * tp_row_linear_reduce_add: tp_row_linear_reduce's sum over ranks (the
- * rank's partial x_shard W^T rounded to bf16, summed in fp32 from rank 0 in
- * order, rounded once) added to the residual stream in place:
+ * rank's partial x_shard W^T stored as `partial_dtype` stores it, summed in
+ * fp32 from rank 0 in order, rounded once to bf16) added to the residual
+ * stream in place:
  *   residual[m, n] = bf16(residual[m, n] + that sum)
- * — the same bits as tp_row_linear_reduce into a buffer followed by
+ * - the same bits as tp_row_linear_reduce into a buffer followed by
  * tp_reduce_add_rmsnorm's residual update. `partials` as in
- * tp_row_linear_reduce (host array of t device pointers, slot `rank`
- * ignored); none may overlap residual ([M, N] bf16). One launch when
- * M <= 64, t <= 16 and N % 4 == 0; otherwise two (the rank's partial is
- * staged in the stream's 16 MiB workspace; then N % 8 == 0, N <= 32768
- * and M N 2 bytes <= 16 MiB, TP_ERR_SHAPE otherwise).
+ * tp_row_linear_reduce (host array of t device pointers of `partial_dtype`,
+ * slot `rank` ignored); none may overlap residual ([M, N] bf16). One launch
+ * when M <= 64, t <= 16 and N % 4 == 0; otherwise two (the rank's partial is
+ * staged in the workspace: M N 2 or 4 bytes of scratch; then N % 8 == 0 and
+ * N <= 32768, TP_ERR_SHAPE otherwise).
  *
  * tp_fold_norm_weight (load time, like tp_shard_weights): the norm's gamma
  * folded into the next linear's weight, w_folded[n, k] = bf16(w[n, k] *
@@ -241,16 +262,19 @@ int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype,
  * M <= 16 (the decode kernel, K split across workgroups as the plain linear
  * would be, or whole rows of K <= 5120 in one): the sums of squares come
  * from the diagonal of h h^T on the matrix cores and r scales the outputs. Otherwise two: tp_add_rmsnorm's kernel (unit weights)
- * writes bf16(h r) into the stream's 16 MiB workspace (M K 2 bytes must fit,
+ * writes bf16(h r) into the workspace (M K 2 bytes of scratch must fit,
  * TP_ERR_SHAPE otherwise), then the plain linear reads it. y / act must not
  * overlap h (TP_ERR_SHAPE). */
 int tp_fold_norm_weight(const void* w, int64_t N, int64_t K, const void* gamma, void* w_folded, void* stream);
 int tp_row_linear_reduce_add(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
-                             const void* const* partials, int t, int rank, void* residual, void* stream);
+                             const void* const* partials, int partial_dtype, int t, int rank, void* residual,
+                             void* workspace, int64_t workspace_bytes, void* stream);
 int tp_rmsnorm_column_linear(const void* h, float eps, int64_t M, int64_t K, const void* w_folded, int64_t N,
-                             const void* bias_or_null, void* y, void* stream);
+                             const void* bias_or_null, void* y, void* workspace, int64_t workspace_bytes,
+                             void* stream);
 int tp_rmsnorm_column_linear_swiglu(const void* h, float eps, int64_t M, int64_t K, const void* w_gate_up_folded,
-                                    int64_t i_shard, void* act, void* stream);
+                                    int64_t i_shard, void* act, void* workspace, int64_t workspace_bytes,
+                                    void* stream);
 
 /* One decode step of the rank's grouped-query attention, with the KV-cache
  * append ([P2 前向执行的实际流程] Step 2: each rank computes attention for its
@@ -271,11 +295,11 @@ int tp_rmsnorm_column_linear_swiglu(const void* h, float eps, int64_t M, int64_t
  * stream: one workgroup per (chunk of 192 cache positions, 64 at d = 256;
  * KV head; sequence) writes a partial record, then the records of each
  * (sequence, head) are combined in chunk order. The records live in the
- * stream's 16 MiB workspace (allocated on the first call on a stream):
- * B nkv ceil(L / chunk) (nq / nkv) (d + 2) floats must fit, TP_ERR_SHAPE
- * otherwise. */
+ * workspace's scratch: B nkv ceil(L / chunk) (nq / nkv) (d + 2) floats must
+ * fit (TP_ERR_SHAPE otherwise; the counters are not used). */
 int tp_decode_attention(const void* qkv, int64_t B, int nq, int nkv, int head_dim, void* k_cache, void* v_cache,
-                        int64_t L, const int32_t* lens, void* ctx, void* stream);
+                        int64_t L, const int32_t* lens, void* ctx, void* workspace, int64_t workspace_bytes,
+                        void* stream);
 
 /* S9a. Vocab-parallel embedding, one shard's contribution: for each token m,
  * out[m, :] = e_shard[ids[m] - rank Vs, :] when rank Vs <= ids[m] <
@@ -293,7 +317,8 @@ int tp_vocab_embed(const int32_t* ids, int64_t M, const void* e_shard, int64_t v
  * give zero logits. Only sampled positions are passed in ([P3 线性层怎么切]:
  * each card computes V/t logits for the positions to be sampled). */
 int tp_lm_head_shard(const void* h, int64_t M, int64_t K, const void* w_lm_shard, int64_t v_shard,
-                     void* logits_shard, int out_dtype, void* stream);
+                     void* logits_shard, int out_dtype, void* workspace, int64_t workspace_bytes,
+                     void* stream);
 
 /* S11. Concatenate t shard logits in vocab order and drop the padding:
  * out[m, r v_shard + j] = shard_logits[r][m, j] for r v_shard + j < vocab
@@ -304,33 +329,74 @@ int tp_concat_logits(const void* const* shard_logits, int t, int64_t M, int64_t 
                      int64_t vocab, int dtype, void* out, void* stream);
 
 /* ------------------------------------------------------------------------
- * Tuning
+ * Every linear through one call, with an explicit kernel plan
  * ------------------------------------------------------------------------ */
 
-/* Override the shape of the decode-sized (M <= 64) linear kernel for every
- * later call in this process: `ksteps` 32-wide k steps per wave, `nwn` waves
- * along the output rows (16 rows each) and `nwk` waves along K per
- * workgroup; K is split across as many workgroups as it takes to cover it.
- * `x_direct` = 1 makes each wave load its activation fragments from global
- * memory instead of sharing a copy staged in LDS. (0, 0, 0, 0) restores the
- * automatic choice. Returns TP_ERR_SHAPE if no such
- * kernel variant is built. A shape whose X chunk does not fit in LDS for a
- * given M, or whose split partials do not fit the workspace, keeps the
- * automatic choice for that call. Results are the same up
- * to fp32 summation order. */
-int tp_tune_skinny(int ksteps, int nwn, int nwk, int x_direct);
+/* Epilogue of a linear (tp_linear_call.epilogue). */
+typedef enum {
+    TP_EPI_STORE = 0,       /* y = x w^T (+ bias), stored as out_dtype: tp_column_linear,
+                               tp_row_linear_partial, tp_lm_head_shard                        */
+    TP_EPI_SWIGLU = 1,      /* w holds 2 n rows [gate | up], y = SwiGLU, [M, n] bf16:
+                               tp_column_linear_swiglu                                        */
+    TP_EPI_REDUCE = 2,      /* y = the sum over ranks: tp_row_linear_reduce                   */
+    TP_EPI_REDUCE_ADD = 3   /* y (the residual) += the sum over ranks: tp_row_linear_reduce_add */
+} tp_epilogue;
 
-/* Force the kernel of the prefill-sized (M > 64) linear for every later
- * call (-1 restores the automatic choice; TP_ERR_RANGE for an unknown index):
- * 0, 1, 2 = direct-to-LDS kernels with 32-wide k-tiles and 256 x 256,
- * 256 x 128, 128 x 128 tiles (weight rows x tokens) on 4 waves; 4, 5, 6 = the
- * same tiles on 8 waves; 7 = 192 x 128 tiles on 4 waves; 8, 9, 10 = 256 x 256,
- * 256 x 128, 128 x 128 tiles on 8 waves with 64-wide k-tiles (K % 64 == 0),
- * 11 = 192 x 128 tiles likewise;
- * 3 = register-staged 128 x 128 tiles, the only one that takes K % 32 != 0.
- * A forced kernel whose K multiple a call does not meet keeps the automatic
- * choice for that call. */
-int tp_tune_tiled(int variant);
+/* Which kernel shape runs a linear. A zero-filled plan is the automatic
+ * choice the named calls make. decode_* (M <= 64; all zero = automatic):
+ * the decode kernel with `decode_ksteps` 32-wide k steps per wave,
+ * `decode_nwn` waves along the output rows (16 rows each), `decode_nwk` waves
+ * along K per workgroup, K split across as many workgroups as it takes to
+ * cover it, and `decode_x_direct` = 1 to load activation fragments per wave
+ * instead of staging them in LDS. prefill_tile (M > 64; 0 = automatic, v + 1
+ * = kernel v): 0, 1, 2 = 256 x 256, 256 x 128, 128 x 128 tiles (weight rows x
+ * tokens) with 32-wide k-tiles on 4 waves; 4, 5, 6 the same on 8 waves;
+ * 7 = 192 x 128 on 4 waves; 8, 9, 10 = 256 x 256, 256 x 128, 128 x 128 on
+ * 8 waves with 64-wide k-tiles (K % 64 == 0); 11 = 192 x 128 likewise;
+ * 3 = register-staged 128 x 128 (any K % 8). A decode shape that is not built
+ * for any token count, or a prefill_tile outside [0, 12], is TP_ERR_RANGE. A
+ * plan this call cannot run (the shape not built for its token count, an X
+ * chunk beyond LDS, split partials beyond the workspace, a K multiple not
+ * met) is replaced by the automatic choice; results then differ only in the
+ * fp32 summation order. */
+typedef struct {
+    int32_t decode_ksteps, decode_nwn, decode_nwk, decode_x_direct;
+    int32_t prefill_tile;
+} tp_linear_plan;
+
+/* Arguments of tp_linear_ex. Every field has the meaning, layout and checks
+ * of the named call the epilogue (and `norm`) selects:
+ *   x [M, K] bf16; w [N, K] bf16 (TP_EPI_SWIGLU: [2 n, K] with n = N);
+ *   bias [N] bf16 or NULL (TP_EPI_STORE only); y [M, N] of out_dtype
+ *   (TP_EPI_SWIGLU: [M, n] bf16; TP_EPI_REDUCE_ADD: the residual, in place);
+ *   partials / partial_dtype / t / rank: the other ranks' partials (host
+ *   array, slot rank ignored) for the two reduce epilogues;
+ *   norm = 1 with eps: x's rows RMS-normalised, gamma folded into w
+ *   (tp_rmsnorm_column_linear(_swiglu); TP_EPI_STORE and TP_EPI_SWIGLU only);
+ *   plan: the kernel shape (tp_linear_plan); workspace as for every call. */
+typedef struct {
+    const void* x;
+    int64_t M, K;
+    const void* w;
+    int64_t N;
+    const void* bias;
+    void* y;
+    int32_t out_dtype;
+    int32_t epilogue;
+    const void* const* partials;
+    int32_t partial_dtype, t, rank;
+    int32_t norm;
+    float eps;
+    tp_linear_plan plan;
+    void* workspace;
+    int64_t workspace_bytes;
+} tp_linear_call;
+
+/* Run the linear `call` describes on `stream`: what the named call of its
+ * epilogue computes, with the kernel shape of call->plan. For sweeps and
+ * for tests that run every kernel variant; the named calls are this call
+ * with the automatic plan. */
+int tp_linear_ex(const tp_linear_call* call, void* stream);
 
 #ifdef __cplusplus
 }

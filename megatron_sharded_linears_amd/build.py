@@ -1,9 +1,12 @@
 """Build libtpshard.so in-tree with hipcc, for gfx950 only.
 
-    python -m megatron_sharded_linears_amd.build
+    python -m megatron_sharded_linears_amd.build            # the library
+    python -m megatron_sharded_linears_amd.build sanitized  # + the host ABI layer under ASan/UBSan
 
-Each source compiles to an object in parallel; the objects link into
-megatron_sharded_linears_amd/libtpshard.so next to this file.
+Each source compiles to an object in parallel under _build/ at the repository
+root; the objects link into megatron_sharded_linears_amd/libtpshard.so next
+to this file. Builds with extra -D flags (tuning) and the sanitized build keep
+their objects and libraries under _build/ too, never beside the sources.
 """
 
 import concurrent.futures
@@ -18,9 +21,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
 
-SOURCES = ["abi.cpp", "memops.hip", "gemm_skinny.hip", "gemm_tiled.hip", "attention.hip"]
+KERNEL_SOURCES = ["memops.hip", "gemm_skinny.hip", "gemm_tiled.hip", "attention.hip"]
+SOURCES = ["abi.cpp"] + KERNEL_SOURCES
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     # never emit packed fp32 arithmetic (v_pk_add/mul/fma_f32)
@@ -30,39 +35,78 @@ FLAGS = [
 ]
 
 
-def _compile(job):
-    src, build_dir, defines = job
-    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _run(cmd, what):
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+        raise RuntimeError(f"{what} failed:\n{err}")
     if err.strip():
         sys.stderr.write(err + "\n")
+
+
+def _compile(job):
+    src, build_dir, defines = job
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + ["-c", os.path.join(CSRC, src), "-o", obj]
+    _run(cmd, f"hipcc on {src}")
     return obj
+
+
+def _objects(build_dir, defines, sources):
+    os.makedirs(build_dir, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
+        return list(ex.map(_compile, [(src, build_dir, tuple(defines)) for src in sources]))
 
 
 def build(verbose=True, lib=None, defines=()):
     """Compile every source and link `lib` (default: the in-tree library).
-    `defines` are extra -D flags, for tuning builds kept outside the tree."""
+    `defines` are extra -D flags, for tuning builds (objects in _build/<tag>)."""
     lib = lib or LIB
-    build_dir = BUILD if not defines else BUILD + "_" + "_".join(d.replace("=", "") for d in defines)
-    os.makedirs(build_dir, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, [(src, build_dir, tuple(defines)) for src in SOURCES]))
+    tag = "obj" if not defines else "_".join(d.replace("=", "") for d in defines)
+    objs = _objects(os.path.join(BUILD, tag), defines, SOURCES)
     tmp = lib + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stderr)
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, "link")
     os.replace(tmp, lib)
     if verbose:
         print(f"built {lib}")
     return lib
 
 
+def build_sanitized(verbose=True):
+    """The library with its host-side ABI layer (abi.cpp: validation, kernel
+    choice, dispatch) compiled by g++ under AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the same gfx950 kernel objects as
+    the in-tree library (built if missing). GPU code is not instrumented. Load
+    it with gcc's libasan preloaded (LD_PRELOAD) and TPSHARD_LIB pointing at
+    the returned path."""
+    out_dir = os.path.join(BUILD, "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    kdir = os.path.join(BUILD, "obj")
+    kobjs = [os.path.join(kdir, s + ".o") for s in KERNEL_SOURCES]
+    if not all(os.path.exists(o) for o in kobjs):
+        kobjs = _objects(kdir, (), KERNEL_SOURCES)
+    abi_obj = os.path.join(out_dir, "abi.cpp.o")
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+    _run(["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(ROCM, "include"), "-I", INCLUDE, "-I", CSRC] + san +
+         ["-c", os.path.join(CSRC, "abi.cpp"), "-o", abi_obj], "g++ (sanitized abi.cpp)")
+    lib = os.path.join(out_dir, "libtpshard_asan.so")
+    _run(["g++", "-shared", "-o", lib + ".tmp", abi_obj] + kobjs + san +
+         ["-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(ROCM, "lib")], "sanitized link")
+    os.replace(lib + ".tmp", lib)
+    if verbose:
+        print(f"built {lib}")
+    return lib
+
+
+def asan_runtime():
+    """Path of gcc's AddressSanitizer runtime, to preload."""
+    return subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+
+
 if __name__ == "__main__":
     build()
+    if len(sys.argv) > 1 and sys.argv[1] == "sanitized":
+        build_sanitized()

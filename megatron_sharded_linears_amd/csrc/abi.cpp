@@ -1,17 +1,15 @@
-// C ABI of libtpshard: host-side validation, shape queries, workspace
-// management and dispatch to the gfx950 kernels. Every entry point checks its
-// arguments before making any HIP call, so argument errors are reported (and
-// testable) without a GPU. No C++ exception escapes: each entry point catches
-// everything and maps it to a tp_status.
+// C ABI of libtpshard: host-side validation, shape queries, kernel choice and
+// dispatch to the gfx950 kernels. Every entry point checks its arguments
+// before making any HIP call, so argument errors are reported (and testable)
+// without a GPU. The library allocates no memory and keeps no state between
+// calls beyond caches of kernel attributes: scratch is the caller's workspace
+// argument. No C++ exception escapes: each entry point catches everything and
+// maps it to a tp_status.
 #include <hip/hip_runtime.h>
 
-#include <algorithm>
-#include <cstdint>
 #include <cmath>
+#include <cstdint>
 #include <cstring>
-#include <map>
-#include <mutex>
-#include <utility>
 
 #include "kernels.h"
 #include "layer_ops.h"
@@ -21,9 +19,20 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // sizes must fit the kernels' int ranges
 constexpr int64_t kSkinnyMaxM = 64;
+constexpr int64_t kMaxNormWidth = 32768;        // one workgroup holds a whole row in registers
+constexpr int64_t kWsCounters = TP_WS_COUNTER_BYTES / 4;
+static_assert(kWsCounters == tpk::kSkinnyWsCounters, "workspace counters");
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool dtype_ok(int d) { return d == TP_BF16 || d == TP_F32; }
+int64_t dtype_bytes(int d) { return d == TP_F32 ? 4 : 2; }
+
+// Byte ranges [a, a + na) and [b, b + nb) intersect (empty ranges never do).
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    if (a == nullptr || b == nullptr || na <= 0 || nb <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
 
 int check_cfg(const tp_model_cfg* c, int t) {
     if (c == nullptr) return TP_ERR_NULL;
@@ -54,110 +63,287 @@ void kv_of_rank(const tp_model_cfg* c, int t, int rank, int* first, int* count) 
 
 // --------------------------------------------------------------- workspace
 
-constexpr int64_t kWsFloats = tpk::kSkinnyWsFloats;
-constexpr int64_t kWsCounters = tpk::kSkinnyWsCounters;
-
-struct StreamWs {
-    float* partials = nullptr;
-    unsigned* counters = nullptr;
-};
-
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, StreamWs> g_ws;
-
-int get_workspace(hipStream_t s, tpk::Workspace* out) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return TP_ERR_HIP;
-    std::lock_guard<std::mutex> lock(g_ws_mu);
-    StreamWs& w = g_ws[std::make_pair(dev, s)];
-    if (w.partials == nullptr) {
-        void* p = nullptr;
-        void* c = nullptr;
-        if (hipMalloc(&p, kWsFloats * sizeof(float)) != hipSuccess) return TP_ERR_ALLOC;
-        if (hipMalloc(&c, kWsCounters * sizeof(unsigned)) != hipSuccess) {
-            (void)hipFree(p);
-            return TP_ERR_ALLOC;
-        }
-        if (hipMemset(c, 0, kWsCounters * sizeof(unsigned)) != hipSuccess) {
-            (void)hipFree(p);
-            (void)hipFree(c);
-            return TP_ERR_HIP;
-        }
-        w.partials = static_cast<float*>(p);
-        w.counters = static_cast<unsigned*>(c);
-    }
-    out->partials = w.partials;
-    out->partial_floats = kWsFloats;
-    out->counters = w.counters;
+// The caller's workspace: counters at the front, fp32 scratch after them.
+// A buffer shorter than the counters offers nothing.
+int view_workspace(void* ws, int64_t bytes, tpk::Workspace* out) {
+    *out = tpk::Workspace{nullptr, 0, nullptr, 0};
+    if (bytes < 0) return TP_ERR_SHAPE;
+    if (bytes == 0) return TP_OK;
+    if (ws == nullptr) return TP_ERR_NULL;
+    if (!aligned16(ws)) return TP_ERR_ALIGNMENT;
+    if (bytes < TP_WS_COUNTER_BYTES) return TP_OK;
+    out->counters = static_cast<unsigned*>(ws);
     out->num_counters = kWsCounters;
+    out->partials = reinterpret_cast<float*>(static_cast<char*>(ws) + TP_WS_COUNTER_BYTES);
+    out->partial_floats = (bytes - TP_WS_COUNTER_BYTES) / 4;
     return TP_OK;
 }
 
-// A process-wide override of the decode kernel's shape, for tuning and for
-// tests that exercise every variant. Zero means automatic.
-int g_force_ksteps = 0, g_force_nwn = 0, g_force_nwk = 0, g_force_xd = 0;
+// Whole 256-byte units at the back of the workspace's scratch for an operand
+// a two-launch path stages; `front` keeps the rest for the linear's own
+// split-K partials.
+int workspace_back(const tpk::Workspace& ws, int64_t bytes, void** out, tpk::Workspace* front) {
+    const int64_t floats = (bytes + 255) / 256 * 64;
+    if (floats > ws.partial_floats) return TP_ERR_SHAPE;
+    *out = ws.partials + (ws.partial_floats - floats);
+    *front = ws;
+    front->partial_floats = ws.partial_floats - floats;
+    return TP_OK;
+}
 
-// Launch one validated linear. a.N is the kernel's row space (for EPI_SWIGLU
-// on the decode kernel: 16-row blocks of 8 gate and 8 up rows).
-// ws_limit: floats of the stream workspace's front a split-K plan may use
-// (the rest may hold an operand the caller staged at the back).
-int launch_linear(const tpk::GemmArgs& a, hipStream_t s, int64_t ws_limit = kWsFloats) {
-    const int64_t M = a.M, N = a.N, K = a.K;
-    hipError_t e;
-    if (M <= kSkinnyMaxM) {
-        tpk::SkinnyPlan p = tpk::plan_skinny(M, N, K, ws_limit);
-        if (p.splits < 1) return TP_ERR_SHAPE;        // no variant's partials fit the workspace
-        if (g_force_ksteps > 0) {
-            tpk::SkinnyPlan f = p;
-            f.ksteps = g_force_ksteps;
-            f.nwn = g_force_nwn;
-            f.nwk = g_force_nwk;
-            f.xd = g_force_xd;
-            f.ntiles = (N + 16LL * f.nwn - 1) / (16LL * f.nwn);
-            const int64_t gk = 32LL * f.ksteps * f.nwk;
-            f.splits = (int)((K + gk - 1) / gk);
-            // a forced shape that does not fit this M (LDS) or the workspace
-            // keeps the automatic plan
-            const bool fits = f.splits == 1 || (tpk::skinny_workspace_floats(f, M, N) <= ws_limit &&
-                                                f.ntiles <= kWsCounters && f.splits <= 65535);
-            if (tpk::skinny_variant_exists(f) && tpk::skinny_plan_fits(f, M) && fits) p = f;
-        }
-        tpk::Workspace ws{nullptr, 0, nullptr, 0};
-        if (p.splits > 1) {
-            const int st = get_workspace(s, &ws);
-            if (st != TP_OK) return st;
-            if (tpk::skinny_workspace_floats(p, M, N) > std::min(ws.partial_floats, ws_limit) ||
-                p.ntiles > ws.num_counters)
-                return TP_ERR_SHAPE;
-        }
-        e = tpk::launch_skinny(a, p, ws, s);
-    } else {
-        e = tpk::launch_tiled(a, s);
+// ------------------------------------------------------------- kernel choice
+
+bool plan_is_auto_decode(const tp_linear_plan& p) {
+    return p.decode_ksteps == 0 && p.decode_nwn == 0 && p.decode_nwk == 0;
+}
+
+// The plan's decode shape exists for some token count, and prefill_tile is
+// in range; otherwise TP_ERR_RANGE.
+int check_plan(const tp_linear_plan& p) {
+    if (p.prefill_tile < 0 || p.prefill_tile > tpk::tiled_variant_count()) return TP_ERR_RANGE;
+    if (plan_is_auto_decode(p)) return TP_OK;
+    for (int mt : {1, 2, 4}) {
+        const tpk::SkinnyPlan sp{mt, p.decode_ksteps, p.decode_nwn, p.decode_nwk, p.decode_x_direct ? 1 : 0, 1, 1};
+        if (tpk::skinny_variant_exists(sp)) return TP_OK;
     }
-    return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+    return TP_ERR_RANGE;
 }
 
-int check_linear(const void* x, int64_t M, int64_t K, const void* w, int64_t N, const void* y) {
-    if (x == nullptr || w == nullptr || y == nullptr) return TP_ERR_NULL;
-    if (M < 0 || N <= 0 || K <= 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return TP_ERR_SHAPE;
-    if (K % 8 != 0) return TP_ERR_ALIGNMENT;
-    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return TP_ERR_ALIGNMENT;
-    return TP_OK;
+bool split_fits(const tpk::SkinnyPlan& p, int64_t M, int64_t N, const tpk::Workspace& ws, int64_t extra_floats) {
+    if (p.splits <= 1) return true;
+    return p.splits <= 65535 && tpk::skinny_workspace_floats(p, M, N) + extra_floats <= ws.partial_floats &&
+           p.ntiles <= ws.num_counters;
 }
 
-int run_linear(const void* x, int64_t M, int64_t K, const void* w, int64_t N, const void* bias,
-               void* y, int out_dtype, void* stream) {
-    const int st = check_linear(x, M, K, w, N, y);
+// Decode-kernel plan for a linear of M <= 64 tokens given the workspace;
+// false when no decode variant fits (then the prefill kernel, which needs no
+// scratch, or a two-launch path runs instead).
+bool decode_plan(int64_t M, int64_t N, int64_t K, const tpk::Workspace& ws, const tp_linear_plan& over,
+                 tpk::SkinnyPlan* out) {
+    tpk::SkinnyPlan p = tpk::plan_skinny(M, N, K, ws.partial_floats, ws.num_counters);
+    if (p.splits < 1) return false;
+    if (!plan_is_auto_decode(over)) {
+        tpk::SkinnyPlan f = p;
+        f.ksteps = over.decode_ksteps;
+        f.nwn = over.decode_nwn;
+        f.nwk = over.decode_nwk;
+        f.xd = over.decode_x_direct ? 1 : 0;
+        f.ntiles = (N + 16LL * f.nwn - 1) / (16LL * f.nwn);
+        const int64_t gk = 32LL * f.ksteps * f.nwk;
+        f.splits = (int)((K + gk - 1) / gk);
+        if (tpk::skinny_variant_exists(f) && tpk::skinny_plan_fits(f, M) && split_fits(f, M, N, ws, 0)) p = f;
+    }
+    *out = p;
+    return true;
+}
+
+// With the norm prologue (M <= 16, whole rows of X in LDS): the plan or false.
+bool decode_norm_plan(int64_t M, int64_t N, int64_t K, const tpk::Workspace& ws, const tp_linear_plan& over,
+                      tpk::SkinnyPlan* out) {
+    if (M > 16) return false;
+    tpk::SkinnyPlan p = tpk::plan_skinny_norm(M, N, K, ws.partial_floats, ws.num_counters);
+    if (!plan_is_auto_decode(over)) {
+        tpk::SkinnyPlan f{1, over.decode_ksteps, over.decode_nwn, over.decode_nwk, over.decode_x_direct ? 1 : 0, 1, 1};
+        f.ntiles = (N + 16LL * f.nwn - 1) / (16LL * f.nwn);
+        const int64_t gk = 32LL * f.ksteps * f.nwk;
+        f.splits = (int)((K + gk - 1) / gk);
+        if (tpk::skinny_norm_plan_fits(f, M, K) &&
+            split_fits(f, M, N, ws, (int64_t)f.splits * f.ntiles * 16))
+            p = f;
+    }
+    if (p.splits < 1) return false;
+    *out = p;
+    return true;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
+
+// One validated linear without the norm (EPI_STORE or EPI_SWIGLU, or a reduce
+// epilogue whose decode plan the caller has checked). a.N is the kernel's row
+// space for EPI_SWIGLU on the decode kernel (16-row blocks of 8 gate and 8
+// up rows) and 2 i_half on the prefill kernel; this sets it.
+int launch_linear(tpk::GemmArgs a, const tpk::Workspace& ws, const tp_linear_plan& over, hipStream_t s) {
+    const bool swiglu = a.epi == tpk::EPI_SWIGLU;
+    if (a.M <= kSkinnyMaxM) {
+        const int64_t n_rows = swiglu ? 16 * ((a.i_half + 7) / 8) : a.N;
+        tpk::SkinnyPlan p;
+        if (decode_plan(a.M, n_rows, a.K, ws, over, &p)) {
+            a.N = n_rows;
+            return hip_status(tpk::launch_skinny(a, p, ws, s));
+        }
+        if (tpk::epi_is_reduce(a.epi)) return TP_ERR_SHAPE;
+    }
+    if (swiglu) a.N = 2 * a.i_half;
+    return hip_status(tpk::launch_tiled(a, s, over.prefill_tile - 1));
+}
+
+// The linear on RMS-normalised rows of a.x (unit weights: gamma is folded
+// into a.w). One launch when the decode kernel can stage whole rows;
+// otherwise the norm writes the normalised rows to the workspace and the
+// plain linear reads them.
+int launch_norm_linear(tpk::GemmArgs a, const tpk::Workspace& ws, const tp_linear_plan& over, hipStream_t s) {
+    const int64_t n_rows = a.epi == tpk::EPI_SWIGLU ? 16 * ((a.i_half + 7) / 8) : a.N;
+    tpk::SkinnyPlan p;
+    if (a.M <= kSkinnyMaxM && decode_norm_plan(a.M, n_rows, a.K, ws, over, &p)) {
+        a.N = n_rows;
+        return hip_status(tpk::launch_skinny(a, p, ws, s));
+    }
+    void* xn = nullptr;
+    tpk::Workspace front;
+    const int st = workspace_back(ws, a.M * a.K * 2, &xn, &front);
     if (st != TP_OK) return st;
-    if (!dtype_ok(out_dtype)) return TP_ERR_DTYPE;
-    if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 1u)) return TP_ERR_ALIGNMENT;
-    if (M == 0) return TP_OK;
+    tpk::PartialPtrs none;
+    std::memset(&none, 0, sizeof(none));
+    const hipError_t e =
+        tpk::launch_add_rmsnorm(none, 0, TP_BF16, a.M, a.K, const_cast<void*>(a.x), nullptr, a.eps, xn, s);
+    if (e != hipSuccess) return TP_ERR_HIP;
+    a.x = xn;
+    a.norm = 0;
+    return launch_linear(a, front, over, s);
+}
+
+// The reduce epilogues: one launch when the decode kernel can sum the peers
+// in its epilogue, otherwise the rank's partial is staged and summed by the
+// reducer (EPI_REDUCE) or the add kernel (EPI_REDUCE_ADD), with the same
+// arithmetic.
+int launch_reduce_linear(tpk::GemmArgs a, const void* const* partials, int partial_dtype, const tpk::Workspace& ws,
+                         const tp_linear_plan& over, hipStream_t s) {
+    const bool add = a.epi == tpk::EPI_REDUCE_ADD;
+    const bool f32 = partial_dtype == TP_F32;
+    tpk::SkinnyPlan p;
+    if (a.M <= kSkinnyMaxM && a.t <= tpk::kMaxFusedPeers && a.N % 4 == 0 &&
+        decode_plan(a.M, a.N, a.K, ws, over, &p)) {
+        a.epi = add ? (f32 ? tpk::EPI_REDUCE_ADD_F32 : tpk::EPI_REDUCE_ADD) : (f32 ? tpk::EPI_REDUCE_F32 : tpk::EPI_REDUCE);
+        return hip_status(tpk::launch_skinny(a, p, ws, s));
+    }
+    const int64_t own_bytes = a.M * a.N * dtype_bytes(partial_dtype);
+    if (add && (a.N % 8 != 0 || a.N > kMaxNormWidth)) return TP_ERR_SHAPE;
+    void* own = a.y;                  // EPI_REDUCE with bf16 partials: staged in `out`, summed in place
+    tpk::Workspace front = ws;
+    if (add || f32) {
+        const int st = workspace_back(ws, own_bytes, &own, &front);
+        if (st != TP_OK) return st;
+    }
+    void* const out = a.y;
+    tpk::GemmArgs b = a;
+    b.y = own;
+    b.epi = tpk::EPI_STORE;
+    b.out_dtype = partial_dtype;
+    b.bias = nullptr;
+    const int st = launch_linear(b, front, over, s);
+    if (st != TP_OK) return st;
+    tpk::PartialPtrs ptrs;
+    std::memset(&ptrs, 0, sizeof(ptrs));
+    for (int i = 0; i < a.t; ++i) ptrs.p[i] = i == a.rank ? own : partials[i];
+    if (add)
+        return hip_status(
+            tpk::launch_add_rmsnorm(ptrs, a.t, partial_dtype, a.M, a.N, out, nullptr, 0.0f, nullptr, s));
+    return hip_status(tpk::launch_reduce(ptrs, a.t, a.M * a.N, partial_dtype, out, TP_BF16, s));
+}
+
+// Validate and run one linear (every named linear call and tp_linear_ex).
+int linear_call(const tp_linear_call& c, hipStream_t s) {
+    if (c.x == nullptr || c.w == nullptr || c.y == nullptr) return TP_ERR_NULL;
+    if (c.M < 0 || c.N <= 0 || c.K <= 0 || c.M >= kMaxDim || c.N >= kMaxDim / 2 || c.K >= kMaxDim) return TP_ERR_SHAPE;
+    if (c.epilogue < TP_EPI_STORE || c.epilogue > TP_EPI_REDUCE_ADD) return TP_ERR_DTYPE;
+    if (c.K % 8 != 0) return TP_ERR_ALIGNMENT;
+    if (!aligned16(c.x) || !aligned16(c.w) || !aligned16(c.y)) return TP_ERR_ALIGNMENT;
+    if (!dtype_ok(c.out_dtype)) return TP_ERR_DTYPE;
+    int st = check_plan(c.plan);
+    if (st != TP_OK) return st;
+    const bool store = c.epilogue == TP_EPI_STORE, swiglu = c.epilogue == TP_EPI_SWIGLU;
+    const bool reduce = c.epilogue == TP_EPI_REDUCE || c.epilogue == TP_EPI_REDUCE_ADD;
+    if (!store && c.out_dtype != TP_BF16) return TP_ERR_DTYPE;
+    if (c.bias != nullptr) {
+        if (!store) return TP_ERR_SHAPE;
+        if (reinterpret_cast<uintptr_t>(c.bias) & 1u) return TP_ERR_ALIGNMENT;
+    }
+    // byte extents: w holds 2 N rows [gate | up] for SwiGLU, y is [M, N]
+    const int64_t x_bytes = c.M * c.K * 2, w_bytes = (swiglu ? 2 : 1) * c.N * c.K * 2;
+    const int64_t y_bytes = c.M * c.N * dtype_bytes(c.out_dtype), b_bytes = c.N * 2;
+    if (overlap(c.y, y_bytes, c.x, x_bytes) || overlap(c.y, y_bytes, c.w, w_bytes) ||
+        overlap(c.y, y_bytes, c.bias, b_bytes))
+        return TP_ERR_SHAPE;
+    if (c.norm != 0) {
+        if (reduce) return TP_ERR_SHAPE;
+        if (!(c.eps >= 0.0f) || !std::isfinite(c.eps)) return TP_ERR_RANGE;
+        if (c.K > kMaxNormWidth) return TP_ERR_SHAPE;
+    }
     tpk::GemmArgs a{};
-    a.x = x; a.w = w; a.bias = bias; a.y = y;
-    a.M = M; a.N = N; a.K = K;
-    a.out_dtype = out_dtype;
-    a.epi = tpk::EPI_STORE;
-    return launch_linear(a, static_cast<hipStream_t>(stream));
+    if (reduce) {
+        if (c.partials == nullptr) return TP_ERR_NULL;
+        if (c.t < 1 || c.t > TP_MAX_SHARDS || c.rank < 0 || c.rank >= c.t) return TP_ERR_RANGE;
+        if (!dtype_ok(c.partial_dtype)) return TP_ERR_DTYPE;
+        const int64_t p_bytes = c.M * c.N * dtype_bytes(c.partial_dtype);
+        for (int i = 0; i < c.t; ++i) {
+            if (i == c.rank) continue;
+            if (c.partials[i] == nullptr) return TP_ERR_NULL;
+            if (!aligned16(c.partials[i])) return TP_ERR_ALIGNMENT;
+            if (overlap(c.partials[i], p_bytes, c.y, y_bytes)) return TP_ERR_SHAPE;
+            if (i < tpk::kMaxFusedPeers) a.peers[i] = c.partials[i];
+        }
+    }
+    tpk::Workspace ws;
+    st = view_workspace(c.workspace, c.workspace_bytes, &ws);
+    if (st != TP_OK) return st;
+    if (c.workspace != nullptr &&
+        (overlap(c.workspace, c.workspace_bytes, c.x, x_bytes) || overlap(c.workspace, c.workspace_bytes, c.w, w_bytes) ||
+         overlap(c.workspace, c.workspace_bytes, c.y, y_bytes)))
+        return TP_ERR_SHAPE;
+    if (c.M == 0) return TP_OK;
+
+    a.x = c.x; a.w = c.w; a.bias = c.bias; a.y = c.y;
+    a.M = c.M; a.N = c.N; a.K = c.K;
+    a.out_dtype = c.out_dtype;
+    a.epi = c.epilogue;
+    a.i_half = swiglu ? c.N : 0;
+    a.t = reduce ? c.t : 0;
+    a.rank = reduce ? c.rank : 0;
+    a.norm = c.norm != 0 ? 1 : 0;
+    a.eps = c.eps;
+    if (reduce) return launch_reduce_linear(a, c.partials, c.partial_dtype, ws, c.plan, s);
+    if (a.norm) return launch_norm_linear(a, ws, c.plan, s);
+    return launch_linear(a, ws, c.plan, s);
+}
+
+tp_linear_call make_call(const void* x, int64_t M, int64_t K, const void* w, int64_t N, void* y, int out_dtype,
+                         int epilogue, void* workspace, int64_t workspace_bytes) {
+    tp_linear_call c;
+    std::memset(&c, 0, sizeof(c));
+    c.x = x; c.M = M; c.K = K; c.w = w; c.N = N; c.y = y;
+    c.out_dtype = out_dtype;
+    c.epilogue = epilogue;
+    c.workspace = workspace;
+    c.workspace_bytes = workspace_bytes;
+    return c;
+}
+
+// Shared validation of the two add + RMSNorm calls; `inputs` are t buffers
+// of M x H elements of in_dtype (t may be 0).
+int add_rmsnorm_call(const void* const* inputs, int t, int in_dtype, int64_t M, int64_t H, void* residual,
+                     const void* gamma, float eps, void* out, void* stream) {
+    if (residual == nullptr || gamma == nullptr || out == nullptr) return TP_ERR_NULL;
+    if (t < 0 || t > TP_MAX_SHARDS) return TP_ERR_RANGE;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return TP_ERR_RANGE;
+    if (!dtype_ok(in_dtype)) return TP_ERR_DTYPE;
+    if (M < 0 || H <= 0 || M >= kMaxDim || H > kMaxNormWidth) return TP_ERR_SHAPE;
+    if (H % 8 != 0 || !aligned16(residual) || !aligned16(gamma) || !aligned16(out)) return TP_ERR_ALIGNMENT;
+    const int64_t act_bytes = M * H * 2, in_bytes = M * H * dtype_bytes(in_dtype);
+    if (overlap(out, act_bytes, residual, act_bytes) || overlap(out, act_bytes, gamma, H * 2) ||
+        overlap(residual, act_bytes, gamma, H * 2))
+        return TP_ERR_SHAPE;
+    tpk::PartialPtrs ptrs;
+    std::memset(&ptrs, 0, sizeof(ptrs));
+    for (int i = 0; i < t; ++i) {
+        if (inputs[i] == nullptr) return TP_ERR_NULL;
+        if (!aligned16(inputs[i])) return TP_ERR_ALIGNMENT;
+        if (overlap(inputs[i], in_bytes, out, act_bytes) || overlap(inputs[i], in_bytes, residual, act_bytes))
+            return TP_ERR_SHAPE;
+        ptrs.p[i] = inputs[i];
+    }
+    if (M == 0) return TP_OK;
+    return hip_status(tpk::launch_add_rmsnorm(ptrs, t, in_dtype, M, H, residual, gamma, eps, out,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -168,13 +354,12 @@ const char* tp_status_string(int status) {
     switch (status) {
     case TP_OK: return "ok";
     case TP_ERR_NULL: return "a required pointer is NULL";
-    case TP_ERR_SHAPE: return "negative, inconsistent or too large sizes";
+    case TP_ERR_SHAPE: return "negative, inconsistent or too large sizes, overlapping buffers, or too little workspace";
     case TP_ERR_DIVISIBILITY: return "a tensor-parallel split rule does not hold (n_h % t, n_kv vs t, I % t)";
     case TP_ERR_ALIGNMENT: return "pointer not 16-byte aligned or a size not a multiple of 8";
-    case TP_ERR_DTYPE: return "unknown dtype or weight kind";
-    case TP_ERR_RANGE: return "t outside [1, 64] or rank outside [0, t)";
+    case TP_ERR_DTYPE: return "unknown dtype, weight kind or epilogue";
+    case TP_ERR_RANGE: return "t outside [1, 64], rank outside [0, t), eps not finite and >= 0, or an unknown kernel plan";
     case TP_ERR_HIP: return "the HIP runtime reported an error";
-    case TP_ERR_ALLOC: return "workspace allocation failed";
     default: return "unknown status";
     }
 }
@@ -230,6 +415,8 @@ int tp_kv_heads_of_rank(const tp_model_cfg* cfg, int t, int rank, int* first, in
     return TP_OK;
 }
 
+int64_t tp_workspace_bytes(void) { return TP_WS_COUNTER_BYTES + tpk::kSkinnyWsFloats * 4; }
+
 int tp_shard_weights(const tp_model_cfg* cfg, int t, int rank, int kind, const void* full_w,
                      void* shard_w, void* stream) {
     try {
@@ -247,6 +434,7 @@ int tp_shard_weights(const tp_model_cfg* cfg, int t, int rank, int kind, const v
         if (m.src_cols % 8 != 0 || m.dst_cols % 8 != 0) return TP_ERR_ALIGNMENT;
         if (!aligned16(full_w) || !aligned16(shard_w)) return TP_ERR_ALIGNMENT;
         if (m.src_rows * m.src_cols >= ((int64_t)1 << 40)) return TP_ERR_SHAPE;
+        if (overlap(shard_w, m.dst_rows * m.dst_cols * 2, full_w, m.src_rows * m.src_cols * 2)) return TP_ERR_SHAPE;
         switch (kind) {
         case TP_W_QKV: {
             m.head_dim = cfg->head_dim;
@@ -277,98 +465,121 @@ int tp_shard_weights(const tp_model_cfg* cfg, int t, int rank, int kind, const v
         default:
             return TP_ERR_DTYPE;
         }
-        const hipError_t e = tpk::launch_shard_copy(m, full_w, shard_w, static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+        return hip_status(tpk::launch_shard_copy(m, full_w, shard_w, static_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_linear_ex(const tp_linear_call* call, void* stream) {
+    try {
+        if (call == nullptr) return TP_ERR_NULL;
+        return linear_call(*call, static_cast<hipStream_t>(stream));
     } catch (...) {
         return TP_ERR_HIP;
     }
 }
 
 int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_shard, int64_t N,
-                     const void* bias_or_null, void* y, void* stream) {
+                     const void* bias_or_null, void* y, void* workspace, int64_t workspace_bytes, void* stream) {
     try {
-        return run_linear(x, M, K, w_shard, N, bias_or_null, y, TP_BF16, stream);
+        tp_linear_call c = make_call(x, M, K, w_shard, N, y, TP_BF16, TP_EPI_STORE, workspace, workspace_bytes);
+        c.bias = bias_or_null;
+        return linear_call(c, static_cast<hipStream_t>(stream));
     } catch (...) {
         return TP_ERR_HIP;
     }
 }
 
 int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard,
-                          int64_t N, void* partial, int partial_dtype, void* stream) {
+                          int64_t N, void* partial, int partial_dtype, void* workspace, int64_t workspace_bytes,
+                          void* stream) {
     try {
-        return run_linear(x_shard, M, K_shard, w_shard, N, nullptr, partial, partial_dtype, stream);
+        const tp_linear_call c =
+            make_call(x_shard, M, K_shard, w_shard, N, partial, partial_dtype, TP_EPI_STORE, workspace, workspace_bytes);
+        return linear_call(c, static_cast<hipStream_t>(stream));
     } catch (...) {
         return TP_ERR_HIP;
     }
 }
 
 int tp_lm_head_shard(const void* h, int64_t M, int64_t K, const void* w_lm_shard, int64_t v_shard,
-                     void* logits_shard, int out_dtype, void* stream) {
+                     void* logits_shard, int out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
     try {
-        return run_linear(h, M, K, w_lm_shard, v_shard, nullptr, logits_shard, out_dtype, stream);
+        const tp_linear_call c =
+            make_call(h, M, K, w_lm_shard, v_shard, logits_shard, out_dtype, TP_EPI_STORE, workspace, workspace_bytes);
+        return linear_call(c, static_cast<hipStream_t>(stream));
     } catch (...) {
         return TP_ERR_HIP;
     }
 }
 
 int tp_column_linear_swiglu(const void* x, int64_t M, int64_t K, const void* w_gate_up, int64_t i_shard,
-                            void* act, void* stream) {
+                            void* act, void* workspace, int64_t workspace_bytes, void* stream) {
     try {
-        if (i_shard <= 0 || i_shard >= kMaxDim / 2) return TP_ERR_SHAPE;
-        const int st = check_linear(x, M, K, w_gate_up, 2 * i_shard, act);
-        if (st != TP_OK) return st;
-        if (M == 0) return TP_OK;
-        tpk::GemmArgs a{};
-        a.x = x; a.w = w_gate_up; a.y = act;
-        a.M = M; a.K = K;
-        a.out_dtype = TP_BF16;
-        a.epi = tpk::EPI_SWIGLU;
-        a.i_half = i_shard;
-        // decode kernel: 16-row blocks of 8 gate + 8 up rows; tiled kernel:
-        // 2 i_shard here, whole tiles of paired rows inside the launcher
-        a.N = M <= kSkinnyMaxM ? 16 * ((i_shard + 7) / 8) : 2 * i_shard;
-        return launch_linear(a, static_cast<hipStream_t>(stream));
+        const tp_linear_call c =
+            make_call(x, M, K, w_gate_up, i_shard, act, TP_BF16, TP_EPI_SWIGLU, workspace, workspace_bytes);
+        return linear_call(c, static_cast<hipStream_t>(stream));
     } catch (...) {
         return TP_ERR_HIP;
     }
 }
 
 int tp_row_linear_reduce(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
-                         const void* const* partials, int t, int rank, void* out, void* stream) {
+                         const void* const* partials, int partial_dtype, int t, int rank, void* out,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
     try {
-        const int st = check_linear(x_shard, M, K_shard, w_shard, N, out);
-        if (st != TP_OK) return st;
-        if (partials == nullptr) return TP_ERR_NULL;
-        if (t < 1 || t > TP_MAX_SHARDS || rank < 0 || rank >= t) return TP_ERR_RANGE;
-        for (int i = 0; i < t; ++i) {
-            if (i == rank) continue;
-            if (partials[i] == nullptr) return TP_ERR_NULL;
-            if (!aligned16(partials[i])) return TP_ERR_ALIGNMENT;
-            if (partials[i] == out) return TP_ERR_SHAPE;
-        }
-        if (M == 0) return TP_OK;
-        hipStream_t s = static_cast<hipStream_t>(stream);
-        tpk::GemmArgs a{};
-        a.x = x_shard; a.w = w_shard; a.y = out;
-        a.M = M; a.N = N; a.K = K_shard;
-        a.out_dtype = TP_BF16;
-        if (M <= kSkinnyMaxM && t <= tpk::kMaxFusedPeers && N % 4 == 0) {
-            a.epi = tpk::EPI_REDUCE;
-            a.t = t;
-            a.rank = rank;
-            for (int i = 0; i < t; ++i) a.peers[i] = i == rank ? nullptr : partials[i];
-            return launch_linear(a, s);
-        }
-        // Two launches with the same arithmetic: the rank's bf16 partial is
-        // written to `out`, then summed in place with the others in rank order.
-        a.epi = tpk::EPI_STORE;
-        const int st2 = launch_linear(a, s);
-        if (st2 != TP_OK) return st2;
-        tpk::PartialPtrs ptrs;
-        std::memset(&ptrs, 0, sizeof(ptrs));
-        for (int i = 0; i < t; ++i) ptrs.p[i] = i == rank ? out : partials[i];
-        const hipError_t e = tpk::launch_reduce(ptrs, t, M * N, TP_BF16, out, TP_BF16, s);
-        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+        tp_linear_call c = make_call(x_shard, M, K_shard, w_shard, N, out, TP_BF16, TP_EPI_REDUCE, workspace,
+                                     workspace_bytes);
+        c.partials = partials;
+        c.partial_dtype = partial_dtype;
+        c.t = t;
+        c.rank = rank;
+        return linear_call(c, static_cast<hipStream_t>(stream));
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_row_linear_reduce_add(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
+                             const void* const* partials, int partial_dtype, int t, int rank, void* residual,
+                             void* workspace, int64_t workspace_bytes, void* stream) {
+    try {
+        tp_linear_call c = make_call(x_shard, M, K_shard, w_shard, N, residual, TP_BF16, TP_EPI_REDUCE_ADD, workspace,
+                                     workspace_bytes);
+        c.partials = partials;
+        c.partial_dtype = partial_dtype;
+        c.t = t;
+        c.rank = rank;
+        return linear_call(c, static_cast<hipStream_t>(stream));
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_rmsnorm_column_linear(const void* h, float eps, int64_t M, int64_t K, const void* w_folded, int64_t N,
+                             const void* bias_or_null, void* y, void* workspace, int64_t workspace_bytes,
+                             void* stream) {
+    try {
+        tp_linear_call c = make_call(h, M, K, w_folded, N, y, TP_BF16, TP_EPI_STORE, workspace, workspace_bytes);
+        c.bias = bias_or_null;
+        c.norm = 1;
+        c.eps = eps;
+        return linear_call(c, static_cast<hipStream_t>(stream));
+    } catch (...) {
+        return TP_ERR_HIP;
+    }
+}
+
+int tp_rmsnorm_column_linear_swiglu(const void* h, float eps, int64_t M, int64_t K, const void* w_gate_up_folded,
+                                    int64_t i_shard, void* act, void* workspace, int64_t workspace_bytes,
+                                    void* stream) {
+    try {
+        tp_linear_call c =
+            make_call(h, M, K, w_gate_up_folded, i_shard, act, TP_BF16, TP_EPI_SWIGLU, workspace, workspace_bytes);
+        c.norm = 1;
+        c.eps = eps;
+        return linear_call(c, static_cast<hipStream_t>(stream));
     } catch (...) {
         return TP_ERR_HIP;
     }
@@ -379,9 +590,9 @@ int tp_swiglu(const void* gu, int64_t M, int64_t i_shard, void* out, void* strea
         if (gu == nullptr || out == nullptr) return TP_ERR_NULL;
         if (M < 0 || i_shard <= 0 || M >= kMaxDim || i_shard >= kMaxDim) return TP_ERR_SHAPE;
         if (i_shard % 8 != 0 || !aligned16(gu) || !aligned16(out)) return TP_ERR_ALIGNMENT;
+        if (overlap(out, M * i_shard * 2, gu, M * i_shard * 4)) return TP_ERR_SHAPE;
         if (M == 0) return TP_OK;
-        const hipError_t e = tpk::launch_swiglu(gu, M, i_shard, out, static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+        return hip_status(tpk::launch_swiglu(gu, M, i_shard, out, static_cast<hipStream_t>(stream)));
     } catch (...) {
         return TP_ERR_HIP;
     }
@@ -394,18 +605,20 @@ int tp_reduce_partials(const void* const* partials, int t, int64_t numel, int in
         if (t < 1 || t > TP_MAX_SHARDS) return TP_ERR_RANGE;
         if (numel < 0) return TP_ERR_SHAPE;
         if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return TP_ERR_DTYPE;
+        const int64_t in_bytes = numel * dtype_bytes(in_dtype), out_bytes = numel * dtype_bytes(out_dtype);
         tpk::PartialPtrs ptrs;
         std::memset(&ptrs, 0, sizeof(ptrs));
         for (int i = 0; i < t; ++i) {
             if (partials[i] == nullptr) return TP_ERR_NULL;
             if (!aligned16(partials[i])) return TP_ERR_ALIGNMENT;
+            // in place only as out == partials[0] with the same element size
+            const bool in_place = i == 0 && partials[0] == out && in_dtype == out_dtype;
+            if (!in_place && overlap(partials[i], in_bytes, out, out_bytes)) return TP_ERR_SHAPE;
             ptrs.p[i] = partials[i];
         }
         if (!aligned16(out)) return TP_ERR_ALIGNMENT;
         if (numel == 0) return TP_OK;
-        const hipError_t e = tpk::launch_reduce(ptrs, t, numel, in_dtype, out, out_dtype,
-                                                static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+        return hip_status(tpk::launch_reduce(ptrs, t, numel, in_dtype, out, out_dtype, static_cast<hipStream_t>(stream)));
     } catch (...) {
         return TP_ERR_HIP;
     }
@@ -420,13 +633,15 @@ int tp_vocab_embed(const int32_t* ids, int64_t M, const void* e_shard, int64_t v
         if (H % 8 != 0 || !aligned16(e_shard) || !aligned16(out_partial) ||
             (reinterpret_cast<uintptr_t>(ids) & 3u))
             return TP_ERR_ALIGNMENT;
-        if (M == 0) return TP_OK;
         const int64_t vs = (vocab + t - 1) / t;
+        const int64_t out_bytes = M * H * 2;
+        if (overlap(out_partial, out_bytes, ids, M * 4) || overlap(out_partial, out_bytes, e_shard, vs * H * 2))
+            return TP_ERR_SHAPE;
+        if (M == 0) return TP_OK;
         const int64_t lo = (int64_t)rank * vs;
         const int64_t hi = lo + vs < vocab ? lo + vs : vocab;
-        const hipError_t e = tpk::launch_vocab_embed(ids, M, e_shard, lo, hi, H, out_partial,
-                                                     static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+        return hip_status(
+            tpk::launch_vocab_embed(ids, M, e_shard, lo, hi, H, out_partial, static_cast<hipStream_t>(stream)));
     } catch (...) {
         return TP_ERR_HIP;
     }
@@ -440,62 +655,23 @@ int tp_concat_logits(const void* const* shard_logits, int t, int64_t M, int64_t 
         if (!dtype_ok(dtype)) return TP_ERR_DTYPE;
         if (M < 0 || vocab <= 0 || M >= kMaxDim || vocab >= kMaxDim) return TP_ERR_SHAPE;
         if (v_shard != (vocab + t - 1) / t) return TP_ERR_SHAPE;
+        const int64_t es = dtype_bytes(dtype);
         tpk::PartialPtrs ptrs;
         std::memset(&ptrs, 0, sizeof(ptrs));
         for (int i = 0; i < t; ++i) {
             if (shard_logits[i] == nullptr) return TP_ERR_NULL;
             if (!aligned16(shard_logits[i])) return TP_ERR_ALIGNMENT;
+            if (overlap(shard_logits[i], M * v_shard * es, out, M * vocab * es)) return TP_ERR_SHAPE;
             ptrs.p[i] = shard_logits[i];
         }
         if (!aligned16(out)) return TP_ERR_ALIGNMENT;
         if (M == 0) return TP_OK;
-        const hipError_t e = tpk::launch_concat(ptrs, t, M, v_shard, vocab, dtype, out,
-                                                static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+        return hip_status(
+            tpk::launch_concat(ptrs, t, M, v_shard, vocab, dtype, out, static_cast<hipStream_t>(stream)));
     } catch (...) {
         return TP_ERR_HIP;
     }
 }
-
-namespace {
-
-constexpr int64_t kMaxNormWidth = 32768;   // one workgroup holds a whole row in registers
-
-bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
-}
-
-// Shared validation of the two add + RMSNorm calls; `inputs` are t buffers
-// of M x H elements of in_dtype (t may be 0).
-int add_rmsnorm_call(const void* const* inputs, int t, int in_dtype, int64_t M, int64_t H, void* residual,
-                     const void* gamma, float eps, void* out, void* stream) {
-    if (residual == nullptr || gamma == nullptr || out == nullptr) return TP_ERR_NULL;
-    if (t < 0 || t > TP_MAX_SHARDS) return TP_ERR_RANGE;
-    if (!(eps >= 0.0f) || !std::isfinite(eps)) return TP_ERR_RANGE;
-    if (!dtype_ok(in_dtype)) return TP_ERR_DTYPE;
-    if (M < 0 || H <= 0 || M >= kMaxDim || H > kMaxNormWidth) return TP_ERR_SHAPE;
-    if (H % 8 != 0 || !aligned16(residual) || !aligned16(gamma) || !aligned16(out)) return TP_ERR_ALIGNMENT;
-    const int64_t act_bytes = M * H * 2, in_bytes = M * H * (in_dtype == TP_F32 ? 4 : 2);
-    if (overlap(out, act_bytes, residual, act_bytes) || overlap(out, act_bytes, gamma, H * 2) ||
-        overlap(residual, act_bytes, gamma, H * 2))
-        return TP_ERR_SHAPE;
-    tpk::PartialPtrs ptrs;
-    std::memset(&ptrs, 0, sizeof(ptrs));
-    for (int i = 0; i < t; ++i) {
-        if (inputs[i] == nullptr) return TP_ERR_NULL;
-        if (!aligned16(inputs[i])) return TP_ERR_ALIGNMENT;
-        if (overlap(inputs[i], in_bytes, out, act_bytes) || overlap(inputs[i], in_bytes, residual, act_bytes))
-            return TP_ERR_SHAPE;
-        ptrs.p[i] = inputs[i];
-    }
-    if (M == 0) return TP_OK;
-    const hipError_t e = tpk::launch_add_rmsnorm(ptrs, t, in_dtype, M, H, residual, gamma, eps, out,
-                                                 static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? TP_OK : TP_ERR_HIP;
-}
-
-}  // namespace
 
 int tp_add_rmsnorm(const void* x_or_null, int64_t M, int64_t H, void* residual, const void* gamma, float eps,
                    void* out, void* stream) {
@@ -518,66 +694,6 @@ int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype,
     }
 }
 
-namespace {
-
-// The back `bytes` of the stream workspace (whole 256-byte units) for an
-// operand a fused call's two-launch path stages; *front is what stays free
-// for the linear's own split-K partials.
-int workspace_back(hipStream_t s, int64_t bytes, void** out, int64_t* front) {
-    tpk::Workspace ws{nullptr, 0, nullptr, 0};
-    const int st = get_workspace(s, &ws);
-    if (st != TP_OK) return st;
-    const int64_t need = (bytes + 255) / 256 * 256;
-    if (need > ws.partial_floats * 4) return TP_ERR_SHAPE;
-    *out = reinterpret_cast<char*>(ws.partials) + (ws.partial_floats * 4 - need);
-    *front = ws.partial_floats - need / 4;
-    return TP_OK;
-}
-
-// The linear a describes on RMS-normalised rows of a.x (unit weights: the
-// norm's gamma is folded into a.w). One launch when the decode kernel can
-// stage whole rows; otherwise the norm writes the normalised rows to the
-// workspace and the plain linear reads them.
-int run_norm_linear(tpk::GemmArgs a, hipStream_t s) {
-    if (a.M <= kSkinnyMaxM) {
-        const tpk::SkinnyPlan p = tpk::plan_skinny_norm(a.M, a.N, a.K);
-        if (p.splits >= 1) {
-            tpk::Workspace ws{nullptr, 0, nullptr, 0};
-            if (p.splits > 1) {
-                // partial tiles, then each split's share of the rows' sums of squares
-                const int st = get_workspace(s, &ws);
-                if (st != TP_OK) return st;
-                if (tpk::skinny_workspace_floats(p, a.M, a.N) + (int64_t)p.splits * p.ntiles * 16 > ws.partial_floats ||
-                    p.ntiles > ws.num_counters)
-                    return TP_ERR_SHAPE;
-            }
-            const hipError_t e = tpk::launch_skinny(a, p, ws, s);
-            return e == hipSuccess ? TP_OK : TP_ERR_HIP;
-        }
-    }
-    void* xn = nullptr;
-    int64_t front = 0;
-    const int st = workspace_back(s, a.M * a.K * 2, &xn, &front);
-    if (st != TP_OK) return st;
-    tpk::PartialPtrs none;
-    std::memset(&none, 0, sizeof(none));
-    const hipError_t e = tpk::launch_add_rmsnorm(none, 0, TP_BF16, a.M, a.K, const_cast<void*>(a.x), nullptr, a.eps,
-                                                 xn, s);
-    if (e != hipSuccess) return TP_ERR_HIP;
-    a.x = xn;
-    a.norm = 0;
-    return launch_linear(a, s, front);
-}
-
-int check_norm_input(const void* h, int64_t K, float eps, const void* y, int64_t M, int64_t n_bytes) {
-    if (!(eps >= 0.0f) || !std::isfinite(eps)) return TP_ERR_RANGE;
-    if (K > kMaxNormWidth) return TP_ERR_SHAPE;
-    if (overlap(y, n_bytes, h, M * K * 2)) return TP_ERR_SHAPE;
-    return TP_OK;
-}
-
-}  // namespace
-
 int tp_fold_norm_weight(const void* w, int64_t N, int64_t K, const void* gamma, void* w_folded, void* stream) {
     try {
         if (w == nullptr || gamma == nullptr || w_folded == nullptr) return TP_ERR_NULL;
@@ -586,113 +702,15 @@ int tp_fold_norm_weight(const void* w, int64_t N, int64_t K, const void* gamma, 
         const int64_t bytes = N * K * 2;
         if ((w_folded != w && overlap(w_folded, bytes, w, bytes)) || overlap(w_folded, bytes, gamma, K * 2))
             return TP_ERR_SHAPE;
-        const hipError_t e = tpk::launch_fold_norm_weight(w, N, K, gamma, w_folded, static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
-    } catch (...) {
-        return TP_ERR_HIP;
-    }
-}
-
-int tp_rmsnorm_column_linear(const void* h, float eps, int64_t M, int64_t K, const void* w_folded, int64_t N,
-                             const void* bias_or_null, void* y, void* stream) {
-    try {
-        const void* w_shard = w_folded;
-        int st = check_linear(h, M, K, w_shard, N, y);
-        if (st != TP_OK) return st;
-        st = check_norm_input(h, K, eps, y, M, M * N * 2);
-        if (st != TP_OK) return st;
-        if (bias_or_null != nullptr && (reinterpret_cast<uintptr_t>(bias_or_null) & 1u)) return TP_ERR_ALIGNMENT;
-        if (M == 0) return TP_OK;
-        tpk::GemmArgs a{};
-        a.x = h; a.w = w_shard; a.bias = bias_or_null; a.y = y;
-        a.M = M; a.N = N; a.K = K;
-        a.out_dtype = TP_BF16;
-        a.epi = tpk::EPI_STORE;
-        a.norm = 1;
-        a.eps = eps;
-        return run_norm_linear(a, static_cast<hipStream_t>(stream));
-    } catch (...) {
-        return TP_ERR_HIP;
-    }
-}
-
-int tp_rmsnorm_column_linear_swiglu(const void* h, float eps, int64_t M, int64_t K, const void* w_gate_up_folded,
-                                    int64_t i_shard, void* act, void* stream) {
-    try {
-        const void* w_gate_up = w_gate_up_folded;
-        if (i_shard <= 0 || i_shard >= kMaxDim / 2) return TP_ERR_SHAPE;
-        int st = check_linear(h, M, K, w_gate_up, 2 * i_shard, act);
-        if (st != TP_OK) return st;
-        st = check_norm_input(h, K, eps, act, M, M * i_shard * 2);
-        if (st != TP_OK) return st;
-        if (M == 0) return TP_OK;
-        tpk::GemmArgs a{};
-        a.x = h; a.w = w_gate_up; a.y = act;
-        a.M = M; a.K = K;
-        a.out_dtype = TP_BF16;
-        a.epi = tpk::EPI_SWIGLU;
-        a.i_half = i_shard;
-        a.N = M <= kSkinnyMaxM ? 16 * ((i_shard + 7) / 8) : 2 * i_shard;
-        a.norm = 1;
-        a.eps = eps;
-        return run_norm_linear(a, static_cast<hipStream_t>(stream));
-    } catch (...) {
-        return TP_ERR_HIP;
-    }
-}
-
-int tp_row_linear_reduce_add(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
-                             const void* const* partials, int t, int rank, void* residual, void* stream) {
-    try {
-        const int st = check_linear(x_shard, M, K_shard, w_shard, N, residual);
-        if (st != TP_OK) return st;
-        if (partials == nullptr) return TP_ERR_NULL;
-        if (t < 1 || t > TP_MAX_SHARDS || rank < 0 || rank >= t) return TP_ERR_RANGE;
-        const int64_t bytes = M * N * 2;
-        for (int i = 0; i < t; ++i) {
-            if (i == rank) continue;
-            if (partials[i] == nullptr) return TP_ERR_NULL;
-            if (!aligned16(partials[i])) return TP_ERR_ALIGNMENT;
-            if (overlap(partials[i], bytes, residual, bytes)) return TP_ERR_SHAPE;
-        }
-        if (overlap(x_shard, M * K_shard * 2, residual, bytes)) return TP_ERR_SHAPE;
-        if (M == 0) return TP_OK;
-        hipStream_t s = static_cast<hipStream_t>(stream);
-        tpk::GemmArgs a{};
-        a.x = x_shard; a.w = w_shard; a.y = residual;
-        a.M = M; a.N = N; a.K = K_shard;
-        a.out_dtype = TP_BF16;
-        if (M <= kSkinnyMaxM && t <= tpk::kMaxFusedPeers && N % 4 == 0) {
-            a.epi = tpk::EPI_REDUCE_ADD;
-            a.t = t;
-            a.rank = rank;
-            for (int i = 0; i < t; ++i) a.peers[i] = i == rank ? nullptr : partials[i];
-            return launch_linear(a, s);
-        }
-        // Two launches with the same arithmetic: the rank's bf16 partial goes
-        // to the back of the workspace, then the sum over ranks in order is
-        // added to the residual (the add + norm kernel without its norm).
-        if (N % 8 != 0 || N > kMaxNormWidth) return TP_ERR_SHAPE;
-        void* own = nullptr;
-        int64_t front = 0;
-        const int st2 = workspace_back(s, bytes, &own, &front);
-        if (st2 != TP_OK) return st2;
-        a.y = own;
-        a.epi = tpk::EPI_STORE;
-        const int st3 = launch_linear(a, s, front);
-        if (st3 != TP_OK) return st3;
-        tpk::PartialPtrs ptrs;
-        std::memset(&ptrs, 0, sizeof(ptrs));
-        for (int i = 0; i < t; ++i) ptrs.p[i] = i == rank ? own : partials[i];
-        const hipError_t e = tpk::launch_add_rmsnorm(ptrs, t, TP_BF16, M, N, residual, nullptr, 0.0f, nullptr, s);
-        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+        return hip_status(tpk::launch_fold_norm_weight(w, N, K, gamma, w_folded, static_cast<hipStream_t>(stream)));
     } catch (...) {
         return TP_ERR_HIP;
     }
 }
 
 int tp_decode_attention(const void* qkv, int64_t B, int nq, int nkv, int head_dim, void* k_cache, void* v_cache,
-                        int64_t L, const int32_t* lens, void* ctx, void* stream) {
+                        int64_t L, const int32_t* lens, void* ctx, void* workspace, int64_t workspace_bytes,
+                        void* stream) {
     try {
         if (qkv == nullptr || k_cache == nullptr || v_cache == nullptr || lens == nullptr || ctx == nullptr)
             return TP_ERR_NULL;
@@ -711,7 +729,13 @@ int tp_decode_attention(const void* qkv, int64_t B, int nq, int nkv, int head_di
             overlap(lens, B * 4, ctx, ctx_bytes) || overlap(lens, B * 4, k_cache, cache_bytes) ||
             overlap(lens, B * 4, v_cache, cache_bytes))
             return TP_ERR_SHAPE;
-        if (B == 0) return TP_OK;
+        tpk::Workspace ws;
+        const int st = view_workspace(workspace, workspace_bytes, &ws);
+        if (st != TP_OK) return st;
+        if (overlap(workspace, workspace_bytes, ctx, ctx_bytes) || overlap(workspace, workspace_bytes, qkv, qkv_bytes) ||
+            overlap(workspace, workspace_bytes, k_cache, cache_bytes) ||
+            overlap(workspace, workspace_bytes, v_cache, cache_bytes))
+            return TP_ERR_SHAPE;
         tpk::AttnArgs a;
         a.qkv = static_cast<const uint16_t*>(qkv);
         a.k_cache = static_cast<uint16_t*>(k_cache);
@@ -725,36 +749,12 @@ int tp_decode_attention(const void* qkv, int64_t B, int nq, int nkv, int head_di
         a.head_dim = head_dim;
         a.qkv_stride = qkv_row;
         a.scale = 1.0f / std::sqrt((float)head_dim);
-        hipStream_t s = static_cast<hipStream_t>(stream);
-        tpk::Workspace ws{nullptr, 0, nullptr, 0};
-        const int st = get_workspace(s, &ws);
-        if (st != TP_OK) return st;
         if (tpk::attention_workspace_floats(a) > ws.partial_floats) return TP_ERR_SHAPE;
-        const hipError_t e = tpk::launch_decode_attention(a, ws, s);
-        return e == hipSuccess ? TP_OK : TP_ERR_HIP;
+        if (B == 0) return TP_OK;
+        return hip_status(tpk::launch_decode_attention(a, ws, static_cast<hipStream_t>(stream)));
     } catch (...) {
         return TP_ERR_HIP;
     }
-}
-
-int tp_tune_skinny(int ksteps, int nwn, int nwk, int x_direct) {
-    if (ksteps == 0 && nwn == 0 && nwk == 0) {
-        g_force_ksteps = g_force_nwn = g_force_nwk = g_force_xd = 0;
-        return TP_OK;
-    }
-    tpk::SkinnyPlan p{1, ksteps, nwn, nwk, x_direct ? 1 : 0, 1, 1};
-    if (!tpk::skinny_variant_exists(p)) return TP_ERR_SHAPE;
-    g_force_ksteps = ksteps;
-    g_force_nwn = nwn;
-    g_force_nwk = nwk;
-    g_force_xd = x_direct ? 1 : 0;
-    return TP_OK;
-}
-
-int tp_tune_tiled(int variant) {
-    if (variant < -1 || variant >= tpk::tiled_variant_count()) return TP_ERR_RANGE;
-    tpk::tiled_force_variant(variant);
-    return TP_OK;
 }
 
 }  // extern "C"

@@ -36,6 +36,9 @@
 //     summed with the other ranks' partials in rank order and rounded once;
 //     the owner waves load those partials right after the first weights.
 //     Both give the same bits as the separate kernels.
+#include <mutex>
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -102,41 +105,50 @@ __device__ __forceinline__ int64_t weight_row(const GemmArgs& a, int64_t v) {
     return (v & 8) ? a.i_half + j : j;
 }
 
-// Other ranks' values of one lane's 4 outputs, bf16 pairs indexed by rank
-// (the own slot unused). When a wave finishes one token tile, the first
-// tile's values are loaded right after its weights; otherwise (and for later
-// tiles of a persistent loop, and in the last split) just before the sum.
-// EPI_REDUCE launches have N % 4 == 0, so a lane's 4 outputs are one 8-byte
-// load per rank. The guards are uniform and one-sided (a branch that merged
-// two values would make each load wait for the one before); lanes past the
-// edge read the start of the peer's buffer instead and discard it.
-// EPI_REDUCE_ADD also holds the lane's 4 residual values (read from y).
-struct PeerVals { uint2 v[kMaxFusedPeers]; uint2 res; };
+// Other ranks' values of one lane's 4 outputs, indexed by rank (the own slot
+// unused): 4 bf16 (8 bytes) per rank, or 4 fp32 (16 bytes) for the _F32
+// epilogues. When a wave finishes one token tile, the first tile's values are
+// loaded right after its weights; otherwise (and for later tiles of a
+// persistent loop, and in the last split) just before the sum. Reduce
+// launches have N % 4 == 0, so a lane's 4 outputs are one aligned load per
+// rank. The guards are uniform and one-sided (a branch that merged two values
+// would make each load wait for the one before); lanes past the edge read the
+// start of the peer's buffer instead and discard it. The _ADD epilogues also
+// hold the lane's 4 residual values (read from y).
+template <int EPI>
+struct PeerVals {
+    using V = typename std::conditional<epi_peers_f32(EPI), uint4, uint2>::type;
+    V v[kMaxFusedPeers];
+    uint2 res;
+};
 
 template <int EPI>
-__device__ __forceinline__ void load_peers(const GemmArgs& a, int64_t m, int64_t n, PeerVals& p) {
+__device__ __forceinline__ void load_peers(const GemmArgs& a, int64_t m, int64_t n, PeerVals<EPI>& p) {
+    using V = typename PeerVals<EPI>::V;
+    constexpr int kElem = epi_peers_f32(EPI) ? 4 : 2;
     const bool ok = m < a.M && n < a.N;
     const int64_t base = ok ? m * a.N + n : 0;
 #pragma unroll
     for (int r = 0; r < kMaxFusedPeers; ++r) {
         if (r < a.t && r != a.rank)
-            p.v[r] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.peers[r]) + base);
+            p.v[r] = *reinterpret_cast<const V*>(reinterpret_cast<const unsigned char*>(a.peers[r]) + base * kElem);
     }
-    if constexpr (EPI == EPI_REDUCE_ADD)
+    if constexpr (epi_is_add(EPI))
         p.res = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.y) + base);
 }
 
-// EPI_REDUCE: out[m, n..n+3] = bf16(sum over ranks in order from rank 0),
-// the own partial rounded as a bf16 partial buffer holds it.
-// EPI_REDUCE_ADD: y[m, n..n+3] = bf16(y + that bf16 sum) (the residual stream).
+// Reduce epilogues: out[m, n..n+3] = bf16(sum over ranks in order from rank
+// 0), the own partial as a partial buffer of the peers' dtype holds it
+// (rounded to bf16, or the fp32 sum itself). _ADD: y[m, n..n+3] = bf16(y +
+// that bf16 sum) (the residual stream).
 template <int EPI>
 __device__ __forceinline__ void reduce_out4(const GemmArgs& a, int64_t m, int64_t n, const float* v,
-                                            const PeerVals& p) {
+                                            const PeerVals<EPI>& p) {
     // Unrolled with constant indices (the values stay in registers); the
     // guards are uniform, so only the t ranks' iterations execute.
     float own[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) own[i] = round_bf16(v[i]);
+    for (int i = 0; i < 4; ++i) own[i] = epi_peers_f32(EPI) ? v[i] : round_bf16(v[i]);
     float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < kMaxFusedPeers; ++r) {
@@ -145,6 +157,11 @@ __device__ __forceinline__ void reduce_out4(const GemmArgs& a, int64_t m, int64_
             if (r == a.rank) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) q[i] = own[i];
+            } else if constexpr (epi_peers_f32(EPI)) {
+                q[0] = __uint_as_float(p.v[r].x);
+                q[1] = __uint_as_float(p.v[r].y);
+                q[2] = __uint_as_float(p.v[r].z);
+                q[3] = __uint_as_float(p.v[r].w);
             } else {
                 q[0] = bf16_to_f32(p.v[r].x & 0xFFFFu);
                 q[1] = bf16_to_f32(p.v[r].x >> 16);
@@ -155,7 +172,7 @@ __device__ __forceinline__ void reduce_out4(const GemmArgs& a, int64_t m, int64_
             for (int i = 0; i < 4; ++i) o[i] = r == 0 ? q[i] : o[i] + q[i];
         }
     }
-    if constexpr (EPI == EPI_REDUCE_ADD) {
+    if constexpr (epi_is_add(EPI)) {
         const float res[4] = {bf16_to_f32(p.res.x & 0xFFFFu), bf16_to_f32(p.res.x >> 16),
                               bf16_to_f32(p.res.y & 0xFFFFu), bf16_to_f32(p.res.y >> 16)};
 #pragma unroll
@@ -169,7 +186,7 @@ __device__ __forceinline__ void reduce_out4(const GemmArgs& a, int64_t m, int64_
 // Every lane of the wave must call it (the SwiGLU pairing swaps lanes).
 template <int EPI>
 __device__ __forceinline__ void finish4(const GemmArgs& a, int64_t m, int64_t n, const float* v, int lane,
-                                        const PeerVals& peers) {
+                                        const PeerVals<EPI>& peers) {
     if constexpr (EPI == EPI_SWIGLU) {
         float u[4];
 #pragma unroll
@@ -189,7 +206,7 @@ __device__ __forceinline__ void finish4(const GemmArgs& a, int64_t m, int64_t n,
         return;
     }
     if (m >= a.M || n >= a.N) return;
-    if constexpr (EPI == EPI_REDUCE || EPI == EPI_REDUCE_ADD) reduce_out4<EPI>(a, m, n, v, peers);
+    if constexpr (epi_is_reduce(EPI)) reduce_out4<EPI>(a, m, n, v, peers);
     else store_out4(a, m, n, v);
 }
 
@@ -240,9 +257,9 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     // ranks' values for the first tile right after its weights (step 2), so
     // they arrive while the weights stream; later tiles of a persistent loop
     // load theirs just before the sum.
-    constexpr bool kReduce = EPI == EPI_REDUCE || EPI == EPI_REDUCE_ADD;
+    constexpr bool kReduce = epi_is_reduce(EPI);
     constexpr bool kPrefetchPeers = kReduce && C::kOwn == 1;
-    PeerVals peers;
+    PeerVals<EPI> peers;
     const int64_t m_own0 = 16 * wk + (lane & 15);          // token of the first owned tile
     bool first_tile = true;
 
@@ -574,7 +591,7 @@ constexpr SkinnyFn skinny_norm_fn() {
 
 struct SkinnyEntry {
     int mt, ksteps, nwn, nwk, xd;
-    SkinnyFn fn[4];   // by epilogue: EPI_STORE, EPI_SWIGLU, EPI_REDUCE, EPI_REDUCE_ADD
+    SkinnyFn fn[kNumEpilogues];   // by epilogue (Epilogue's order)
     SkinnyFn fn_norm[2];   // with the norm prologue: EPI_STORE, EPI_SWIGLU (or nullptr)
     int threads;
     SkinnyLdsFn lds;
@@ -584,7 +601,9 @@ struct SkinnyEntry {
 #define TP_SK(MT, KS, NN, NK, XD)                                                                  \
     {MT, KS, NN, NK, XD,                                                                           \
      {skinny_kernel<MT, KS, NN, NK, XD, EPI_STORE>, skinny_kernel<MT, KS, NN, NK, XD, EPI_SWIGLU>,    \
-      skinny_kernel<MT, KS, NN, NK, XD, EPI_REDUCE>, skinny_kernel<MT, KS, NN, NK, XD, EPI_REDUCE_ADD>}, \
+      skinny_kernel<MT, KS, NN, NK, XD, EPI_REDUCE>, skinny_kernel<MT, KS, NN, NK, XD, EPI_REDUCE_ADD>, \
+      skinny_kernel<MT, KS, NN, NK, XD, EPI_REDUCE_F32>,                                            \
+      skinny_kernel<MT, KS, NN, NK, XD, EPI_REDUCE_ADD_F32>},                                       \
      {skinny_norm_fn<MT, KS, NN, NK, XD, EPI_STORE>(), skinny_norm_fn<MT, KS, NN, NK, XD, EPI_SWIGLU>()}, \
      SkinnyCfg<MT, KS, NN, NK, XD>::kThreads,                                                       \
      SkinnyCfg<MT, KS, NN, NK, XD>::lds_bytes, SkinnyCfg<MT, KS, NN, NK, XD>::kGroupK}
@@ -609,9 +628,19 @@ const SkinnyEntry kSkinnyTable[] = {TP_SK_MT1, TP_SK_MTN(2), TP_SK_MTN(4)};
 
 constexpr int kMaxLds = 160 * 1024 - 1024;   // dynamic LDS; the rest is the kernel's static LDS
 constexpr int kNumSkinny = sizeof(kSkinnyTable) / sizeof(kSkinnyTable[0]);
-int g_lds_attr[kNumSkinny][6] = {};         // dynamic LDS limit set so far per kernel
-int g_occupancy[kNumSkinny][6][2] = {};     // cached (lds bytes, workgroups per CU)
-int g_num_cus[16] = {};
+constexpr int kSlots = kNumEpilogues + 2;     // kernels per entry: the epilogues, then the norm prologue's two
+constexpr int kMaxDevices = 16;
+
+// Per-device launch state, filled on first use: the dynamic-LDS limit set so
+// far on each kernel, its occupancy at a given LDS size, the CU count. Read
+// and written under one mutex, so concurrent host threads are safe.
+struct DeviceLaunchState {
+    int lds_attr[kNumSkinny][kSlots] = {};
+    int occupancy[kNumSkinny][kSlots][2] = {};    // (lds bytes, workgroups per CU)
+    int num_cus = 0;
+};
+std::mutex g_state_mu;
+DeviceLaunchState g_state[kMaxDevices];
 
 int find_skinny(const SkinnyPlan& p) {
     for (int i = 0; i < kNumSkinny; ++i) {
@@ -656,14 +685,18 @@ bool skinny_norm_plan_fits(const SkinnyPlan& p, int64_t M, int64_t K) {
 // split 4 ways over 1024-wide groups for weights with few 16-row tiles,
 // otherwise the variant covering K in one workgroup with the least waste),
 // or splits = 0 when none fits (the caller then normalises separately).
-SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K) {
+SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64_t ws_counters) {
     struct Rule { int64_t kmax; int ks, nwn, nwk; };
     if ((N + 15) / 16 < 128 && K >= 2048) {
         SkinnyPlan p{1, 8, 1, 4, 0, 1, 1};
         const int idx = find_skinny(p);
         if (idx >= 0) {
             p = make_plan(kSkinnyTable[idx], N, K);
-            if (skinny_norm_plan_fits(p, M, K)) return p;
+            // partial tiles, then each split's share of the rows' sums of squares
+            const bool ws_ok = p.splits == 1 || (skinny_workspace_floats(p, M, N) + (int64_t)p.splits * p.ntiles * 16 <=
+                                                     ws_floats &&
+                                                 p.ntiles <= ws_counters);
+            if (ws_ok && skinny_norm_plan_fits(p, M, K)) return p;
         }
     }
     static const Rule rules[] = {{512, 4, 1, 4}, {1024, 8, 1, 4}, {2048, 8, 1, 8}, {4096, 16, 1, 8}, {5120, 20, 1, 8}};
@@ -691,7 +724,7 @@ SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K) {
 // (the weight once, the fp32 partial round trip when K is split across
 // workgroups, a quarter weight for X re-reads from L2) divided by how well the
 // grid fills the 256 CUs.
-SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats) {
+SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64_t ws_counters) {
     const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     struct Rule { int64_t kmax; int ks, nwn, nwk, xd; };
     auto first_fit = [&](const Rule* rules, int n, SkinnyPlan* out) {
@@ -702,7 +735,7 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats) {
             const int idx = find_skinny(p);
             if (idx < 0 || !skinny_plan_fits(p, M)) continue;
             p = make_plan(kSkinnyTable[idx], N, K);
-            if (p.splits > 1 && (p.splits * M * N > ws_floats || p.ntiles > kSkinnyWsCounters)) continue;
+            if (p.splits > 1 && (p.splits * M * N > ws_floats || p.ntiles > ws_counters)) continue;
             *out = p;
             return true;
         }
@@ -731,7 +764,7 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats) {
     for (const SkinnyEntry& e : kSkinnyTable) {
         if (e.mt != mt || e.lds(xrows_for(e, M)) > kMaxLds) continue;
         const SkinnyPlan p = make_plan(e, N, K);
-        if (p.splits > 1 && (p.splits * M * N > ws_floats || p.ntiles > kSkinnyWsCounters)) continue;
+        if (p.splits > 1 && (p.splits * M * N > ws_floats || p.ntiles > ws_counters)) continue;
         if (p.splits > 65535) continue;
         const double wgs = (double)p.ntiles * (double)p.splits;
         double bytes = 2.0 * (double)N * (double)K;
@@ -757,48 +790,50 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
     if (idx < 0) return hipErrorInvalidValue;
     const SkinnyEntry* e = &kSkinnyTable[idx];
     const int epi = a.epi;
-    if (epi < 0 || epi > 3) return hipErrorInvalidValue;
+    if (epi < 0 || epi >= kNumEpilogues) return hipErrorInvalidValue;
     const bool norm = a.norm != 0;
     if (norm && (epi > EPI_SWIGLU || !skinny_norm_plan_fits(p, a.M, a.K))) return hipErrorInvalidValue;
     const SkinnyFn fn = norm ? e->fn_norm[epi] : e->fn[epi];
     if (fn == nullptr) return hipErrorInvalidValue;
-    const int slot = norm ? 4 + epi : epi;      // kernel state below is per function
+    const int slot = norm ? kNumEpilogues + epi : epi;      // launch state below is per function
     const int xrows = xrows_for(*e, a.M);
     const int lds = e->lds(xrows);
     if (lds > kMaxLds) return hipErrorInvalidValue;
-    if (lds > 65536 && lds > g_lds_attr[idx][slot]) {
-        const hipError_t ae = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (ae != hipSuccess) return ae;
-        g_lds_attr[idx][slot] = lds;
-    }
+    int dev = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he != hipSuccess) return he;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     int64_t grid_x = p.ntiles;
-    if (p.splits == 1 && !p.xd) {
-        // Unsplit: as many workgroups as fit on the GPU at once, each looping
-        // over row tiles (X is staged once per workgroup).
-        int dev = 0;
-        hipError_t he = hipGetDevice(&dev);
-        if (he != hipSuccess) return he;
-        if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
-        if (g_num_cus[dev] == 0) {
-            he = hipDeviceGetAttribute(&g_num_cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+    {
+        std::lock_guard<std::mutex> lock(g_state_mu);
+        DeviceLaunchState& st = g_state[dev];
+        if (lds > 65536 && lds > st.lds_attr[idx][slot]) {
+            he = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             if (he != hipSuccess) return he;
+            st.lds_attr[idx][slot] = lds;
         }
-        int* occ = g_occupancy[idx][slot];
-        if (occ[0] != lds || occ[1] == 0) {
-            int per_cu = 0;
-            he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn),
-                                                              e->threads, lds);
-            if (he != hipSuccess) return he;
-            occ[0] = lds;
-            occ[1] = per_cu > 0 ? per_cu : 1;
+        if (p.splits == 1 && !p.xd) {
+            // Unsplit: as many workgroups as fit on the GPU at once, each
+            // looping over row tiles (X is staged once per workgroup).
+            if (st.num_cus == 0) {
+                he = hipDeviceGetAttribute(&st.num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+                if (he != hipSuccess) return he;
+            }
+            int* occ = st.occupancy[idx][slot];
+            if (occ[0] != lds || occ[1] == 0) {
+                int per_cu = 0;
+                he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), e->threads,
+                                                                  lds);
+                if (he != hipSuccess) return he;
+                occ[0] = lds;
+                occ[1] = per_cu > 0 ? per_cu : 1;
+            }
+            const int64_t cap = (int64_t)occ[1] * st.num_cus;
+            if (grid_x > cap) grid_x = cap;
         }
-        const int64_t cap = (int64_t)occ[1] * g_num_cus[dev];
-        if (grid_x > cap) grid_x = cap;
     }
     dim3 grid((unsigned)grid_x, (unsigned)p.splits);
-    hipLaunchKernelGGL(fn, grid, dim3(e->threads), lds, s, a, p.splits, p.ntiles, xrows, ws.partials,
-                       ws.counters);
+    hipLaunchKernelGGL(fn, grid, dim3(e->threads), lds, s, a, p.splits, p.ntiles, xrows, ws.partials, ws.counters);
     return hipGetLastError();
 }
 

@@ -23,6 +23,8 @@
 // global -> LDS loads in a 4-stage ring (details below). tiled_reg_kernel
 // (any K % 8 == 0): k-tiles of 64 go global -> VGPR -> LDS, double buffered,
 // 128-byte rows XOR-swizzled by (row / 2) mod 8.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -723,17 +725,18 @@ const TiledEntry kTiled[] = {
 #undef TP_DMA
 #undef TP_DMA64
 constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);
-bool g_tiled_attr[kNumTiled] = {};
-int g_tiled_force = -1;
+constexpr int kMaxDevices = 16;
+// Whether each kernel's dynamic-LDS limit is set, per device; setting it is
+// idempotent, so a race between host threads only repeats the call.
+std::atomic<bool> g_tiled_attr[kMaxDevices][kNumTiled] = {};
 
 }  // namespace
 
 int tiled_variant_count() { return kNumTiled; }
-void tiled_force_variant(int idx) { g_tiled_force = idx; }
 
 // EPI_SWIGLU: a.N is 2 * i_half on entry (used to pick the tile shape); the
 // kernel's row space is then whole tiles of paired gate and up rows.
-hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant) {
     // Kernel choice, from MI355X measurements at the Llama-8B and Qwen-32B
     // prefill shard shapes, all on 8 waves: 256 x 256 tiles when they give at
     // least 192 tiles; else 256 x 128 tiles when those do; else 128 x 128
@@ -752,14 +755,16 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
     else if (a.K % 64 != 0) best = 4 + shape;
     else if (shape == 1 && tiles(256, 128) < kCus && tiles(192, 128) <= kCus) best = 11;
     else best = 8 + shape;
-    if (g_tiled_force >= 0 && g_tiled_force < kNumTiled && a.K % kTiled[g_tiled_force].kmul == 0)
-        best = g_tiled_force;
+    if (variant >= 0 && variant < kNumTiled && a.K % kTiled[variant].kmul == 0) best = variant;
     const TiledEntry& e = kTiled[best];
-    if (!g_tiled_attr[best]) {
-        const hipError_t ae = hipFuncSetAttribute(reinterpret_cast<const void*>(e.fn),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize, e.lds);
-        if (ae != hipSuccess) return ae;
-        g_tiled_attr[best] = true;
+    int dev = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he != hipSuccess) return he;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!g_tiled_attr[dev][best].load(std::memory_order_acquire)) {
+        he = hipFuncSetAttribute(reinterpret_cast<const void*>(e.fn), hipFuncAttributeMaxDynamicSharedMemorySize, e.lds);
+        if (he != hipSuccess) return he;
+        g_tiled_attr[dev][best].store(true, std::memory_order_release);
     }
     GemmArgs b = a;
     if (a.epi == EPI_SWIGLU) b.N = (int64_t)e.bn * ((a.i_half + e.bn / 2 - 1) / (e.bn / 2));

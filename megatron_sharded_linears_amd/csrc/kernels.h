@@ -45,16 +45,23 @@ enum Epilogue : int {
     EPI_SWIGLU = 1,   // weight rows [gate (i_half); up (i_half)]; y[m, j] = silu(bf16(g)) * bf16(u), bf16
     EPI_REDUCE = 2,   // y = bf16(sum over t partials in order), own = bf16(acc) at position `rank`
     EPI_REDUCE_ADD = 3,   // as EPI_REDUCE, then y = bf16(y + that sum): y is the residual, in place
+    // The same two with fp32 peers: the own partial enters the sum unrounded.
+    EPI_REDUCE_F32 = 4,
+    EPI_REDUCE_ADD_F32 = 5,
 };
+constexpr int kNumEpilogues = 6;
+constexpr bool epi_is_reduce(int e) { return e >= EPI_REDUCE && e != EPI_SWIGLU; }
+constexpr bool epi_is_add(int e) { return e == EPI_REDUCE_ADD || e == EPI_REDUCE_ADD_F32; }
+constexpr bool epi_peers_f32(int e) { return e == EPI_REDUCE_F32 || e == EPI_REDUCE_ADD_F32; }
 
 constexpr int kMaxFusedPeers = 16;   // t limit of the fused reduce epilogue
 
 // Linear Y[M, N] = X[M, K] W[N, K]^T (+ bias[N]); out_dtype TP_BF16 / TP_F32.
 // With EPI_SWIGLU, N is the kernel's row space (groups of gate rows paired
 // with the same up rows, see the kernels), the weight holds 2 * i_half rows
-// and y is [M, i_half]. With EPI_REDUCE (decode kernel only, N % 4 == 0), y
-// is [M, N] bf16 and peers[i] (bf16 [M, N], i != rank) are the other ranks'
-// partials.
+// and y is [M, i_half]. With the reduce epilogues (decode kernel only,
+// N % 4 == 0), y is [M, N] bf16 and peers[i] ([M, N] bf16, or fp32 for the
+// _F32 epilogues; i != rank) are the other ranks' partials.
 struct GemmArgs {
     const void* x;
     const void* w;
@@ -72,8 +79,9 @@ struct GemmArgs {
     const void* peers[kMaxFusedPeers];
 };
 
-// Scratch for K split across workgroups: fp32 partial tiles and one arrival
-// counter per output tile. Counters must be zero before a launch; every
+// Caller-owned scratch (the C ABI's workspace argument): fp32 partial tiles
+// and one arrival counter per output tile for K split across workgroups, the
+// attention's chunk records. Counters must be zero before a launch; every
 // kernel that uses them leaves them zero again.
 struct Workspace {
     float* partials;
@@ -93,24 +101,26 @@ struct SkinnyPlan {
     int64_t ntiles;  // workgroups along N
 };
 
-// Workspace the library keeps per (device, stream) for split-K partials.
+// The workspace size the planner's choices were measured with.
 constexpr int64_t kSkinnyWsFloats = (int64_t)4 << 20;   // 16 MiB
 constexpr int64_t kSkinnyWsCounters = 65536;
 
-// ws_floats: the workspace floats a K split may use (less than the whole
-// workspace when the caller keeps an operand at its back).
-SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats = kSkinnyWsFloats);
+// ws_floats / ws_counters: the scratch floats and counters a K split may use
+// (zero: keep K in one workgroup).
+SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64_t ws_counters);
 bool skinny_variant_exists(const SkinnyPlan& p);
 bool skinny_plan_fits(const SkinnyPlan& p, int64_t M);   // LDS need for M tokens within limits
 // The norm prologue's plan (splits == 0: no variant stages whole rows of K
 // for M tokens; normalise separately) and its fit test.
-SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K);
+SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64_t ws_counters);
 bool skinny_norm_plan_fits(const SkinnyPlan& p, int64_t M, int64_t K);
 int64_t skinny_workspace_floats(const SkinnyPlan& p, int64_t M, int64_t N);
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace& ws, hipStream_t s);
 
-hipError_t launch_tiled(const GemmArgs& a, hipStream_t s);   // EPI_STORE or EPI_SWIGLU (a.N = 2 i_half)
+// EPI_STORE or EPI_SWIGLU (a.N = 2 i_half). variant: a kernel index in
+// [0, tiled_variant_count()), or -1 for the automatic choice; one whose K
+// multiple the call does not meet is replaced by the automatic choice.
+hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant = -1);
 int tiled_variant_count();
-void tiled_force_variant(int idx);   // -1: automatic
 
 }  // namespace tpk

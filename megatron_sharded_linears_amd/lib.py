@@ -39,14 +39,30 @@ KIND = {"qkv": TP_W_QKV, "o": TP_W_O, "gate_up": TP_W_GATE_UP, "down": TP_W_DOWN
         "embed": TP_W_EMBED, "lm_head": TP_W_LM_HEAD}
 
 STATUS_NAMES = {0: "TP_OK", -1: "TP_ERR_NULL", -2: "TP_ERR_SHAPE", -3: "TP_ERR_DIVISIBILITY",
-                -4: "TP_ERR_ALIGNMENT", -5: "TP_ERR_DTYPE", -6: "TP_ERR_RANGE",
-                -7: "TP_ERR_HIP", -8: "TP_ERR_ALLOC"}
+                -4: "TP_ERR_ALIGNMENT", -5: "TP_ERR_DTYPE", -6: "TP_ERR_RANGE", -7: "TP_ERR_HIP"}
+
+TP_EPI_STORE, TP_EPI_SWIGLU, TP_EPI_REDUCE, TP_EPI_REDUCE_ADD = range(4)
+TP_WS_COUNTER_BYTES = 262144
 
 
 class tp_model_cfg(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("intermediate", ctypes.c_int32), ("vocab", ctypes.c_int32)]
+
+
+class tp_linear_plan(ctypes.Structure):
+    _fields_ = [("decode_ksteps", ctypes.c_int32), ("decode_nwn", ctypes.c_int32), ("decode_nwk", ctypes.c_int32),
+                ("decode_x_direct", ctypes.c_int32), ("prefill_tile", ctypes.c_int32)]
+
+
+class tp_linear_call(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("w", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("bias", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("out_dtype", ctypes.c_int32), ("epilogue", ctypes.c_int32),
+                ("partials", ctypes.POINTER(ctypes.c_void_p)), ("partial_dtype", ctypes.c_int32),
+                ("t", ctypes.c_int32), ("rank", ctypes.c_int32), ("norm", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("plan", tp_linear_plan), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
 
 
 class TPError(RuntimeError):
@@ -62,31 +78,33 @@ _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 _cfgp = ctypes.POINTER(tp_model_cfg)
 _ptr_array = ctypes.POINTER(ctypes.c_void_p)
 
+_ws = [_vp, _i64]           # workspace, workspace_bytes
+
 _PROTOS = {
     "tp_status_string": (ctypes.c_char_p, [_int]),
     "tp_full_shape": (_int, [_cfgp, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "tp_shard_shape": (_int, [_cfgp, _int, _int, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "tp_vocab_shard_rows": (_i64, [_i64, _int]),
     "tp_kv_heads_of_rank": (_int, [_cfgp, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
+    "tp_workspace_bytes": (_i64, []),
     "tp_shard_weights": (_int, [_cfgp, _int, _int, _int, _vp, _vp, _vp]),
-    "tp_column_linear": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "tp_column_linear": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp] + _ws + [_vp]),
     "tp_swiglu": (_int, [_vp, _i64, _i64, _vp, _vp]),
-    "tp_column_linear_swiglu": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp]),
-    "tp_row_linear_reduce": (_int, [_vp, _i64, _i64, _vp, _i64, _ptr_array, _int, _int, _vp, _vp]),
-    "tp_row_linear_reduce_add": (_int, [_vp, _i64, _i64, _vp, _i64, _ptr_array, _int, _int, _vp, _vp]),
+    "tp_column_linear_swiglu": (_int, [_vp, _i64, _i64, _vp, _i64, _vp] + _ws + [_vp]),
+    "tp_row_linear_reduce": (_int, [_vp, _i64, _i64, _vp, _i64, _ptr_array, _int, _int, _int, _vp] + _ws + [_vp]),
+    "tp_row_linear_reduce_add": (_int, [_vp, _i64, _i64, _vp, _i64, _ptr_array, _int, _int, _int, _vp] + _ws + [_vp]),
     "tp_fold_norm_weight": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
-    "tp_rmsnorm_column_linear": (_int, [_vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
-    "tp_rmsnorm_column_linear_swiglu": (_int, [_vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp]),
-    "tp_row_linear_partial": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp]),
+    "tp_rmsnorm_column_linear": (_int, [_vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp, _vp] + _ws + [_vp]),
+    "tp_rmsnorm_column_linear_swiglu": (_int, [_vp, ctypes.c_float, _i64, _i64, _vp, _i64, _vp] + _ws + [_vp]),
+    "tp_row_linear_partial": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int] + _ws + [_vp]),
     "tp_reduce_partials": (_int, [_ptr_array, _int, _i64, _int, _vp, _int, _vp]),
     "tp_vocab_embed": (_int, [_vp, _i64, _vp, _i64, _int, _int, _i64, _vp, _vp]),
-    "tp_lm_head_shard": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int, _vp]),
+    "tp_lm_head_shard": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _int] + _ws + [_vp]),
     "tp_concat_logits": (_int, [_ptr_array, _int, _i64, _i64, _i64, _int, _vp, _vp]),
     "tp_add_rmsnorm": (_int, [_vp, _i64, _i64, _vp, _vp, ctypes.c_float, _vp, _vp]),
     "tp_reduce_add_rmsnorm": (_int, [_ptr_array, _int, _int, _i64, _i64, _vp, _vp, ctypes.c_float, _vp, _vp]),
-    "tp_decode_attention": (_int, [_vp, _i64, _int, _int, _int, _vp, _vp, _i64, _vp, _vp, _vp]),
-    "tp_tune_skinny": (_int, [_int, _int, _int, _int]),
-    "tp_tune_tiled": (_int, [_int]),
+    "tp_decode_attention": (_int, [_vp, _i64, _int, _int, _int, _vp, _vp, _i64, _vp, _vp] + _ws + [_vp]),
+    "tp_linear_ex": (_int, [ctypes.POINTER(tp_linear_call), _vp]),
 }
 for _name, (_res, _args) in _PROTOS.items():
     _f = getattr(_lib, _name)
@@ -183,12 +201,84 @@ def tp_kv_heads_of_rank(cfg, t, rank):
     return f.value, c.value
 
 
-def tp_tune_skinny(ksteps=0, nwn=0, nwk=0, x_direct=0):
-    _check(_lib.tp_tune_skinny(ksteps, nwn, nwk, x_direct), "tp_tune_skinny")
+def tp_workspace_bytes():
+    return int(_lib.tp_workspace_bytes())
 
 
-def tp_tune_tiled(variant=-1):
-    _check(_lib.tp_tune_tiled(variant), "tp_tune_tiled")
+# --------------------------------------------------------------- workspace
+
+_default_ws = {}
+
+
+def make_workspace(nbytes=None, device=None):
+    """A zero-filled device buffer to pass as `workspace=` (the counters at its
+    front must start at zero; every call leaves them zero). Calls that share
+    one workspace must be ordered on one stream."""
+    n = tp_workspace_bytes() if nbytes is None else int(nbytes)
+    return torch.zeros(n, dtype=torch.uint8, device=device if device is not None else "cuda")
+
+
+def default_workspace(device=None):
+    """The workspace the wrappers use when none is passed: one per device,
+    made on first use (outside any graph capture). For calls on one stream;
+    callers on several streams pass workspaces of their own."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    ws = _default_ws.get(dev.index)
+    if ws is None:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("no default workspace yet on this device: make one call (or default_workspace()) "
+                               "before capturing a graph, or pass workspace=")
+        ws = make_workspace(device=dev)
+        torch.cuda.synchronize(dev)
+        _default_ws[dev.index] = ws
+    return ws
+
+
+def _ws_args(workspace, like):
+    """(pointer, bytes) of a workspace: a uint8 device tensor, None for the
+    device's default, or 0 for none at all."""
+    if isinstance(workspace, int) and workspace == 0:
+        return None, 0
+    ws = default_workspace(like.device) if workspace is None else workspace
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def _plan(plan):
+    """tp_linear_plan from a dict: decode=(ksteps, nwn, nwk, x_direct) and/or
+    tile=<prefill kernel index>."""
+    p = tp_linear_plan(0, 0, 0, 0, 0)
+    if plan is None:
+        return p
+    if "decode" in plan and plan["decode"] is not None:
+        p.decode_ksteps, p.decode_nwn, p.decode_nwk, p.decode_x_direct = (int(v) for v in plan["decode"])
+    if "tile" in plan and plan["tile"] is not None:
+        p.prefill_tile = int(plan["tile"]) + 1
+    return p
+
+
+def _linear_ex(x, M, K, w, N, y, out_dtype, epilogue, bias=None, partials=None, partial_dtype=TP_BF16, t=0, rank=0,
+               norm_eps=None, plan=None, workspace=None, stream=None, where="tp_linear_ex"):
+    """Any linear through tp_linear_ex with an explicit kernel plan."""
+    c = tp_linear_call()
+    c.x, c.M, c.K, c.w, c.N = x, M, K, w, N
+    c.bias = bias
+    c.y = y
+    c.out_dtype, c.epilogue = out_dtype, epilogue
+    keep = None
+    if partials is not None:
+        keep = (ctypes.c_void_p * len(partials))(*partials)
+        c.partials = ctypes.cast(keep, _ptr_array)
+    c.partial_dtype, c.t, c.rank = partial_dtype, t, rank
+    c.norm = 0 if norm_eps is None else 1
+    c.eps = 0.0 if norm_eps is None else float(norm_eps)
+    c.plan = _plan(plan)
+    c.workspace, c.workspace_bytes = workspace
+    _check(_lib.tp_linear_ex(ctypes.byref(c), _stream(stream)), where)
+    del keep
 
 
 # ------------------------------------------------------------ device calls
@@ -216,16 +306,23 @@ def _linear_shapes(x, w, y, name):
     return M, K, N
 
 
-def tp_column_linear(x, w_shard, y, bias=None, stream=None):
+def tp_column_linear(x, w_shard, y, bias=None, workspace=None, plan=None, stream=None):
+    """y = x w_shard^T (+ bias). `workspace`: a uint8 device tensor (None: the
+    device's default, 0: none); `plan`: an explicit kernel shape
+    ({"decode": (ksteps, nwn, nwk, x_direct)} or {"tile": index}) run through
+    tp_linear_ex, for sweeps and variant tests."""
     M, K, N = _linear_shapes(x, w_shard, y, "tp_column_linear")
     b = None
     if bias is not None:
         b = _dev(bias, "bias", torch.bfloat16, 1)
         if bias.shape[0] != N:
             raise ValueError("bias length != N")
-    _check(_lib.tp_column_linear(_dev(x, "x", torch.bfloat16, 2), M, K, _dev(w_shard, "w_shard", torch.bfloat16, 2),
-                                 N, b, _dev(y, "y", torch.bfloat16, 2), _stream(stream)),
-           "tp_column_linear")
+    xp, wp, yp = _dev(x, "x", torch.bfloat16, 2), _dev(w_shard, "w_shard", torch.bfloat16, 2), _dev(y, "y", torch.bfloat16, 2)
+    ws = _ws_args(workspace, x)
+    if plan is not None:
+        _linear_ex(xp, M, K, wp, N, yp, TP_BF16, TP_EPI_STORE, bias=b, plan=plan, workspace=ws, stream=stream)
+        return y
+    _check(_lib.tp_column_linear(xp, M, K, wp, N, b, yp, *ws, _stream(stream)), "tp_column_linear")
     return y
 
 
@@ -238,66 +335,77 @@ def tp_swiglu(gu, out, stream=None):
     return out
 
 
-def tp_column_linear_swiglu(x, w_gate_up, act, stream=None):
+def _swiglu_shapes(x, w, act, name):
     M, K = x.shape
-    two_i, K2 = w_gate_up.shape
+    two_i, K2 = w.shape
     if K != K2 or two_i % 2 or tuple(act.shape) != (M, two_i // 2):
-        raise ValueError("tp_column_linear_swiglu: need x [M, K], w_gate_up [2 I, K], act [M, I]")
-    _check(_lib.tp_column_linear_swiglu(_dev(x, "x", torch.bfloat16, 2), M, K,
-                                        _dev(w_gate_up, "w_gate_up", torch.bfloat16, 2), two_i // 2,
-                                        _dev(act, "act", torch.bfloat16, 2), _stream(stream)),
-           "tp_column_linear_swiglu")
+        raise ValueError(f"{name}: need x [M, K], w_gate_up [2 I, K], act [M, I]")
+    return M, K, two_i // 2
+
+
+def tp_column_linear_swiglu(x, w_gate_up, act, workspace=None, plan=None, stream=None):
+    M, K, Is = _swiglu_shapes(x, w_gate_up, act, "tp_column_linear_swiglu")
+    xp, wp, ap = _dev(x, "x", torch.bfloat16, 2), _dev(w_gate_up, "w_gate_up", torch.bfloat16, 2), _dev(act, "act", torch.bfloat16, 2)
+    ws = _ws_args(workspace, x)
+    if plan is not None:
+        _linear_ex(xp, M, K, wp, Is, ap, TP_BF16, TP_EPI_SWIGLU, plan=plan, workspace=ws, stream=stream)
+        return act
+    _check(_lib.tp_column_linear_swiglu(xp, M, K, wp, Is, ap, *ws, _stream(stream)), "tp_column_linear_swiglu")
     return act
 
 
-def tp_row_linear_reduce(x_shard, w_shard, partials, rank, out, stream=None):
-    """`partials`: t entries; entry `rank` is ignored (None allowed), the others
-    are the other ranks' bf16 [M, N] partials."""
-    M, K, N = _linear_shapes(x_shard, w_shard, out, "tp_row_linear_reduce")
+def _peer_ptrs(partials, rank, M, N):
+    """Device pointers of the other ranks' partials (slot `rank` ignored, None
+    allowed) and their common dtype code."""
     t = len(partials)
     if t < 1 or t > TP_MAX_SHARDS:
         raise ValueError("need 1..64 partials")
+    dts = {p.dtype for i, p in enumerate(partials) if i != rank and p is not None}
+    if len(dts) > 1:
+        raise ValueError("partials differ in dtype")
+    dt = dts.pop() if dts else torch.bfloat16
     ptrs = []
     for i, p in enumerate(partials):
         if i == rank:
             ptrs.append(0)
             continue
-        _dev(p, f"partials[{i}]", torch.bfloat16, 2)
+        _dev(p, f"partials[{i}]", dt, 2)
         if tuple(p.shape) != (M, N):
             raise ValueError(f"partials[{i}] must be [M, N]")
         ptrs.append(p.data_ptr())
+    return ptrs, _dtype_code(dt)
+
+
+def _row_reduce(name, epilogue, x_shard, w_shard, partials, rank, y, workspace, plan, stream):
+    M, K, N = _linear_shapes(x_shard, w_shard, y, name)
+    ptrs, pdt = _peer_ptrs(partials, rank, M, N)
+    t = len(partials)
+    xp, wp, yp = _dev(x_shard, "x_shard", torch.bfloat16, 2), _dev(w_shard, "w_shard", torch.bfloat16, 2), \
+        _dev(y, "out" if epilogue == TP_EPI_REDUCE else "residual", torch.bfloat16, 2)
+    ws = _ws_args(workspace, x_shard)
+    if plan is not None:
+        _linear_ex(xp, M, K, wp, N, yp, TP_BF16, epilogue, partials=ptrs, partial_dtype=pdt, t=t, rank=rank,
+                   plan=plan, workspace=ws, stream=stream, where=name)
+        return y
     arr = (ctypes.c_void_p * t)(*ptrs)
-    _check(_lib.tp_row_linear_reduce(_dev(x_shard, "x_shard", torch.bfloat16, 2), M, K,
-                                     _dev(w_shard, "w_shard", torch.bfloat16, 2), N,
-                                     ctypes.cast(arr, _ptr_array), t, rank,
-                                     _dev(out, "out", torch.bfloat16, 2), _stream(stream)),
-           "tp_row_linear_reduce")
-    return out
+    _check(getattr(_lib, name)(xp, M, K, wp, N, ctypes.cast(arr, _ptr_array), pdt, t, rank, yp, *ws, _stream(stream)),
+           name)
+    return y
 
 
-def tp_row_linear_reduce_add(x_shard, w_shard, partials, rank, residual, stream=None):
+def tp_row_linear_reduce(x_shard, w_shard, partials, rank, out, workspace=None, plan=None, stream=None):
+    """`partials`: t entries; entry `rank` is ignored (None allowed), the others
+    are the other ranks' [M, N] partials, all bf16 or all fp32 (the rank's own
+    partial then enters the sum as that dtype stores it)."""
+    return _row_reduce("tp_row_linear_reduce", TP_EPI_REDUCE, x_shard, w_shard, partials, rank, out, workspace, plan,
+                       stream)
+
+
+def tp_row_linear_reduce_add(x_shard, w_shard, partials, rank, residual, workspace=None, plan=None, stream=None):
     """residual <- bf16(residual + bf16(sum over ranks in order)), the rank's
     own partial being x_shard W^T; `partials` as in tp_row_linear_reduce."""
-    M, K, N = _linear_shapes(x_shard, w_shard, residual, "tp_row_linear_reduce_add")
-    t = len(partials)
-    if t < 1 or t > TP_MAX_SHARDS:
-        raise ValueError("need 1..64 partials")
-    ptrs = []
-    for i, p in enumerate(partials):
-        if i == rank:
-            ptrs.append(0)
-            continue
-        _dev(p, f"partials[{i}]", torch.bfloat16, 2)
-        if tuple(p.shape) != (M, N):
-            raise ValueError(f"partials[{i}] must be [M, N]")
-        ptrs.append(p.data_ptr())
-    arr = (ctypes.c_void_p * t)(*ptrs)
-    _check(_lib.tp_row_linear_reduce_add(_dev(x_shard, "x_shard", torch.bfloat16, 2), M, K,
-                                         _dev(w_shard, "w_shard", torch.bfloat16, 2), N,
-                                         ctypes.cast(arr, _ptr_array), t, rank,
-                                         _dev(residual, "residual", torch.bfloat16, 2), _stream(stream)),
-           "tp_row_linear_reduce_add")
-    return residual
+    return _row_reduce("tp_row_linear_reduce_add", TP_EPI_REDUCE_ADD, x_shard, w_shard, partials, rank, residual,
+                       workspace, plan, stream)
 
 
 def tp_fold_norm_weight(w, gamma, w_folded, stream=None):
@@ -313,7 +421,7 @@ def tp_fold_norm_weight(w, gamma, w_folded, stream=None):
     return w_folded
 
 
-def tp_rmsnorm_column_linear(h, eps, w_folded, y, bias=None, stream=None):
+def tp_rmsnorm_column_linear(h, eps, w_folded, y, bias=None, workspace=None, plan=None, stream=None):
     """y = RMSNorm(h) W^T (+ bias) with the norm's gamma folded into w_folded
     (tp_fold_norm_weight); the normalised rows are not written."""
     M, K, N = _linear_shapes(h, w_folded, y, "tp_rmsnorm_column_linear")
@@ -322,33 +430,69 @@ def tp_rmsnorm_column_linear(h, eps, w_folded, y, bias=None, stream=None):
         b = _dev(bias, "bias", torch.bfloat16, 1)
         if bias.shape[0] != N:
             raise ValueError("bias length != N")
-    _check(_lib.tp_rmsnorm_column_linear(_dev(h, "h", torch.bfloat16, 2), float(eps), M, K,
-                                         _dev(w_folded, "w_folded", torch.bfloat16, 2), N, b,
-                                         _dev(y, "y", torch.bfloat16, 2), _stream(stream)),
+    hp, wp, yp = _dev(h, "h", torch.bfloat16, 2), _dev(w_folded, "w_folded", torch.bfloat16, 2), _dev(y, "y", torch.bfloat16, 2)
+    ws = _ws_args(workspace, h)
+    if plan is not None:
+        _linear_ex(hp, M, K, wp, N, yp, TP_BF16, TP_EPI_STORE, bias=b, norm_eps=eps, plan=plan, workspace=ws,
+                   stream=stream)
+        return y
+    _check(_lib.tp_rmsnorm_column_linear(hp, float(eps), M, K, wp, N, b, yp, *ws, _stream(stream)),
            "tp_rmsnorm_column_linear")
     return y
 
 
-def tp_rmsnorm_column_linear_swiglu(h, eps, w_gate_up_folded, act, stream=None):
+def tp_rmsnorm_column_linear_swiglu(h, eps, w_gate_up_folded, act, workspace=None, plan=None, stream=None):
     """act = SwiGLU of RMSNorm(h) W_gate_up^T, gamma folded into the weight."""
-    M, K = h.shape
-    two_i, K2 = w_gate_up_folded.shape
-    if K != K2 or two_i % 2 or tuple(act.shape) != (M, two_i // 2):
-        raise ValueError("tp_rmsnorm_column_linear_swiglu: need h [M, K], w_gate_up [2 I, K], act [M, I]")
-    _check(_lib.tp_rmsnorm_column_linear_swiglu(_dev(h, "h", torch.bfloat16, 2), float(eps), M, K,
-                                                _dev(w_gate_up_folded, "w_gate_up_folded", torch.bfloat16, 2),
-                                                two_i // 2, _dev(act, "act", torch.bfloat16, 2), _stream(stream)),
+    M, K, Is = _swiglu_shapes(h, w_gate_up_folded, act, "tp_rmsnorm_column_linear_swiglu")
+    hp, wp, ap = (_dev(h, "h", torch.bfloat16, 2), _dev(w_gate_up_folded, "w_gate_up_folded", torch.bfloat16, 2),
+                  _dev(act, "act", torch.bfloat16, 2))
+    ws = _ws_args(workspace, h)
+    if plan is not None:
+        _linear_ex(hp, M, K, wp, Is, ap, TP_BF16, TP_EPI_SWIGLU, norm_eps=eps, plan=plan, workspace=ws, stream=stream)
+        return act
+    _check(_lib.tp_rmsnorm_column_linear_swiglu(hp, float(eps), M, K, wp, Is, ap, *ws, _stream(stream)),
            "tp_rmsnorm_column_linear_swiglu")
     return act
 
 
-def tp_row_linear_partial(x_shard, w_shard, partial, stream=None):
+def tp_row_linear_partial(x_shard, w_shard, partial, workspace=None, plan=None, stream=None):
     M, K, N = _linear_shapes(x_shard, w_shard, partial, "tp_row_linear_partial")
-    _check(_lib.tp_row_linear_partial(_dev(x_shard, "x_shard", torch.bfloat16, 2), M, K,
-                                      _dev(w_shard, "w_shard", torch.bfloat16, 2), N,
-                                      _dev(partial, "partial", partial.dtype, 2), _dtype_code(partial.dtype),
-                                      _stream(stream)), "tp_row_linear_partial")
+    xp, wp = _dev(x_shard, "x_shard", torch.bfloat16, 2), _dev(w_shard, "w_shard", torch.bfloat16, 2)
+    pp, dt = _dev(partial, "partial", partial.dtype, 2), _dtype_code(partial.dtype)
+    ws = _ws_args(workspace, x_shard)
+    if plan is not None:
+        _linear_ex(xp, M, K, wp, N, pp, dt, TP_EPI_STORE, plan=plan, workspace=ws, stream=stream)
+        return partial
+    _check(_lib.tp_row_linear_partial(xp, M, K, wp, N, pp, dt, *ws, _stream(stream)), "tp_row_linear_partial")
     return partial
+
+
+_EPI = {"store": TP_EPI_STORE, "swiglu": TP_EPI_SWIGLU, "reduce": TP_EPI_REDUCE, "reduce_add": TP_EPI_REDUCE_ADD}
+
+
+def tp_linear_ex(x, w, y, epilogue="store", bias=None, partials=None, rank=0, eps=None, plan=None,
+                 workspace=None, stream=None):
+    """Any linear through the C call tp_linear_ex: `epilogue` "store" (y = x
+    w^T (+ bias), bf16 or fp32 y), "swiglu" (w [2 I, K], y [M, I]), "reduce"
+    or "reduce_add" (`partials` and `rank` as in tp_row_linear_reduce); `eps`
+    given: the rows of x RMS-normalised (gamma folded into w); `plan`: the
+    kernel shape, as in tp_column_linear."""
+    e = _EPI[epilogue]
+    M, K = x.shape
+    if e == TP_EPI_SWIGLU:
+        M, K, N = _swiglu_shapes(x, w, y, "tp_linear_ex")
+    else:
+        M, K, N = _linear_shapes(x, w, y, "tp_linear_ex")
+    xp, wp = _dev(x, "x", torch.bfloat16, 2), _dev(w, "w", torch.bfloat16, 2)
+    yp, dt = _dev(y, "y", y.dtype, 2), _dtype_code(y.dtype)
+    b = None if bias is None else _dev(bias, "bias", torch.bfloat16, 1)
+    ptrs, pdt, t = None, TP_BF16, 0
+    if e in (TP_EPI_REDUCE, TP_EPI_REDUCE_ADD):
+        ptrs, pdt = _peer_ptrs(partials, rank, M, N)
+        t = len(partials)
+    _linear_ex(xp, M, K, wp, N, yp, dt, e, bias=b, partials=ptrs, partial_dtype=pdt, t=t, rank=rank, norm_eps=eps,
+               plan=plan, workspace=_ws_args(workspace, x), stream=stream)
+    return y
 
 
 def tp_reduce_partials(partials, out, stream=None):
@@ -417,7 +561,7 @@ def tp_reduce_add_rmsnorm(partials, residual, gamma, eps, out, stream=None):
     return out
 
 
-def tp_decode_attention(qkv, k_cache, v_cache, lens, nq, ctx, stream=None):
+def tp_decode_attention(qkv, k_cache, v_cache, lens, nq, ctx, workspace=None, stream=None):
     """One decode step of the rank's GQA attention: the new K, V of each
     sequence go to position lens[b] of the caches, then ctx = attention of
     its nq query heads over positions 0..lens[b]. Caches [B, nkv, L, d]."""
@@ -438,7 +582,7 @@ def tp_decode_attention(qkv, k_cache, v_cache, lens, nq, ctx, stream=None):
     _check(_lib.tp_decode_attention(ctypes.c_void_p(qkv.data_ptr()), B, nq, nkv, d,
                                     ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()), L,
                                     ctypes.c_void_p(lens.data_ptr()), ctypes.c_void_p(ctx.data_ptr()),
-                                    _stream(stream)), "tp_decode_attention")
+                                    *_ws_args(workspace, qkv), _stream(stream)), "tp_decode_attention")
     return ctx
 
 
@@ -455,11 +599,15 @@ def tp_vocab_embed(ids, e_shard, vocab, t, rank, out_partial, stream=None):
     return out_partial
 
 
-def tp_lm_head_shard(h, w_lm_shard, logits_shard, stream=None):
+def tp_lm_head_shard(h, w_lm_shard, logits_shard, workspace=None, plan=None, stream=None):
     M, K, N = _linear_shapes(h, w_lm_shard, logits_shard, "tp_lm_head_shard")
-    _check(_lib.tp_lm_head_shard(_dev(h, "h", torch.bfloat16, 2), M, K, _dev(w_lm_shard, "w_lm_shard", torch.bfloat16, 2),
-                                 N, _dev(logits_shard, "logits_shard", logits_shard.dtype, 2),
-                                 _dtype_code(logits_shard.dtype), _stream(stream)), "tp_lm_head_shard")
+    hp, wp = _dev(h, "h", torch.bfloat16, 2), _dev(w_lm_shard, "w_lm_shard", torch.bfloat16, 2)
+    lp, dt = _dev(logits_shard, "logits_shard", logits_shard.dtype, 2), _dtype_code(logits_shard.dtype)
+    ws = _ws_args(workspace, h)
+    if plan is not None:
+        _linear_ex(hp, M, K, wp, N, lp, dt, TP_EPI_STORE, plan=plan, workspace=ws, stream=stream)
+        return logits_shard
+    _check(_lib.tp_lm_head_shard(hp, M, K, wp, N, lp, dt, *ws, _stream(stream)), "tp_lm_head_shard")
     return logits_shard
 
 

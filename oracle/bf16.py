@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE ONLY. Nothing in the product path may import this module.
 
 The pages fix bf16 as the storage type of activations: the per-token
 all-reduce payload of Llama-3.1-8B is hidden 4096 x 2 B = 8 KiB ("张量、流水线与
-数据并行", section 每 token 的通信量), and the whole estimate there is "激活按
-bf16". They do not name a rounding mode; the oracle takes IEEE round to nearest,
-ties to even, the binary default.
+数据并行", section 每 token 的通信量), and that page's whole traffic estimate
+assumes two-byte activations. They do not name a rounding mode; the oracle takes
+IEEE round to nearest, ties to even, the binary default.
 
 bfloat16 is binary32 with the fraction cut to 7 stored bits: same exponent
 range (normal exponents -126..127), 8 significant bits, gradual underflow down

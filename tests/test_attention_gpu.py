@@ -120,6 +120,6 @@ def test_empty_batch_is_a_no_op():
     ctx = torch.full((1, nq * d), 7.0, dtype=torch.bfloat16, device=DEV)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     S = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    assert lib._lib.tp_decode_attention(P(qkv), 0, nq, nkv, d, P(kc), P(vc), L, P(lens), P(ctx), S) == 0
+    assert lib._lib.tp_decode_attention(P(qkv), 0, nq, nkv, d, P(kc), P(vc), L, P(lens), P(ctx), None, 0, S) == 0
     torch.cuda.synchronize()
     assert (f64(ctx) == 7.0).all() and (f64(kc) == 1.0).all()

@@ -29,18 +29,18 @@ def empty(shape, dtype=torch.bfloat16):
     return torch.empty(shape, dtype=dtype, device=DEV)
 
 
-def separate_swiglu(x, w, i_s):
+def separate_swiglu(x, w, i_s, plan=None):
     gu = empty((x.shape[0], 2 * i_s))
-    lib.tp_column_linear(x, w, gu)
+    lib.tp_column_linear(x, w, gu, plan=plan)
     act = empty((x.shape[0], i_s))
     lib.tp_swiglu(gu, act)
     return act
 
 
-def fused_swiglu(x, w, i_s):
+def fused_swiglu(x, w, i_s, plan=None):
     act = empty((x.shape[0], i_s))
     act.fill_(float("nan"))                      # every element must be written
-    lib.tp_column_linear_swiglu(x, w, act)
+    lib.tp_column_linear_swiglu(x, w, act, plan=plan)
     return act
 
 
@@ -65,14 +65,12 @@ def test_column_linear_swiglu_same_bits_as_separate_calls(M, Is, K):
 def test_every_prefill_tile_shape_fused_swiglu(variant):
     """The SwiGLU epilogue pairs gate and up rows inside each tile (first
     and second half of its rows): every tile shape, ragged widths."""
-    lib.tp_tune_tiled(variant)
-    try:
-        for (M, Is, K) in [(300, 520, 256), (130, 200, 1024), (257, 96, 64)]:
-            x = dev(I.normal_bf16((SEED, 20, M, Is, K), (M, K)))
-            w = dev(I.normal_bf16((SEED, 21, M, Is, K), (2 * Is, K), 0.05))
-            assert np.array_equal(bits(fused_swiglu(x, w, Is)), bits(separate_swiglu(x, w, Is))), (variant, M, Is, K)
-    finally:
-        lib.tp_tune_tiled(-1)
+    plan = {"tile": variant}
+    for (M, Is, K) in [(300, 520, 256), (130, 200, 1024), (257, 96, 64)]:
+        x = dev(I.normal_bf16((SEED, 20, M, Is, K), (M, K)))
+        w = dev(I.normal_bf16((SEED, 21, M, Is, K), (2 * Is, K), 0.05))
+        assert np.array_equal(bits(fused_swiglu(x, w, Is, plan)), bits(separate_swiglu(x, w, Is, plan))), \
+            (variant, M, Is, K)
 
 
 @pytest.mark.parametrize("M,Is,K", [(16, 100, 256), (3, 13, 72), (64, 1, 8), (100, 37, 136)])
@@ -90,36 +88,37 @@ def test_column_linear_swiglu_ragged_width_exact_integer(M, Is, K):
 
 @pytest.mark.parametrize("ks,nn,nk,xd", SKINNY_VARIANTS)
 def test_every_decode_variant_fused_epilogues(ks, nn, nk, xd):
-    lib.tp_tune_skinny(ks, nn, nk, xd)
-    try:
-        for (M, Is, K) in [(16, 136, 1032), (40, 48, 4104)]:
-            x = dev(I.normal_bf16((SEED, 5, M, Is, K), (M, K)))
-            w = dev(I.normal_bf16((SEED, 6, M, Is, K), (2 * Is, K), 0.05))
-            assert np.array_equal(bits(fused_swiglu(x, w, Is)), bits(separate_swiglu(x, w, Is))), (M, Is, K)
-        for (M, N, K, t, rank) in [(16, 200, 1032, 8, 3), (33, 64, 4104, 3, 0)]:
-            x = dev(I.normal_bf16((SEED, 7, M, N, K), (M, K)))
-            w = dev(I.normal_bf16((SEED, 8, M, N, K), (N, K), 0.05))
-            peers = [dev(I.normal_bf16((SEED, 9, M, N, i), (M, N))) for i in range(t)]
-            assert np.array_equal(bits(fused_reduce(x, w, peers, rank)), bits(separate_reduce(x, w, peers, rank)))
-    finally:
-        lib.tp_tune_skinny(0, 0, 0, 0)
+    plan = {"decode": (ks, nn, nk, xd)}
+    for (M, Is, K) in [(16, 136, 1032), (40, 48, 4104)]:
+        x = dev(I.normal_bf16((SEED, 5, M, Is, K), (M, K)))
+        w = dev(I.normal_bf16((SEED, 6, M, Is, K), (2 * Is, K), 0.05))
+        assert np.array_equal(bits(fused_swiglu(x, w, Is, plan)), bits(separate_swiglu(x, w, Is, plan))), (M, Is, K)
+    for (M, N, K, t, rank) in [(16, 200, 1032, 8, 3), (33, 64, 4104, 3, 0)]:
+        x = dev(I.normal_bf16((SEED, 7, M, N, K), (M, K)))
+        w = dev(I.normal_bf16((SEED, 8, M, N, K), (N, K), 0.05))
+        for dt in (torch.bfloat16, torch.float32):
+            peers = [dev(I.normal_bf16((SEED, 9, M, N, i), (M, N))).to(dt) for i in range(t)]
+            assert np.array_equal(bits(fused_reduce(x, w, peers, rank, plan)),
+                                  bits(separate_reduce(x, w, peers, rank, plan))), (M, N, K, t, rank, dt)
 
 
-def separate_reduce(x, w, peers, rank):
+def separate_reduce(x, w, peers, rank, plan=None):
+    """The rank's partial stored in the peers' dtype, then the reducer."""
     parts = list(peers)
-    parts[rank] = empty((x.shape[0], w.shape[0]))
-    lib.tp_row_linear_partial(x, w, parts[rank])
+    dt = next(p.dtype for i, p in enumerate(peers) if i != rank) if len(peers) > 1 else torch.bfloat16
+    parts[rank] = empty((x.shape[0], w.shape[0]), dt)
+    lib.tp_row_linear_partial(x, w, parts[rank], plan=plan)
     out = empty((x.shape[0], w.shape[0]))
     lib.tp_reduce_partials(parts, out)
     return out
 
 
-def fused_reduce(x, w, peers, rank):
+def fused_reduce(x, w, peers, rank, plan=None):
     out = empty((x.shape[0], w.shape[0]))
     out.fill_(float("nan"))
     parts = list(peers)
     parts[rank] = None
-    lib.tp_row_linear_reduce(x, w, parts, rank, out)
+    lib.tp_row_linear_reduce(x, w, parts, rank, out, plan=plan)
     return out
 
 
@@ -159,6 +158,41 @@ def test_row_linear_reduce_exact_integer(M, N, K, t):
     ref = oracle.all_reduce_sum(ps)
     assert np.all(np.abs(ref) <= 256)
     assert np.array_equal(f64(got), ref)
+
+
+@pytest.mark.parametrize("M,N,K", REDUCE_SHAPES)
+@pytest.mark.parametrize("t", [1, 2, 8, 16, 17])
+def test_row_linear_reduce_fp32_partials_same_bits_as_separate_calls(M, N, K, t):
+    """fp32 partial storage: the rank's own partial enters the sum as its
+    fp32 accumulator (unrounded), as tp_row_linear_partial into an fp32
+    buffer followed by tp_reduce_partials gives; one launch up to 16 ranks,
+    two beyond (the own partial staged in the workspace)."""
+    x = dev(I.normal_bf16((SEED, 30, M, N, K), (M, K)))
+    w = dev(I.normal_bf16((SEED, 31, M, N, K), (N, K), 0.05))
+    peers = [dev(I.normal_bf16((SEED, 32, M, N, t, i), (M, N), 0.5)).float() for i in range(t)]
+    for rank in sorted({0, t - 1}):
+        got = fused_reduce(x, w, peers, rank)
+        assert np.array_equal(bits(got), bits(separate_reduce(x, w, peers, rank))), (M, N, K, t, rank)
+    own = oracle.linear(f64(x.cpu()), f64(w.cpu()))
+    ps = [f64(p) for p in peers]
+    ps[t - 1] = own
+    assert_close(f64(got), oracle.all_reduce_sum(ps), f"fused reduce fp32 {(M, N, K, t)}")
+
+
+@pytest.mark.parametrize("M,N,K,t", [(16, 4096, 512, 8), (64, 300, 4104, 16), (90, 128, 200, 4), (16, 4096, 1792, 17)])
+def test_row_linear_reduce_fp32_partials_exact_integer(M, N, K, t):
+    """Integers in {-1, 0, 1} and peers in [-64, 64]: the fp32 own partial
+    and the fp32 sum are exact integers (below 2^24), so the one rounding to
+    bf16 is of the exact sum: bit-exact against the oracle."""
+    x = I.small_int_bf16((SEED, 33, M, N, K), (M, K))
+    w = I.small_int_bf16((SEED, 34, M, N, K), (N, K))
+    peers = [I.small_int_bf16((SEED, 35, M, N, i), (M, N), -64, 64).float() for i in range(t)]
+    rank = t // 2
+    got = fused_reduce(dev(x), dev(w), [dev(p) for p in peers], rank)
+    ps = [f64(p) for p in peers]
+    ps[rank] = oracle.linear(f64(x), f64(w))
+    ref = oracle.all_reduce_sum(ps)
+    assert np.array_equal(bits(got), oracle.bf16_bits(oracle.round_bf16(ref)))
 
 
 def test_row_linear_reduce_skipping_a_rank_fails_the_tolerance():

@@ -47,13 +47,14 @@ REDUCE_ADD_CASES = [(16, 512, 4096, 8, 0), (16, 1792, 4096, 8, 3), (16, 128, 256
                     (64, 896, 4096, 16, 2), (16, 64, 512, 17, 4), (100, 512, 1024, 4, 1)]
 
 
+@pytest.mark.parametrize("pdt", [torch.bfloat16, torch.float32], ids=["bf16_partials", "fp32_partials"])
 @pytest.mark.parametrize("M,K,N,t,rank", REDUCE_ADD_CASES)
-def test_row_linear_reduce_add(M, K, N, t, rank):
+def test_row_linear_reduce_add(M, K, N, t, rank, pdt):
     key = (SEED, 1, M, K, N, t)
     x = I.normal_bf16(key + (0,), (M, K))
     w = I.normal_bf16(key + (1,), (N, K), 0.02)
     res = I.normal_bf16(key + (2,), (M, N))
-    peers = [None if r == rank else dev(I.normal_bf16(key + (3, r), (M, N), 0.5)) for r in range(t)]
+    peers = [None if r == rank else dev(I.normal_bf16(key + (3, r), (M, N), 0.5)).to(pdt) for r in range(t)]
     # separate: the sum over ranks, then the residual add on the host (one
     # fp32 add of two bf16 values, rounded to nearest even, as the kernels do)
     red = empty((M, N))

@@ -92,27 +92,24 @@ SKINNY_VARIANTS = (
 
 @pytest.mark.parametrize("ks,nn,nk,xd", SKINNY_VARIANTS)
 def test_every_decode_kernel_variant_exact_and_deterministic(ks, nn, nk, xd):
-    lib.tp_tune_skinny(ks, nn, nk, xd)
-    try:
-        for (M, N, K) in [(16, 768, 4096), (64, 200, 1032), (3, 50, 520), (40, 96, 8192)]:
-            x = I.small_int_bf16((SEED, 3, M, N, K), (M, K))
-            w = I.small_int_bf16((SEED, 4, M, N, K), (N, K))
-            ref = oracle.linear(f64(x), f64(w))
-            xd, wd = dev(x), dev(w)
-            y1 = empty((M, N), torch.float32)
-            y2 = empty((M, N), torch.float32)
-            lib.tp_row_linear_partial(xd, wd, y1)
-            lib.tp_row_linear_partial(xd, wd, y2)
-            assert np.array_equal(f64(y1), ref), (M, N, K)
-            # random values too: must be bitwise reproducible (fixed split order)
-            xr = dev(I.normal_bf16((SEED, 5, M, K), (M, K)))
-            wr = dev(I.normal_bf16((SEED, 6, N, K), (N, K), 0.02))
-            lib.tp_row_linear_partial(xr, wr, y1)
-            lib.tp_row_linear_partial(xr, wr, y2)
-            assert torch.equal(y1, y2)
-            assert_close(f64(y1), oracle.linear(f64(xr.cpu()), f64(wr.cpu())), f"variant {(ks, nn, nk, xd)} {(M, N, K)}")
-    finally:
-        lib.tp_tune_skinny(0, 0, 0, 0)
+    plan = {"decode": (ks, nn, nk, xd)}
+    for (M, N, K) in [(16, 768, 4096), (64, 200, 1032), (3, 50, 520), (40, 96, 8192)]:
+        x = I.small_int_bf16((SEED, 3, M, N, K), (M, K))
+        w = I.small_int_bf16((SEED, 4, M, N, K), (N, K))
+        ref = oracle.linear(f64(x), f64(w))
+        xd_, wd = dev(x), dev(w)
+        y1 = empty((M, N), torch.float32)
+        y2 = empty((M, N), torch.float32)
+        lib.tp_row_linear_partial(xd_, wd, y1, plan=plan)
+        lib.tp_row_linear_partial(xd_, wd, y2, plan=plan)
+        assert np.array_equal(f64(y1), ref), (M, N, K)
+        # random values too: must be bitwise reproducible (fixed split order)
+        xr = dev(I.normal_bf16((SEED, 5, M, K), (M, K)))
+        wr = dev(I.normal_bf16((SEED, 6, N, K), (N, K), 0.02))
+        lib.tp_row_linear_partial(xr, wr, y1, plan=plan)
+        lib.tp_row_linear_partial(xr, wr, y2, plan=plan)
+        assert torch.equal(y1, y2)
+        assert_close(f64(y1), oracle.linear(f64(xr.cpu()), f64(wr.cpu())), f"variant {(ks, nn, nk, xd)} {(M, N, K)}")
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 6000, 4096), (3, 8008, 4104)])
@@ -133,37 +130,30 @@ def test_split_k_partials_are_never_stale():
     gets new inputs, so a partial read before its writer's store was visible
     (a stale value from the previous call) would break exactness."""
     for variant in [(4, 4, 1, 0), (4, 2, 2, 0), (8, 4, 2, 0)]:
-        lib.tp_tune_skinny(*variant)
-        try:
-            for it in range(6):
-                M, N, K = (16, 1000, 4096) if it % 2 == 0 else (40, 777, 2056)
-                x = I.small_int_bf16((SEED, 30, it) + variant, (M, K))
-                w = I.small_int_bf16((SEED, 31, it) + variant, (N, K))
-                y = empty((M, N), torch.float32)
-                lib.tp_row_linear_partial(dev(x), dev(w), y)
-                assert np.array_equal(f64(y), oracle.linear(f64(x), f64(w))), (variant, it)
-        finally:
-            lib.tp_tune_skinny(0, 0, 0, 0)
+        for it in range(6):
+            M, N, K = (16, 1000, 4096) if it % 2 == 0 else (40, 777, 2056)
+            x = I.small_int_bf16((SEED, 30, it) + variant, (M, K))
+            w = I.small_int_bf16((SEED, 31, it) + variant, (N, K))
+            y = empty((M, N), torch.float32)
+            lib.tp_row_linear_partial(dev(x), dev(w), y, plan={"decode": variant})
+            assert np.array_equal(f64(y), oracle.linear(f64(x), f64(w))), (variant, it)
 
 
 @pytest.mark.parametrize("variant", list(range(12)))
 def test_every_prefill_tile_shape_exact(variant):
-    lib.tp_tune_tiled(variant)
-    try:
-        for (M, N, K) in [(65, 70, 64), (300, 257, 200), (512, 768, 1032), (2048, 300, 640), (130, 1024, 4096),
-                          (700, 520, 96), (257, 4100, 32), (300, 257, 192), (129, 130, 128)]:
-            x = I.small_int_bf16((SEED, 40, M, N, K), (M, K))
-            w = I.small_int_bf16((SEED, 41, M, N, K), (N, K))
-            y = empty((M, N), torch.float32)
-            lib.tp_row_linear_partial(dev(x), dev(w), y)
-            assert np.array_equal(f64(y), oracle.linear(f64(x), f64(w))), (variant, M, N, K)
-            b = I.normal_bf16((SEED, 42, N), (N,))
-            yb = empty((M, N))
-            xr, wr = I.normal_bf16((SEED, 43, M, K), (M, K)), I.normal_bf16((SEED, 44, N, K), (N, K), 0.02)
-            lib.tp_column_linear(dev(xr), dev(wr), yb, bias=dev(b))
-            assert_close(f64(yb), oracle.linear(f64(xr), f64(wr), f64(b)), f"tile {variant} {(M, N, K)}")
-    finally:
-        lib.tp_tune_tiled(-1)
+    plan = {"tile": variant}
+    for (M, N, K) in [(65, 70, 64), (300, 257, 200), (512, 768, 1032), (2048, 300, 640), (130, 1024, 4096),
+                      (700, 520, 96), (257, 4100, 32), (300, 257, 192), (129, 130, 128)]:
+        x = I.small_int_bf16((SEED, 40, M, N, K), (M, K))
+        w = I.small_int_bf16((SEED, 41, M, N, K), (N, K))
+        y = empty((M, N), torch.float32)
+        lib.tp_row_linear_partial(dev(x), dev(w), y, plan=plan)
+        assert np.array_equal(f64(y), oracle.linear(f64(x), f64(w))), (variant, M, N, K)
+        b = I.normal_bf16((SEED, 42, N), (N,))
+        yb = empty((M, N))
+        xr, wr = I.normal_bf16((SEED, 43, M, K), (M, K)), I.normal_bf16((SEED, 44, N, K), (N, K), 0.02)
+        lib.tp_column_linear(dev(xr), dev(wr), yb, bias=dev(b), plan=plan)
+        assert_close(f64(yb), oracle.linear(f64(xr), f64(wr), f64(b)), f"tile {variant} {(M, N, K)}")
 
 
 # ------------------------------------------------ linears, random tolerance
