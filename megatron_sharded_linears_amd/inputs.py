@@ -58,3 +58,13 @@ def device_normal_bf16(shape, std, seed, device="cuda"):
     if std != 1.0:
         t.mul_(std)
     return t.to(torch.bfloat16)
+
+
+def device_small_int_bf16(shape, seed, lo=-1, hi=1, device="cuda"):
+    """bf16 tensor of integers drawn uniformly from [lo, hi] on the device with
+    a seeded torch generator: exact-integer inputs at sizes too large to draw
+    on the host quickly (sums of products of these are exact in fp32 while
+    below 2^24)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return torch.randint(lo, hi + 1, shape, generator=g, device=device, dtype=torch.int32).to(torch.bfloat16)
