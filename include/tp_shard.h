@@ -398,6 +398,26 @@ typedef struct {
  * with the automatic plan. */
 int tp_linear_ex(const tp_linear_call* call, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Without allocation or workspace
+ * ------------------------------------------------------------------------ */
+
+/* For callers that can neither allocate nor pass device memory of their own
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): tp_column_linear without the workspace argument. Its split-K
+ * scratch is a fixed array in the library's device memory, one copy per GPU,
+ * held until the process ends: TP_WS_COUNTER_BYTES of arrival counters and
+ * 4 MiB of fp32 partials. The call takes the kernel plan tp_column_linear
+ * takes with a workspace of tp_workspace_bytes() and gives the same bits;
+ * when that plan's partials (splits x M x N floats) exceed 4 MiB it returns
+ * TP_ERR_SHAPE and launches nothing. All calls on one GPU share that GPU's
+ * array: calls that overlap on one GPU (different streams or host threads)
+ * race; calls ordered on one stream do not. The first call on a device also
+ * launches a small kernel on `stream` that clears the counters. Arguments and
+ * errors otherwise as tp_column_linear. */
+int tp_column_linear_noalloc(const void* x, int64_t M, int64_t K, const void* w_shard, int64_t N,
+                             const void* bias_or_null, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

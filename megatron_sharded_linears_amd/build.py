@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
 
-KERNEL_SOURCES = ["memops.hip", "gemm_skinny.hip", "gemm_tiled.hip", "attention.hip"]
+KERNEL_SOURCES = ["memops.hip", "gemm_skinny.hip", "gemm_tiled.hip", "attention.hip", "noalloc.hip"]
 SOURCES = ["abi.cpp"] + KERNEL_SOURCES
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

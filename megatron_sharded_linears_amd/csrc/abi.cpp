@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "abi_internal.h"
 #include "kernels.h"
 #include "layer_ops.h"
 #include "tp_shard.h"
@@ -241,8 +242,9 @@ int launch_reduce_linear(tpk::GemmArgs a, const void* const* partials, int parti
     return hip_status(tpk::launch_reduce(ptrs, a.t, a.M * a.N, partial_dtype, out, TP_BF16, s));
 }
 
-// Validate and run one linear (every named linear call and tp_linear_ex).
-int linear_call(const tp_linear_call& c, hipStream_t s) {
+// Validate one linear (every named linear call and tp_linear_ex) and fill
+// the kernel arguments and the workspace view; host only.
+int validate_linear(const tp_linear_call& c, tpk::GemmArgs* out, tpk::Workspace* ws_out) {
     if (c.x == nullptr || c.w == nullptr || c.y == nullptr) return TP_ERR_NULL;
     if (c.M < 0 || c.N <= 0 || c.K <= 0 || c.M >= kMaxDim || c.N >= kMaxDim / 2 || c.K >= kMaxDim) return TP_ERR_SHAPE;
     if (c.epilogue < TP_EPI_STORE || c.epilogue > TP_EPI_REDUCE_ADD) return TP_ERR_DTYPE;
@@ -283,15 +285,12 @@ int linear_call(const tp_linear_call& c, hipStream_t s) {
             if (i < tpk::kMaxFusedPeers) a.peers[i] = c.partials[i];
         }
     }
-    tpk::Workspace ws;
-    st = view_workspace(c.workspace, c.workspace_bytes, &ws);
+    st = view_workspace(c.workspace, c.workspace_bytes, ws_out);
     if (st != TP_OK) return st;
     if (c.workspace != nullptr &&
         (overlap(c.workspace, c.workspace_bytes, c.x, x_bytes) || overlap(c.workspace, c.workspace_bytes, c.w, w_bytes) ||
          overlap(c.workspace, c.workspace_bytes, c.y, y_bytes)))
         return TP_ERR_SHAPE;
-    if (c.M == 0) return TP_OK;
-
     a.x = c.x; a.w = c.w; a.bias = c.bias; a.y = c.y;
     a.M = c.M; a.N = c.N; a.K = c.K;
     a.out_dtype = c.out_dtype;
@@ -301,10 +300,24 @@ int linear_call(const tp_linear_call& c, hipStream_t s) {
     a.rank = reduce ? c.rank : 0;
     a.norm = c.norm != 0 ? 1 : 0;
     a.eps = c.eps;
-    if (reduce) return launch_reduce_linear(a, c.partials, c.partial_dtype, ws, c.plan, s);
+    *out = a;
+    return TP_OK;
+}
+
+int linear_call_impl(const tp_linear_call& c, hipStream_t s) {
+    tpk::GemmArgs a;
+    tpk::Workspace ws;
+    const int st = validate_linear(c, &a, &ws);
+    if (st != TP_OK) return st;
+    if (c.M == 0) return TP_OK;
+    if (c.epilogue == TP_EPI_REDUCE || c.epilogue == TP_EPI_REDUCE_ADD)
+        return launch_reduce_linear(a, c.partials, c.partial_dtype, ws, c.plan, s);
     if (a.norm) return launch_norm_linear(a, ws, c.plan, s);
     return launch_linear(a, ws, c.plan, s);
 }
+
+// Alias so the named calls below read as before.
+int linear_call(const tp_linear_call& c, hipStream_t s) { return linear_call_impl(c, s); }
 
 tp_linear_call make_call(const void* x, int64_t M, int64_t K, const void* w, int64_t N, void* y, int out_dtype,
                          int epilogue, void* workspace, int64_t workspace_bytes) {
@@ -758,3 +771,36 @@ int tp_decode_attention(const void* qkv, int64_t B, int nq, int nkv, int head_di
 }
 
 }  // extern "C"
+
+namespace tpabi {
+
+int linear_call(const tp_linear_call& c, hipStream_t s) { return linear_call_impl(c, s); }
+
+int linear_scratch_need(const tp_linear_call& c, int64_t* floats, int64_t* counters) {
+    *floats = 0;
+    *counters = 0;
+    tp_linear_call v = c;
+    v.workspace = nullptr;
+    v.workspace_bytes = 0;
+    tpk::GemmArgs a;
+    tpk::Workspace none;
+    const int st = validate_linear(v, &a, &none);
+    if (st != TP_OK) return st;
+    if (c.M == 0 || c.M > kSkinnyMaxM) return TP_OK;      // the prefill kernel needs no scratch
+    // Only the plain and SwiGLU linears without the norm are asked about:
+    // the plan launch_linear would take with the tuned workspace size.
+    if (c.epilogue != TP_EPI_STORE && c.epilogue != TP_EPI_SWIGLU) return TP_ERR_SHAPE;
+    if (c.norm != 0) return TP_ERR_SHAPE;
+    const tpk::Workspace tuned{reinterpret_cast<float*>(16), tpk::kSkinnyWsFloats, reinterpret_cast<unsigned*>(16),
+                               tpk::kSkinnyWsCounters};
+    const int64_t n_rows = c.epilogue == TP_EPI_SWIGLU ? 16 * ((c.N + 7) / 8) : c.N;
+    tpk::SkinnyPlan p;
+    if (!decode_plan(c.M, n_rows, c.K, tuned, c.plan, &p)) return TP_OK;
+    if (p.splits > 1) {
+        *floats = tpk::skinny_workspace_floats(p, c.M, n_rows);
+        *counters = p.ntiles;
+    }
+    return TP_OK;
+}
+
+}  // namespace tpabi

@@ -105,6 +105,7 @@ _PROTOS = {
     "tp_reduce_add_rmsnorm": (_int, [_ptr_array, _int, _int, _i64, _i64, _vp, _vp, ctypes.c_float, _vp, _vp]),
     "tp_decode_attention": (_int, [_vp, _i64, _int, _int, _int, _vp, _vp, _i64, _vp, _vp] + _ws + [_vp]),
     "tp_linear_ex": (_int, [ctypes.POINTER(tp_linear_call), _vp]),
+    "tp_column_linear_noalloc": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _PROTOS.items():
     _f = getattr(_lib, _name)
@@ -323,6 +324,23 @@ def tp_column_linear(x, w_shard, y, bias=None, workspace=None, plan=None, stream
         _linear_ex(xp, M, K, wp, N, yp, TP_BF16, TP_EPI_STORE, bias=b, plan=plan, workspace=ws, stream=stream)
         return y
     _check(_lib.tp_column_linear(xp, M, K, wp, N, b, yp, *ws, _stream(stream)), "tp_column_linear")
+    return y
+
+
+def tp_column_linear_noalloc(x, w_shard, y, bias=None, stream=None):
+    """tp_column_linear with its scratch in the library's fixed per-GPU array
+    (no workspace, no allocation); TPError TP_ERR_SHAPE when the plan's split
+    partials exceed that array."""
+    M, K, N = _linear_shapes(x, w_shard, y, "tp_column_linear_noalloc")
+    b = None
+    if bias is not None:
+        b = _dev(bias, "bias", torch.bfloat16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias length != N")
+    _check(_lib.tp_column_linear_noalloc(_dev(x, "x", torch.bfloat16, 2), M, K,
+                                         _dev(w_shard, "w_shard", torch.bfloat16, 2), N, b,
+                                         _dev(y, "y", torch.bfloat16, 2), _stream(stream)),
+           "tp_column_linear_noalloc")
     return y
 
 

@@ -372,3 +372,18 @@ def test_sanitized_build_is_the_one_loaded():
     maps = open("/proc/self/maps").read()
     assert "libasan" in maps
     assert lib.library_path().endswith("libtpshard_asan.so") and lib.library_path() in maps
+
+
+def test_noalloc_linear_validates_and_rejects_large_plans_before_any_hip_call():
+    """tp_column_linear_noalloc checks its arguments, and that the plan
+    tp_column_linear would take fits its fixed 4 MiB of partials, on the host
+    before its first HIP call."""
+    f = C.tp_column_linear_noalloc
+    assert f(NULL, 16, 64, B, 32, NULL, Y, S) == -1
+    assert f(A, 16, 60, B, 32, NULL, Y, S) == -4
+    assert f(A, 16, 64, B, 32, NULL, ctypes.c_void_p(0x10000 + 256), S) == -2   # y inside x
+    assert f(A, 0, 64, B, 32, NULL, Y, S) == 0
+    X, W, Yb = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x3000000), ctypes.c_void_p(0x8000000)
+    # 64 tokens of a 4096 x 4096 weight: K split 8 ways, 8 x 64 x 4096 fp32
+    # partials (8 MiB) do not fit: rejected, nothing launched
+    assert f(X, 64, 4096, W, 4096, NULL, Yb, S) == -2
