@@ -1,7 +1,8 @@
 """Build libtpshard.so in-tree with hipcc, for gfx950 only.
 
-    python -m megatron_sharded_linears_amd.build            # the library
-    python -m megatron_sharded_linears_amd.build sanitized  # + the host ABI layer under ASan/UBSan
+    python -m megatron_sharded_linears_amd.build                # the library
+    python -m megatron_sharded_linears_amd.build --incremental  # recompile changed sources only
+    python -m megatron_sharded_linears_amd.build sanitized      # + the host ABI layer under ASan/UBSan
 
 Each source compiles to an object in parallel under _build/ at the repository
 root; the objects link into megatron_sharded_linears_amd/libtpshard.so next
@@ -46,26 +47,36 @@ def _run(cmd, what):
         sys.stderr.write(err + "\n")
 
 
+def _newest_header():
+    paths = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    paths += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
+    return max(os.path.getmtime(p) for p in paths)
+
+
 def _compile(job):
-    src, build_dir, defines = job
+    src, build_dir, defines, incremental = job
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    if incremental and os.path.exists(obj) and os.path.getmtime(obj) > max(
+            os.path.getmtime(os.path.join(CSRC, src)), _newest_header()):
+        return obj
     cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + ["-c", os.path.join(CSRC, src), "-o", obj]
     _run(cmd, f"hipcc on {src}")
     return obj
 
 
-def _objects(build_dir, defines, sources):
+def _objects(build_dir, defines, sources, incremental=False):
     os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
-        return list(ex.map(_compile, [(src, build_dir, tuple(defines)) for src in sources]))
+        return list(ex.map(_compile, [(src, build_dir, tuple(defines), incremental) for src in sources]))
 
 
-def build(verbose=True, lib=None, defines=()):
+def build(verbose=True, lib=None, defines=(), incremental=False):
     """Compile every source and link `lib` (default: the in-tree library).
-    `defines` are extra -D flags, for tuning builds (objects in _build/<tag>)."""
+    `defines` are extra -D flags, for tuning builds (objects in _build/<tag>).
+    incremental: reuse objects newer than their source and every header."""
     lib = lib or LIB
     tag = "obj" if not defines else "_".join(d.replace("=", "") for d in defines)
-    objs = _objects(os.path.join(BUILD, tag), defines, SOURCES)
+    objs = _objects(os.path.join(BUILD, tag), defines, SOURCES, incremental)
     tmp = lib + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, "link")
     os.replace(tmp, lib)
@@ -107,6 +118,6 @@ def asan_runtime():
 
 
 if __name__ == "__main__":
-    build()
-    if len(sys.argv) > 1 and sys.argv[1] == "sanitized":
+    build(incremental="--incremental" in sys.argv)
+    if "sanitized" in sys.argv:
         build_sanitized()
