@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--separate", action="store_true",
                    help="time the step through the separate calls (no fused SwiGLU / reduce epilogues)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--step-only", action="store_true",
+                   help="time the captured step only and print its figures (for a kernel trace of the step)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--counters", action="store_true",
                    help="run under rocprofv3 --pmc: a plain copy of known size, then W+K eager steps; "
@@ -157,6 +159,20 @@ class Rank:
             self.peer_logits = [dn((Ms, vs), 1.0, 80 + j) for j in range(t - 1)]
             self.full_logits = torch.empty((Ms, w.vocab), dtype=bf, device=dev)
 
+    def make_fp32_partials(self):
+        """fp32 copies of the other ranks' partial sums and fp32 buffers for
+        the rank's own (the variant that stores partials in fp32)."""
+        import torch
+        if hasattr(self, "po32"):
+            return
+        M, H = self.w.tokens, self.w.hidden
+        self.po32 = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        self.pd32 = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        cache = {}
+        for L in self.layers:
+            for k in ("peers_o", "peers_d"):
+                L[k + "32"] = [cache.setdefault(id(p), p.float()) for p in L[k]]
+
     def work(self):
         """Algorithmic flops and bytes per step, by op."""
         w = self.w
@@ -194,13 +210,19 @@ class Rank:
         return ops
 
 
-def build_ops(R, lib, fused_swiglu=True, fused_reduce=True):
+def build_ops(R, lib, fused_swiglu=True, fused_reduce=True, fp32_partials=False):
     """The step as a list of (name, fn, args): every call of one pass. Fused
-    calls replace gate_up + SwiGLU and a row-parallel linear + its reduce."""
+    calls replace gate_up + SwiGLU and a row-parallel linear + its reduce.
+    fp32_partials: the row-parallel linears' partial sums (the rank's own and
+    the other ranks') are stored in fp32 instead of bf16."""
     w = R.w
     t = w.t
     ops = []
     h = R.x
+    if fp32_partials:
+        R.make_fp32_partials()
+    po, pd = (R.po32, R.pd32) if fp32_partials else (R.po, R.pd)
+    pk_o, pk_d = ("peers_o32", "peers_d32") if fp32_partials else ("peers_o", "peers_d")
     if R.vocab:
         ops.append(("embed", lib.tp_vocab_embed, (R.ids, R.embed, w.vocab, t, 0, R.ze)))
         ops.append(("embed_reduce", lib.tp_reduce_partials, ([R.ze] + R.peers_e, R.h)))
@@ -208,20 +230,20 @@ def build_ops(R, lib, fused_swiglu=True, fused_reduce=True):
     for L in R.layers:
         ops.append(("qkv", lib.tp_column_linear, (h, L["qkv"], R.qkv)))
         if fused_reduce:
-            ops.append(("o_reduce", lib.tp_row_linear_reduce, (L["ctx"], L["o"], [None] + L["peers_o"], 0, R.y1)))
+            ops.append(("o_reduce", lib.tp_row_linear_reduce, (L["ctx"], L["o"], [None] + L[pk_o], 0, R.y1)))
         else:
-            ops.append(("o", lib.tp_row_linear_partial, (L["ctx"], L["o"], R.po)))
-            ops.append(("reduce", lib.tp_reduce_partials, ([R.po] + L["peers_o"], R.y1)))
+            ops.append(("o", lib.tp_row_linear_partial, (L["ctx"], L["o"], po)))
+            ops.append(("reduce", lib.tp_reduce_partials, ([po] + L[pk_o], R.y1)))
         if fused_swiglu:
             ops.append(("gate_up_swiglu", lib.tp_column_linear_swiglu, (R.y1, L["gate_up"], R.act)))
         else:
             ops.append(("gate_up", lib.tp_column_linear, (R.y1, L["gate_up"], R.gu)))
             ops.append(("swiglu", lib.tp_swiglu, (R.gu, R.act)))
         if fused_reduce:
-            ops.append(("down_reduce", lib.tp_row_linear_reduce, (R.act, L["down"], [None] + L["peers_d"], 0, R.h)))
+            ops.append(("down_reduce", lib.tp_row_linear_reduce, (R.act, L["down"], [None] + L[pk_d], 0, R.h)))
         else:
-            ops.append(("down", lib.tp_row_linear_partial, (R.act, L["down"], R.pd)))
-            ops.append(("reduce", lib.tp_reduce_partials, ([R.pd] + L["peers_d"], R.h)))
+            ops.append(("down", lib.tp_row_linear_partial, (R.act, L["down"], pd)))
+            ops.append(("reduce", lib.tp_reduce_partials, ([pd] + L[pk_d], R.h)))
         h = R.h
     if R.vocab:
         hs = h[h.shape[0] - R.hs_rows:]
@@ -363,6 +385,62 @@ def capture(torch, ops, only=None, repeat=1):
                 run_ops(ops, only)
     torch.cuda.synchronize()
     return g
+
+
+ROTATE_BYTES = 512 << 20    # distinct memory a per-op graph streams: twice the 256 MiB last-level cache
+
+
+def _tensors(args):
+    import torch
+    for a in args:
+        if isinstance(a, torch.Tensor):
+            yield a
+        elif isinstance(a, (list, tuple)):
+            yield from _tensors(a)
+
+
+def _clone_args(args):
+    import torch
+
+    def c(a):
+        if isinstance(a, torch.Tensor):
+            return a.clone()
+        if isinstance(a, list):
+            return [c(x) for x in a]
+        return a
+    return tuple(c(a) for a in args)
+
+
+def rotated_launches(ops, name, min_launches=8):
+    """The op's launches of one step, then the same launches on clones of
+    every operand, repeated until the launches touch at least ROTATE_BYTES of
+    distinct memory (and number at least `min_launches`): replayed back to
+    back, no launch finds its operands in a cache from the one before."""
+    base = [op for op in ops if op[0] == name]
+    out, seen = list(base), {}
+    for _, _, a in base:
+        for x in _tensors(a):
+            seen[x.data_ptr()] = x.numel() * x.element_size()
+    while sum(seen.values()) < ROTATE_BYTES or len(out) < min_launches:
+        for n, f, a in base:
+            ca = _clone_args(a)
+            for x in _tensors(ca):
+                seen[x.data_ptr()] = x.numel() * x.element_size()
+            out.append((n, f, ca))
+    return out, sum(seen.values())
+
+
+def time_rotated(torch, ops, name, reps):
+    """Microseconds per launch of op `name`: its rotated launches
+    (rotated_launches) captured into one graph, replayed `reps` times between
+    events on the replaying stream. Returns (us, distinct bytes)."""
+    launches, distinct = rotated_launches(ops, name)
+    g = capture(torch, launches)
+    ms = time_graph(torch, g, reps, 2)
+    n = len(launches)
+    del g, launches
+    torch.cuda.empty_cache()
+    return ms * 1e3 / n, distinct
 
 
 def time_graph(torch, g, reps, warmup):
@@ -600,7 +678,66 @@ def summarize_trace(path, top=30):
               f"{min(ds) / 1e3:8.2f} {max(ds) / 1e3:8.2f} {sum(ds) / 1e6:9.2f}")
 
 
+def summarize_step_trace(trace_csv, run_log, out=None):
+    """Kernel time per step from a rocprofv3 --kernel-trace (csv) of
+    `bench.py --step-only`: the dispatches of the last K (timed) replays,
+    per kernel and summed, against the step time the same run measured, and
+    the GEMM launches' algorithmic bytes over their summed durations."""
+    import csv
+    import re
+    with open(run_log) as f:
+        run = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            m = re.search(r"(\w+_kernel)(<[^>]*>)?", r["Kernel_Name"])
+            short = (m.group(1) + (m.group(2) or "")) if m else r["Kernel_Name"][:60]
+            wgs = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), f"{short} x{wgs}"))
+    rows.sort()
+    n_steps_trace, K = run["steps_in_trace"], run["steps"]
+    # The timed replays are the trace's last dispatches (set-up kernels such
+    # as the seeded generators come first): the step's length is the
+    # smallest period of the kernel sequence over its last K repeats.
+    names = [k for _, _, k in rows]
+    per = next((p for p in range(1, len(names) // K + 1)
+                if all(names[-1 - i] == names[-1 - i - p] for i in range(p * (K - 1)))), None)
+    if per is None:
+        raise SystemExit("no step period found in the trace")
+    timed = rows[-K * per:]
+    span_ms = (timed[-1][1] - timed[0][0]) / 1e6 / K
+    groups = {}
+    for a, b, k in timed:
+        groups.setdefault(k, []).append(b - a)
+    total_us = sum(b - a for a, b, _ in timed) / 1e3 / K
+    gemm_us = sum(b - a for a, b, k in timed if is_gemm_kernel(k)) / 1e3 / K
+    gemm_n = sum(1 for _, _, k in timed if is_gemm_kernel(k)) // K
+    alg = run["gemm_algorithmic_bytes_per_step"]
+    gbps = alg / (gemm_us * 1e-6) / 1e9
+    lines = [f"workload {run['workload']}: {per} dispatches per step; the last {K} of "
+             f"{n_steps_trace} passes (the timed graph replays)",
+             "", "| kernel x workgroups | per step | avg us | us per step |", "|---|---:|---:|---:|"]
+    for k, ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {len(ds) // K} | {sum(ds) / len(ds) / 1e3:.2f} | {sum(ds) / 1e3 / K:.2f} |")
+    lines += ["",
+              f"- sum of dispatch durations per step: {total_us:.1f} us",
+              f"- span of a traced step (first start to last end, averaged): {span_ms * 1e3:.1f} us",
+              f"- step time the traced run measured with events (ms_per_step): {run['ms_per_step'] * 1e3:.1f} us",
+              f"- GEMM dispatches per step: {gemm_n} (expected {run['gemm_launches_per_step']}), "
+              f"summed {gemm_us:.1f} us",
+              f"- GEMM algorithmic bytes per step: {alg} -> {gbps:.1f} GB/s over their summed durations, "
+              f"{gbps / HBM_PEAK_GBPS:.4f} of {HBM_PEAK_GBPS:.0f} GB/s"]
+    text = "\n".join(lines)
+    print(text)
+    if out:
+        with open(out, "w") as f:
+            f.write(text + "\n")
+
+
 def main():
+    if len(sys.argv) in (4, 5) and sys.argv[1] == "--summarize-step-trace":
+        summarize_step_trace(*sys.argv[2:])
+        return
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2])
         return
@@ -658,6 +795,20 @@ def main():
                           "source_sha256": gemm_source_sha256()}), flush=True)
         return
 
+    flops_step = sum(work[k][0] * work[k][1] for k in gemm_ops)
+    gemm_bytes_step = sum(work[k][0] * work[k][2] for k in gemm_ops)
+    if args.step_only:
+        # one eager pass (before capture), W warm-up replays, K timed replays
+        ms_step, wall_s = time_step(torch, ops, args.steps, args.warmup)
+        print(json.dumps({"workload": w.name, "ms_per_step": round(ms_step, 4), "steps": args.steps,
+                          "warmup": args.warmup, "steps_in_trace": 1 + args.warmup + args.steps,
+                          "value": round(flops_step / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+                          "gemm_launches_per_step": sum(work[k][0] for k in gemm_ops),
+                          "gemm_algorithmic_bytes_per_step": gemm_bytes_step,
+                          "gemm_flops_per_step": flops_step,
+                          "launches_per_step": len(ops)}), flush=True)
+        return
+
     # --- eager: the same calls issued one by one from Python
     for _ in range(args.warmup):
         run_ops(ops)
@@ -676,6 +827,17 @@ def main():
         ms_step = ms_eager
     # the same step through the other set of calls, for comparison
     ms_alt, _ = time_step(torch, alt_ops, args.steps, args.warmup)
+    # partial sums stored in bf16 or fp32, the reduce fused into the linear or
+    # a call of its own (decode; at prefill sizes the reduce is always separate)
+    partials = {}
+    for p32 in (False, True):
+        d = {}
+        for fr in ((True, False) if w.tokens <= 64 else (False,)):
+            ms_p = time_step(torch, build_ops(R, lib, fused_swiglu=fused, fused_reduce=fr, fp32_partials=p32),
+                             args.steps, args.warmup)[0]
+            d["reduce_fused" if fr else "reduce_separate"] = round(ms_p, 4)
+        partials["fp32" if p32 else "bf16"] = d
+    partials["default"] = "bf16"
     # and with the residual stream and the RMSNorms of a real layer
     norm_ops = build_norm_ops(R, lib)
     ms_norm, _ = time_step(torch, norm_ops, args.steps, args.warmup)
@@ -692,37 +854,25 @@ def main():
     op_names = names + [n for n in ("reduce",) if n not in names]
     for name in op_names:
         n_per_step, flops, byts = work[name]
-        repeat = max(1, -(-32 // n_per_step))   # at least 32 launches per replay
-        g = capture(torch, ops if name in names else alt_ops, only=name, repeat=repeat)
-        ms = time_graph(torch, g, args.steps, 2)
-        del g
-        us = ms * 1e3 / (n_per_step * repeat)
+        us, distinct = time_rotated(torch, ops if name in names else alt_ops, name, args.steps)
         per_op[name] = {"launches_per_step": n_per_step, "us_per_launch": round(us, 3),
                         "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                         "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2) if flops else None,
-                        "bytes_per_launch": byts}
+                        "bytes_per_launch": byts, "distinct_MiB": round(distinct / 2**20)}
 
     attn = None
     if layer_ops:
-        n_at = work["attention"][0]
-        g = capture(torch, layer_ops, only="attention", repeat=1)
-        us_at = time_graph(torch, g, args.steps, 2) * 1e3 / n_at
-        del g
+        us_at, _ = time_rotated(torch, layer_ops, "attention", args.steps)
         attn = {"us_per_call": round(us_at, 3), "GBps": round(work["attention"][2] / (us_at * 1e-6) / 1e9, 1),
                 "frac_of_hbm": round(work["attention"][2] / (us_at * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                 "bytes_per_call": work["attention"][2], "kv_len": KV_LEN, "kv_capacity": KV_CAP,
                 "q_heads": R.nq_r, "kv_heads": R.nkv_r}
-    n_norm = work["reduce_norm"][0]
-    g = capture(torch, norm_ops, only="reduce_norm", repeat=max(1, -(-32 // n_norm)))
-    us_norm = time_graph(torch, g, args.steps, 2) * 1e3 / (n_norm * max(1, -(-32 // n_norm)))
-    del g
+    us_norm, _ = time_rotated(torch, norm_ops, "reduce_norm", args.steps)
 
     copy = measure_copy(torch, lib, I, w)
 
-    flops_step = sum(work[k][0] * work[k][1] for k in gemm_ops)
     value = flops_step / (ms_step * 1e-3) / 1e12
     gemm_us = sum(per_op[k]["us_per_launch"] * work[k][0] for k in gemm_ops)
-    gemm_bytes_step = sum(work[k][0] * work[k][2] for k in gemm_ops)
     achieved = gemm_bytes_step / (gemm_us * 1e-6) / 1e9
     red = per_op["reduce"]
     st = stored_traffic(w.name)
@@ -772,6 +922,7 @@ def main():
         "eager_ms_per_step": round(ms_eager, 4),
         "gemm_only_TFLOPs": round(flops_step / (gemm_us * 1e-6) / 1e12, 2),
         "step_GBps": round(sum(work[k][0] * work[k][2] for k in names) / (ms_step * 1e-3) / 1e9, 1),
+        "partial_storage_ms_per_step": partials,
         "alt_path": {"calls": "separate" if fused else "fused", "ms_per_step": round(ms_alt, 4),
                      "value": round(flops_step / (ms_alt * 1e-3) / 1e12, 3)},
         "with_norms": {"calls": "input norm; per layer qkv, o partial, sum + residual add + RMSNorm "
