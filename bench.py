@@ -343,6 +343,17 @@ def build_layer_ops(R, lib, fused_norm, eps=1e-5):
 
 
 GEMM_OPS = ("qkv", "o", "gate_up", "down", "lm_head", "o_reduce", "gate_up_swiglu", "down_reduce")
+# (M, N, K) of each GEMM op's product, for the vendor-GEMM comparison
+GEMM_SHAPES = {
+    "qkv": lambda R: (R.w.tokens,) + tuple(R.shapes["qkv"]),
+    "o": lambda R: (R.w.tokens,) + tuple(R.shapes["o"]),
+    "o_reduce": lambda R: (R.w.tokens,) + tuple(R.shapes["o"]),
+    "gate_up": lambda R: (R.w.tokens,) + tuple(R.shapes["gate_up"]),
+    "gate_up_swiglu": lambda R: (R.w.tokens,) + tuple(R.shapes["gate_up"]),
+    "down": lambda R: (R.w.tokens,) + tuple(R.shapes["down"]),
+    "down_reduce": lambda R: (R.w.tokens,) + tuple(R.shapes["down"]),
+    "lm_head": lambda R: (R.hs_rows, R.vs, R.w.hidden),
+}
 KV_LEN = 2048      # tokens cached per sequence before the decode step (the pages' prefill chunk)
 KV_CAP = 2304      # cache capacity per sequence
 
@@ -441,6 +452,23 @@ def time_rotated(torch, ops, name, reps):
     del g, launches
     torch.cuda.empty_cache()
     return ms * 1e3 / n, distinct
+
+
+def vendor_mm_us(torch, M, N, K, reps):
+    """The same product as a plain bf16 GEMM through torch.mm (hipBLASLt on
+    ROCm), Y = X W^T with W rotated over at least ROTATE_BYTES of distinct
+    weights like the per-op timings: context for the shard GEMMs (the
+    library's calls add the epilogues)."""
+    n = max(8, -(-ROTATE_BYTES // (N * K * 2)))
+    x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+    ws = [(torch.randn((N, K), device="cuda") * 0.02).to(torch.bfloat16) for _ in range(n)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ops = [("mm", lambda w: torch.mm(x, w.t(), out=y), (w,)) for w in ws]
+    g = capture(torch, ops)
+    ms = time_graph(torch, g, reps, 2)
+    del g, ws, ops
+    torch.cuda.empty_cache()
+    return ms * 1e3 / n
 
 
 def time_graph(torch, g, reps, warmup):
@@ -859,6 +887,9 @@ def main():
                         "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                         "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2) if flops else None,
                         "bytes_per_launch": byts, "distinct_MiB": round(distinct / 2**20)}
+        if name in GEMM_SHAPES:
+            Mv, Nv, Kv = GEMM_SHAPES[name](R)
+            per_op[name]["vendor_mm_us"] = round(vendor_mm_us(torch, Mv, Nv, Kv, args.steps), 3)
 
     attn = None
     if layer_ops:

@@ -130,6 +130,10 @@ int tp_kv_heads_of_rank(const tp_model_cfg* cfg, int t, int rank, int* first, in
  * B nkv ceil(L / chunk) (nq / nkv) (d + 2) = 4 Mi floats). */
 int64_t tp_workspace_bytes(void);
 
+/* Number of tiled kernel shapes a tp_linear_plan's prefill_tile may name
+ * (prefill_tile = v + 1 for v in [0, count)). Host only. */
+int tp_prefill_tile_count(void);
+
 /* ------------------------------------------------------------------------
  * Device calls
  * ------------------------------------------------------------------------ */
@@ -348,17 +352,20 @@ typedef enum {
  * `decode_nwn` waves along the output rows (16 rows each), `decode_nwk` waves
  * along K per workgroup, K split across as many workgroups as it takes to
  * cover it, and `decode_x_direct` = 1 to load activation fragments per wave
- * instead of staging them in LDS. prefill_tile (M > 64; 0 = automatic, v + 1
- * = kernel v): 0, 1, 2 = 256 x 256, 256 x 128, 128 x 128 tiles (weight rows x
- * tokens) with 32-wide k-tiles on 4 waves; 4, 5, 6 the same on 8 waves;
- * 7 = 192 x 128 on 4 waves; 8, 9, 10 = 256 x 256, 256 x 128, 128 x 128 on
- * 8 waves with 64-wide k-tiles (K % 64 == 0); 11 = 192 x 128 likewise;
- * 3 = register-staged 128 x 128 (any K % 8). A decode shape that is not built
- * for any token count, or a prefill_tile outside [0, 12], is TP_ERR_RANGE. A
- * plan this call cannot run (the shape not built for its token count, an X
- * chunk beyond LDS, split partials beyond the workspace, a K multiple not
- * met) is replaced by the automatic choice; results then differ only in the
- * fp32 summation order. */
+ * instead of staging them in LDS. prefill_tile (0 = automatic, v + 1 =
+ * tiled kernel v, which then runs at any token count M, decode sizes
+ * included, except for the reduce epilogues): 0, 1, 2 = 256 x 256,
+ * 256 x 128, 128 x 128 tiles (weight rows x tokens) with 32-wide k-tiles on
+ * 4 waves; 4, 5, 6 the same on 8 waves; 7 = 192 x 128 on 4 waves;
+ * 8, 9, 10 = 256 x 256, 256 x 128, 128 x 128 on 8 waves with 64-wide
+ * k-tiles (K % 64 == 0); 11 = 192 x 128 likewise; 12, 13 = 64 x 64 and
+ * 128 x 64 on 4 waves and 14 = 64 x 64 on 2 waves, 64-wide k-tiles (tiles
+ * for 64 tokens); 3 = register-staged 128 x 128 (any K % 8). A decode shape
+ * that is not built for any token count, or a prefill_tile outside
+ * [0, tp_prefill_tile_count()], is TP_ERR_RANGE. A plan this call cannot run
+ * (the shape not built for its token count, an X chunk beyond LDS, split
+ * partials beyond the workspace, a K multiple not met) is replaced by the
+ * automatic choice; results then differ only in the fp32 summation order. */
 typedef struct {
     int32_t decode_ksteps, decode_nwn, decode_nwk, decode_x_direct;
     int32_t prefill_tile;

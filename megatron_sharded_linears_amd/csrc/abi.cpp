@@ -165,7 +165,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
 // up rows) and 2 i_half on the prefill kernel; this sets it.
 int launch_linear(tpk::GemmArgs a, const tpk::Workspace& ws, const tp_linear_plan& over, hipStream_t s) {
     const bool swiglu = a.epi == tpk::EPI_SWIGLU;
-    if (a.M <= kSkinnyMaxM) {
+    // an explicit prefill tile runs the tiled kernel at any token count
+    const bool tiled_asked = over.prefill_tile > 0 && !tpk::epi_is_reduce(a.epi);
+    const bool decode_asked = !plan_is_auto_decode(over);
+    if (a.M <= kSkinnyMaxM && !tiled_asked && (decode_asked || !tpk::tiled_wins_at_decode(a))) {
         const int64_t n_rows = swiglu ? 16 * ((a.i_half + 7) / 8) : a.N;
         tpk::SkinnyPlan p;
         if (decode_plan(a.M, n_rows, a.K, ws, over, &p)) {
@@ -429,6 +432,8 @@ int tp_kv_heads_of_rank(const tp_model_cfg* cfg, int t, int rank, int* first, in
 }
 
 int64_t tp_workspace_bytes(void) { return TP_WS_COUNTER_BYTES + tpk::kSkinnyWsFloats * 4; }
+
+int tp_prefill_tile_count(void) { return tpk::tiled_variant_count(); }
 
 int tp_shard_weights(const tp_model_cfg* cfg, int t, int rank, int kind, const void* full_w,
                      void* shard_w, void* stream) {

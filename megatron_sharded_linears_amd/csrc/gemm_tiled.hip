@@ -721,6 +721,9 @@ const TiledEntry kTiled[] = {
     TP_DMA64(256, 128, 3, 4),
     TP_DMA64(128, 128, 3, 4),
     TP_DMA64(192, 128, 3, 4),
+    TP_DMA64(64, 64, 4, 2),
+    TP_DMA64(128, 64, 4, 2),
+    TP_DMA64(64, 64, 6, 1),
 };
 #undef TP_DMA
 #undef TP_DMA64
@@ -733,6 +736,21 @@ std::atomic<bool> g_tiled_attr[kMaxDevices][kNumTiled] = {};
 }  // namespace
 
 int tiled_variant_count() { return kNumTiled; }
+
+// Measured on MI355X at 64 tokens (weights rotated past the last-level
+// cache): with K >= 2048 and at least 48 tiles of 64 weight rows, 64 x 64
+// tiles streaming K through a 4-stage ring beat the decode kernel, whose
+// K split then re-stages all 64 tokens' activations per 16 weight rows and
+// sums fp32 partials across workgroups (LM head 8016 x 4096: 27.1 against
+// 40.2 us; 3584 x 4096: 24.8 against 27.0 us). With fewer rows or shorter K
+// the decode kernel wins (1792 x 4096: 17.3 against 24.5 us; 4096 x 896:
+// 7.2 against 9.5 us).
+bool tiled_wins_at_decode(const GemmArgs& a) {
+    if (a.M <= 32 || a.K < 2048 || a.K % 64 != 0 || a.norm != 0) return false;
+    if (a.epi != EPI_STORE && a.epi != EPI_SWIGLU) return false;
+    const int64_t rows = a.epi == EPI_SWIGLU ? 2 * a.i_half : a.N;
+    return (rows + 63) / 64 >= 48;
+}
 
 // EPI_SWIGLU: a.N is 2 * i_half on entry (used to pick the tile shape); the
 // kernel's row space is then whole tiles of paired gate and up rows.
@@ -750,7 +768,8 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant) {
     auto tiles = [&](int bn, int bm) { return ((a.N + bn - 1) / bn) * ((a.M + bm - 1) / bm); };
     const int shape = tiles(256, 256) >= 192 ? 0 : tiles(256, 128) >= 192 ? 1 : 2;
     int best;
-    if (a.K % 32 != 0) best = 3;
+    if (a.M <= 64 && a.K % 64 == 0) best = 12;       // 64 x 64 tiles for decode sizes
+    else if (a.K % 32 != 0) best = 3;
     else if (a.K <= 1024) best = 6;
     else if (a.K % 64 != 0) best = 4 + shape;
     else if (shape == 1 && tiles(256, 128) < kCus && tiles(192, 128) <= kCus) best = 11;

@@ -120,6 +120,9 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
 // EPI_STORE or EPI_SWIGLU (a.N = 2 i_half). variant: a kernel index in
 // [0, tiled_variant_count()), or -1 for the automatic choice; one whose K
 // multiple the call does not meet is replaced by the automatic choice.
+// Whether a decode-sized linear (M <= 64) runs faster on the tiled kernel's
+// 64 x 64 tiles than on the decode kernel (store or SwiGLU epilogue only).
+bool tiled_wins_at_decode(const GemmArgs& a);
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant = -1);
 int tiled_variant_count();
 

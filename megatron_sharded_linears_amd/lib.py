@@ -87,6 +87,7 @@ _PROTOS = {
     "tp_vocab_shard_rows": (_i64, [_i64, _int]),
     "tp_kv_heads_of_rank": (_int, [_cfgp, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
     "tp_workspace_bytes": (_i64, []),
+    "tp_prefill_tile_count": (ctypes.c_int, []),
     "tp_shard_weights": (_int, [_cfgp, _int, _int, _int, _vp, _vp, _vp]),
     "tp_column_linear": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp] + _ws + [_vp]),
     "tp_swiglu": (_int, [_vp, _i64, _i64, _vp, _vp]),
@@ -204,6 +205,11 @@ def tp_kv_heads_of_rank(cfg, t, rank):
 
 def tp_workspace_bytes():
     return int(_lib.tp_workspace_bytes())
+
+
+def tp_prefill_tile_count():
+    """Tiled kernel shapes a plan's "tile" may name (0 .. count - 1)."""
+    return int(_lib.tp_prefill_tile_count())
 
 
 # --------------------------------------------------------------- workspace

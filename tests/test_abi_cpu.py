@@ -241,7 +241,10 @@ def test_linear_ex_validates_call_and_plan():
     assert f(None, S) == -1
     assert f(ctypes.byref(_call(M=0)), S) == 0
     assert f(ctypes.byref(_call(M=0, epilogue=4)), S) == -5                  # unknown epilogue
-    assert f(ctypes.byref(_call(M=0, plan={"tile": 12})), S) == -6           # 12 tile kernels: 0..11
+    nt = C.tp_prefill_tile_count()
+    assert nt == lib.tp_prefill_tile_count() == 15
+    assert f(ctypes.byref(_call(M=0, plan={"tile": nt})), S) == -6           # tile kernels 0 .. nt - 1
+    assert f(ctypes.byref(_call(M=0, plan={"tile": nt - 1})), S) == 0
     assert f(ctypes.byref(_call(M=0, plan={"tile": 11})), S) == 0
     assert f(ctypes.byref(_call(M=0, plan={"decode": (3, 4, 2, 0)})), S) == -6   # no such decode kernel
     assert f(ctypes.byref(_call(M=0, plan={"decode": (8, 4, 2, 0)})), S) == 0

@@ -139,11 +139,14 @@ def test_split_k_partials_are_never_stale():
             assert np.array_equal(f64(y), oracle.linear(f64(x), f64(w))), (variant, it)
 
 
-@pytest.mark.parametrize("variant", list(range(12)))
+@pytest.mark.parametrize("variant", list(range(lib.tp_prefill_tile_count())))
 def test_every_prefill_tile_shape_exact(variant):
+    """Every tiled kernel shape (an explicit tile plan runs it at any token
+    count, decode sizes included)."""
     plan = {"tile": variant}
     for (M, N, K) in [(65, 70, 64), (300, 257, 200), (512, 768, 1032), (2048, 300, 640), (130, 1024, 4096),
-                      (700, 520, 96), (257, 4100, 32), (300, 257, 192), (129, 130, 128)]:
+                      (700, 520, 96), (257, 4100, 32), (300, 257, 192), (129, 130, 128),
+                      (64, 520, 4096), (33, 130, 128), (16, 70, 64), (1, 257, 256)]:
         x = I.small_int_bf16((SEED, 40, M, N, K), (M, K))
         w = I.small_int_bf16((SEED, 41, M, N, K), (N, K))
         y = empty((M, N), torch.float32)
@@ -260,6 +263,18 @@ def test_reduce_integer_exact_and_random(t, numel):
     if t == 1:
         lib.tp_reduce_partials([dev(parts[0])], out)
         assert np.array_equal(bits(out), bits(parts[0]))
+
+
+@pytest.mark.parametrize("t", [2, 3, 8])
+def test_reduce_wide_launch_ragged(t):
+    """Sums of at least 65536 vectors run the wide launch (512 threads, two
+    vectors per thread): a length whose last block is partly empty and whose
+    last 5 elements fall outside the 8-element vectors."""
+    numel = 65536 * 8 + 8 * 1023 + 5
+    parts = [I.small_int_bf16((SEED, 18, t, i), (numel,), -8, 8) for i in range(t)]
+    out = empty((numel,))
+    lib.tp_reduce_partials([dev(p) for p in parts], out)
+    assert np.array_equal(f64(out), oracle.all_reduce_sum([f64(p) for p in parts]))
 
 
 def test_reduce_fp32_partials_in_place_and_signed_zero():
