@@ -683,6 +683,80 @@ def summarize_counters(fetch_csv, write_csv, run_json, out=None):
 
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
+NUM_SIMDS = 1024                # 256 CUs x 4 SIMDs
+NUM_XCDS = 8                    # GRBM_GUI_ACTIVE comes summed over the XCDs' instances
+
+
+def summarize_mfma(pmc_csv, trace_csv, run_json, out=None):
+    """Matrix-core use of the step's GEMM launches from one rocprofv3 --pmc
+    pass of `bench.py --counters` with MFMA_COUNTERS and a --kernel-trace
+    pass of the same command (durations), per kernel shape: the MFMA busy
+    fraction (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 1024 SIMDs),
+    the busy-CU fraction, the shader clock the dispatch ran at
+    (GRBM_GUI_ACTIVE over its duration) and the bf16 MFMA rate (512 flop per
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 over the duration). GRBM_GUI_ACTIVE is
+    reported summed over its 8 per-XCD instances: one XCD's busy cycles are
+    that over 8. The counter window spans a little more than the kernel
+    (setup and drain around each serialised dispatch), so the clock of short
+    dispatches reads high."""
+    import csv
+    import re
+    with open(run_json) as f:
+        run = json.loads([ln for ln in f if ln.startswith("{")][-1])
+
+    def short(r):
+        m = re.search(r"(\w+_kernel)(<[^>]*>)?", r["Kernel_Name"])
+        name = (m.group(1) + (m.group(2) or "")) if m else r["Kernel_Name"][:60]
+        return f"{name} grid={r['Grid_Size']}" if r.get("Grid_Size") else name
+
+    cnt = {}
+    with open(pmc_csv) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] in MFMA_COUNTERS:
+                d = cnt.setdefault(short(r), {})
+                d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    dur = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            m = re.search(r"(\w+_kernel)(<[^>]*>)?", r["Kernel_Name"])
+            name = (m.group(1) + (m.group(2) or "")) if m else r["Kernel_Name"][:60]
+            g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            dur.setdefault(f"{name} grid={g}", []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    steps = run["steps"]
+    lines = [f"workload {run['workload']}: GEMM launches of {steps} eager steps",
+             "", "| kernel | per step | avg us | GUI_ACTIVE cycles | clock GHz | MFMA busy | CUs busy | bf16 MFMA TFLOP/s |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    tot = {"busy": 0.0, "gui": 0.0, "flop": 0.0, "ns": 0.0}
+    for k in sorted(cnt, key=lambda k: -sum(dur.get(k, [0]))):
+        if not is_gemm_kernel(k) or k not in dur:
+            continue
+        c = cnt[k]
+        n = len(c["GRBM_GUI_ACTIVE"])
+        avg = {name: sum(v) / len(v) for name, v in c.items()}
+        ns = sum(dur[k]) / len(dur[k])
+        gui = avg["GRBM_GUI_ACTIVE"] / NUM_XCDS
+        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * NUM_SIMDS)
+        cu = avg["SQ_BUSY_CU_CYCLES"] / (gui * 256)
+        flop = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        lines.append(f"| `{k}` | {n // steps} | {ns / 1e3:.2f} | {gui:.0f} | {gui / ns:.2f} | {busy:.3f} | "
+                     f"{cu:.3f} | {flop / ns / 1e3:.1f} |")
+        tot["busy"] += avg["SQ_VALU_MFMA_BUSY_CYCLES"] * n
+        tot["gui"] += gui * n
+        tot["flop"] += flop * n
+        tot["ns"] += ns * n
+    if tot["gui"]:
+        lines += ["", f"- over all GEMM launches: MFMA busy {tot['busy'] / (tot['gui'] * NUM_SIMDS):.3f} of the "
+                      f"SIMD-cycles, {tot['flop'] / tot['ns'] / 1e3:.1f} TFLOP/s of bf16 MFMA work over their "
+                      f"summed durations ({tot['flop'] / tot['ns'] / 1e3 / BF16_PEAK_TFLOPS:.3f} of "
+                      f"{BF16_PEAK_TFLOPS:.0f})"]
+    text = "\n".join(lines)
+    print(text)
+    if out:
+        with open(out, "w") as f:
+            f.write(text + "\n")
+
+
 def summarize_trace(path, top=30):
     """Per (kernel, workgroups) duration stats from a rocprofv3
     --kernel-trace --output-format csv trace: a row per distinct launch shape,
@@ -768,6 +842,9 @@ def main():
         return
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2])
+        return
+    if len(sys.argv) in (5, 6) and sys.argv[1] == "--summarize-mfma":
+        summarize_mfma(*sys.argv[2:])
         return
     if len(sys.argv) in (5, 6) and sys.argv[1] == "--summarize-counters":
         summarize_counters(*sys.argv[2:])
