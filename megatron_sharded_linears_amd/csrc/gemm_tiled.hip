@@ -752,6 +752,65 @@ bool tiled_wins_at_decode(const GemmArgs& a) {
     return (rows + 63) / 64 >= 48;
 }
 
+namespace {
+
+// Launch tiled kernel v over tokens [m0, M) of `a` (a contiguous block of
+// X's and Y's rows).
+hipError_t launch_variant(const GemmArgs& a, int v, int64_t m0, hipStream_t s) {
+    const TiledEntry& e = kTiled[v];
+    int dev = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he != hipSuccess) return he;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!g_tiled_attr[dev][v].load(std::memory_order_acquire)) {
+        he = hipFuncSetAttribute(reinterpret_cast<const void*>(e.fn), hipFuncAttributeMaxDynamicSharedMemorySize, e.lds);
+        if (he != hipSuccess) return he;
+        g_tiled_attr[dev][v].store(true, std::memory_order_release);
+    }
+    GemmArgs b = a;
+    const bool swiglu = a.epi == EPI_SWIGLU;
+    if (swiglu) b.N = (int64_t)e.bn * ((a.i_half + e.bn / 2 - 1) / (e.bn / 2));
+    if (m0 > 0) {
+        const int64_t y_cols = swiglu ? a.i_half : a.N;
+        const int64_t y_elem = a.out_dtype == TP_F32 ? 4 : 2;
+        b.x = static_cast<const unsigned char*>(a.x) + m0 * a.K * 2;
+        b.y = static_cast<unsigned char*>(a.y) + m0 * y_cols * y_elem;
+        b.M = a.M - m0;
+    }
+    const int tn = (int)((b.N + e.bn - 1) / e.bn);
+    const int tm = (int)((b.M + e.bm - 1) / e.bm);
+    const int ntiles = tn * tm;
+    const int grid = ((ntiles + kXcds - 1) / kXcds) * kXcds;
+    hipLaunchKernelGGL(e.fn, dim3(grid), dim3(e.threads), e.lds, s, b, tn, tm);
+    return hipGetLastError();
+}
+
+// Sustained bf16 rate of a whole chip's worth of each 64-wide-k-tile shape
+// (TFLOP/s, MI355X counters at the prefill shard shapes: 2 x 256 x 256 and
+// 256 x 128 on 8 waves, 192 x 128, 128 x 128), for the split below.
+double tile_rate(int v) {
+    switch (v) {
+    case 8: return 990.0;
+    case 9: return 830.0;
+    case 11: return 745.0;
+    case 10: return 600.0;
+    default: return 0.0;
+    }
+}
+
+// Estimated microseconds of variant v over tokens [m0, M): whole waves of
+// tiles over the 256 CUs (a partly filled wave costs a full one).
+double region_us(const GemmArgs& a, int v, int64_t m0) {
+    const TiledEntry& e = kTiled[v];
+    const int64_t rows = a.epi == EPI_SWIGLU ? (int64_t)e.bn * ((a.i_half + e.bn / 2 - 1) / (e.bn / 2)) : a.N;
+    const int64_t tiles = ((rows + e.bn - 1) / e.bn) * ((a.M - m0 + e.bm - 1) / e.bm);
+    const int64_t waves = (tiles + kCus - 1) / kCus;
+    const double tile_flop = 2.0 * e.bn * e.bm * (double)a.K;
+    return (double)waves * tile_flop / (tile_rate(v) * 1e12 / kCus) * 1e6;
+}
+
+}  // namespace
+
 // EPI_SWIGLU: a.N is 2 * i_half on entry (used to pick the tile shape); the
 // kernel's row space is then whole tiles of paired gate and up rows.
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant) {
@@ -774,25 +833,41 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant) {
     else if (a.K % 64 != 0) best = 4 + shape;
     else if (shape == 1 && tiles(256, 128) < kCus && tiles(192, 128) <= kCus) best = 11;
     else best = 8 + shape;
-    if (variant >= 0 && variant < kNumTiled && a.K % kTiled[variant].kmul == 0) best = variant;
-    const TiledEntry& e = kTiled[best];
-    int dev = 0;
-    hipError_t he = hipGetDevice(&dev);
-    if (he != hipSuccess) return he;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    if (!g_tiled_attr[dev][best].load(std::memory_order_acquire)) {
-        he = hipFuncSetAttribute(reinterpret_cast<const void*>(e.fn), hipFuncAttributeMaxDynamicSharedMemorySize, e.lds);
-        if (he != hipSuccess) return he;
-        g_tiled_attr[dev][best].store(true, std::memory_order_release);
+    if (variant >= 0 && variant < kNumTiled && a.K % kTiled[variant].kmul == 0) return launch_variant(a, variant, 0, s);
+    // Wave quantisation: when the last wave of 256 x 256 tiles would leave
+    // most CUs idle (Qwen-32B t = 8 down: 320 tiles, 1.25 waves), the
+    // first token rows keep those tiles and the rest run as a second launch
+    // of smaller tiles, if the estimate (whole waves at each shape's measured
+    // rate, plus one launch) says so. Every tile shape sums K in the same
+    // order with the same MFMA, so the split changes no bit of the result.
+    if (best == 8) {
+        const TiledEntry& big = kTiled[8];
+        const double alone = region_us(a, 8, 0);
+        double best_us = alone;
+        int64_t best_m0 = 0;
+        int best_tail = -1;
+        for (int64_t m0 = big.bm; m0 < a.M; m0 += big.bm) {
+            GemmArgs h = a;
+            h.M = m0;                                   // the head: tokens [0, m0)
+            const double head_us = region_us(h, 8, 0);
+            for (int v : {9, 11, 10}) {
+                const double us = head_us + region_us(a, v, m0) + 3.0;
+                if (us < best_us) {
+                    best_us = us;
+                    best_m0 = m0;
+                    best_tail = v;
+                }
+            }
+        }
+        if (best_tail >= 0 && best_us < 0.97 * alone) {
+            GemmArgs h = a;
+            h.M = best_m0;
+            const hipError_t he = launch_variant(h, 8, 0, s);
+            if (he != hipSuccess) return he;
+            return launch_variant(a, best_tail, best_m0, s);
+        }
     }
-    GemmArgs b = a;
-    if (a.epi == EPI_SWIGLU) b.N = (int64_t)e.bn * ((a.i_half + e.bn / 2 - 1) / (e.bn / 2));
-    const int tn = (int)((b.N + e.bn - 1) / e.bn);
-    const int tm = (int)((b.M + e.bm - 1) / e.bm);
-    const int ntiles = tn * tm;
-    const int grid = ((ntiles + kXcds - 1) / kXcds) * kXcds;
-    hipLaunchKernelGGL(e.fn, dim3(grid), dim3(e.threads), e.lds, s, b, tn, tm);
-    return hipGetLastError();
+    return launch_variant(a, best, 0, s);
 }
 
 }  // namespace tpk
