@@ -475,6 +475,27 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     //    invalidates the whole L2 of the XCD, once per workgroup.
     // 4 consecutive floats per lane: two 64-bit stores when 8-byte aligned.
     const bool pair = (N % 2 == 0) && (n_out + 3 < N);
+    // counters == nullptr: the partial tiles are summed by skinny_split_finish
+    // in a second launch (the kernel boundary publishes them): plain stores.
+    if (counters == nullptr) {
+#pragma unroll
+        for (int o = 0; o < C::kOwn; ++o) {
+            const int mt = wk + NWK * o;
+            const int64_t m = 16 * mt + (lane & 15);
+            if (mt < MT && m < M) {
+                float* p = ws + ((int64_t)split * M + m) * N + n_out;
+                if (pair) {
+                    *reinterpret_cast<float2*>(p) = make_float2(fin[o][0], fin[o][1]);
+                    *reinterpret_cast<float2*>(p + 2) = make_float2(fin[o][2], fin[o][3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (n_out + i < N) p[i] = fin[o][i];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int o = 0; o < C::kOwn; ++o) {
         const int mt = wk + NWK * o;
@@ -574,6 +595,63 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
         }
     }
     if (tid == 0) atomicExch(&counters[tile], 0u);
+}
+
+// Second launch of a K split whose partial tiles were written without
+// arrival counters: one thread per 4 consecutive outputs of the kernel's row
+// space (EPI_SWIGLU: per 4 gate rows of a 16-row block, the up rows 8 higher),
+// the splits summed in split order from 0.f, then the epilogue of the
+// single-launch split: the same arithmetic, so the same bits.
+template <int EPI>
+__global__ void __launch_bounds__(256)
+skinny_split_finish(GemmArgs a, int splits, const float* __restrict__ ws) {
+    const int64_t M = a.M, N = a.N;
+    const int64_t groups = EPI == EPI_SWIGLU ? N / 8 : (N + 3) / 4;   // per token row
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= M * groups) return;
+    const int64_t m = g / groups;
+    const int64_t q = g - m * groups;
+    const int64_t n = EPI == EPI_SWIGLU ? 16 * (q >> 1) + 4 * (q & 1) : 4 * q;
+    auto sum4 = [&](int64_t n0, float* v) {
+        v[0] = v[1] = v[2] = v[3] = 0.f;
+        for (int sp = 0; sp < splits; ++sp) {
+            const float* p = ws + ((int64_t)sp * M + m) * N + n0;
+            if (n0 + 3 < N && N % 4 == 0) {
+                const float4 t = *reinterpret_cast<const float4*>(p);
+                v[0] += t.x;
+                v[1] += t.y;
+                v[2] += t.z;
+                v[3] += t.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (n0 + i < N) v[i] += p[i];
+            }
+        }
+    };
+    float v[4];
+    sum4(n, v);
+    if constexpr (EPI == EPI_SWIGLU) {
+        float u[4];
+        sum4(n + 8, u);
+        const int64_t j = (n >> 4) * 8 + (n & 7);      // first of the 4 gate columns
+        if (j >= a.i_half) return;
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = silu_f32(round_bf16(v[i])) * round_bf16(u[i]);
+        uint16_t* y = reinterpret_cast<uint16_t*>(a.y) + m * a.i_half + j;
+        if (j + 3 < a.i_half && a.i_half % 4 == 0) {
+            *reinterpret_cast<uint2*>(y) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        } else {
+            for (int i = 0; i < 4; ++i) if (j + i < a.i_half) y[i] = (uint16_t)f32_to_bf16(o[i]);
+        }
+    } else if constexpr (epi_is_reduce(EPI)) {
+        PeerVals<EPI> peers;
+        load_peers<EPI>(a, m, n, peers);
+        reduce_out4<EPI>(a, m, n, v, peers);
+    } else {
+        store_out4(a, m, n, v);
+    }
 }
 
 typedef void (*SkinnyFn)(GemmArgs, int, int64_t, int, float*, unsigned*);
@@ -753,9 +831,12 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64
         if ((N + 15) / 16 < 128 && K >= 2048 && first_fit(few_tiles, 1, &chosen)) return chosen;
         if (first_fit(rules, 5, &chosen)) return chosen;
     } else if (mt == 4) {
-        // M in (32, 64]: measured winners at the Llama-8B t=16 shard shapes.
+        // M in (32, 64]: measured winners at the Llama-8B t=16 shard shapes
+        // (weights rotated past the last-level cache; gate_up 1792 x 4096:
+        // 64-row tiles split 8 ways in two launches, 16.8 us, against 17.2
+        // for 16-row tiles split 4 ways in one).
         static const Rule rules_small_n[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 4, 1, 4, 1}};
-        static const Rule rules_mid_n[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 8, 1, 4, 0}};
+        static const Rule rules_mid_n[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 4, 4, 4, 0}};
         static const Rule rules[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 8, 4, 2, 0}};
         if (first_fit(N <= 1024 ? rules_small_n : N <= 2048 ? rules_mid_n : rules, 3, &chosen)) return chosen;
     }
@@ -833,8 +914,42 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
         }
     }
     dim3 grid((unsigned)grid_x, (unsigned)p.splits);
+    if (skinny_split_launches(p, a) == 2) {
+        // The partial tiles in one launch, their sum and the epilogue in a
+        // second: with 64 tokens a split tile holds up to 64 KB of partials
+        // per split, which one last-arriving workgroup would read alone
+        // (MI355X, Llama t = 16 gate_up: the 224 workgroups of 64-row
+        // tiles finish their partials by ~10 us, the last arrivals then
+        // take another 6-7 us).
+        hipLaunchKernelGGL(fn, grid, dim3(e->threads), lds, s, a, p.splits, p.ntiles, xrows, ws.partials,
+                           static_cast<unsigned*>(nullptr));
+        he = hipGetLastError();
+        if (he != hipSuccess) return he;
+        const int64_t groups = epi == EPI_SWIGLU ? a.N / 8 : (a.N + 3) / 4;
+        const int64_t threads = a.M * groups;
+        const dim3 g2((unsigned)((threads + 255) / 256));
+        switch (epi) {
+        case EPI_STORE: hipLaunchKernelGGL(skinny_split_finish<EPI_STORE>, g2, dim3(256), 0, s, a, p.splits, ws.partials); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL(skinny_split_finish<EPI_SWIGLU>, g2, dim3(256), 0, s, a, p.splits, ws.partials); break;
+        case EPI_REDUCE: hipLaunchKernelGGL(skinny_split_finish<EPI_REDUCE>, g2, dim3(256), 0, s, a, p.splits, ws.partials); break;
+        case EPI_REDUCE_ADD: hipLaunchKernelGGL(skinny_split_finish<EPI_REDUCE_ADD>, g2, dim3(256), 0, s, a, p.splits, ws.partials); break;
+        case EPI_REDUCE_F32: hipLaunchKernelGGL(skinny_split_finish<EPI_REDUCE_F32>, g2, dim3(256), 0, s, a, p.splits, ws.partials); break;
+        case EPI_REDUCE_ADD_F32: hipLaunchKernelGGL(skinny_split_finish<EPI_REDUCE_ADD_F32>, g2, dim3(256), 0, s, a, p.splits, ws.partials); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(fn, grid, dim3(e->threads), lds, s, a, p.splits, p.ntiles, xrows, ws.partials, ws.counters);
     return hipGetLastError();
+}
+
+// A K split at more than 32 tokens over 64-row tiles (not with the norm,
+// whose split shares of the sums of squares need the single-launch
+// exchange) runs as two launches. With 16-row tiles the last arrival reads
+// 16 KB per split and the second launch costs more than it saves (Llama
+// t = 16 qkv, 16 rows x 8 splits: 9.9 us in one launch, 10.9 in two).
+int skinny_split_launches(const SkinnyPlan& p, const GemmArgs& a) {
+    return (p.splits > 1 && p.mt == 4 && p.nwn >= 4 && a.norm == 0) ? 2 : 1;
 }
 
 }  // namespace tpk

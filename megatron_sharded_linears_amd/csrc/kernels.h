@@ -115,6 +115,9 @@ bool skinny_plan_fits(const SkinnyPlan& p, int64_t M);   // LDS need for M token
 SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64_t ws_counters);
 bool skinny_norm_plan_fits(const SkinnyPlan& p, int64_t M, int64_t K);
 int64_t skinny_workspace_floats(const SkinnyPlan& p, int64_t M, int64_t N);
+// Launches a decode-sized linear takes under plan p (2: the split partial
+// tiles, then their sum and the epilogue).
+int skinny_split_launches(const SkinnyPlan& p, const GemmArgs& a);
 hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace& ws, hipStream_t s);
 
 // EPI_STORE or EPI_SWIGLU (a.N = 2 i_half). variant: a kernel index in

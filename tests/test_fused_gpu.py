@@ -98,8 +98,15 @@ def test_every_decode_variant_fused_epilogues(ks, nn, nk, xd):
         w = dev(I.normal_bf16((SEED, 8, M, N, K), (N, K), 0.05))
         for dt in (torch.bfloat16, torch.float32):
             peers = [dev(I.normal_bf16((SEED, 9, M, N, i), (M, N))).to(dt) for i in range(t)]
-            assert np.array_equal(bits(fused_reduce(x, w, peers, rank, plan)),
-                                  bits(separate_reduce(x, w, peers, rank, plan))), (M, N, K, t, rank, dt)
+            summed = fused_reduce(x, w, peers, rank, plan)
+            assert np.array_equal(bits(summed), bits(separate_reduce(x, w, peers, rank, plan))), \
+                (M, N, K, t, rank, dt)
+            # the residual-add epilogue: y = bf16(y + the bf16 sum over ranks)
+            res = dev(I.normal_bf16((SEED, 10, M, N), (M, N)))
+            want = (res.float() + summed.float()).to(torch.bfloat16)
+            parts = [None if i == rank else p for i, p in enumerate(peers)]
+            lib.tp_row_linear_reduce_add(x, w, parts, rank, res, plan=plan)
+            assert np.array_equal(bits(res), bits(want)), (M, N, K, t, rank, dt, "add")
 
 
 def separate_reduce(x, w, peers, rank, plan=None):
