@@ -523,7 +523,7 @@ struct Dma64Cfg {
 __device__ __forceinline__ int swz128(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
 
 template <int BN, int BM, int NS, int WGM>
-__global__ void __launch_bounds__(128 * WGM, 1)
+__global__ void __launch_bounds__(128 * WGM, (Dma64Cfg<BN, BM, NS, WGM>::kLdsBytes <= 80 * 1024 ? 2 : 1))
 tiled_dma64_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     using C = Dma64Cfg<BN, BM, NS, WGM>;
     extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -745,6 +745,7 @@ const TiledEntry kTiled[] = {
     TP_DMA64(64, 64, 4, 2),
     TP_DMA64(128, 64, 4, 2),
     TP_DMA64(64, 64, 6, 1),
+    TP_DMA64(128, 128, 2, 2),
 };
 #undef TP_DMA
 #undef TP_DMA64
@@ -844,7 +845,11 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant) {
     // register-staged kernel for any other K. With 64-wide k-tiles, 256 x 128
     // tiles that leave CUs idle give way to 192 x 128 tiles when those fill
     // at most one pass of the chip (Llama-8B t = 2 qkv: 192 tiles of
-    // 256 x 128 take 70 us, 256 of 192 x 128 take 62 us).
+    // 256 x 128 take 70 us, 256 of 192 x 128 take 62 us), and otherwise to
+    // 128 x 128 tiles on 4 waves with two 64-wide stages, small enough (64 KB
+    // of LDS, 134 VGPRs) for two workgroups per CU, whose barriers and loads
+    // then interleave (Llama-8B t = 2 down 132.8 -> 124.3 us, o 44.6 -> 42.7,
+    // timed alternately with the 8-wave 256 x 128 tiles).
     auto tiles = [&](int bn, int bm) { return ((a.N + bn - 1) / bn) * ((a.M + bm - 1) / bm); };
     const int shape = tiles(256, 256) >= 192 ? 0 : tiles(256, 128) >= 192 ? 1 : 2;
     int best;
@@ -853,6 +858,7 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant) {
     else if (a.K <= 1024) best = 6;
     else if (a.K % 64 != 0) best = 4 + shape;
     else if (shape == 1 && tiles(256, 128) < kCus && tiles(192, 128) <= kCus) best = 11;
+    else if (shape == 1) best = 15;
     else best = 8 + shape;
     if (variant >= 0 && variant < kNumTiled && a.K % kTiled[variant].kmul == 0) return launch_variant(a, variant, 0, s);
     // Wave quantisation: when the last wave of 256 x 256 tiles would leave
