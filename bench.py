@@ -441,14 +441,28 @@ def rotated_launches(ops, name, min_launches=8):
     return out, sum(seen.values())
 
 
-def time_rotated(torch, ops, name, reps):
+def time_rotated(torch, ops, name, reps, spread=None):
     """Microseconds per launch of op `name`: its rotated launches
     (rotated_launches) captured into one graph, replayed `reps` times between
-    events on the replaying stream. Returns (us, distinct bytes)."""
+    events on the replaying stream. Returns (us, distinct bytes); `spread`, a
+    dict, receives the 10th, 50th and 90th percentiles of the per-replay
+    figure (each replay bracketed by its own events)."""
     launches, distinct = rotated_launches(ops, name)
     g = capture(torch, launches)
     ms = time_graph(torch, g, reps, 2)
     n = len(launches)
+    if spread is not None:
+        per = []
+        for _ in range(max(reps, 10)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            b.synchronize()
+            per.append(a.elapsed_time(b) * 1e3 / n)
+        per.sort()
+        q = lambda f: per[min(len(per) - 1, int(f * len(per)))]
+        spread.update({"us_p10": round(q(0.1), 3), "us_p50": round(q(0.5), 3), "us_p90": round(q(0.9), 3)})
     del g, launches
     torch.cuda.empty_cache()
     return ms * 1e3 / n, distinct
@@ -561,9 +575,27 @@ def cpu_baseline(w, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    # the unsharded layer's four products once, for scale (one rank's share
+    # is 1/t of them); decode sizes only (at prefill sizes it would take
+    # minutes of float64)
+    unsharded_s = None
+    if M <= 64:
+        full = {k: lib.tp_full_shape(cfg, k) for k in ("qkv", "o", "gate_up", "down")}
+        rng = np.random.default_rng(w.index)
+        t1 = time.perf_counter()
+        for k in full:
+            Wf = rng.standard_normal(full[k]) * 0.02
+            oracle.linear(rng.standard_normal((M, full[k][1])), Wf)
+        unsharded_s = round(time.perf_counter() - t1, 3)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {"value": flops_layer * n / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{n} layer passes (qkv, o, reduce, gate_up, SwiGLU, down, reduce at this workload's "
-                      f"rank-share shapes, float64 NumPy) over 2 seeded layers in {el:.1f} s"}
+                      f"rank-share shapes, float64 NumPy) over 2 seeded layers in {el:.1f} s",
+            "affinity_cpus": affinity, "os_cpu_count": os.cpu_count(), "blas_threads": int(cores),
+            "unsharded_layer_products_s": unsharded_s}
 
 
 # ------------------------------------------------------------------- main
@@ -665,6 +697,14 @@ def summarize_counters(fetch_csv, write_csv, run_json, out=None):
     if launches < run["gemm_launches_per_step"]:
         raise SystemExit(f"found {launches} GEMM launches per step, fewer than the {run['gemm_launches_per_step']} calls")
     alg = run["gemm_algorithmic_bytes_per_step"]
+    other = []
+    for k in sorted(set(fetch) | set(write)):
+        if is_gemm_kernel(k) or k.startswith("shard_copy_kernel"):
+            continue
+        fv, wv = fetch.get(k, []), write.get(k, [])
+        if fv and wv:
+            other.append({"kernel": k, "launches": len(fv), "fetch_bytes_per_launch": round(sum(fv) / len(fv) * f_fetch),
+                          "write_bytes_per_launch": round(sum(wv) / len(wv) * f_write)})
     d = {"workload": run["workload"], "source_sha256": run["source_sha256"],
          "copy_bytes": nb, "fetch_scale": round(f_fetch, 5), "write_scale": round(f_write, 5),
          "gemm_calls_per_step": run["gemm_launches_per_step"],
@@ -672,11 +712,15 @@ def summarize_counters(fetch_csv, write_csv, run_json, out=None):
          "write_bytes_per_step": round(write_step), "traffic_bytes_per_step": round(fetch_step + write_step),
          "algorithmic_bytes_per_step": alg, "traffic_over_algorithmic": round((fetch_step + write_step) / alg, 4),
          "per_kernel": [{"kernel": k, "launches_per_step": n, "fetch_bytes_per_launch": round(fb),
-                         "write_bytes_per_launch": round(wb)} for k, n, fb, wb in rows]}
+                         "write_bytes_per_launch": round(wb)} for k, n, fb, wb in rows],
+         "other_kernels": other}
     print(f"copy of {nb} B: FETCH_SIZE scale {f_fetch:.4f}, WRITE_SIZE scale {f_write:.4f}")
     print(f"{'kernel':56s} {'launches/step':>13s} {'fetch_MiB/launch':>16s} {'write_MiB/launch':>16s}")
     for k, n, fb, wb in rows:
         print(f"{k[:56]:56s} {n:13d} {fb / 2**20:16.3f} {wb / 2**20:16.3f}")
+    for o in other:
+        print(f"{o['kernel'][:56]:56s} {o['launches']:13d} {o['fetch_bytes_per_launch'] / 2**20:16.3f} "
+              f"{o['write_bytes_per_launch'] / 2**20:16.3f}  (all launches of the run)")
     print(f"per step: traffic {(fetch_step + write_step) / 2**20:.2f} MiB, algorithmic {alg / 2**20:.2f} MiB, "
           f"ratio {(fetch_step + write_step) / alg:.4f}")
     if out:
@@ -905,6 +949,10 @@ def main():
         del src, dst
         for _ in range(args.warmup + args.steps):
             run_ops(ops)
+        # and the sums over ranks of the separate-call path (their traffic is
+        # reported per launch, beside the step's GEMMs)
+        for _ in range(args.warmup + args.steps):
+            run_ops([op for op in alt_ops if op[0] == "reduce"])
         torch.cuda.synchronize()
         print(json.dumps({"workload": w.name, "copy_bytes": full[0] * full[1] * 2, "copy_launches": 3,
                           "steps": args.warmup + args.steps,
@@ -972,11 +1020,12 @@ def main():
     op_names = names + [n for n in ("reduce",) if n not in names]
     for name in op_names:
         n_per_step, flops, byts = work[name]
-        us, distinct = time_rotated(torch, ops if name in names else alt_ops, name, args.steps)
+        spread = {}
+        us, distinct = time_rotated(torch, ops if name in names else alt_ops, name, args.steps, spread)
         per_op[name] = {"launches_per_step": n_per_step, "us_per_launch": round(us, 3),
                         "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                         "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2) if flops else None,
-                        "bytes_per_launch": byts, "distinct_MiB": round(distinct / 2**20)}
+                        "bytes_per_launch": byts, "distinct_MiB": round(distinct / 2**20), **spread}
         if name in GEMM_SHAPES:
             Mv, Nv, Kv = GEMM_SHAPES[name](R)
             per_op[name]["vendor_mm_us"] = round(vendor_mm_us(torch, Mv, Nv, Kv, args.steps), 3)
@@ -991,6 +1040,24 @@ def main():
     us_norm, _ = time_rotated(torch, norm_ops, "reduce_norm", args.steps)
 
     copy = measure_copy(torch, lib, I, w)
+
+    # the step's sums over ranks alone, back to back (the separate-call
+    # path's 2 per layer): launched one by one from Python, and replayed as
+    # a captured graph (the count problem of the decode all-reduces)
+    red_ops = [op for op in alt_ops if op[0] == "reduce"]
+    for _ in range(3):
+        run_ops(red_ops)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        run_ops(red_ops)
+    b.record()
+    torch.cuda.synchronize()
+    red_eager_us = a.elapsed_time(b) * 1e3 / (args.steps * len(red_ops))
+    g = capture(torch, red_ops)
+    red_graph_us = time_graph(torch, g, args.steps, 2) * 1e3 / len(red_ops)
+    del g
 
     value = flops_step / (ms_step * 1e-3) / 1e12
     gemm_us = sum(per_op[k]["us_per_launch"] * work[k][0] for k in gemm_ops)
@@ -1039,7 +1106,12 @@ def main():
         "roofline": roofline,
         "reduce": {"GBps": red["GBps"], "frac": round(red["GBps"] / HBM_PEAK_GBPS, 4),
                    "us_per_call": red["us_per_launch"], "calls_per_step": work["reduce"][0],
-                   "bytes_per_call": work["reduce"][2]},
+                   "bytes_per_call": work["reduce"][2],
+                   "sequence": {"calls": len(red_ops), "eager_us_per_call": round(red_eager_us, 3),
+                                "graph_us_per_call": round(red_graph_us, 3)},
+                   "note": ("latency-bound at this size: a launch and one memory round trip "
+                            f"({work['reduce'][2] / 8e12 * 1e6:.2f} us of HBM time per call)")
+                   if work["reduce"][2] < (8 << 20) else "bandwidth-bound"},
         "eager_ms_per_step": round(ms_eager, 4),
         "gemm_only_TFLOPs": round(flops_step / (gemm_us * 1e-6) / 1e12, 2),
         "step_GBps": round(sum(work[k][0] * work[k][2] for k in names) / (ms_step * 1e-3) / 1e9, 1),
