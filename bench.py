@@ -647,6 +647,12 @@ def stored_traffic(workload):
 GEMM_KERNELS = ("skinny_kernel", "skinny_split_finish", "tiled_dma_kernel", "tiled_dma64_kernel", "tiled_reg_kernel")
 
 
+# the library's other kernels (the step's sums, embedding, concatenation,
+# norms, attention), whose traffic the counter summary lists per launch
+LIBRARY_KERNELS = ("reduce_kernel", "vocab_embed_kernel", "concat_", "add_rmsnorm_kernel", "swiglu_kernel",
+                   "attn_chunk_kernel", "attn_merge_kernel", "fold_norm_weight_kernel")
+
+
 def is_gemm_kernel(name):
     return any(k in name for k in GEMM_KERNELS)
 
@@ -699,7 +705,7 @@ def summarize_counters(fetch_csv, write_csv, run_json, out=None):
     alg = run["gemm_algorithmic_bytes_per_step"]
     other = []
     for k in sorted(set(fetch) | set(write)):
-        if is_gemm_kernel(k) or k.startswith("shard_copy_kernel"):
+        if is_gemm_kernel(k) or "at::" in k or not any(k.startswith(n) for n in LIBRARY_KERNELS):
             continue
         fv, wv = fetch.get(k, []), write.get(k, [])
         if fv and wv:
