@@ -56,8 +56,8 @@ METRIC = "shard-GEMM TFLOP/s + reduce GB/s (% roofline), Llama-8B t=8 decode B=1
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="llama8b_t8_decode_m16")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of the captured step")
     p.add_argument("--separate", action="store_true",
@@ -899,6 +899,19 @@ def summarize_step_trace(trace_csv, run_log, out=None):
             f.write(text + "\n")
 
 
+def layer_linears(work, per_op, gemm_ops):
+    """TFLOP/s and GB/s of the step's per-layer linears (qkv, o, gate_up,
+    down and their fused forms) from their per-op durations."""
+    ops = [k for k in gemm_ops if k != "lm_head"]
+    us = sum(per_op[k]["us_per_launch"] * work[k][0] for k in ops)
+    fl = sum(work[k][0] * work[k][1] for k in ops)
+    by = sum(work[k][0] * work[k][2] for k in ops)
+    layers = work[ops[0]][0]
+    return {"ops": ops, "us_per_layer": round(us / layers, 3), "TFLOPs": round(fl / (us * 1e-6) / 1e12, 3),
+            "GBps": round(by / (us * 1e-6) / 1e9, 1), "frac_of_hbm": round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "frac_of_bf16": round(fl / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
 def main():
     if len(sys.argv) in (4, 5) and sys.argv[1] == "--summarize-step-trace":
         summarize_step_trace(*sys.argv[2:])
@@ -1120,6 +1133,9 @@ def main():
                    if work["reduce"][2] < (8 << 20) else "bandwidth-bound"},
         "eager_ms_per_step": round(ms_eager, 4),
         "gemm_only_TFLOPs": round(flops_step / (gemm_us * 1e-6) / 1e12, 2),
+        # the four per-layer linears alone (no embedding, LM head or
+        # concatenation): the workload's shard-GEMM figure proper
+        "layer_linears": layer_linears(work, per_op, gemm_ops),
         "step_GBps": round(sum(work[k][0] * work[k][2] for k in names) / (ms_step * 1e-3) / 1e9, 1),
         "partial_storage_ms_per_step": partials,
         "alt_path": {"calls": "separate" if fused else "fused", "ms_per_step": round(ms_alt, 4),
