@@ -612,28 +612,47 @@ skinny_split_finish(GemmArgs a, int splits, const float* __restrict__ ws) {
     const int64_t m = g / groups;
     const int64_t q = g - m * groups;
     const int64_t n = EPI == EPI_SWIGLU ? 16 * (q >> 1) + 4 * (q & 1) : 4 * q;
-    auto sum4 = [&](int64_t n0, float* v) {
-        v[0] = v[1] = v[2] = v[3] = 0.f;
-        for (int sp = 0; sp < splits; ++sp) {
-            const float* p = ws + ((int64_t)sp * M + m) * N + n0;
-            if (n0 + 3 < N && N % 4 == 0) {
-                const float4 t = *reinterpret_cast<const float4*>(p);
-                v[0] += t.x;
-                v[1] += t.y;
-                v[2] += t.z;
-                v[3] += t.w;
-            } else {
+    // The splits' values of 4 outputs at n0 (and, for SwiGLU, of the up
+    // rows at n0 + 8), 8 splits per round: every load of a round is issued
+    // before the first add, so a round costs one memory round trip; the adds
+    // then run in split order from 0.f.
+    constexpr int kRound = 8;
+    constexpr int kCols = EPI == EPI_SWIGLU ? 2 : 1;
+    const bool vec = n + 3 < N && N % 4 == 0;
+    float acc[kCols][4] = {};
+    for (int sp0 = 0; sp0 < splits; sp0 += kRound) {
+        float4 t[kRound][kCols];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (n0 + i < N) v[i] += p[i];
+        for (int j = 0; j < kRound; ++j) {
+            const int sp = sp0 + j < splits ? sp0 + j : splits - 1;   // clamped: in bounds, unused past splits
+#pragma unroll
+            for (int c = 0; c < kCols; ++c) {
+                const int64_t n0 = n + 8 * c;
+                const float* p = ws + ((int64_t)sp * M + m) * N + n0;
+                if (vec) {
+                    t[j][c] = *reinterpret_cast<const float4*>(p);
+                } else {
+                    t[j][c] = make_float4(n0 < N ? p[0] : 0.f, n0 + 1 < N ? p[1] : 0.f, n0 + 2 < N ? p[2] : 0.f,
+                                          n0 + 3 < N ? p[3] : 0.f);
+                }
             }
         }
-    };
-    float v[4];
-    sum4(n, v);
+#pragma unroll
+        for (int j = 0; j < kRound; ++j) {
+            if (sp0 + j < splits) {
+#pragma unroll
+                for (int c = 0; c < kCols; ++c) {
+                    acc[c][0] += t[j][c].x;
+                    acc[c][1] += t[j][c].y;
+                    acc[c][2] += t[j][c].z;
+                    acc[c][3] += t[j][c].w;
+                }
+            }
+        }
+    }
+    float v[4] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
     if constexpr (EPI == EPI_SWIGLU) {
-        float u[4];
-        sum4(n + 8, u);
+        const float u[4] = {acc[kCols - 1][0], acc[kCols - 1][1], acc[kCols - 1][2], acc[kCols - 1][3]};
         const int64_t j = (n >> 4) * 8 + (n & 7);      // first of the 4 gate columns
         if (j >= a.i_half) return;
         float o[4];
