@@ -851,10 +851,10 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64
         if (first_fit(rules, 5, &chosen)) return chosen;
     } else if (mt == 4) {
         // M in (32, 64]: measured winners at the Llama-8B t=16 shard shapes
-        // (weights rotated past the last-level cache; gate_up 1792 x 4096:
-        // 64-row tiles split 8 ways in two launches, 16.8 us, against 17.2
-        // for 16-row tiles split 4 ways in one).
-        static const Rule rules_small_n[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 4, 1, 4, 1}};
+        // (weights rotated past the last-level cache, K splits in two
+        // launches; gate_up 1792 x 4096: 64-row tiles split 8 ways, 14.2 us;
+        // qkv 512 x 4096: 16-row tiles split 8 ways with X staged, 8.2 us).
+        static const Rule rules_small_n[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 4, 1, 4, 0}};
         static const Rule rules_mid_n[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 4, 4, 4, 0}};
         static const Rule rules[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 8, 4, 2, 0}};
         if (first_fit(N <= 1024 ? rules_small_n : N <= 2048 ? rules_mid_n : rules, 3, &chosen)) return chosen;
@@ -962,13 +962,15 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
     return hipGetLastError();
 }
 
-// A K split at more than 32 tokens over 64-row tiles (not with the norm,
-// whose split shares of the sums of squares need the single-launch
-// exchange) runs as two launches. With 16-row tiles the last arrival reads
-// 16 KB per split and the second launch costs more than it saves (Llama
-// t = 16 qkv, 16 rows x 8 splits: 9.9 us in one launch, 10.9 in two).
+// A K split at more than 32 tokens (not with the norm, whose split shares of
+// the sums of squares need the single-launch exchange) runs as two launches:
+// with 64 tokens a split tile holds 4-16 KB of partials per split per 16
+// rows, which the one last-arriving workgroup of the single-launch exchange
+// would read alone after an arrival round trip (Llama t = 16 qkv, 16 rows x
+// 8 splits: 10.0 us in one launch, 8.7 in two; gate_up, 64 rows x 8 splits:
+// 16.8 in one, 14.4 in two).
 int skinny_split_launches(const SkinnyPlan& p, const GemmArgs& a) {
-    return (p.splits > 1 && p.mt == 4 && p.nwn >= 4 && a.norm == 0) ? 2 : 1;
+    return (p.splits > 1 && p.mt == 4 && a.norm == 0) ? 2 : 1;
 }
 
 }  // namespace tpk
