@@ -82,11 +82,15 @@ __device__ __forceinline__ int64_t tile_w_row(const GemmArgs& a, int64_t v) {
 
 // SwiGLU of 4 gate values and their up values: y[m, j..j+3], bf16, with the
 // gate_up outputs rounded to bf16 first as the unfused path stores them.
-__device__ __forceinline__ void swiglu_out4(const GemmArgs& a, int64_t m, int64_t j, float4 g, float4 u) {
+__device__ __forceinline__ void swiglu4(float4 g, float4 u, float* o) {
     const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
-    float o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = silu_f32(round_bf16(gv[i])) * round_bf16(uv[i]);
+}
+
+__device__ __forceinline__ void swiglu_out4(const GemmArgs& a, int64_t m, int64_t j, float4 g, float4 u) {
+    float o[4];
+    swiglu4(g, u, o);
     uint16_t* y = reinterpret_cast<uint16_t*>(a.y) + m * a.i_half + j;
     if (j + 3 < a.i_half && a.i_half % 4 == 0) {
         *reinterpret_cast<uint2*>(y) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
@@ -120,6 +124,133 @@ __device__ __forceinline__ void store_out4(const GemmArgs& a, int64_t m, int64_t
     }
 }
 
+// Tile epilogue, shared by the tiled kernels. The accumulators leave in
+// block rows i (32 weight rows of each of the two wave halves): acc[i][j][e]
+// holds D row 8 (e / 4) + 4 (lane / 32) + e % 4 and token lane % 32 of block
+// (i, j). A block row goes to LDS with constant register indices, as
+// slab[half][token][32 rows + pad], then every thread writes runs of 4 rows
+// of Y. The loop over block rows is not unrolled and the generic store path
+// (bias, ragged edges, fp32 or bf16) is a plain loop, so the epilogue's code
+// stays small: unrolled, it ran to ~18,000 instructions per kernel, whose
+// instruction fetch took ~13 us per 256 x 256 tile. Interior tiles without
+// bias take a fast path that issues every slab read before the stores.
+constexpr int kSlabStride = 36;                     // floats per token row (32 + pad)
+
+template <int BN, int BM>
+__device__ __forceinline__ bool tile_interior(const GemmArgs& a, int64_t m0, int64_t n0, int tile_n) {
+    if (m0 + BM > a.M) return false;
+    if (a.epi == EPI_SWIGLU) return (int64_t)(tile_n + 1) * (BN / 2) <= a.i_half && a.i_half % 4 == 0;
+    return n0 + BN <= a.N && a.N % 4 == 0 && a.bias == nullptr;
+}
+
+template <int BN, int BM, int THREADS>
+__device__ __forceinline__ void store_block_row(const GemmArgs& a, const float* slab, int i, int tid, int64_t m0,
+                                                int64_t n0, int tile_n, bool interior) {
+    constexpr int kWN = BN / 2;
+    constexpr int kRuns = 2 * BM * 8;               // (half, token, run of 4 rows)
+    static_assert(kRuns % THREADS == 0, "store loop must divide evenly");
+    static_assert((kRuns / 2) % THREADS == 0, "SwiGLU store loop must divide evenly");
+    constexpr int kIt = kRuns / THREADS;
+    constexpr int kItS = kRuns / 2 / THREADS;       // SwiGLU: gate half paired with up half
+    const int64_t M = a.M, N = a.N;
+    if (a.epi == EPI_SWIGLU) {
+        if (interior) {
+            float4 g[kItS], u[kItS];
+#pragma unroll
+            for (int it = 0; it < kItS; ++it) {
+                const int q = tid + it * THREADS;
+                g[it] = *reinterpret_cast<const float4*>(slab + (q >> 3) * kSlabStride + 4 * (q & 7));
+                u[it] = *reinterpret_cast<const float4*>(slab + (BM + (q >> 3)) * kSlabStride + 4 * (q & 7));
+            }
+#pragma unroll
+            for (int it = 0; it < kItS; ++it) {
+                const int q = tid + it * THREADS;
+                const int64_t j = (int64_t)tile_n * kWN + i * 32 + 4 * (q & 7);
+                float o[4];
+                swiglu4(g[it], u[it], o);
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + (m0 + (q >> 3)) * a.i_half + j) =
+                    make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            }
+        } else {
+#pragma unroll 1
+            for (int it = 0; it < kItS; ++it) {
+                const int q = tid + it * THREADS;
+                const int mt = q >> 3;
+                const int run = q & 7;
+                const int64_t m = m0 + mt;
+                const int64_t j = (int64_t)tile_n * kWN + i * 32 + 4 * run;
+                if (m < M && j < a.i_half)
+                    swiglu_out4(a, m, j, *reinterpret_cast<const float4*>(slab + mt * kSlabStride + 4 * run),
+                                *reinterpret_cast<const float4*>(slab + (BM + mt) * kSlabStride + 4 * run));
+            }
+        }
+        return;
+    }
+    // run q: half q / (8 BM), token (q mod 8 BM) / 8, rows 4 (q mod 8) of the block row
+    auto token = [&](int q) { return (q % (BM * 8)) >> 3; };
+    auto slab_at = [&](int q) { return slab + ((q / (BM * 8)) * BM + token(q)) * kSlabStride + 4 * (q & 7); };
+    auto col = [&](int q) { return n0 + (q / (BM * 8)) * kWN + i * 32 + 4 * (q & 7); };
+    if (interior) {
+        float4 v[kIt];
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) v[it] = *reinterpret_cast<const float4*>(slab_at(tid + it * THREADS));
+        if (a.out_dtype == TP_F32) {
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int q = tid + it * THREADS;
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + (m0 + token(q)) * N + col(q)) = v[it];
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int q = tid + it * THREADS;
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + (m0 + token(q)) * N + col(q)) =
+                    make_uint2(pack_bf16x2(v[it].x, v[it].y), pack_bf16x2(v[it].z, v[it].w));
+            }
+        }
+        return;
+    }
+#pragma unroll 1
+    for (int it = 0; it < kIt; ++it) {
+        const int q = tid + it * THREADS;
+        const int64_t m = m0 + token(q);
+        const int64_t n = col(q);
+        if (m < M && n < N) {
+            const float4 v = *reinterpret_cast<const float4*>(slab_at(q));
+            float o[4] = {v.x, v.y, v.z, v.w};
+            store_out4(a, m, n, o);
+        }
+    }
+}
+
+// The whole epilogue: block rows one at a time through the slab at `lds`
+// (the stage ring is free by then).
+template <int BN, int BM, int THREADS, int BLKN, int BLKM, int WM_ROWS, typename Acc>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& a, unsigned char* lds, Acc& acc, int tid, int wn,
+                                              int wm, int64_t m0, int64_t n0, int tile_n) {
+    float* slab = reinterpret_cast<float*>(lds);
+    const int lane = tid & 63;
+    const bool interior = tile_interior<BN, BM>(a, m0, n0, tile_n);
+#pragma unroll 1
+    for (int i = 0; i < BLKN; ++i) {
+        static_for<BLKN>([&](auto I) {
+            if (i == decltype(I)::value) {
+                static_for<BLKM>([&](auto j) {
+                    const int mt = wm * WM_ROWS + j * 32 + (lane & 31);
+                    static_for<4>([&](auto g) {
+                        const f32x4_t v = {acc[I][j][4 * g], acc[I][j][4 * g + 1], acc[I][j][4 * g + 2],
+                                           acc[I][j][4 * g + 3]};
+                        *reinterpret_cast<f32x4_t*>(slab + (wn * BM + mt) * kSlabStride + 8 * g + 4 * (lane >> 5)) = v;
+                    });
+                });
+            }
+        });
+        lds_barrier();
+        store_block_row<BN, BM, THREADS>(a, slab, i, tid, m0, n0, tile_n, interior);
+        lds_barrier();
+    }
+}
+
 template <int BN, int BM>
 __global__ void __launch_bounds__(kThreads, 1)
 tiled_reg_kernel(GemmArgs a, int tiles_n, int tiles_m) {
@@ -141,7 +272,7 @@ tiled_reg_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     const int wave = tid >> 6;
     const int wn = wave >> 1;
     const int wm = wave & 1;
-    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t M = a.M, K = a.K;
     const int64_t n0 = (int64_t)tile_n * BN;
     const int64_t m0 = (int64_t)tile_m * BM;
     const bf16_t* __restrict__ X = reinterpret_cast<const bf16_t*>(a.x);
@@ -230,56 +361,7 @@ tiled_reg_kernel(GemmArgs a, int tiles_n, int tiles_m) {
         }
     }
 
-    // Epilogue, one block row i at a time. acc[i][j][e] holds D row (weight
-    // row) 8 (e / 4) + 4 (lane / 32) + e % 4 and column (token) lane % 32 of
-    // block (i, j). The accumulators go to LDS with constant indices (so they
-    // stay in registers), as slab[wn][token][32 rows], then all 256 threads
-    // write rows of Y with 16-byte runs.
-    float* slab = reinterpret_cast<float*>(lds);
-    constexpr int kSlabStride = 36;                     // floats per token row (32 + pad)
-    static_for<C::kBlkN>([&](auto i) {
-        static_for<C::kBlkM>([&](auto j) {
-            const int mt = wm * C::kWM + j * 32 + (lane & 31);
-            static_for<4>([&](auto g) {
-                const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                *reinterpret_cast<f32x4_t*>(slab + (wn * BM + mt) * kSlabStride + 8 * g + 4 * (lane >> 5)) = v;
-            });
-        });
-        __syncthreads();
-        // 2 slabs x BM tokens x 8 runs of 4 rows
-        constexpr int kRuns = 2 * BM * 8;
-        static_assert(kRuns % kThreads == 0, "store loop must divide evenly");
-        static_assert((kRuns / 2) % kThreads == 0, "SwiGLU store loop must divide evenly");
-        if (a.epi == EPI_SWIGLU) {
-#pragma unroll
-            for (int it = 0; it < kRuns / 2 / kThreads; ++it) {
-                const int q = tid + it * kThreads;
-                const int mt = q >> 3;
-                const int run = q & 7;
-                const int64_t m = m0 + mt;
-                const int64_t j = (int64_t)tile_n * C::kWN + i * 32 + 4 * run;
-                if (m < M && j < a.i_half)
-                    swiglu_out4(a, m, j, *reinterpret_cast<const float4*>(slab + mt * kSlabStride + 4 * run),
-                                *reinterpret_cast<const float4*>(slab + (BM + mt) * kSlabStride + 4 * run));
-            }
-        } else
-#pragma unroll
-        for (int it = 0; it < kRuns / kThreads; ++it) {
-            const int q = tid + it * kThreads;
-            const int half = q / (BM * 8);
-            const int rem = q - half * (BM * 8);
-            const int mt = rem >> 3;
-            const int run = rem & 7;
-            const int64_t m = m0 + mt;
-            const int64_t n = n0 + half * C::kWN + i * 32 + 4 * run;
-            if (m < M && n < N) {
-                const float4 v = *reinterpret_cast<const float4*>(slab + (half * BM + mt) * kSlabStride + 4 * run);
-                float o[4] = {v.x, v.y, v.z, v.w};
-                store_out4(a, m, n, o);
-            }
-        }
-        __syncthreads();
-    });
+    tile_epilogue<BN, BM, kThreads, C::kBlkN, C::kBlkM, C::kWM>(a, lds_raw, acc, tid, wn, wm, m0, n0, tile_n);
 }
 
 #undef TP_TILED_LOAD
@@ -344,7 +426,7 @@ tiled_dma_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     const int wave = tid >> 6;
     const int wn = wave / WGM;
     const int wm = wave % WGM;
-    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t M = a.M, K = a.K;
     const int64_t n0 = (int64_t)tile_n * BN;
     const int64_t m0 = (int64_t)tile_m * BM;
     const bf16_t* __restrict__ X = reinterpret_cast<const bf16_t*>(a.x);
@@ -447,51 +529,7 @@ tiled_dma_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     wait_vmcnt<0>();
     __syncthreads();
 
-    // Epilogue (as in the register-staged kernel): LDS slab per block row.
-    float* slab = reinterpret_cast<float*>(lds8);
-    constexpr int kSlabStride = 36;
-    static_for<C::kBlkN>([&](auto i) {
-        static_for<C::kBlkM>([&](auto j) {
-            const int mt = wm * C::kWM + j * 32 + (lane & 31);
-            static_for<4>([&](auto g) {
-                const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                *reinterpret_cast<f32x4_t*>(slab + (wn * BM + mt) * kSlabStride + 8 * g + 4 * (lane >> 5)) = v;
-            });
-        });
-        __syncthreads();
-        constexpr int kRuns = 2 * BM * 8;
-        static_assert(kRuns % C::kThreadsWG == 0, "store loop must divide evenly");
-        static_assert((kRuns / 2) % C::kThreadsWG == 0, "SwiGLU store loop must divide evenly");
-        if (a.epi == EPI_SWIGLU) {
-#pragma unroll
-            for (int it = 0; it < kRuns / 2 / C::kThreadsWG; ++it) {
-                const int q = tid + it * C::kThreadsWG;
-                const int mt = q >> 3;
-                const int run = q & 7;
-                const int64_t m = m0 + mt;
-                const int64_t j = (int64_t)tile_n * C::kWN + i * 32 + 4 * run;
-                if (m < M && j < a.i_half)
-                    swiglu_out4(a, m, j, *reinterpret_cast<const float4*>(slab + mt * kSlabStride + 4 * run),
-                                *reinterpret_cast<const float4*>(slab + (BM + mt) * kSlabStride + 4 * run));
-            }
-        } else
-#pragma unroll
-        for (int it = 0; it < kRuns / C::kThreadsWG; ++it) {
-            const int q = tid + it * C::kThreadsWG;
-            const int half = q / (BM * 8);
-            const int rem = q - half * (BM * 8);
-            const int mt = rem >> 3;
-            const int run = rem & 7;
-            const int64_t m = m0 + mt;
-            const int64_t n = n0 + half * C::kWN + i * 32 + 4 * run;
-            if (m < M && n < N) {
-                const float4 v = *reinterpret_cast<const float4*>(slab + (half * BM + mt) * kSlabStride + 4 * run);
-                float o[4] = {v.x, v.y, v.z, v.w};
-                store_out4(a, m, n, o);
-            }
-        }
-        __syncthreads();
-    });
+    tile_epilogue<BN, BM, C::kThreadsWG, C::kBlkN, C::kBlkM, C::kWM>(a, lds8, acc, tid, wn, wm, m0, n0, tile_n);
 }
 
 // ---------------------------------------------------------------------------
@@ -499,8 +537,13 @@ tiled_dma_kernel(GemmArgs a, int tiles_n, int tiles_m) {
 // line (8 lanes x 16 B), where 32-wide k-tiles fetch each line in two halves
 // a k-tile apart; and there is one barrier per 64 of K. On the prefill shard
 // shapes it runs 3-10 % faster than the 32-wide kernel with the same tile. LDS stage: W tile [BN][64] then X tile [BM][64], 128-byte rows,
-// 16-byte chunks XOR-swizzled by row mod 8 (8 consecutive rows read by 8
-// lanes hit 8 different bank groups). After the barrier of k-tile kt every
+// 16-byte chunks XOR-swizzled by (row / 2) mod 8. A 16-byte LDS read is
+// served 16 lanes at a time across 64 four-byte banks (256 bytes): the 16
+// consecutive rows that 16 lanes read are 8 pairs of rows 128 bytes apart,
+// and the swizzle gives the 8 rows of each parity 8 different 16-byte bank
+// groups, so the 16 reads take all 64 banks once. (A swizzle by row mod 8
+// sends rows r and r + 8 to the same banks: measured 0.96 bank-conflict
+// cycles per LDS access on the 256 x 256 tile.) After the barrier of k-tile kt every
 // wave has finished reading stage kt, so the DMA of k-tile kt + NS goes into
 // its slot: NS stages are in flight from the prologue on.
 template <int BN, int BM, int NS, int WGM>
@@ -520,7 +563,7 @@ struct Dma64Cfg {
     static_assert(NS >= 2 && NS * kInstrPerWave <= 63, "stages in flight must fit the load counter");
 };
 
-__device__ __forceinline__ int swz128(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz128(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
 template <int BN, int BM, int NS, int WGM>
 __global__ void __launch_bounds__(128 * WGM, (Dma64Cfg<BN, BM, NS, WGM>::kLdsBytes <= 80 * 1024 ? 2 : 1))
@@ -541,7 +584,7 @@ tiled_dma64_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     const int wave = tid >> 6;
     const int wn = wave / WGM;
     const int wm = wave % WGM;
-    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t M = a.M, K = a.K;
     const int64_t n0 = (int64_t)tile_n * BN;
     const int64_t m0 = (int64_t)tile_m * BM;
     const bf16_t* __restrict__ X = reinterpret_cast<const bf16_t*>(a.x);
@@ -558,7 +601,7 @@ tiled_dma64_kernel(GemmArgs a, int tiles_n, int tiles_m) {
         const bool is_w = instr < C::kInstrW;
         const int rbase = (is_w ? instr : instr - C::kInstrW) * 8;
         const int r = rbase + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
         int64_t g;
         if (is_w) {
             g = tile_w_row<BN>(a, n0 + r);
@@ -586,18 +629,23 @@ tiled_dma64_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     const int orow = lane & 31;
     const int ohalf = lane >> 5;
     bf16x8_t fa[2][C::kBlkN], fb[2][C::kBlkM];
+    // Fragments are read in the order the MFMAs below consume them (A0, every
+    // B, then A1, A2, ...): LDS reads return in order, so the first MFMAs of
+    // a step wait only for the first reads of the previous step.
     auto read_frags = [&](auto buf, int kt, int s) {
         const unsigned char* ws = lds8 + (kt % NS) * C::kStageBytes;
         const unsigned char* xs = ws + BN * 128;
         const int c = 2 * s + ohalf;
-        static_for<C::kBlkN>([&](auto i) {
+        auto read_a = [&](auto i) {
             fa[buf][i] = __builtin_bit_cast(bf16x8_t,
                 *reinterpret_cast<const u32x4_t*>(ws + swz128(wn * C::kWN + i * 32 + orow, c)));
-        });
+        };
+        read_a(std::integral_constant<int, 0>{});
         static_for<C::kBlkM>([&](auto j) {
             fb[buf][j] = __builtin_bit_cast(bf16x8_t,
                 *reinterpret_cast<const u32x4_t*>(xs + swz128(wm * C::kWM + j * 32 + orow, c)));
         });
+        static_for<C::kBlkN - 1>([&](auto i) { read_a(std::integral_constant<int, decltype(i)::value + 1>{}); });
     };
     auto mfmas = [&](auto buf) {
         static_for<C::kBlkN>([&](auto i) {
@@ -668,51 +716,7 @@ tiled_dma64_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     wait_vmcnt<0>();
     __syncthreads();
 
-    // Epilogue: as in the 32-wide kernel.
-    float* slab = reinterpret_cast<float*>(lds8);
-    constexpr int kSlabStride = 36;
-    static_for<C::kBlkN>([&](auto i) {
-        static_for<C::kBlkM>([&](auto j) {
-            const int mt = wm * C::kWM + j * 32 + (lane & 31);
-            static_for<4>([&](auto g) {
-                const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                *reinterpret_cast<f32x4_t*>(slab + (wn * BM + mt) * kSlabStride + 8 * g + 4 * (lane >> 5)) = v;
-            });
-        });
-        __syncthreads();
-        constexpr int kRuns = 2 * BM * 8;
-        static_assert(kRuns % C::kThreadsWG == 0, "store loop must divide evenly");
-        static_assert((kRuns / 2) % C::kThreadsWG == 0, "SwiGLU store loop must divide evenly");
-        if (a.epi == EPI_SWIGLU) {
-#pragma unroll
-            for (int it = 0; it < kRuns / 2 / C::kThreadsWG; ++it) {
-                const int q = tid + it * C::kThreadsWG;
-                const int mt = q >> 3;
-                const int run = q & 7;
-                const int64_t m = m0 + mt;
-                const int64_t j = (int64_t)tile_n * C::kWN + i * 32 + 4 * run;
-                if (m < M && j < a.i_half)
-                    swiglu_out4(a, m, j, *reinterpret_cast<const float4*>(slab + mt * kSlabStride + 4 * run),
-                                *reinterpret_cast<const float4*>(slab + (BM + mt) * kSlabStride + 4 * run));
-            }
-        } else
-#pragma unroll
-        for (int it = 0; it < kRuns / C::kThreadsWG; ++it) {
-            const int q = tid + it * C::kThreadsWG;
-            const int half = q / (BM * 8);
-            const int rem = q - half * (BM * 8);
-            const int mt = rem >> 3;
-            const int run = rem & 7;
-            const int64_t m = m0 + mt;
-            const int64_t n = n0 + half * C::kWN + i * 32 + 4 * run;
-            if (m < M && n < N) {
-                const float4 v = *reinterpret_cast<const float4*>(slab + (half * BM + mt) * kSlabStride + 4 * run);
-                float o[4] = {v.x, v.y, v.z, v.w};
-                store_out4(a, m, n, o);
-            }
-        }
-        __syncthreads();
-    });
+    tile_epilogue<BN, BM, C::kThreadsWG, C::kBlkN, C::kBlkM, C::kWM>(a, lds8, acc, tid, wn, wm, m0, n0, tile_n);
 }
 
 typedef void (*TiledFn)(GemmArgs, int, int);

@@ -61,7 +61,7 @@ def test_column_linear_swiglu_same_bits_as_separate_calls(M, Is, K):
     assert_close(f64(got), oracle.swiglu(gu[:, :Is], gu[:, Is:]), f"fused swiglu {(M, Is, K)}")
 
 
-@pytest.mark.parametrize("variant", list(range(12)))
+@pytest.mark.parametrize("variant", list(range(lib.tp_prefill_tile_count())))
 def test_every_prefill_tile_shape_fused_swiglu(variant):
     """The SwiGLU epilogue pairs gate and up rows inside each tile (first
     and second half of its rows): every tile shape, ragged widths."""
