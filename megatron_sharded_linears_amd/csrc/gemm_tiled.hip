@@ -401,6 +401,18 @@ struct DmaCfg {
 
 __device__ __forceinline__ int swz64(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
 
+// Barrier for the kernels that stream k-tiles into LDS with
+// global_load_lds: this wave's LDS reads are complete (lgkmcnt 0) and every
+// wave has arrived; which stages have landed is the caller's explicit
+// vmcnt wait. lds_barrier's release fence covers LDS writes, and LDS DMA
+// counts on vmcnt, so the compiler puts a vmcnt(0) in front of it: a ring
+// of three or more stages would then keep no stage beyond the next one in
+// flight across a barrier. The memory clobber keeps the compiler from
+// moving LDS accesses across the barrier.
+__device__ __forceinline__ void dma_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -503,7 +515,7 @@ tiled_dma_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     const int pro = ktiles < NS - 1 ? ktiles : NS - 1;
     for (int kt = 0; kt < pro; ++kt) issue(kt);
     wait_stage(pro - 1);
-    lds_barrier();
+    dma_barrier();
     read_frags(std::integral_constant<int, kF0>{}, 0, 0);
 
     // The last k-tile is peeled off so that the loop body has no branch
@@ -518,7 +530,7 @@ tiled_dma_kernel(GemmArgs a, int tiles_n, int tiles_m) {
         // stages issued after kt + 1: up to kt + NS - 2
         const int last = kt + NS - 2 < ktiles - 1 ? kt + NS - 2 : ktiles - 1;
         wait_stage(last - (kt + 1));
-        lds_barrier();   // every wave's part of stage kt + 1 has landed; stage kt - 1 is free
+        dma_barrier();   // every wave's part of stage kt + 1 has landed; stage kt - 1 is free
         if (kt + NS - 1 < ktiles) issue(kt + NS - 1);
         read_frags(std::integral_constant<int, kF0>{}, kt + 1, 0);
         mfmas(std::integral_constant<int, kF1>{});
@@ -682,7 +694,7 @@ tiled_dma64_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     const int pro = ktiles < NS ? ktiles : NS;
     for (int kt = 0; kt < pro; ++kt) issue(kt);
     wait_stage(pro - 1);
-    lds_barrier();
+    dma_barrier();
     read_frags(F0{}, 0, 0);
 
     // The last k-tile runs after the loop, so the loop body has no branch
@@ -700,7 +712,7 @@ tiled_dma64_kernel(GemmArgs a, int tiles_n, int tiles_m) {
         // stages issued after kt + 1: up to kt + NS - 1
         const int last = kt + NS - 1 < ktiles - 1 ? kt + NS - 1 : ktiles - 1;
         wait_stage(last - (kt + 1));
-        lds_barrier();   // stage kt + 1 has landed; every wave is done with stage kt
+        dma_barrier();   // stage kt + 1 has landed; every wave is done with stage kt
         if (kt + NS < ktiles) issue(kt + NS);
         read_frags(F0{}, kt + 1, 0);
         mfmas(F1{});
