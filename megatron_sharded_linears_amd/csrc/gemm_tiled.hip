@@ -131,9 +131,11 @@ __device__ __forceinline__ void store_out4(const GemmArgs& a, int64_t m, int64_t
 // slab[half][token][32 rows + pad], then every thread writes runs of 4 rows
 // of Y. The loop over block rows is not unrolled and the generic store path
 // (bias, ragged edges, fp32 or bf16) is a plain loop, so the epilogue's code
-// stays small: unrolled, it ran to ~18,000 instructions per kernel, whose
-// instruction fetch took ~13 us per 256 x 256 tile. Interior tiles without
-// bias take a fast path that issues every slab read before the stores.
+// stays small (fully unrolled, the kernel ran to ~18,000 instructions and
+// its epilogue took 13 us per 256 x 256 tile; this form takes 8, about what
+// a whole chip of tiles writing 128 KB each at once needs). Interior tiles
+// without bias take a fast path that issues every slab read before the
+// stores.
 constexpr int kSlabStride = 36;                     // floats per token row (32 + pad)
 
 template <int BN, int BM>
