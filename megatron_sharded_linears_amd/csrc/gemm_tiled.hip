@@ -70,6 +70,12 @@ struct TileCfg {
     static constexpr int kLdsBytes = 2 * kStageElems * 2;
 };
 
+// Output row stride (elements) and SwiGLU up-row offset of a launch.
+__device__ __forceinline__ int64_t out_ld(const GemmArgs& a) {
+    return a.ldy != 0 ? a.ldy : (a.epi == EPI_SWIGLU ? a.i_half : a.N);
+}
+__device__ __forceinline__ int64_t up_rows(const GemmArgs& a) { return a.up_off != 0 ? a.up_off : a.i_half; }
+
 // Weight row of kernel row v for tiles of BN rows, or -1 past the end.
 // EPI_SWIGLU: tile b holds gate rows [b BN/2, (b+1) BN/2), then the same up rows.
 template <int BN>
@@ -77,7 +83,7 @@ __device__ __forceinline__ int64_t tile_w_row(const GemmArgs& a, int64_t v) {
     if (a.epi != EPI_SWIGLU) return v < a.N ? v : -1;
     const int64_t j = (v / BN) * (BN / 2) + (v % (BN / 2));
     if (j >= a.i_half) return -1;
-    return (v % BN) >= BN / 2 ? a.i_half + j : j;
+    return (v % BN) >= BN / 2 ? up_rows(a) + j : j;
 }
 
 // SwiGLU of 4 gate values and their up values: y[m, j..j+3], bf16, with the
@@ -91,8 +97,9 @@ __device__ __forceinline__ void swiglu4(float4 g, float4 u, float* o) {
 __device__ __forceinline__ void swiglu_out4(const GemmArgs& a, int64_t m, int64_t j, float4 g, float4 u) {
     float o[4];
     swiglu4(g, u, o);
-    uint16_t* y = reinterpret_cast<uint16_t*>(a.y) + m * a.i_half + j;
-    if (j + 3 < a.i_half && a.i_half % 4 == 0) {
+    const int64_t ld = out_ld(a);
+    uint16_t* y = reinterpret_cast<uint16_t*>(a.y) + m * ld + j;
+    if (j + 3 < a.i_half && ld % 4 == 0) {
         *reinterpret_cast<uint2*>(y) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     } else {
         for (int i = 0; i < 4; ++i) if (j + i < a.i_half) y[i] = (uint16_t)f32_to_bf16(o[i]);
@@ -111,8 +118,9 @@ __device__ __forceinline__ void store_out4(const GemmArgs& a, int64_t m, int64_t
         for (int i = 0; i < 4; ++i)
             if (n + i < a.N) o[i] += bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[n + i]);
     }
-    const int64_t base = m * a.N + n;
-    const bool full = (n + 3 < a.N) && (a.N % 4 == 0);
+    const int64_t ld = out_ld(a);
+    const int64_t base = m * ld + n;
+    const bool full = (n + 3 < a.N) && (ld % 4 == 0);
     if (a.out_dtype == TP_F32) {
         float* y = reinterpret_cast<float*>(a.y);
         if (full) *reinterpret_cast<float4*>(y + base) = make_float4(o[0], o[1], o[2], o[3]);
@@ -141,8 +149,8 @@ constexpr int kSlabStride = 36;                     // floats per token row (32 
 template <int BN, int BM>
 __device__ __forceinline__ bool tile_interior(const GemmArgs& a, int64_t m0, int64_t n0, int tile_n) {
     if (m0 + BM > a.M) return false;
-    if (a.epi == EPI_SWIGLU) return (int64_t)(tile_n + 1) * (BN / 2) <= a.i_half && a.i_half % 4 == 0;
-    return n0 + BN <= a.N && a.N % 4 == 0 && a.bias == nullptr;
+    if (a.epi == EPI_SWIGLU) return (int64_t)(tile_n + 1) * (BN / 2) <= a.i_half && out_ld(a) % 4 == 0;
+    return n0 + BN <= a.N && out_ld(a) % 4 == 0 && a.bias == nullptr;
 }
 
 template <int BN, int BM, int THREADS>
@@ -154,7 +162,7 @@ __device__ __forceinline__ void store_block_row(const GemmArgs& a, const float* 
     static_assert((kRuns / 2) % THREADS == 0, "SwiGLU store loop must divide evenly");
     constexpr int kIt = kRuns / THREADS;
     constexpr int kItS = kRuns / 2 / THREADS;       // SwiGLU: gate half paired with up half
-    const int64_t M = a.M, N = a.N;
+    const int64_t M = a.M, N = a.N, ld = out_ld(a);
     if (a.epi == EPI_SWIGLU) {
         if (interior) {
             float4 g[kItS], u[kItS];
@@ -170,7 +178,7 @@ __device__ __forceinline__ void store_block_row(const GemmArgs& a, const float* 
                 const int64_t j = (int64_t)tile_n * kWN + i * 32 + 4 * (q & 7);
                 float o[4];
                 swiglu4(g[it], u[it], o);
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + (m0 + (q >> 3)) * a.i_half + j) =
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + (m0 + (q >> 3)) * ld + j) =
                     make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
         } else {
@@ -200,13 +208,13 @@ __device__ __forceinline__ void store_block_row(const GemmArgs& a, const float* 
 #pragma unroll
             for (int it = 0; it < kIt; ++it) {
                 const int q = tid + it * THREADS;
-                *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + (m0 + token(q)) * N + col(q)) = v[it];
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + (m0 + token(q)) * ld + col(q)) = v[it];
             }
         } else {
 #pragma unroll
             for (int it = 0; it < kIt; ++it) {
                 const int q = tid + it * THREADS;
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + (m0 + token(q)) * N + col(q)) =
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + (m0 + token(q)) * ld + col(q)) =
                     make_uint2(pack_bf16x2(v[it].x, v[it].y), pack_bf16x2(v[it].z, v[it].w));
             }
         }
@@ -764,6 +772,7 @@ const TiledEntry kTiled[] = {
     TP_DMA64(128, 64, 4, 2),
     TP_DMA64(64, 64, 6, 1),
     TP_DMA64(128, 128, 2, 2),
+    TP_DMA64(192, 256, 2, 4),
 };
 #undef TP_DMA
 #undef TP_DMA64
@@ -811,7 +820,7 @@ hipError_t launch_variant(const GemmArgs& a, int v, int64_t m0, hipStream_t s) {
     const bool swiglu = a.epi == EPI_SWIGLU;
     if (swiglu) b.N = (int64_t)e.bn * ((a.i_half + e.bn / 2 - 1) / (e.bn / 2));
     if (m0 > 0) {
-        const int64_t y_cols = swiglu ? a.i_half : a.N;
+        const int64_t y_cols = a.ldy != 0 ? a.ldy : (swiglu ? a.i_half : a.N);
         const int64_t y_elem = a.out_dtype == TP_F32 ? 4 : 2;
         b.x = static_cast<const unsigned char*>(a.x) + m0 * a.K * 2;
         b.y = static_cast<unsigned char*>(a.y) + m0 * y_cols * y_elem;
@@ -879,6 +888,49 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant) {
     else if (shape == 1) best = 15;
     else best = 8 + shape;
     if (variant >= 0 && variant < kNumTiled && a.K % kTiled[variant].kmul == 0) return launch_variant(a, variant, 0, s);
+    // Weight-row split: when 256 x 256 tiles make between one and two waves,
+    // one whole wave of them takes the first weight rows and a second launch
+    // of 192 x 256 tiles (0.75 of the work per tile, one exact wave where the
+    // shapes allow) takes the rest, instead of a second wave of 256 x 256
+    // tiles that leaves CUs idle (Llama-8B t = 2 gate_up, 2048 x 14336 x
+    // 4096: 256 + 256 tiles, 215 against 224 us, timed alternately; Qwen-32B
+    // t = 8 gate_up, 256 + 240 tiles: no change). Each output keeps its
+    // tile's K order, so the split changes no bit.
+    if (best == 8) {
+        const int64_t t8 = tiles(256, 256);
+        const int64_t tm = (a.M + 255) / 256;
+        const int64_t head_n = kCus / tm;
+        const int64_t head_rows = head_n * 256;
+        const int64_t tail_rows = a.N - head_rows;
+        const int64_t tail_tiles = tail_rows > 0 ? ((tail_rows + 191) / 192) * tm : 0;
+        if (t8 > kCus && t8 < 2 * kCus && head_n >= 1 && head_n * tm * 10 >= kCus * 9 && tail_rows > 0 &&
+            tail_tiles <= kCus && tail_tiles * 10 >= kCus * 6) {
+            const bool sw = a.epi == EPI_SWIGLU;
+            const int64_t y_elem = a.out_dtype == TP_F32 ? 4 : 2;
+            GemmArgs h = a, t = a;
+            if (sw) {
+                const int64_t g0 = head_rows / 2;      // gate rows in the head
+                h.i_half = g0;
+                h.N = 2 * g0;
+                t.i_half = a.i_half - g0;
+                t.N = 2 * t.i_half;
+                t.w = static_cast<const unsigned char*>(a.w) + g0 * a.K * 2;
+                t.y = static_cast<unsigned char*>(a.y) + g0 * 2;
+                h.up_off = t.up_off = a.i_half;
+                h.ldy = t.ldy = a.i_half;
+            } else {
+                h.N = head_rows;
+                t.N = a.N - head_rows;
+                t.w = static_cast<const unsigned char*>(a.w) + head_rows * a.K * 2;
+                t.y = static_cast<unsigned char*>(a.y) + head_rows * y_elem;
+                if (a.bias != nullptr) t.bias = static_cast<const unsigned char*>(a.bias) + head_rows * 2;
+                h.ldy = t.ldy = a.N;
+            }
+            const hipError_t he = launch_variant(h, 8, 0, s);
+            if (he != hipSuccess) return he;
+            return launch_variant(t, 16, 0, s);
+        }
+    }
     // Wave quantisation: when the last wave of 256 x 256 tiles would leave
     // most CUs idle (Qwen-32B t = 8 down: 320 tiles, 1.25 waves), the
     // first token rows keep those tiles and the rest run as a second launch

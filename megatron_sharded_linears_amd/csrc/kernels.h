@@ -77,6 +77,12 @@ struct GemmArgs {
     int norm;
     float eps;
     const void* peers[kMaxFusedPeers];
+    // Prefill kernels only (0: the defaults). ldy: elements between output
+    // rows (N, or i_half with SwiGLU); up_off: weight rows from a gate row to
+    // its up row (i_half). Set when a launch covers a block of the weight
+    // rows of a larger product.
+    int64_t ldy = 0;
+    int64_t up_off = 0;
 };
 
 // Caller-owned scratch (the C ABI's workspace argument): fp32 partial tiles
