@@ -73,6 +73,17 @@ def test_every_prefill_tile_shape_fused_swiglu(variant):
             (variant, M, Is, K)
 
 
+def test_weight_row_split_swiglu():
+    """SwiGLU over the planner's weight-row split (2048 tokens, I_shard = 6008:
+    256 x 256 tiles for the first 4096 gate/up row pairs, then 192 x 256 tiles
+    with a ragged last one): the fused epilogue against the separate calls,
+    bit for bit, every element written."""
+    M, Is, K = 2048, 6008, 128
+    x = dev(I.normal_bf16((SEED, 70, M, Is, K), (M, K)))
+    w = dev(I.normal_bf16((SEED, 71, M, Is, K), (2 * Is, K), 0.05))
+    assert np.array_equal(bits(fused_swiglu(x, w, Is)), bits(separate_swiglu(x, w, Is)))
+
+
 @pytest.mark.parametrize("M,Is,K", [(16, 100, 256), (3, 13, 72), (64, 1, 8), (100, 37, 136)])
 def test_column_linear_swiglu_ragged_width_exact_integer(M, Is, K):
     """I_shard not a multiple of 8 (no separate tp_swiglu to compare with):

@@ -159,6 +159,32 @@ def test_every_prefill_tile_shape_exact(variant):
         assert_close(f64(yb), oracle.linear(f64(xr), f64(wr), f64(b)), f"tile {variant} {(M, N, K)}")
 
 
+@pytest.mark.parametrize("N", [12008, 14336])
+def test_weight_row_split_exact(N):
+    """2048 tokens and between one and two waves of 256 x 256 tiles: the
+    planner runs one whole wave of them on the first weight rows and 192 x 256
+    tiles on the rest (a ragged last tile at N = 12008). Exact-integer inputs
+    (|sums| <= 64, exact in bf16 too): the fp32 row partial and the bf16
+    column linear with bias against the oracle, every element, and one launch
+    of 256 x 256 tiles over the whole product gives the same bits."""
+    M, K = 2048, 64
+    x = dev(I.small_int_bf16((SEED, 60, N), (M, K)))
+    w = dev(I.small_int_bf16((SEED, 61, N), (N, K)))
+    b = dev(I.small_int_bf16((SEED, 62, N), (N,)))
+    ref = oracle.linear(f64(x), f64(w))
+    y = empty((M, N), torch.float32)
+    y.fill_(float("nan"))
+    lib.tp_row_linear_partial(x, w, y)
+    assert np.array_equal(f64(y), ref), N
+    yb = empty((M, N))
+    yb.fill_(float("nan"))
+    lib.tp_column_linear(x, w, yb, bias=b)
+    assert np.array_equal(f64(yb), ref + f64(b)[None, :]), N
+    y8 = empty((M, N))
+    lib.tp_column_linear(x, w, y8, bias=b, plan={"tile": 8})
+    assert torch.equal(yb.view(torch.int16), y8.view(torch.int16)), N
+
+
 # ------------------------------------------------ linears, random tolerance
 
 @pytest.mark.parametrize("M,N,K", [(16, 768, 4096), (64, 1792, 4096), (1, 1000, 256), (200, 300, 512), (2048, 256, 1024)])
