@@ -855,17 +855,26 @@ def summarize_step_trace(trace_csv, run_log, out=None):
     # The timed replays are the trace's last dispatches (set-up kernels such
     # as the seeded generators come first): the step's length is the
     # smallest period of the kernel sequence over its last K repeats.
-    # A step of identical layers repeats with the layer's period too: the
-    # step's is the first multiple of the smallest period that covers at
-    # least the step's calls (every call launches at least one kernel).
+    # A step of identical layers repeats with the layer's period too, and a
+    # call may launch more than one kernel: the step's period is the multiple
+    # of the smallest one, covering at least the step's calls, whose K
+    # repeats span the time the run measured for K steps.
     names = [k for _, _, k in rows]
     q = next((p for p in range(1, len(names) // K + 1)
               if all(names[-1 - i] == names[-1 - i - p] for i in range(p * (K - 1)))), None)
     if q is None:
         raise SystemExit("no step period found in the trace")
-    per = q * -(-run["launches_per_step"] // q)
-    if K * per > len(rows) or any(names[-1 - i] != names[-1 - i - per] for i in range(per * (K - 1))):
-        raise SystemExit(f"the trace does not repeat every {per} dispatches over {K} steps")
+
+    def span_ms_of(per):
+        t = rows[-K * per:]
+        return (t[-1][1] - t[0][0]) / 1e6 / K
+
+    cands = [q * j for j in range(-(-run["launches_per_step"] // q), 4 * run["launches_per_step"] // q + 2)
+             if K * q * j <= len(rows) and
+             all(names[-1 - i] == names[-1 - i - q * j] for i in range(q * j * (K - 1)))]
+    if not cands:
+        raise SystemExit(f"the trace does not repeat with a period of {q} dispatches over {K} steps")
+    per = min(cands, key=lambda p: abs(span_ms_of(p) - run["ms_per_step"]))
     timed = rows[-K * per:]
     span_ms = (timed[-1][1] - timed[0][0]) / 1e6 / K
     groups = {}

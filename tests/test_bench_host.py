@@ -1,5 +1,6 @@
-"""Host-side pieces of bench.py: the counter summary's scaling and the rule
-that a stored traffic figure is reported only for unchanged kernel sources."""
+"""Host-side pieces of bench.py: the counter summary's scaling, the step
+period of a kernel trace, and the rule that a stored traffic figure is
+reported only for unchanged kernel sources."""
 
 import csv
 import json
@@ -57,3 +58,32 @@ def test_stored_traffic_needs_unchanged_sources(tmp_path, monkeypatch):
     assert bench.stored_traffic("a")["traffic_bytes_per_step"] == 7
     assert bench.stored_traffic("b") is None
     assert bench.stored_traffic("missing") is None
+
+
+def test_step_trace_period_with_identical_layers_and_two_launch_calls(tmp_path):
+    """A step of 4 identical layers whose GEMM call launches two kernels:
+    the layer's period (3 dispatches) repeats too, so the step's 12
+    dispatches are found from the step time the run measured."""
+    layer = [("skinny_kernel<1>", 10), ("skinny_split_finish<0>", 5), ("reduce_kernel<0>", 3)]
+    K, layers, gap = 3, 4, 2
+    rows, t = [], 0
+    for name, dur in [("setup_kernel", 7)] * 2:
+        rows.append((t, t + dur, name)); t += dur + gap
+    for _ in range(K + 2):                       # warm-up passes, then the K timed steps
+        for _ in range(layers):
+            for name, dur in layer:
+                rows.append((t, t + dur, name)); t += dur + gap
+    step_ns = layers * sum(d + gap for _, d in layer)
+    with open(tmp_path / "trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Workgroup_Size_X"])
+        for a, b, name in rows:
+            w.writerow([f"void tpk::{name}(args)", a, b, 256, 256])
+    run = {"workload": "x", "ms_per_step": step_ns / 1e6, "steps": K, "steps_in_trace": K + 2,
+           "gemm_launches_per_step": layers, "launches_per_step": 2 * layers,
+           "gemm_algorithmic_bytes_per_step": 1000, "gemm_flops_per_step": 2000}
+    (tmp_path / "run.log").write_text(json.dumps(run) + "\n")
+    bench.summarize_step_trace(str(tmp_path / "trace.csv"), str(tmp_path / "run.log"), str(tmp_path / "out.txt"))
+    text = (tmp_path / "out.txt").read_text()
+    assert f"{layers * len(layer)} dispatches per step" in text
+    assert f"GEMM dispatches per step: {2 * layers}" in text
