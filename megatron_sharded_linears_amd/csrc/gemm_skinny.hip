@@ -718,7 +718,11 @@ struct SkinnyEntry {
     TP_SK(MT, 4, 1, 4, 0), TP_SK(MT, 8, 1, 4, 0), TP_SK(MT, 4, 4, 2, 0), TP_SK(MT, 8, 4, 2, 0),         \
     TP_SK(MT, 4, 4, 4, 0), TP_SK(MT, 4, 2, 8, 0), TP_SK(MT, 4, 1, 4, 1)
 
-const SkinnyEntry kSkinnyTable[] = {TP_SK_MT1, TP_SK_MTN(2), TP_SK_MTN(4)};
+// (and variants whose k-steps cover the Llama-8B shards' K = 256, 896 and
+// 1792 exactly, so that no wave loads X and W only to multiply zeros)
+const SkinnyEntry kSkinnyTable[] = {TP_SK_MT1, TP_SK_MTN(2), TP_SK_MTN(4), TP_SK(4, 2, 1, 4, 1),
+                                    TP_SK(1, 7, 1, 8, 0), TP_SK(1, 7, 1, 8, 1), TP_SK(4, 7, 1, 4, 0),
+                                    TP_SK(4, 7, 1, 4, 1)};
 #undef TP_SK_MT1
 #undef TP_SK_MTN
 #undef TP_SK
@@ -844,20 +848,26 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64
         // groups; otherwise cover K in one workgroup.
         static const Rule few_tiles[] = {{1 << 30, 8, 1, 4, 0}};
         static const Rule rules[] = {
-            {512, 4, 1, 4, 1}, {1024, 8, 1, 4, 1}, {2048, 8, 1, 8, 0}, {4096, 16, 1, 8, 0},
+            {512, 4, 1, 4, 1}, {1024, 8, 1, 4, 1}, {1792, 7, 1, 8, 0}, {2048, 8, 1, 8, 0}, {4096, 16, 1, 8, 0},
             {5120, 20, 1, 8, 0},
         };
         if ((N + 15) / 16 < 128 && K >= 2048 && first_fit(few_tiles, 1, &chosen)) return chosen;
-        if (first_fit(rules, 5, &chosen)) return chosen;
+        if (first_fit(rules, 6, &chosen)) return chosen;
     } else if (mt == 4) {
         // M in (32, 64]: measured winners at the Llama-8B t=16 shard shapes
         // (weights rotated past the last-level cache, K splits in two
         // launches; gate_up 1792 x 4096: 64-row tiles split 8 ways, 14.2 us;
-        // qkv 512 x 4096: 16-row tiles split 8 ways with X staged, 8.2 us).
-        static const Rule rules_small_n[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 4, 1, 4, 0}};
-        static const Rule rules_mid_n[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 4, 4, 4, 0}};
-        static const Rule rules[] = {{512, 4, 1, 4, 1}, {1024, 8, 1, 4, 0}, {1 << 30, 8, 4, 2, 0}};
-        if (first_fit(N <= 1024 ? rules_small_n : N <= 2048 ? rules_mid_n : rules, 3, &chosen)) return chosen;
+        // qkv 512 x 4096: 16-row tiles split 8 ways with X staged, 8.2 us;
+        // o 4096 x 256 and down 4096 x 896 with the sum over 16 ranks: 4
+        // waves whose k-steps cover K exactly, X loaded per wave, 6.4 and
+        // 10.2 us against 7.6 and 11.1 for the next-larger coverage).
+        static const Rule rules_small_n[] = {{256, 2, 1, 4, 1}, {512, 4, 1, 4, 1}, {896, 7, 1, 4, 1},
+                                             {1024, 8, 1, 4, 0}, {1 << 30, 4, 1, 4, 0}};
+        static const Rule rules_mid_n[] = {{256, 2, 1, 4, 1}, {512, 4, 1, 4, 1}, {896, 7, 1, 4, 1},
+                                           {1024, 8, 1, 4, 0}, {1 << 30, 4, 4, 4, 0}};
+        static const Rule rules[] = {{256, 2, 1, 4, 1}, {512, 4, 1, 4, 1}, {896, 7, 1, 4, 1},
+                                     {1024, 8, 1, 4, 0}, {1 << 30, 8, 4, 2, 0}};
+        if (first_fit(N <= 1024 ? rules_small_n : N <= 2048 ? rules_mid_n : rules, 5, &chosen)) return chosen;
     }
     SkinnyPlan best{mt, 8, 4, 2, 0, 0, 0};   // splits = 0: nothing fits (the caller reports it)
     double best_cost = -1.0;

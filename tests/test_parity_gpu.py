@@ -87,7 +87,8 @@ SKINNY_VARIANTS = (
                         (8, 4, 4), (4, 4, 4), (8, 1, 8), (8, 2, 8), (4, 2, 8), (4, 1, 16), (8, 1, 16),
                         (16, 1, 8), (16, 2, 4), (16, 4, 2)]]
     + [v + (1,) for v in [(4, 1, 4), (8, 1, 4), (8, 1, 8), (4, 1, 16), (8, 1, 16), (16, 1, 8), (4, 2, 8)]]
-    + [(20, 1, 8, 0)])
+    + [(20, 1, 8, 0), (7, 1, 8, 0), (7, 1, 8, 1)]
+    + [(2, 1, 4, 1), (7, 1, 4, 0), (7, 1, 4, 1)])     # these three are built for 33-64 tokens only
 
 
 @pytest.mark.parametrize("ks,nn,nk,xd", SKINNY_VARIANTS)
