@@ -138,18 +138,19 @@ bool decode_plan(int64_t M, int64_t N, int64_t K, const tpk::Workspace& ws, cons
     return true;
 }
 
-// With the norm prologue (M <= 16, whole rows of X in LDS): the plan or false.
+// With the norm folded into the decode kernel (M <= 16 or 33..64 tokens, X
+// staged in LDS by 16-row tile groups): the plan or false.
 bool decode_norm_plan(int64_t M, int64_t N, int64_t K, const tpk::Workspace& ws, const tp_linear_plan& over,
                       tpk::SkinnyPlan* out) {
-    if (M > 16) return false;
+    if ((M > 16 && M <= 32) || M > 64) return false;
     tpk::SkinnyPlan p = tpk::plan_skinny_norm(M, N, K, ws.partial_floats, ws.num_counters);
     if (!plan_is_auto_decode(over)) {
-        tpk::SkinnyPlan f{1, over.decode_ksteps, over.decode_nwn, over.decode_nwk, over.decode_x_direct ? 1 : 0, 1, 1};
+        tpk::SkinnyPlan f{M <= 16 ? 1 : 4, over.decode_ksteps, over.decode_nwn, over.decode_nwk,
+                          over.decode_x_direct ? 1 : 0, 1, 1};
         f.ntiles = (N + 16LL * f.nwn - 1) / (16LL * f.nwn);
         const int64_t gk = 32LL * f.ksteps * f.nwk;
         f.splits = (int)((K + gk - 1) / gk);
-        if (tpk::skinny_norm_plan_fits(f, M, K) &&
-            split_fits(f, M, N, ws, (int64_t)f.splits * f.ntiles * 16))
+        if (tpk::skinny_norm_plan_fits(f, M, K) && split_fits(f, M, N, ws, tpk::skinny_norm_ss_floats(f, M)))
             p = f;
     }
     if (p.splits < 1) return false;

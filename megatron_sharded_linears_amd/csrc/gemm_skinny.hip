@@ -210,20 +210,23 @@ __device__ __forceinline__ void finish4(const GemmArgs& a, int64_t m, int64_t n,
     else store_out4(a, m, n, v);
 }
 
-// NORM = 1 (one 16-token tile, X staged in LDS): the RMSNorm of X's rows
+// NORM = 1 (X staged in LDS, one 16-row group): the RMSNorm of X's rows
 // with gamma already folded into W (tp_fold_norm_weight): y = r_m (x_m .
 // w'_n), r_m = 1 / sqrt(sum_k x_mk^2 / K + eps). sum_k x_mk^2 is the diagonal
-// of X X^T, one more MFMA per k-step on the X fragments already in registers
-// (the matrix cores idle otherwise), so the norm adds no per-element work.
-// With K split across workgroups each publishes its share of the sums next
-// to its partial tile and the last to arrive adds them in split order.
+// of X X^T, one more MFMA per k-step and token tile on the X fragments
+// already in registers (the matrix cores idle otherwise), so the norm adds no
+// per-element work. With K split across workgroups each publishes its share
+// of the sums next to its partial tile and the last to arrive (one token
+// tile), or the finish kernel of a two-launch split (up to 4 token tiles),
+// adds them in split order.
 template <int MT, int KSTEPS, int NWN, int NWK, int XD, int EPI, int NORM = 0>
 __global__ void __launch_bounds__(64 * NWN * NWK)
 skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restrict__ ws,
               unsigned* __restrict__ counters) {
     using C = SkinnyCfg<MT, KSTEPS, NWN, NWK, XD>;
-    static_assert(!NORM || (!XD && MT == 1 && NWN == 1 && NWK > 1), "the norm needs one tile of X in LDS");
-    __shared__ float s_gram[NORM ? NWK * 4 * 64 : 1];    // NORM: each wave's X X^T fragment
+    static_assert(!NORM || (!XD && (MT == 1 || (MT == 4 && NWN <= 4)) && (MT == 4 || NWN == 1) && NWK > 1),
+                  "the norm needs X staged in LDS (and one row group for one token tile)");
+    __shared__ float s_gram[NORM ? NWK * MT * 4 * 64 : 1];    // NORM: each wave's X X^T fragments
     extern __shared__ __align__(16) unsigned char smem[];
     bf16_t* xs = reinterpret_cast<bf16_t*>(smem);                       // [xrows][kXStride]
     float* red = reinterpret_cast<float*>(smem + (XD ? 0 : (size_t)xrows * C::kXStride * 2));
@@ -351,8 +354,15 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     // accumulators when NWK == 1, else the in-order sum of the NWK waves'
     // accumulators read back from LDS.
     float fin[C::kOwn][4];
-    float rnorm = 1.0f;      // NORM: this lane's row scale, from the first tile (X is the same for all)
-    float ss_part = 0.f;     // NORM with K split: this workgroup's share of the row's sum of squares
+    // NORM: the row scale of each owned token tile's row lane % 16, from the
+    // first tile (X is the same for all), and with K split this workgroup's
+    // share of the row's sum of squares
+    float rnorm[C::kOwn], ss_part[C::kOwn];
+#pragma unroll
+    for (int o = 0; o < C::kOwn; ++o) {
+        rnorm[o] = 1.0f;
+        ss_part[o] = 0.f;
+    }
     for (;;) {
         const int64_t n_out = tile * C::kRows + wn * 16 + 4 * (lane >> 4);   // first of this lane's 4 rows
 
@@ -368,7 +378,9 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
         // 4. MFMAs: acc[mt] holds D[n = 4*(lane/16) + i][m = 16*mt + lane%16].
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        f32x4_t gram = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t gram[NORM ? MT : 1];
+#pragma unroll
+        for (int mt = 0; mt < (NORM ? MT : 1); ++mt) gram[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             const bool k_ok = k_wave + 32 * s < K;
@@ -384,9 +396,9 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
                                    : make_uint4(0u, 0u, 0u, 0u);
                 }
                 acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, xv), acc[mt], 0, 0, 0);
-                if (NORM && first_tile)
-                    gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv),
-                                                                   __builtin_bit_cast(bf16x8_t, xv), gram, 0, 0, 0);
+                if (NORM && first_tile && wn == 0)       // one row group is enough
+                    gram[NORM ? mt : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, xv), __builtin_bit_cast(bf16x8_t, xv), gram[NORM ? mt : 0], 0, 0, 0);
             }
         }
 
@@ -397,9 +409,12 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     red[(((wk * NWN + wn) * MT + mt) * 4 + i) * 64 + lane] = acc[mt][i];
-            if (NORM && first_tile) {
+            // (the first row group computes X X^T and writes it)
+            if (NORM && first_tile && wn == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s_gram[(wk * 4 + i) * 64 + lane] = gram[i];
+                for (int mt = 0; mt < (NORM ? MT : 1); ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s_gram[((wk * MT + mt) * 4 + i) * 64 + lane] = gram[mt][i];
             }
             lds_barrier();
 #pragma unroll
@@ -416,23 +431,28 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
                 }
             }
             if constexpr (NORM) {
-                // X X^T[m][m] sits in lane m + 16 (m / 4), element m % 4, of
-                // each wave's fragment; summed over the waves in order.
+                // X X^T[m][m] of token tile mt sits in lane m + 16 (m / 4),
+                // element m % 4, of each wave's fragment for that tile;
+                // summed over the waves in order.
                 if (first_tile) {
                     const int m = lane & 15;
                     const int src = (m % 4) * 64 + m + 16 * (m / 4);
-                    float ss = s_gram[src];
 #pragma unroll
-                    for (int w = 1; w < NWK; ++w) ss += s_gram[w * 4 * 64 + src];
-                    ss_part = ss;
-                    rnorm = 1.0f / sqrtf(ss / (float)K + a.eps);
+                    for (int o = 0; o < C::kOwn; ++o) {
+                        const int mt = wk + NWK * o < MT ? wk + NWK * o : 0;   // unowned: any in-bounds tile
+                        float ss = s_gram[mt * 4 * 64 + src];
+#pragma unroll
+                        for (int w = 1; w < NWK; ++w) ss += s_gram[(w * MT + mt) * 4 * 64 + src];
+                        ss_part[o] = ss;
+                        rnorm[o] = 1.0f / sqrtf(ss / (float)K + a.eps);
+                    }
                 }
-                // with K split, the row's sum is complete only in step 7
+                // with K split, the row's sum is complete only after the split
                 if (splits == 1) {
 #pragma unroll
                     for (int o = 0; o < C::kOwn; ++o)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) fin[o][i] *= rnorm;
+                        for (int i = 0; i < 4; ++i) fin[o][i] *= rnorm[o];
                 }
             }
             lds_barrier();     // the buffer is rewritten for the next tile
@@ -478,6 +498,17 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     // counters == nullptr: the partial tiles are summed by skinny_split_finish
     // in a second launch (the kernel boundary publishes them): plain stores.
     if (counters == nullptr) {
+        // NORM: this split's share of each row's sum of squares, [split][M]
+        // after the partial tiles (every row tile computes the same; tile 0
+        // publishes it)
+        if (NORM && tile == 0 && wn == 0 && lane < 16) {
+#pragma unroll
+            for (int o = 0; o < C::kOwn; ++o) {
+                const int mt = wk + NWK * o;
+                const int64_t m = 16 * mt + lane;
+                if (mt < MT && m < M) ws[(int64_t)splits * M * N + (int64_t)split * M + m] = ss_part[o];
+            }
+        }
 #pragma unroll
         for (int o = 0; o < C::kOwn; ++o) {
             const int mt = wk + NWK * o;
@@ -519,7 +550,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     // partial tiles ([split][tile][16] floats), published the same way
     float* const ws_ss = ws + (int64_t)splits * M * N;
     if (NORM && wk == 0 && lane < 16)
-        __hip_atomic_store(ws_ss + ((int64_t)split * ntiles + tile) * 16 + lane, ss_part, __ATOMIC_RELAXED,
+        __hip_atomic_store(ws_ss + ((int64_t)split * ntiles + tile) * 16 + lane, ss_part[0], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -534,7 +565,9 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     //    loads of up to 8 splits are issued back to back before any is used,
     //    so they cost one memory round trip, not one each.
     if constexpr (NORM) {
-        // the row's sum of squares over the splits, in split order
+        // the row's sum of squares over the splits, in split order (one
+        // token tile: the host finishes every split of 64 tokens in a second
+        // launch, skinny_split_launches)
         float ss = 0.f;
         for (int sp0 = 0; sp0 < splits; sp0 += 8) {
             float t[8];
@@ -548,7 +581,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
             for (int j = 0; j < 8; ++j)
                 if (sp0 + j < splits) ss += t[j];
         }
-        rnorm = 1.0f / sqrtf(ss / (float)K + a.eps);
+        rnorm[0] = 1.0f / sqrtf(ss / (float)K + a.eps);
     }
 #pragma unroll
     for (int o = 0; o < C::kOwn; ++o) {
@@ -589,7 +622,7 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
             }
             if constexpr (NORM) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] *= rnorm;
+                for (int i = 0; i < 4; ++i) v[i] *= rnorm[0];
             }
             finish4<EPI>(a, m, n_out, v, lane, peers);
         }
@@ -619,12 +652,19 @@ skinny_split_finish(GemmArgs a, int splits, const float* __restrict__ ws) {
     constexpr int kRound = 8;
     constexpr int kCols = EPI == EPI_SWIGLU ? 2 : 1;
     const bool vec = n + 3 < N && N % 4 == 0;
+    const bool norm = a.norm != 0;
+    // with the norm, the splits' shares of the row's sum of squares ([split][M]
+    // after the partial tiles) load in the same rounds
+    const float* pss = ws + (int64_t)splits * M * N + m;
     float acc[kCols][4] = {};
+    float ss = 0.f;
     for (int sp0 = 0; sp0 < splits; sp0 += kRound) {
         float4 t[kRound][kCols];
+        float tss[kRound];
 #pragma unroll
         for (int j = 0; j < kRound; ++j) {
             const int sp = sp0 + j < splits ? sp0 + j : splits - 1;   // clamped: in bounds, unused past splits
+            tss[j] = norm ? pss[(int64_t)sp * M] : 0.f;
 #pragma unroll
             for (int c = 0; c < kCols; ++c) {
                 const int64_t n0 = n + 8 * c;
@@ -647,8 +687,18 @@ skinny_split_finish(GemmArgs a, int splits, const float* __restrict__ ws) {
                     acc[c][2] += t[j][c].z;
                     acc[c][3] += t[j][c].w;
                 }
+                ss += tss[j];
             }
         }
+    }
+    if (norm) {
+        // the row's sum of squares, summed in split order: the scale applies
+        // before the epilogue
+        const float r = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+#pragma unroll
+        for (int c = 0; c < kCols; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[c][i] *= r;
     }
     float v[4] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
     if constexpr (EPI == EPI_SWIGLU) {
@@ -677,10 +727,11 @@ typedef void (*SkinnyFn)(GemmArgs, int, int64_t, int, float*, unsigned*);
 typedef int (*SkinnyLdsFn)(int);
 
 // The norm-prologue kernel of a shape, for the column linears (EPI_STORE,
-// EPI_SWIGLU), built only for one 16-token tile, X in LDS, one row group.
+// EPI_SWIGLU), built for one 16-token tile with one row group, or four
+// token tiles, X in LDS.
 template <int MT, int KS, int NN, int NK, int XD, int EPI>
 constexpr SkinnyFn skinny_norm_fn() {
-    if constexpr (MT == 1 && XD == 0 && NN == 1 && NK > 1 && EPI <= EPI_SWIGLU)
+    if constexpr (((MT == 1 && NN == 1) || MT == 4) && XD == 0 && NK > 1 && EPI <= EPI_SWIGLU)
         return skinny_kernel<MT, KS, NN, NK, XD, EPI, 1>;
     else
         return nullptr;
@@ -774,20 +825,42 @@ bool skinny_plan_fits(const SkinnyPlan& p, int64_t M) {
 // With the norm: one 16-token tile whose whole rows (K <= the variant's K
 // coverage) sit in LDS.
 bool skinny_norm_plan_fits(const SkinnyPlan& p, int64_t M, int64_t K) {
+    (void)K;
     const int idx = find_skinny(p);
     if (idx < 0) return false;
     const SkinnyEntry& e = kSkinnyTable[idx];
-    if (e.fn_norm[0] == nullptr || M > 16) return false;
+    if (e.fn_norm[0] == nullptr || M > 16 * e.mt) return false;
     // dynamic LDS (staged rows, reduction buffer) + static (X X^T fragments, flags)
-    return e.lds(xrows_for(e, M)) + e.nwk * 4 * 64 * 4 + 512 <= 160 * 1024;
+    return e.lds(xrows_for(e, M)) + e.nwk * e.mt * 4 * 64 * 4 + 512 <= 160 * 1024;
+}
+
+// Workspace floats a norm plan needs beyond the split partials: the splits'
+// shares of the rows' sums of squares ([split][tile][16] for the single-
+// launch exchange of one token tile, [split][M] beside the partials of a
+// two-launch split).
+int64_t skinny_norm_ss_floats(const SkinnyPlan& p, int64_t M) {
+    if (p.splits <= 1) return 0;
+    return p.mt == 4 ? (int64_t)p.splits * M : (int64_t)p.splits * p.ntiles * 16;
 }
 
 // Decode shape for a linear with the norm: as plan_skinny for M <= 16 (K
 // split 4 ways over 1024-wide groups for weights with few 16-row tiles,
-// otherwise the variant covering K in one workgroup with the least waste),
-// or splits = 0 when none fits (the caller then normalises separately).
+// otherwise the variant covering K in one workgroup with the least waste);
+// for M in (32, 64] the plain linear's plan when it stages X in LDS (its K
+// splits run in two launches); splits = 0 when none fits (the caller then
+// normalises separately).
 SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64_t ws_counters) {
     struct Rule { int64_t kmax; int ks, nwn, nwk; };
+    if (M > 32) {
+        if (M <= 64) {
+            const SkinnyPlan p = plan_skinny(M, N, K, ws_floats, ws_counters);
+            const bool ws_ok =
+                p.splits == 1 || skinny_workspace_floats(p, M, N) + skinny_norm_ss_floats(p, M) <= ws_floats;
+            if (p.splits >= 1 && ws_ok && skinny_norm_plan_fits(p, M, K)) return p;
+        }
+        SkinnyPlan none{4, 0, 0, 0, 0, 0, 0};
+        return none;
+    }
     if ((N + 15) / 16 < 128 && K >= 2048) {
         SkinnyPlan p{1, 8, 1, 4, 0, 1, 1};
         const int idx = find_skinny(p);
@@ -972,15 +1045,16 @@ hipError_t launch_skinny(const GemmArgs& a, const SkinnyPlan& p, const Workspace
     return hipGetLastError();
 }
 
-// A K split at more than 32 tokens (not with the norm, whose split shares of
-// the sums of squares need the single-launch exchange) runs as two launches:
-// with 64 tokens a split tile holds 4-16 KB of partials per split per 16
-// rows, which the one last-arriving workgroup of the single-launch exchange
-// would read alone after an arrival round trip (Llama t = 16 qkv, 16 rows x
-// 8 splits: 10.0 us in one launch, 8.7 in two; gate_up, 64 rows x 8 splits:
-// 16.8 in one, 14.4 in two).
+// A K split at more than 32 tokens runs as two launches (with the norm, the
+// splits' shares of the sums of squares go beside the partials and the
+// second launch applies the scale): with 64 tokens a split tile holds 4-16 KB
+// of partials per split per 16 rows, which the one last-arriving workgroup
+// of the single-launch exchange would read alone after an arrival round trip
+// (Llama t = 16 qkv, 16 rows x 8 splits: 10.0 us in one launch, 8.7 in two;
+// gate_up, 64 rows x 8 splits: 16.8 in one, 14.4 in two).
 int skinny_split_launches(const SkinnyPlan& p, const GemmArgs& a) {
-    return (p.splits > 1 && p.mt == 4 && a.norm == 0) ? 2 : 1;
+    (void)a;
+    return (p.splits > 1 && p.mt == 4) ? 2 : 1;
 }
 
 }  // namespace tpk

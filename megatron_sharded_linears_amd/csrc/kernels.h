@@ -120,6 +120,7 @@ bool skinny_plan_fits(const SkinnyPlan& p, int64_t M);   // LDS need for M token
 // for M tokens; normalise separately) and its fit test.
 SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64_t ws_counters);
 bool skinny_norm_plan_fits(const SkinnyPlan& p, int64_t M, int64_t K);
+int64_t skinny_norm_ss_floats(const SkinnyPlan& p, int64_t M);
 int64_t skinny_workspace_floats(const SkinnyPlan& p, int64_t M, int64_t N);
 // Launches a decode-sized linear takes under plan p (2: the split partial
 // tiles, then their sum and the epilogue).

@@ -70,7 +70,7 @@ def test_row_linear_reduce_add(M, K, N, t, rank, pdt):
 # (M, K, N): qkv rank shares of the decode workloads and the tiny one, a
 # ragged token count, one token, and the two-launch paths (M = 64, M = 200)
 NORM_LINEAR_CASES = [(16, 4096, 768), (16, 4096, 512), (16, 256, 192), (5, 2048, 300), (1, 1024, 64),
-                     (64, 4096, 512), (200, 512, 384)]
+                     (64, 4096, 512), (40, 4096, 520), (64, 600, 96), (24, 1024, 64), (200, 512, 384)]
 
 
 def normed(h, g):
@@ -129,7 +129,7 @@ def test_rmsnorm_column_linear(M, K, N):
 
 
 @pytest.mark.parametrize("M,K,Is", [(16, 4096, 1792), (16, 4096, 896), (16, 256, 512), (7, 1024, 200),
-                                    (64, 4096, 896), (130, 256, 512)])
+                                    (64, 4096, 896), (40, 2048, 300), (130, 256, 512)])
 def test_rmsnorm_column_linear_swiglu(M, K, Is):
     key = (SEED, 3, M, K, Is)
     h = I.normal_bf16(key + (0,), (M, K), 3.0)
