@@ -73,6 +73,13 @@ NORM_LINEAR_CASES = [(16, 4096, 768), (16, 4096, 512), (16, 256, 192), (5, 2048,
                      (64, 4096, 512), (40, 4096, 520), (64, 600, 96), (24, 1024, 64), (200, 512, 384)]
 
 
+def row_scaled(h):
+    """Rows at scales 2^-3 .. 2^3 (exact in bf16): RMSNorm cancels them, so a
+    row normalised with another row's sum of squares is off by up to 64x."""
+    sc = torch.tensor([2.0 ** ((m % 7) - 3) for m in range(h.shape[0])], dtype=torch.float32)
+    return (h.float() * sc[:, None]).to(torch.bfloat16)
+
+
 def normed(h, g):
     """The oracle's RMSNorm of h rounded to bf16 (the normalised row as stored)."""
     return oracle.round_bf16(oracle.rms_norm(f64(h), f64(g), EPS))
@@ -108,7 +115,7 @@ def test_fold_norm_weight_bitexact(N, K):
 @pytest.mark.parametrize("M,K,N", NORM_LINEAR_CASES)
 def test_rmsnorm_column_linear(M, K, N):
     key = (SEED, 2, M, K, N)
-    h = I.normal_bf16(key + (0,), (M, K), 3.0)
+    h = row_scaled(I.normal_bf16(key + (0,), (M, K), 3.0))
     g = gamma(key + (1,), K)
     w = I.normal_bf16(key + (2,), (N, K), 0.02)
     b = I.normal_bf16(key + (3,), (N,))
@@ -132,7 +139,7 @@ def test_rmsnorm_column_linear(M, K, N):
                                     (64, 4096, 896), (40, 2048, 300), (130, 256, 512)])
 def test_rmsnorm_column_linear_swiglu(M, K, Is):
     key = (SEED, 3, M, K, Is)
-    h = I.normal_bf16(key + (0,), (M, K), 3.0)
+    h = row_scaled(I.normal_bf16(key + (0,), (M, K), 3.0))
     g = gamma(key + (1,), K)
     w = I.normal_bf16(key + (2,), (2 * Is, K), 0.02)
     act = empty((M, Is))
@@ -144,23 +151,26 @@ def test_rmsnorm_column_linear_swiglu(M, K, Is):
     assert_close(f64(act), oracle.swiglu(gate, up), f"rmsnorm_column_linear_swiglu {(M, K, Is)}")
 
 
-def test_norm_linear_scale_invariance_and_per_row():
+@pytest.mark.parametrize("M,K,N,row", [(16, 4096, 768, 3), (40, 4096, 520, 37), (64, 4096, 512, 63),
+                                       (64, 4096, 512, 17)])
+def test_norm_linear_scale_invariance_and_per_row(M, K, N, row):
     """RMSNorm is invariant to scaling a row (up to eps) and rows are
-    independent: scaling row 3 by 2^k (exact in bf16) leaves every output
-    row's value within the bar, and the other rows' bits unchanged."""
-    M, K, N = 16, 4096, 768
-    key = (SEED, 4)
+    independent: scaling one row by 2^3 (exact in bf16) leaves every output
+    row's value within the bar, and the other rows' bits unchanged (16 tokens:
+    one launch; 40 and 64: K split over two launches, the scaled row in the
+    ragged last token tile or an inner one)."""
+    key = (SEED, 4, M, K, N)
     h = I.normal_bf16(key + (0,), (M, K))
     g = gamma(key + (1,), K)
     w = folded(I.normal_bf16(key + (2,), (N, K), 0.02), g)
     y1, y2 = empty((M, N)), empty((M, N))
     lib.tp_rmsnorm_column_linear(dev(h), EPS, w, y1)
     h2 = h.clone()
-    h2[3] = h2[3] * 8.0
+    h2[row] = h2[row] * 8.0
     lib.tp_rmsnorm_column_linear(dev(h2), EPS, w, y2)
-    other = [m for m in range(M) if m != 3]
+    other = [m for m in range(M) if m != row]
     assert np.array_equal(bits(y1[other]), bits(y2[other]))
-    assert_close(f64(y2[3:4]), f64(y1[3:4]), "scaled row")
+    assert_close(f64(y2[row:row + 1]), f64(y1[row:row + 1]), "scaled row")
 
 
 def test_fused_norm_step_matches_oracle_chain():
