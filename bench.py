@@ -1003,6 +1003,12 @@ def main():
                           "launches_per_step": len(ops)}), flush=True)
         return
 
+    t_start = time.perf_counter()
+
+    def note(what):
+        # progress on stderr (the JSON line alone goes to stdout)
+        print(f"bench: {what} done at {time.perf_counter() - t_start:.0f} s", file=sys.stderr, flush=True)
+
     # --- eager: the same calls issued one by one from Python
     for _ in range(args.warmup):
         run_ops(ops)
@@ -1014,6 +1020,7 @@ def main():
     b.record()
     torch.cuda.synchronize()
     ms_eager = a.elapsed_time(b) / args.steps
+    note("eager step")
 
     # --- timed region: exactly K steps, each the replay of the captured step
     ms_step, wall_s = time_step(torch, ops, args.steps, args.warmup)
@@ -1021,6 +1028,7 @@ def main():
         ms_step = ms_eager
     # the same step through the other set of calls, for comparison
     ms_alt, _ = time_step(torch, alt_ops, args.steps, args.warmup)
+    note("graph step and the other calls' step")
     # partial sums stored in bf16 or fp32, the reduce fused into the linear or
     # a call of its own (decode; at prefill sizes the reduce is always separate)
     partials = {}
@@ -1032,6 +1040,7 @@ def main():
             d["reduce_fused" if fr else "reduce_separate"] = round(ms_p, 4)
         partials["fp32" if p32 else "bf16"] = d
     partials["default"] = "bf16"
+    note("partial storage steps")
     # and with the residual stream and the RMSNorms of a real layer
     norm_ops = build_norm_ops(R, lib)
     ms_norm, _ = time_step(torch, norm_ops, args.steps, args.warmup)
@@ -1042,6 +1051,7 @@ def main():
     fused_norm = ms_norm_fused is not None and ms_norm_fused < ms_norm
     layer_ops = build_layer_ops(R, lib, fused_norm) if R.attn else None
     ms_layer = time_step(torch, layer_ops, args.steps, args.warmup)[0] if layer_ops else None
+    note("norm and layer steps")
 
     # --- per kernel: each op's launches of one step, captured and replayed K times
     per_op = {}
@@ -1057,6 +1067,7 @@ def main():
         if name in GEMM_SHAPES:
             Mv, Nv, Kv = GEMM_SHAPES[name](R)
             per_op[name]["vendor_mm_us"] = round(vendor_mm_us(torch, Mv, Nv, Kv, args.steps), 3)
+        note(f"per-op {name}")
 
     attn = None
     if layer_ops:
@@ -1068,6 +1079,7 @@ def main():
     us_norm, _ = time_rotated(torch, norm_ops, "reduce_norm", args.steps)
 
     copy = measure_copy(torch, lib, I, w)
+    note("attention, norm call and copy")
 
     # the step's sums over ranks alone, back to back (the separate-call
     # path's 2 per layer): launched one by one from Python, and replayed as
@@ -1172,6 +1184,7 @@ def main():
     }
 
     if not args.no_cpu:
+        note("GPU measurements")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

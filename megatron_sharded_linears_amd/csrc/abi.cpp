@@ -134,6 +134,8 @@ bool decode_plan(int64_t M, int64_t N, int64_t K, const tpk::Workspace& ws, cons
         f.splits = (int)((K + gk - 1) / gk);
         if (tpk::skinny_variant_exists(f) && tpk::skinny_plan_fits(f, M) && split_fits(f, M, N, ws, 0)) p = f;
     }
+    // per-wave X loads read W and X through buffer resources (32-bit offsets)
+    if (p.xd && (N * K * 2 > tpk::kMaxBufferBytes || M * K * 2 > tpk::kMaxBufferBytes)) return false;
     *out = p;
     return true;
 }

@@ -41,6 +41,20 @@ __device__ __forceinline__ float4 ld_nt16f(const void* p) {
     return __builtin_bit_cast(float4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
 }
 
+// Buffer resources: a scalar base and extent in bytes (a read past the
+// extent returns zeros), addressed by 32-bit lane offsets plus an immediate
+// or scalar offset, so an operand read this way stays below kMaxBufferBytes
+// (kernels.h). Word 3 of an untyped buffer resource: 32-bit data format, no
+// swizzle, no index stride.
+constexpr int kRawBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_source(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, kRawBufferWord3);
+}
+__device__ __forceinline__ uint4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
     return __uint_as_float(b << 16);
 }

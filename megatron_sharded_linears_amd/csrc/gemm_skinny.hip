@@ -309,21 +309,28 @@ skinny_kernel(GemmArgs a, int splits, int64_t ntiles, int xrows, float* __restri
     };
     // XD: each step's weight and X fragments are issued together, so the
     //     MFMA of step s waits only for loads 0..s (the load counter is in
-    //     order) and X never holds back the weight stream.
+    //     order) and X never holds back the weight stream. They are read
+    //     through buffer resources: one 32-bit offset per lane and row, the
+    //     k-steps as immediate offsets, no clamping (a k past K reads the
+    //     next row, or zeros past the extent, and meets a zeroed weight
+    //     fragment at the MFMA; token rows past M read zeros and feed outputs
+    //     that are never stored). Against 64-bit clamped addresses: Llama-8B
+    //     t = 16 (64 tokens) o + sum 8.15 -> 8.0 us, down + sum 11.45 ->
+    //     10.85; t = 8 o + sum 4.68 -> 4.58 (MI355X, timed alternately; the
+    //     LDS-staged variants ran slower this way and keep plain loads).
+    //     The host plans XD only for operands within kMaxBufferBytes.
     uint4 xd[XD ? KSTEPS : 1][XD ? MT : 1];
     if constexpr (XD) {
+        const __amdgpu_buffer_rsrc_t rs_w = buffer_source(W, (EPI == EPI_SWIGLU ? 2 * a.i_half : N) * K * 2);
+        const __amdgpu_buffer_rsrc_t rs_x = buffer_source(X, M * K * 2);
         const int64_t row = weight_row<EPI>(a, tile * C::kRows + wn * 16 + (lane & 15));
-        const bf16_t* wrow = W + (row >= 0 ? row : 0) * K;
+        const uint32_t w_off = (uint32_t)(((row >= 0 ? row : 0) * K + k_wave) * 2);
+        const uint32_t x_off = (uint32_t)(((int64_t)(lane & 15) * K + k_wave) * 2);
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            const int64_t k = k_wave + 32 * s;
-            wr[s] = *reinterpret_cast<const uint4*>(wrow + (k < K ? k : 0));
+            wr[s] = buffer_ld16(rs_w, w_off + 64 * s);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                // token rows past M feed outputs that are never stored
-                const int64_t m = 16 * mt + (lane & 15);
-                xd[s][mt] = *reinterpret_cast<const uint4*>(X + (m < M ? m : 0) * K + (k < K ? k : 0));
-            }
+            for (int mt = 0; mt < MT; ++mt) xd[s][mt] = buffer_ld16(rs_x, x_off + (uint32_t)(32 * mt * K) + 64 * s);
         }
     } else {
         load_w(tile, wr);

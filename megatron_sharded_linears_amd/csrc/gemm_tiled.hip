@@ -86,23 +86,17 @@ __device__ __forceinline__ int64_t tile_w_row(const GemmArgs& a, int64_t v) {
     return (v % BN) >= BN / 2 ? up_rows(a) + j : j;
 }
 
-// The DMA kernels read their sources through buffer resources: a scalar base
-// and extent (a read past the extent returns zeros), 32-bit lane offsets, and
-// the k-tile's byte offset in the scalar offset operand. Against
-// global_load_lds with 64-bit lane addresses this staged the same bytes 3-8%
-// faster per prefill linear (MI355X, the Llama-8B t = 2 and Qwen-32B t = 8
-// shard shapes, timed alternately). The launcher keeps both extents below
-// 4 GiB (kMaxBufferBytes).
-constexpr int kRawBufferWord3 = 0x00020000;   // resource word 3 of an untyped buffer (32-bit data format)
+// The DMA kernels read their sources through buffer resources (common.h):
+// 32-bit lane offsets, and the k-tile's byte offset in the scalar offset
+// operand. Against global_load_lds with 64-bit lane addresses this staged the
+// same bytes 3-8% faster per prefill linear (MI355X, the Llama-8B t = 2 and
+// Qwen-32B t = 8 shard shapes, timed alternately). The launcher keeps both
+// extents within kMaxBufferBytes.
 
 // Weight rows a launch reads: every row for a plain linear; gate rows
 // [0, i_half) and up rows [up_rows, up_rows + i_half) with SwiGLU.
 __host__ __device__ __forceinline__ int64_t w_rows_read(const GemmArgs& a) {
     return a.epi == EPI_SWIGLU ? (a.up_off != 0 ? a.up_off : a.i_half) + a.i_half : a.N;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_source(const void* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, kRawBufferWord3);
 }
 
 // SwiGLU of 4 gate values and their up values: y[m, j..j+3], bf16, with the
@@ -477,8 +471,8 @@ tiled_dma_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     // Per-lane DMA source rows (clamped into the matrix: rows past the end
     // only feed outputs that are never stored) and swizzled chunks, as byte
     // offsets into the weight's or X's buffer resource.
-    const __amdgpu_buffer_rsrc_t rs_w = dma_source(W, w_rows_read(a) * K * 2);
-    const __amdgpu_buffer_rsrc_t rs_x = dma_source(X, M * K * 2);
+    const __amdgpu_buffer_rsrc_t rs_w = buffer_source(W, w_rows_read(a) * K * 2);
+    const __amdgpu_buffer_rsrc_t rs_x = buffer_source(X, M * K * 2);
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // uniform: picks a resource
     uint32_t voff[C::kInstrPerWave];
     bool from_w[C::kInstrPerWave];
@@ -644,8 +638,8 @@ tiled_dma64_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     // that are never stored); lane l of an instruction fills LDS chunk l % 8
     // of row l / 8 with the global chunk that the swizzle puts there, read
     // at a byte offset into the weight's or X's buffer resource.
-    const __amdgpu_buffer_rsrc_t rs_w = dma_source(W, w_rows_read(a) * K * 2);
-    const __amdgpu_buffer_rsrc_t rs_x = dma_source(X, M * K * 2);
+    const __amdgpu_buffer_rsrc_t rs_w = buffer_source(W, w_rows_read(a) * K * 2);
+    const __amdgpu_buffer_rsrc_t rs_x = buffer_source(X, M * K * 2);
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // uniform: picks a resource
     uint32_t voff[C::kInstrPerWave];
     bool from_w[C::kInstrPerWave];
@@ -813,8 +807,7 @@ const TiledEntry kTiled[] = {
 #undef TP_DMA
 #undef TP_DMA64
 constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);
-constexpr int kRegVariant = 3;                      // register-staged: plain global loads, any K % 8
-constexpr int64_t kMaxBufferBytes = 0xFFFFFFFFLL;   // largest extent a buffer resource addresses
+constexpr int kRegVariant = 3;   // register-staged: plain global loads, any K % 8
 constexpr int kMaxDevices = 16;
 // Whether each kernel's dynamic-LDS limit is set, per device; setting it is
 // idempotent, so a race between host threads only repeats the call.

@@ -97,6 +97,12 @@ struct Workspace {
 };
 
 // Plan of a decode-sized (M <= 64) linear; describes how K is split.
+// Largest extent in bytes that a buffer resource addresses with 32-bit
+// offsets: the prefill DMA kernels and the decode kernel's per-wave loads
+// read through buffer resources, so their operands stay at or below it (the
+// launchers pick other kernels beyond).
+constexpr int64_t kMaxBufferBytes = 0xFFFFFFFFLL;
+
 struct SkinnyPlan {
     int mt;          // token tiles of 16
     int ksteps;      // 32-wide k steps per wave
