@@ -56,8 +56,10 @@ METRIC = "shard-GEMM TFLOP/s + reduce GB/s (% roofline), Llama-8B t=8 decode B=1
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=1000)
-    p.add_argument("--warmup", type=int, default=50)
+    # defaults: 1000 timed steps (50 warm-up) at decode sizes, 50 (5) at
+    # prefill sizes, so that every workload's run takes minutes
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="llama8b_t8_decode_m16")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of the captured step")
     p.add_argument("--separate", action="store_true",
@@ -946,6 +948,10 @@ def main():
     from megatron_sharded_linears_amd.workloads import BY_NAME
 
     w = BY_NAME[args.workload]
+    if args.steps is None:
+        args.steps = 1000 if w.tokens <= 64 else 50
+    if args.warmup is None:
+        args.warmup = 50 if w.tokens <= 64 else 5
     torch.cuda.set_device(0)
     R = Rank(w, lib, I, torch)
     torch.cuda.synchronize()
