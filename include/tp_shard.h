@@ -368,7 +368,11 @@ typedef enum {
  * [0, tp_prefill_tile_count()], is TP_ERR_RANGE. A plan this call cannot run
  * (the shape not built for its token count, an X chunk beyond LDS, split
  * partials beyond the workspace, a K multiple not met) is replaced by the
- * automatic choice; results then differ only in the fp32 summation order. */
+ * automatic choice; results then differ only in the fp32 summation order.
+ * Every tiled shape but 3, and the decode shapes with decode_x_direct = 1,
+ * address their operands with 32-bit byte offsets: a weight or activation of
+ * 4 GiB or more runs those tiles on shape 3 instead (same bits), and the
+ * per-wave decode plan is not used for it. */
 typedef struct {
     int32_t decode_ksteps, decode_nwn, decode_nwk, decode_x_direct;
     int32_t prefill_tile;
