@@ -166,6 +166,14 @@ __device__ __forceinline__ bool tile_interior(const GemmArgs& a, int64_t m0, int
     return n0 + BN <= a.N && out_ld(a) % 4 == 0 && a.bias == nullptr;
 }
 
+// 4 bf16 outputs with the non-temporal hint: a wave of tiles writes its whole
+// output in one burst at the end, which nothing in the launch reads back
+// (Llama-8B t = 2: o 38.9 -> 37.4 us, gate_up + SwiGLU 214.6 -> 211.5, qkv and
+// down ~1% faster; Qwen-32B t = 8 unchanged; timed alternately).
+__device__ __forceinline__ void store_bf16x4_nt(uint16_t* p, float a0, float a1, float a2, float a3) {
+    __builtin_nontemporal_store(u32x2_t{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)}, reinterpret_cast<u32x2_t*>(p));
+}
+
 template <int BN, int BM, int THREADS>
 __device__ __forceinline__ void store_block_row(const GemmArgs& a, const float* slab, int i, int tid, int64_t m0,
                                                 int64_t n0, int tile_n, bool interior) {
@@ -191,8 +199,7 @@ __device__ __forceinline__ void store_block_row(const GemmArgs& a, const float* 
                 const int64_t j = (int64_t)tile_n * kWN + i * 32 + 4 * (q & 7);
                 float o[4];
                 swiglu4(g[it], u[it], o);
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + (m0 + (q >> 3)) * ld + j) =
-                    make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                store_bf16x4_nt(reinterpret_cast<uint16_t*>(a.y) + (m0 + (q >> 3)) * ld + j, o[0], o[1], o[2], o[3]);
             }
         } else {
 #pragma unroll 1
@@ -227,8 +234,8 @@ __device__ __forceinline__ void store_block_row(const GemmArgs& a, const float* 
 #pragma unroll
             for (int it = 0; it < kIt; ++it) {
                 const int q = tid + it * THREADS;
-                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + (m0 + token(q)) * ld + col(q)) =
-                    make_uint2(pack_bf16x2(v[it].x, v[it].y), pack_bf16x2(v[it].z, v[it].w));
+                store_bf16x4_nt(reinterpret_cast<uint16_t*>(a.y) + (m0 + token(q)) * ld + col(q), v[it].x, v[it].y,
+                                v[it].z, v[it].w);
             }
         }
         return;
