@@ -362,8 +362,9 @@ typedef enum {
  * 128 x 64 on 4 waves and 14 = 64 x 64 on 2 waves, 64-wide k-tiles (tiles
  * for 64 tokens); 15 = 128 x 128 on 4 waves with two 64-wide stages (two
  * workgroups per CU); 16 = 192 x 256 on 8 waves (the last weight rows of a
- * product whose 256 x 256 tiles make between one and two waves); 3 =
- * register-staged 128 x 128 (any K % 8). A decode shape
+ * product whose 256 x 256 tiles make between one and two waves); 17 =
+ * 128 x 256 on 8 waves with three 64-wide stages; 3 = register-staged
+ * 128 x 128 (any K % 8). A decode shape
  * that is not built for any token count, or a prefill_tile outside
  * [0, tp_prefill_tile_count()], is TP_ERR_RANGE. A plan this call cannot run
  * (the shape not built for its token count, an X chunk beyond LDS, split

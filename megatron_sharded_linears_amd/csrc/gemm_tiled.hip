@@ -810,6 +810,7 @@ const TiledEntry kTiled[] = {
     TP_DMA64(64, 64, 6, 1),
     TP_DMA64(128, 128, 2, 2),
     TP_DMA64(192, 256, 2, 4),
+    TP_DMA64(128, 256, 3, 4),
 };
 #undef TP_DMA
 #undef TP_DMA64
@@ -915,11 +916,14 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant) {
     // register-staged kernel for any other K. With 64-wide k-tiles, 256 x 128
     // tiles that leave CUs idle give way to 192 x 128 tiles when those fill
     // at most one pass of the chip (Llama-8B t = 2 qkv: 192 tiles of
-    // 256 x 128 take 70 us, 256 of 192 x 128 take 62 us), and otherwise to
-    // 128 x 128 tiles on 4 waves with two 64-wide stages, small enough (64 KB
-    // of LDS, 134 VGPRs) for two workgroups per CU, whose barriers and loads
-    // then interleave (Llama-8B t = 2 down 132.8 -> 124.3 us, o 44.6 -> 42.7,
-    // timed alternately with the 8-wave 256 x 128 tiles).
+    // 256 x 128 take 70 us, 256 of 192 x 128 take 62 us); to 128 x 256 tiles
+    // (weight rows x tokens, three stages) when those fill 90-100% of one
+    // pass (Llama-8B t = 2 down 118.5 -> 109.4 us, o 39.5 -> 37.6, against
+    // the 128 x 128 tiles below; worse wherever they leave a pass part-full);
+    // and otherwise to 128 x 128 tiles on 4 waves with two 64-wide stages,
+    // small enough (64 KB of LDS, 134 VGPRs) for two workgroups per CU, whose
+    // barriers and loads then interleave (Llama-8B t = 2 down 132.8 -> 124.3
+    // us, o 44.6 -> 42.7, timed alternately with the 8-wave 256 x 128 tiles).
     auto tiles = [&](int bn, int bm) { return ((a.N + bn - 1) / bn) * ((a.M + bm - 1) / bm); };
     const int shape = tiles(256, 256) >= 192 ? 0 : tiles(256, 128) >= 192 ? 1 : 2;
     int best;
@@ -928,6 +932,7 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant) {
     else if (a.K <= 1024) best = 6;
     else if (a.K % 64 != 0) best = 4 + shape;
     else if (shape == 1 && tiles(256, 128) < kCus && tiles(192, 128) <= kCus) best = 11;
+    else if (shape == 1 && tiles(128, 256) <= kCus && tiles(128, 256) * 10 >= kCus * 9) best = 17;
     else if (shape == 1) best = 15;
     else best = 8 + shape;
     if (variant >= 0 && variant < kNumTiled && a.K % kTiled[variant].kmul == 0) return launch_variant(a, variant, 0, s);

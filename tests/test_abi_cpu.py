@@ -242,7 +242,7 @@ def test_linear_ex_validates_call_and_plan():
     assert f(ctypes.byref(_call(M=0)), S) == 0
     assert f(ctypes.byref(_call(M=0, epilogue=4)), S) == -5                  # unknown epilogue
     nt = C.tp_prefill_tile_count()
-    assert nt == lib.tp_prefill_tile_count() == 17
+    assert nt == lib.tp_prefill_tile_count() == 18
     assert f(ctypes.byref(_call(M=0, plan={"tile": nt})), S) == -6           # tile kernels 0 .. nt - 1
     assert f(ctypes.byref(_call(M=0, plan={"tile": nt - 1})), S) == 0
     assert f(ctypes.byref(_call(M=0, plan={"tile": 11})), S) == 0
