@@ -801,6 +801,9 @@ int linear_scratch_need(const tp_linear_call& c, int64_t* floats, int64_t* count
     if (c.norm != 0) return TP_ERR_SHAPE;
     const tpk::Workspace tuned{reinterpret_cast<float*>(16), tpk::kSkinnyWsFloats, reinterpret_cast<unsigned*>(16),
                                tpk::kSkinnyWsCounters};
+    // as launch_linear: an explicit tile, or the tiled kernel's win at this
+    // shape, runs the prefill kernel, which needs no scratch
+    if (c.plan.prefill_tile > 0 || (plan_is_auto_decode(c.plan) && tpk::tiled_wins_at_decode(a))) return TP_OK;
     const int64_t n_rows = c.epilogue == TP_EPI_SWIGLU ? 16 * ((c.N + 7) / 8) : c.N;
     tpk::SkinnyPlan p;
     if (!decode_plan(c.M, n_rows, c.K, tuned, c.plan, &p)) return TP_OK;

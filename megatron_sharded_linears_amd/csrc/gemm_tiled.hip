@@ -832,12 +832,15 @@ int tiled_variant_count() { return kNumTiled; }
 // sums fp32 partials across workgroups (LM head 8016 x 4096: 27.1 against
 // 40.2 us; 3584 x 4096: 24.8 against 27.0 us). With fewer rows or shorter K
 // the decode kernel wins (1792 x 4096: 17.3 against 24.5 us; 4096 x 896:
-// 7.2 against 9.5 us).
+// 7.2 against 9.5 us). At 17-32 tokens only weights of LM-head size do
+// (16032 x 4096 at 24 and 32 tokens: 30.7 and 30.9 against 49.5 and 54.6 us;
+// 3584 x 4096: 20.8 and 21.0 against 16.7 and 17.8), and at 16 tokens none
+// (16032 x 4096: 30.6 against 27.6 us).
 bool tiled_wins_at_decode(const GemmArgs& a) {
-    if (a.M <= 32 || a.K < 2048 || a.K % 64 != 0 || a.norm != 0) return false;
+    if (a.M <= 16 || a.K < 2048 || a.K % 64 != 0 || a.norm != 0) return false;
     if (a.epi != EPI_STORE && a.epi != EPI_SWIGLU) return false;
     const int64_t rows = a.epi == EPI_SWIGLU ? 2 * a.i_half : a.N;
-    return (rows + 63) / 64 >= 48;
+    return (rows + 63) / 64 >= (a.M <= 32 ? 128 : 48);
 }
 
 namespace {

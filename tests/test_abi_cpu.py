@@ -387,6 +387,7 @@ def test_noalloc_linear_validates_and_rejects_large_plans_before_any_hip_call():
     assert f(A, 16, 64, B, 32, NULL, ctypes.c_void_p(0x10000 + 256), S) == -2   # y inside x
     assert f(A, 0, 64, B, 32, NULL, Y, S) == 0
     X, W, Yb = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x3000000), ctypes.c_void_p(0x8000000)
-    # 64 tokens of a 4096 x 4096 weight: K split 8 ways, 8 x 64 x 4096 fp32
-    # partials (8 MiB) do not fit: rejected, nothing launched
-    assert f(X, 64, 4096, W, 4096, NULL, Yb, S) == -2
+    # 64 tokens of a 2816 x 4096 weight (44 tiles of 64 rows: the decode
+    # kernel): K split 8 ways, 8 x 64 x 2816 fp32 partials (5.8 MB) do not
+    # fit: rejected, nothing launched
+    assert f(X, 64, 4096, W, 2816, NULL, Yb, S) == -2

@@ -63,6 +63,8 @@ LIN_SHAPES = [
     (1, 7, 8), (5, 64, 40), (16, 100, 264), (16, 771, 1032), (17, 33, 72),
     (33, 200, 520), (64, 64, 4104), (64, 129, 136),
     (65, 70, 64), (130, 257, 200), (300, 128, 1032), (256, 384, 4096),
+    # 17-32 tokens on a weight of LM-head size: the 64 x 64 tiled kernel
+    (24, 8200, 2048), (32, 8192, 2112),
 ]
 
 
