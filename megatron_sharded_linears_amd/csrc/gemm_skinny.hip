@@ -906,7 +906,14 @@ SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K, int64_t ws_floats, 
 // workgroups, a quarter weight for X re-reads from L2) divided by how well the
 // grid fills the 256 CUs.
 SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64_t ws_counters) {
-    const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    // 17-32 tokens run the 64-token plans (rows past M masked), which beat
+    // the 32-token tiles' cost-model choice (24 tokens, weights rotated past
+    // the last-level cache: qkv 768 x 4096 10.7 -> 8.8 us, o 4096 x 512 with
+    // the sum over 8 ranks 7.35 -> 5.23, gate_up 1792 x 4096 11.4 -> 10.7),
+    // except on weights of more than 2048 rows with K in (1024, 2048]
+    // (down 4096 x 1792 with the sum: 11.3 against 12.5 us).
+    const bool tiles32 = M > 16 && M <= 32 && N > 2048 && K > 1024 && K <= 2048;
+    const int mt = M <= 16 ? 1 : (tiles32 ? 2 : 4);
     struct Rule { int64_t kmax; int ks, nwn, nwk, xd; };
     auto first_fit = [&](const Rule* rules, int n, SkinnyPlan* out) {
         for (int i = 0; i < n; ++i) {

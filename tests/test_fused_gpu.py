@@ -47,7 +47,7 @@ def fused_swiglu(x, w, i_s, plan=None):
 # (M, I_shard, K): Llama-8B t=8 decode (16, 1792, 4096) and t=16 (64, 896,
 # 4096), ragged tails, the tiled path (M > 64) with 256- and 128-row tiles
 SWIGLU_SHAPES = [(16, 1792, 4096), (64, 896, 4096), (1, 8, 64), (7, 904, 520), (33, 96, 1032),
-                 (65, 136, 200), (300, 520, 256), (256, 1024, 2048), (130, 64, 4104)]
+                 (65, 136, 200), (300, 520, 256), (256, 1024, 2048), (130, 64, 4104), (24, 896, 4096)]
 
 
 @pytest.mark.parametrize("M,Is,K", SWIGLU_SHAPES)
@@ -142,7 +142,7 @@ def fused_reduce(x, w, peers, rank, plan=None):
 
 # (M, N, K_shard): Llama-8B t=8 o and down, t=16 o; ragged; tiled (M > 64)
 REDUCE_SHAPES = [(16, 4096, 512), (16, 4096, 1792), (64, 4096, 256), (5, 100, 40), (33, 130, 264),
-                 (100, 256, 128), (300, 72, 520)]
+                 (100, 256, 128), (300, 72, 520), (24, 4096, 512), (32, 4096, 1792)]
 
 
 @pytest.mark.parametrize("M,N,K", REDUCE_SHAPES)

@@ -65,6 +65,9 @@ LIN_SHAPES = [
     (65, 70, 64), (130, 257, 200), (300, 128, 1032), (256, 384, 4096),
     # 17-32 tokens on a weight of LM-head size: the 64 x 64 tiled kernel
     (24, 8200, 2048), (32, 8192, 2112),
+    # 17-32 tokens on the decode kernel: the 64-token plans (K split in two
+    # launches), and the 32-token tiles for long rows with K in (1024, 2048]
+    (24, 768, 4096), (29, 1800, 4104), (32, 2100, 1792),
 ]
 
 
