@@ -262,12 +262,16 @@ int tp_reduce_add_rmsnorm(const void* const* partials, int t, int partial_dtype,
  *   y[m, n] = r_m sum_k h[m, k] w_folded[n, k],  r_m = 1 / sqrt(mean_k h[m, k]^2 + eps)
  * (= RMSNorm(h) gamma W^T up to the rounding of the folded weight), the
  * normalised rows never written. h: [M, K] bf16 (the residual stream, read
- * only); eps finite and >= 0 (TP_ERR_RANGE); K <= 32768. One launch when
- * M <= 16 (the decode kernel, K split across workgroups as the plain linear
- * would be, or whole rows of K <= 5120 in one): the sums of squares come
- * from the diagonal of h h^T on the matrix cores and r scales the outputs. Otherwise two: tp_add_rmsnorm's kernel (unit weights)
- * writes bf16(h r) into the workspace (M K 2 bytes of scratch must fit,
- * TP_ERR_SHAPE otherwise), then the plain linear reads it. y / act must not
+ * only); eps finite and >= 0 (TP_ERR_RANGE); K <= 32768. When M <= 64 and
+ * the decode kernel's plan stages X in LDS, the norm is folded into it: the
+ * sums of squares come from the diagonal of h h^T on the matrix cores and r
+ * scales the outputs (one launch at M <= 16, K split across workgroups as
+ * the plain linear would be or whole rows of K <= 5120 in one; at 17-64
+ * tokens one launch, or two when K is split: the partial tiles with each
+ * split's share of the sums of squares, then the sum that applies r).
+ * Otherwise two: tp_add_rmsnorm's kernel (unit weights) writes bf16(h r)
+ * into the workspace (M K 2 bytes of scratch must fit, TP_ERR_SHAPE
+ * otherwise), then the plain linear reads it. y / act must not
  * overlap h (TP_ERR_SHAPE). */
 int tp_fold_norm_weight(const void* w, int64_t N, int64_t K, const void* gamma, void* w_folded, void* stream);
 int tp_row_linear_reduce_add(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,

@@ -140,11 +140,11 @@ bool decode_plan(int64_t M, int64_t N, int64_t K, const tpk::Workspace& ws, cons
     return true;
 }
 
-// With the norm folded into the decode kernel (M <= 16 or 33..64 tokens, X
-// staged in LDS by 16-row tile groups): the plan or false.
+// With the norm folded into the decode kernel (M <= 64 tokens on 16- or
+// 64-token tiles, X staged in LDS by 16-row tile groups): the plan or false.
 bool decode_norm_plan(int64_t M, int64_t N, int64_t K, const tpk::Workspace& ws, const tp_linear_plan& over,
                       tpk::SkinnyPlan* out) {
-    if ((M > 16 && M <= 32) || M > 64) return false;
+    if (M > 64) return false;
     tpk::SkinnyPlan p = tpk::plan_skinny_norm(M, N, K, ws.partial_floats, ws.num_counters);
     if (!plan_is_auto_decode(over)) {
         tpk::SkinnyPlan f{M <= 16 ? 1 : 4, over.decode_ksteps, over.decode_nwn, over.decode_nwk,

@@ -853,12 +853,12 @@ int64_t skinny_norm_ss_floats(const SkinnyPlan& p, int64_t M) {
 // Decode shape for a linear with the norm: as plan_skinny for M <= 16 (K
 // split 4 ways over 1024-wide groups for weights with few 16-row tiles,
 // otherwise the variant covering K in one workgroup with the least waste);
-// for M in (32, 64] the plain linear's plan when it stages X in LDS (its K
-// splits run in two launches); splits = 0 when none fits (the caller then
-// normalises separately).
+// for M in (16, 64] the plain linear's plan when it uses 64-token tiles and
+// stages X in LDS (its K splits run in two launches); splits = 0 when none
+// fits (the caller then normalises separately).
 SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K, int64_t ws_floats, int64_t ws_counters) {
     struct Rule { int64_t kmax; int ks, nwn, nwk; };
-    if (M > 32) {
+    if (M > 16) {
         if (M <= 64) {
             const SkinnyPlan p = plan_skinny(M, N, K, ws_floats, ws_counters);
             const bool ws_ok =
@@ -900,8 +900,9 @@ SkinnyPlan plan_skinny_norm(int64_t M, int64_t N, int64_t K, int64_t ws_floats, 
 // between workgroups) with the variant whose K coverage fits K with the least
 // waste, except when the weight has too few 16-row tiles to fill the GPU,
 // where K is split 4 ways (an exchange costs a few serialized memory round
-// trips at the end of the kernel, worth it only then). M in (32, 64]: the
-// measured winners per K and N. Otherwise a cost model counts HBM bytes
+// trips at the end of the kernel, worth it only then). M in (16, 64]: the
+// measured winners per K and N for 64-token tiles (see below for the 32-token
+// exception). Otherwise a cost model counts HBM bytes
 // (the weight once, the fp32 partial round trip when K is split across
 // workgroups, a quarter weight for X re-reads from L2) divided by how well the
 // grid fills the 256 CUs.

@@ -72,7 +72,8 @@ def test_row_linear_reduce_add(M, K, N, t, rank, pdt):
 # 33-64 tokens with K <= 1024 (K within one workgroup: the norm in one launch)
 NORM_LINEAR_CASES = [(16, 4096, 768), (16, 4096, 512), (16, 256, 192), (5, 2048, 300), (1, 1024, 64),
                      (64, 4096, 512), (40, 4096, 520), (64, 600, 96), (24, 1024, 64), (200, 512, 384),
-                     (64, 1024, 192), (48, 1024, 256), (33, 960, 100)]
+                     (64, 1024, 192), (48, 1024, 256), (33, 960, 100), (24, 4096, 768), (30, 4096, 520),
+                     (17, 1024, 64)]
 
 
 def row_scaled(h):
@@ -139,7 +140,7 @@ def test_rmsnorm_column_linear(M, K, N):
 
 @pytest.mark.parametrize("M,K,Is", [(16, 4096, 1792), (16, 4096, 896), (16, 256, 512), (7, 1024, 200),
                                     (64, 4096, 896), (40, 2048, 300), (130, 256, 512), (64, 1024, 256),
-                                    (50, 1024, 120)])
+                                    (50, 1024, 120), (24, 4096, 896)])
 def test_rmsnorm_column_linear_swiglu(M, K, Is):
     key = (SEED, 3, M, K, Is)
     h = row_scaled(I.normal_bf16(key + (0,), (M, K), 3.0))
@@ -155,7 +156,7 @@ def test_rmsnorm_column_linear_swiglu(M, K, Is):
 
 
 @pytest.mark.parametrize("M,K,N,row", [(16, 4096, 768, 3), (40, 4096, 520, 37), (64, 4096, 512, 63),
-                                       (64, 4096, 512, 17), (64, 1024, 192, 50)])
+                                       (64, 4096, 512, 17), (64, 1024, 192, 50), (24, 4096, 768, 23)])
 def test_norm_linear_scale_invariance_and_per_row(M, K, N, row):
     """RMSNorm is invariant to scaling a row (up to eps) and rows are
     independent: scaling one row by 2^3 (exact in bf16) leaves every output
