@@ -17,15 +17,18 @@
 //     all of them (MI355X, against token-fastest order over whole columns:
 //     Qwen-32B t = 8 o_proj 76.6 -> 66.2 us, gate_up 290 -> 283 us).
 //   * Epilogue: accumulators go through LDS one block row at a time, then all
-//     threads write rows of Y in 16-byte runs (bias added there).
+//     threads write rows of Y in runs of 4 outputs (bias added there; interior
+//     tiles' bf16 outputs with the non-temporal hint).
 //   * SwiGLU epilogue: a tile's first BN/2 rows are gate rows and its last
 //     BN/2 the same up rows, i.e. the two wave rows' halves of the LDS slab,
 //     so a thread reads a gate run and its up run and writes 4 outputs.
 //
-// tiled_dma_kernel (K % 32 == 0): k-tiles of 32 land in LDS by direct
-// global -> LDS loads in a 4-stage ring (details below). tiled_reg_kernel
-// (any K % 8 == 0): k-tiles of 64 go global -> VGPR -> LDS, double buffered,
-// 128-byte rows XOR-swizzled by (row / 2) mod 8.
+// tiled_dma_kernel (K % 32 == 0) and tiled_dma64_kernel (K % 64 == 0):
+// k-tiles land in LDS by direct global -> LDS loads (buffer_load ... lds
+// through buffer resources) in rings of 2-4 stages (details below).
+// tiled_reg_kernel (any K % 8 == 0, and operands of 4 GiB or more): k-tiles
+// of 64 go global -> VGPR -> LDS, double buffered, 128-byte rows
+// XOR-swizzled by (row / 2) mod 8.
 #include <atomic>
 
 #include "common.h"
