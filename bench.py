@@ -960,9 +960,12 @@ def main():
     # The step: fused calls where they are one launch (SwiGLU always; the
     # reduce at decode sizes, where the linear's epilogue sums the partials).
     fused = not args.separate
-    fused_reduce = fused and w.tokens <= 64
+    # the sum over ranks fused into the row-parallel linear wherever the
+    # library fuses it: every decode size, and prefill sizes at t <= 2
+    fuse_sum = w.tokens <= 64 or w.t <= 2
+    fused_reduce = fused and fuse_sum
     ops = build_ops(R, lib, fused_swiglu=fused, fused_reduce=fused_reduce)
-    alt_ops = build_ops(R, lib, fused_swiglu=not fused, fused_reduce=(not fused) and w.tokens <= 64)
+    alt_ops = build_ops(R, lib, fused_swiglu=not fused, fused_reduce=(not fused) and fuse_sum)
     names = []
     for n, _, _ in ops:
         if n not in names:
@@ -1035,12 +1038,14 @@ def main():
     # the same step through the other set of calls, for comparison
     ms_alt, _ = time_step(torch, alt_ops, args.steps, args.warmup)
     note("graph step and the other calls' step")
-    # partial sums stored in bf16 or fp32, the reduce fused into the linear or
-    # a call of its own (decode; at prefill sizes the reduce is always separate)
+    # partial sums stored in bf16 or fp32, the sum over ranks through the
+    # fused call (tp_row_linear_reduce) or a call of its own (where the
+    # library fuses the sum: decode sizes, and bf16 partials at prefill
+    # sizes at t <= 2)
     partials = {}
     for p32 in (False, True):
         d = {}
-        for fr in ((True, False) if w.tokens <= 64 else (False,)):
+        for fr in ((True, False) if fuse_sum and (w.tokens <= 64 or not p32) else (False,)):
             ms_p = time_step(torch, build_ops(R, lib, fused_swiglu=fused, fused_reduce=fr, fp32_partials=p32),
                              args.steps, args.warmup)[0]
             d["reduce_fused" if fr else "reduce_separate"] = round(ms_p, 4)

@@ -223,6 +223,15 @@ int launch_reduce_linear(tpk::GemmArgs a, const void* const* partials, int parti
         a.epi = add ? (f32 ? tpk::EPI_REDUCE_ADD_F32 : tpk::EPI_REDUCE_ADD) : (f32 ? tpk::EPI_REDUCE_F32 : tpk::EPI_REDUCE);
         return hip_status(tpk::launch_skinny(a, p, ws, s));
     }
+    // prefill sizes, two ranks, bf16 partials, automatic plan: the sum over
+    // ranks in the 64-wide-k-tile kernel's epilogue (no staged partial, no
+    // second launch; the same bits)
+    if (a.M > kSkinnyMaxM && !add && !f32 && a.t <= tpk::kTiledReduceRanks && a.N % 4 == 0 && a.K % 64 == 0 &&
+        over.prefill_tile == 0 && plan_is_auto_decode(over) && a.N * a.K * 2 <= tpk::kMaxBufferBytes &&
+        a.M * a.K * 2 <= tpk::kMaxBufferBytes) {
+        a.epi = tpk::EPI_REDUCE;
+        return hip_status(tpk::launch_tiled(a, s, -1));
+    }
     const int64_t own_bytes = a.M * a.N * dtype_bytes(partial_dtype);
     if (add && (a.N % 8 != 0 || a.N > kMaxNormWidth)) return TP_ERR_SHAPE;
     void* own = a.y;                  // EPI_REDUCE with bf16 partials: staged in `out`, summed in place

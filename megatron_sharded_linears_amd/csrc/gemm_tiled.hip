@@ -177,7 +177,7 @@ __device__ __forceinline__ void store_bf16x4_nt(uint16_t* p, float a0, float a1,
     __builtin_nontemporal_store(u32x2_t{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)}, reinterpret_cast<u32x2_t*>(p));
 }
 
-template <int BN, int BM, int THREADS>
+template <int BN, int BM, int THREADS, int RED = 0>
 __device__ __forceinline__ void store_block_row(const GemmArgs& a, const float* slab, int i, int tid, int64_t m0,
                                                 int64_t n0, int tile_n, bool interior) {
     constexpr int kWN = BN / 2;
@@ -223,6 +223,54 @@ __device__ __forceinline__ void store_block_row(const GemmArgs& a, const float* 
     auto token = [&](int q) { return (q % (BM * 8)) >> 3; };
     auto slab_at = [&](int q) { return slab + ((q / (BM * 8)) * BM + token(q)) * kSlabStride + 4 * (q & 7); };
     auto col = [&](int q) { return n0 + (q / (BM * 8)) * kWN + i * 32 + 4 * (q & 7); };
+    if constexpr (RED) {
+        // The sum over the ranks (t <= kTiledReduceRanks, bf16 partials
+        // [M, N], N % 4 == 0): the rank's partial rounded to bf16 as a partial
+        // buffer holds it, the t ranks added in rank order in fp32, one
+        // rounding; the same bits as the GEMM into a buffer followed by the
+        // reducer. The other ranks' 4 values of every run of this block row
+        // are loaded before any is used (runs past the edge read the buffers'
+        // start and store nothing).
+        uint2 pv[kIt][kTiledReduceRanks];
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int q = tid + it * THREADS;
+            const int64_t m = m0 + token(q), n = col(q);
+            const int64_t off = (m < M && n < N) ? m * N + n : 0;
+#pragma unroll
+            for (int r = 0; r < kTiledReduceRanks; ++r)
+                if (r < a.t && r != a.rank)
+                    pv[it][r] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.peers[r]) + off);
+        }
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int q = tid + it * THREADS;
+            const int64_t m = m0 + token(q), n = col(q);
+            const float4 v = *reinterpret_cast<const float4*>(slab_at(q));
+            const float own[4] = {round_bf16(v.x), round_bf16(v.y), round_bf16(v.z), round_bf16(v.w)};
+            float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < kTiledReduceRanks; ++r) {
+                if (r < a.t) {
+                    float qv[4];
+                    if (r == a.rank) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) qv[e] = own[e];
+                    } else {
+                        qv[0] = bf16_to_f32(pv[it][r].x & 0xFFFFu);
+                        qv[1] = bf16_to_f32(pv[it][r].x >> 16);
+                        qv[2] = bf16_to_f32(pv[it][r].y & 0xFFFFu);
+                        qv[3] = bf16_to_f32(pv[it][r].y >> 16);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = r == 0 ? qv[e] : o[e] + qv[e];
+                }
+            }
+            if (m < M && n < N)
+                store_bf16x4_nt(reinterpret_cast<uint16_t*>(a.y) + m * N + n, o[0], o[1], o[2], o[3]);
+        }
+        return;
+    }
     if (interior) {
         float4 v[kIt];
 #pragma unroll
@@ -258,7 +306,7 @@ __device__ __forceinline__ void store_block_row(const GemmArgs& a, const float* 
 
 // The whole epilogue: block rows one at a time through the slab at `lds`
 // (the stage ring is free by then).
-template <int BN, int BM, int THREADS, int BLKN, int BLKM, int WM_ROWS, typename Acc>
+template <int BN, int BM, int THREADS, int BLKN, int BLKM, int WM_ROWS, int RED = 0, typename Acc>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, unsigned char* lds, Acc& acc, int tid, int wn,
                                               int wm, int64_t m0, int64_t n0, int tile_n) {
     float* slab = reinterpret_cast<float*>(lds);
@@ -279,7 +327,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, unsigned char* 
             }
         });
         lds_barrier();
-        store_block_row<BN, BM, THREADS>(a, slab, i, tid, m0, n0, tile_n, interior);
+        store_block_row<BN, BM, THREADS, RED>(a, slab, i, tid, m0, n0, tile_n, interior);
         lds_barrier();
     }
 }
@@ -618,7 +666,7 @@ struct Dma64Cfg {
 
 __device__ __forceinline__ int swz128(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
-template <int BN, int BM, int NS, int WGM>
+template <int BN, int BM, int NS, int WGM, int RED = 0>
 __global__ void __launch_bounds__(128 * WGM, (Dma64Cfg<BN, BM, NS, WGM>::kLdsBytes <= 80 * 1024 ? 2 : 1))
 tiled_dma64_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     using C = Dma64Cfg<BN, BM, NS, WGM>;
@@ -777,7 +825,7 @@ tiled_dma64_kernel(GemmArgs a, int tiles_n, int tiles_m) {
     wait_vmcnt<0>();
     __syncthreads();
 
-    tile_epilogue<BN, BM, C::kThreadsWG, C::kBlkN, C::kBlkM, C::kWM>(a, lds8, acc, tid, wn, wm, m0, n0, tile_n);
+    tile_epilogue<BN, BM, C::kThreadsWG, C::kBlkN, C::kBlkM, C::kWM, RED>(a, lds8, acc, tid, wn, wm, m0, n0, tile_n);
 }
 
 typedef void (*TiledFn)(GemmArgs, int, int);
@@ -788,18 +836,20 @@ struct TiledEntry {
     int lds;
     int threads;
     bool buffer;       // sources read through buffer resources (extents < 4 GiB)
+    TiledFn fn_red;    // the same tile with the sum over ranks as its epilogue, or null
 };
 
 #define TP_DMA(BN, BM, NS, WGM) \
-    {BN, BM, 32, tiled_dma_kernel<BN, BM, NS, WGM>, DmaCfg<BN, BM, NS, WGM>::kLdsBytes, DmaCfg<BN, BM, NS, WGM>::kThreadsWG, true}
+    {BN, BM, 32, tiled_dma_kernel<BN, BM, NS, WGM>, DmaCfg<BN, BM, NS, WGM>::kLdsBytes, DmaCfg<BN, BM, NS, WGM>::kThreadsWG, \
+     true, nullptr}
 #define TP_DMA64(BN, BM, NS, WGM) \
     {BN, BM, 64, tiled_dma64_kernel<BN, BM, NS, WGM>, Dma64Cfg<BN, BM, NS, WGM>::kLdsBytes, \
-     Dma64Cfg<BN, BM, NS, WGM>::kThreadsWG, true}
+     Dma64Cfg<BN, BM, NS, WGM>::kThreadsWG, true, tiled_dma64_kernel<BN, BM, NS, WGM, 1>}
 const TiledEntry kTiled[] = {
     TP_DMA(256, 256, 4, 2),
     TP_DMA(256, 128, 4, 2),
     TP_DMA(128, 128, 4, 2),
-    {128, 128, 8, tiled_reg_kernel<128, 128>, TileCfg<128, 128>::kLdsBytes, kThreads, false},
+    {128, 128, 8, tiled_reg_kernel<128, 128>, TileCfg<128, 128>::kLdsBytes, kThreads, false, nullptr},
     TP_DMA(256, 256, 4, 4),
     TP_DMA(256, 128, 4, 4),
     TP_DMA(128, 128, 4, 4),
@@ -822,7 +872,7 @@ constexpr int kRegVariant = 3;   // register-staged: plain global loads, any K %
 constexpr int kMaxDevices = 16;
 // Whether each kernel's dynamic-LDS limit is set, per device; setting it is
 // idempotent, so a race between host threads only repeats the call.
-std::atomic<bool> g_tiled_attr[kMaxDevices][kNumTiled] = {};
+std::atomic<bool> g_tiled_attr[kMaxDevices][2][kNumTiled] = {};   // [device][reduce epilogue][variant]
 
 }  // namespace
 
@@ -852,14 +902,17 @@ namespace {
 // X's and Y's rows).
 hipError_t launch_variant(const GemmArgs& a, int v, int64_t m0, hipStream_t s) {
     const TiledEntry& e = kTiled[v];
+    const int red = epi_is_reduce(a.epi) ? 1 : 0;
+    const TiledFn fn = red ? e.fn_red : e.fn;
+    if (fn == nullptr) return hipErrorInvalidValue;     // no reduce epilogue on this shape (the host avoids it)
     int dev = 0;
     hipError_t he = hipGetDevice(&dev);
     if (he != hipSuccess) return he;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    if (!g_tiled_attr[dev][v].load(std::memory_order_acquire)) {
-        he = hipFuncSetAttribute(reinterpret_cast<const void*>(e.fn), hipFuncAttributeMaxDynamicSharedMemorySize, e.lds);
+    if (!g_tiled_attr[dev][red][v].load(std::memory_order_acquire)) {
+        he = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, e.lds);
         if (he != hipSuccess) return he;
-        g_tiled_attr[dev][v].store(true, std::memory_order_release);
+        g_tiled_attr[dev][red][v].store(true, std::memory_order_release);
     }
     GemmArgs b = a;
     const bool swiglu = a.epi == EPI_SWIGLU;
@@ -875,12 +928,12 @@ hipError_t launch_variant(const GemmArgs& a, int v, int64_t m0, hipStream_t s) {
     // offsets: a weight or X of 4 GiB or more takes the register-staged
     // kernel (same MFMA, same K order, so the same bits).
     if (e.buffer && (w_rows_read(b) * b.K * 2 > kMaxBufferBytes || b.M * b.K * 2 > kMaxBufferBytes))
-        return launch_variant(a, kRegVariant, m0, s);
+        return red ? hipErrorInvalidValue : launch_variant(a, kRegVariant, m0, s);
     const int tn = (int)((b.N + e.bn - 1) / e.bn);
     const int tm = (int)((b.M + e.bm - 1) / e.bm);
     const int ntiles = tn * tm;
     const int grid = ((ntiles + kXcds - 1) / kXcds) * kXcds;
-    hipLaunchKernelGGL(e.fn, dim3(grid), dim3(e.threads), e.lds, s, b, tn, tm);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(e.threads), e.lds, s, b, tn, tm);
     return hipGetLastError();
 }
 
@@ -944,6 +997,9 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t s, int variant) {
     else if (shape == 1) best = 15;
     else best = 8 + shape;
     if (variant >= 0 && variant < kNumTiled && a.K % kTiled[variant].kmul == 0) return launch_variant(a, variant, 0, s);
+    // the sum over ranks indexes the other ranks' [M, N] buffers with the
+    // launch's own M and N: one launch over the whole product
+    if (epi_is_reduce(a.epi)) return launch_variant(a, best, 0, s);
     // Weight-row split: when 256 x 256 tiles make between one and two waves,
     // one whole wave of them takes the first weight rows and a second launch
     // of 192 x 256 tiles (0.75 of the work per tile, one exact wave where the

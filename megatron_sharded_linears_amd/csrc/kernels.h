@@ -55,6 +55,7 @@ constexpr bool epi_is_add(int e) { return e == EPI_REDUCE_ADD || e == EPI_REDUCE
 constexpr bool epi_peers_f32(int e) { return e == EPI_REDUCE_F32 || e == EPI_REDUCE_ADD_F32; }
 
 constexpr int kMaxFusedPeers = 16;   // t limit of the fused reduce epilogue
+constexpr int kTiledReduceRanks = 2;  // t limit of the sum over ranks in the prefill kernel's epilogue
 
 // Linear Y[M, N] = X[M, K] W[N, K]^T (+ bias[N]); out_dtype TP_BF16 / TP_F32.
 // With EPI_SWIGLU, N is the kernel's row space (groups of gate rows paired

@@ -161,7 +161,31 @@ def test_row_linear_reduce_same_bits_as_separate_calls(M, N, K, t):
     assert_close(f64(got), oracle.all_reduce_sum(ps), f"fused reduce {(M, N, K, t)}")
 
 
-@pytest.mark.parametrize("M,N,K,t", [(16, 4096, 192, 8), (64, 300, 72, 16), (90, 128, 200, 4), (1, 8, 8, 2)])
+# prefill sizes at one or two ranks, where the sum over ranks is the tiled
+# kernel's epilogue: Llama-3.1-8B t = 2 o and down at 2048 tokens, and ragged
+# token counts and widths over several tiles
+PREFILL_REDUCE_SHAPES = [(2048, 4096, 2048), (2048, 4096, 7168), (333, 1000, 256), (129, 4100, 512), (65, 264, 64)]
+
+
+@pytest.mark.parametrize("M,N,K", PREFILL_REDUCE_SHAPES)
+@pytest.mark.parametrize("t", [1, 2])
+def test_row_linear_reduce_prefill_same_bits_as_separate_calls(M, N, K, t):
+    x = I.device_normal_bf16((M, K), 1.0, SEED + 40 + M + K, DEV)
+    w = I.device_normal_bf16((N, K), 0.03, SEED + 41 + N + K, DEV)
+    peers = [I.device_normal_bf16((M, N), 0.5, SEED + 42 + i, DEV) for i in range(t)]
+    for rank in range(t):
+        got = fused_reduce(x, w, peers, rank)
+        assert np.array_equal(bits(got), bits(separate_reduce(x, w, peers, rank))), (M, N, K, t, rank)
+    # the oracle on sampled rows (first, last and a spread between)
+    rows = sorted(set(np.linspace(0, M - 1, min(M, 48)).astype(int).tolist()))
+    own = oracle.round_bf16(oracle.linear(f64(x[rows].cpu()), f64(w.cpu())))
+    ps = [f64(p[rows].cpu()) for p in peers]
+    ps[t - 1] = own
+    assert_close(f64(got[rows].cpu()), oracle.all_reduce_sum(ps), f"fused prefill reduce {(M, N, K, t)}")
+
+
+@pytest.mark.parametrize("M,N,K,t", [(16, 4096, 192, 8), (64, 300, 72, 16), (90, 128, 200, 4), (1, 8, 8, 2),
+                                     (300, 520, 192, 2), (129, 1000, 128, 1)])
 def test_row_linear_reduce_exact_integer(M, N, K, t):
     """Small integers everywhere, sized so that the own partial (|p| <= K)
     and the sum (|s| <= K + 8 (t - 1)) stay within 256, where every integer
