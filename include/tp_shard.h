@@ -202,8 +202,10 @@ int tp_column_linear_swiglu(const void* x, int64_t M, int64_t K, const void* w_g
  * [M, N] buffers of `partial_dtype` that must not overlap `out`
  * (TP_ERR_SHAPE). out: [M, N] bf16. Gives the same bits as
  * tp_row_linear_partial (partial_dtype) into partials[rank] followed by
- * tp_reduce_partials (bf16 out). M <= 64 with t <= 16 and N % 4 == 0 is one
- * launch (the sum is the linear's epilogue); otherwise the own partial is
+ * tp_reduce_partials (bf16 out). One launch, the sum being the linear's
+ * epilogue, when N % 4 == 0 and either M <= 64 with t <= 16, or M > 64 with
+ * t <= 2, TP_BF16 partials, K_shard % 64 == 0 and no forced plan (the prefill
+ * tile's store reads the peer's partial); otherwise the own partial is
  * staged (in `out` for TP_BF16, in the workspace for TP_F32: M N 4 bytes of
  * scratch, TP_ERR_SHAPE if short) and the reducer sums the t buffers. */
 int tp_row_linear_reduce(const void* x_shard, int64_t M, int64_t K_shard, const void* w_shard, int64_t N,
